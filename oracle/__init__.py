@@ -1,0 +1,207 @@
+"""CPU oracle for the ZeRO mixed-precision optimizer step -- TEST INFRASTRUCTURE.
+
+Only the tests, the smoke check and the benchmark's CPU-baseline leg may import
+this package.  The product path (``zero_mixed_precision_amd``) never imports,
+links or calls it, and it shares no code with the GPU library.
+
+The arithmetic lives in ``oracle.c`` (plain scalar C loops, fp32 per the
+memory table of "DeepSpeed complete guide" section 2); this module is the
+ctypes binding plus the step sequence of one ZeRO optimizer step:
+
+    accumulate (K > 1)  ->  overflow check  ->  Adam or skip  ->  scaler update
+
+("DeepSpeed complete guide" section 5.1: backward scales and accumulates,
+step() updates; section 4.2: dynamic loss scaling; "DeepSpeed" overview, core
+features: gradient accumulation and dynamic loss scaling).  The bucket packing
+oracle is in ``oracle.packing``.
+
+Parity pins: every function here is pinned by the ``-m "not gpu"`` tests in
+``tests/test_oracle_*.py``.  Hysteresis >= 2, ``consecutive_hysteresis``, the
+static scale and a non power-of-two floor are parity unpinned (no graded
+workload exercises them and the pages give only the keys' one-line meaning).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+CFLAGS = ["-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off",
+          "-fno-fast-math", "-fexcess-precision=standard", "-mno-fma"]
+
+
+def build(force: bool = True) -> str:
+    """Compile oracle.c with gcc into liboracle.so (plain scalar code)."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp"
+        subprocess.run(["gcc", *CFLAGS, "-o", tmp, _SRC, "-lm"], check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+class ZoScaler(ctypes.Structure):
+    """Mirror of ``zo_scaler`` in oracle.c."""
+    _fields_ = [
+        ("scale", ctypes.c_float),
+        ("min_scale", ctypes.c_float),
+        ("window", ctypes.c_int32),
+        ("good_steps", ctypes.c_int32),
+        ("hysteresis", ctypes.c_int32),
+        ("hyst_left", ctypes.c_int32),
+        ("dynamic", ctypes.c_int32),
+        ("consecutive_hysteresis", ctypes.c_int32),
+        ("applied", ctypes.c_int64),
+        ("iters", ctypes.c_int64),
+        ("skipped", ctypes.c_int64),
+    ]
+
+    def as_dict(self) -> dict:
+        return {name: getattr(self, name) for name, _ in self._fields_}
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build(force=True)
+        L = ctypes.CDLL(_LIB)
+        vp, i64, i32, f32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_float
+        L.zo_dec16.argtypes, L.zo_dec16.restype = [ctypes.c_uint16], f32
+        L.zo_enc16.argtypes, L.zo_enc16.restype = [f32], ctypes.c_uint16
+        L.zo_dec16_array.argtypes, L.zo_dec16_array.restype = [vp, vp, i64], None
+        L.zo_enc16_array.argtypes, L.zo_enc16_array.restype = [vp, vp, i64], None
+        L.zo_accumulate.argtypes, L.zo_accumulate.restype = [vp, vp, i64, i32], None
+        L.zo_any_nonfinite16.argtypes, L.zo_any_nonfinite16.restype = [vp, i64], i32
+        L.zo_any_nonfinite32.argtypes, L.zo_any_nonfinite32.restype = [vp, i64], i32
+        L.zo_adam_scalars.argtypes = [i64, f32, f32, f32, ctypes.POINTER(f32), ctypes.POINTER(f32)]
+        L.zo_adam_scalars.restype = None
+        L.zo_adam.argtypes = [vp, i32, i64, vp, vp, vp, vp, f32, i32, i64, f32, f32, f32, f32, f32]
+        L.zo_adam.restype = None
+        L.zo_scaler_init.argtypes = [ctypes.POINTER(ZoScaler), f32, f32, i32, i32, i32, i32]
+        L.zo_scaler_init.restype = None
+        L.zo_scaler_update.argtypes = [ctypes.POINTER(ZoScaler), i32]
+        L.zo_scaler_update.restype = None
+        L.zo_scaler_sizeof.argtypes, L.zo_scaler_sizeof.restype = [], i64
+        assert L.zo_scaler_sizeof() == ctypes.sizeof(ZoScaler)
+        _lib = L
+    return _lib
+
+
+def _ptr(a: np.ndarray) -> int:
+    assert a.flags["C_CONTIGUOUS"]
+    return a.ctypes.data
+
+
+# -- element codecs ----------------------------------------------------------
+
+def dec16(h: np.ndarray) -> np.ndarray:
+    """binary16 bit patterns (uint16) -> float32, from the format definition."""
+    h = np.ascontiguousarray(h, dtype=np.uint16)
+    out = np.empty(h.shape, np.float32)
+    lib().zo_dec16_array(_ptr(h), _ptr(out), h.size)
+    return out
+
+
+def enc16(x: np.ndarray) -> np.ndarray:
+    """float32 -> binary16 bit patterns (uint16), round to nearest even."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    out = np.empty(x.shape, np.uint16)
+    lib().zo_enc16_array(_ptr(x), _ptr(out), x.size)
+    return out
+
+
+# -- the four steps ------------------------------------------------------------
+
+def accumulate(acc: np.ndarray, g16: np.ndarray, overwrite: bool) -> None:
+    assert acc.dtype == np.float32 and g16.dtype == np.uint16 and acc.size == g16.size
+    lib().zo_accumulate(_ptr(acc), _ptr(g16), acc.size, int(bool(overwrite)))
+
+
+def any_nonfinite(grad: np.ndarray) -> bool:
+    if grad.dtype == np.uint16:
+        return bool(lib().zo_any_nonfinite16(_ptr(grad), grad.size))
+    assert grad.dtype == np.float32
+    return bool(lib().zo_any_nonfinite32(_ptr(grad), grad.size))
+
+
+def adam_scalars(t: int, lr: float, beta1: float, beta2: float) -> tuple[float, float]:
+    """(step_size, rbc2) of applied step t, as fp32 values."""
+    a, b = ctypes.c_float(), ctypes.c_float()
+    lib().zo_adam_scalars(int(t), lr, beta1, beta2, ctypes.byref(a), ctypes.byref(b))
+    return a.value, b.value
+
+
+def adam(grad, master, m, v, p16, *, scale, accum_steps, t, lr, beta1, beta2, eps,
+         weight_decay=0.0) -> None:
+    """One applied Adam step, in place on master/m/v/p16 (see oracle.c)."""
+    n = master.size
+    for a, dt in ((master, np.float32), (m, np.float32), (v, np.float32), (p16, np.uint16)):
+        assert a.dtype == dt and a.size == n and a.flags["C_CONTIGUOUS"]
+    assert grad.size == n and grad.dtype in (np.uint16, np.float32)
+    lib().zo_adam(_ptr(grad), int(grad.dtype == np.float32), n, _ptr(master), _ptr(m), _ptr(v),
+                  _ptr(p16), scale, int(accum_steps), int(t), lr, beta1, beta2, eps, weight_decay)
+
+
+class Scaler:
+    """Dynamic loss scaler state machine (oracle.c ``zo_scaler``)."""
+
+    def __init__(self, init_scale=2.0 ** 16, min_scale=1.0, window=1000, hysteresis=1,
+                 dynamic=True, consecutive_hysteresis=False):
+        self.s = ZoScaler()
+        lib().zo_scaler_init(ctypes.byref(self.s), init_scale, min_scale, int(window),
+                             int(hysteresis), int(bool(dynamic)), int(bool(consecutive_hysteresis)))
+
+    def update(self, overflow: bool) -> None:
+        lib().zo_scaler_update(ctypes.byref(self.s), int(bool(overflow)))
+
+    @property
+    def scale(self) -> float:
+        return self.s.scale
+
+    @property
+    def applied(self) -> int:
+        return self.s.applied
+
+    def as_dict(self) -> dict:
+        return self.s.as_dict()
+
+
+class State:
+    """The flat partition's model state (fp16 params, fp32 master/m/v) plus the scaler."""
+
+    def __init__(self, master, m, v, p16, scaler: Scaler):
+        self.master, self.m, self.v, self.p16, self.scaler = master, m, v, p16, scaler
+
+
+def step(state: State, grads, *, lr, beta1, beta2, eps, weight_decay=0.0) -> bool:
+    """One full ZeRO optimizer step of the oracle; returns the overflow flag.
+
+    ``grads`` is one uint16 array (K = 1: the fp16 gradient is consumed
+    directly) or a list of K uint16 micro-batch gradients (K > 1: summed into
+    an fp32 buffer in micro-batch order first).
+    """
+    if isinstance(grads, np.ndarray):
+        grads = [grads]
+    K = len(grads)
+    if K == 1:
+        grad = np.ascontiguousarray(grads[0], dtype=np.uint16)
+    else:
+        grad = np.empty(state.master.size, np.float32)
+        for k, g in enumerate(grads):
+            accumulate(grad, np.ascontiguousarray(g, dtype=np.uint16), overwrite=(k == 0))
+    overflow = any_nonfinite(grad)
+    if not overflow:
+        adam(grad, state.master, state.m, state.v, state.p16,
+             scale=state.scaler.scale, accum_steps=K, t=state.scaler.applied + 1,
+             lr=lr, beta1=beta1, beta2=beta2, eps=eps, weight_decay=weight_decay)
+    state.scaler.update(overflow)
+    return overflow
