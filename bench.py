@@ -1,0 +1,326 @@
+"""Benchmark of the ZeRO mixed-precision optimizer step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload zero2_7b]
+
+One step = the whole per-rank hot path over one synthetic batch: (K > 1:
+bucketed fp16 -> fp32 accumulation of every micro-batch, the last one with the
+fused inf/NaN check; K = 1: the inf/NaN check of the fp16 gradient), the gated
+fused Adam update with the fp16 copy, and the loss-scale update.  Inputs are
+resident in HBM before the timed region; gradients are drawn on the device
+(distinct buffers, reused cyclically when they do not all fit).
+
+Prints one JSON line.  ``value`` is parameters updated per second (Gparams/s)
+over the timed steps; ``roofline`` is the Adam kernel's algorithmic HBM
+bandwidth (28 B/element with an fp16 gradient, 30 with the fp32 buffer) over
+its average duration, timed with HIP events on the launch stream, against
+the 8 TB/s HBM3E peak; ``traffic`` comes from the committed rocprofv3 counter
+summary when it was taken on the current kernel source.  ``cpu_baseline`` times
+the CPU oracle on a bounded slice of the same workload.
+
+    python bench.py --mode copy    # plain-copy and step-shaped data-movement references
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0
+METRIC = "Gparams/s per Adam step + achieved HBM GB/s (% of MI355X peak)"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "adam_traffic_zero2_7b.json")
+KERNEL_SRC = os.path.join(ROOT, "zero_mixed_precision_amd", "csrc", "dszero.hip")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+
+
+def load_traffic(workload: str):
+    """Per-launch HBM bytes of the Adam kernel from the committed counter summary,
+    or None if it is missing or was taken on another kernel source."""
+    try:
+        rec = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_sha256_16") != kernel_source_hash() or rec.get("workload") != workload:
+        return None
+    return rec.get("traffic_bytes_per_launch")
+
+
+# ----------------------------------------------------------------------------
+# GPU leg
+# ----------------------------------------------------------------------------
+
+def gpu_run(args):
+    import numpy as np
+    import torch
+
+    import synth
+    from synth.workloads import BETA1, BETA2, EPS, LR, MASTER_SIGMA, WD, WORKLOADS, ragged_numels
+    from zero_mixed_precision_amd import _lib, FlatLayout
+
+    w = WORKLOADS[args.workload]
+    n, K = w.psi, w.K
+    dev = torch.device("cuda:0")
+    props = torch.cuda.get_device_properties(dev)
+    log(f"device: {props.name} CUs={props.multi_processor_count} mem={props.total_memory / 2**30:.0f} GiB")
+    stream = torch.cuda.current_stream()
+    tabs = synth.DeviceTables(torch, dev)
+
+    master = torch.empty(n, dtype=torch.float32, device=dev)
+    synth.device_fill_master32(torch, tabs, master, w.master_key(), MASTER_SIGMA)
+    m = torch.zeros(n, dtype=torch.float32, device=dev)
+    v = torch.zeros(n, dtype=torch.float32, device=dev)
+    p16 = torch.empty(n, dtype=torch.int16, device=dev)
+    synth.device_fill_grad16(torch, tabs, p16, w.p16_key(), synth.GradSpec(0.02, 1.0))
+    acc = torch.empty(n, dtype=torch.float32, device=dev) if K > 1 else None
+    st = torch.zeros(64, dtype=torch.uint8, device=dev)
+    _lib.ds_state_init(st, w.init_scale, w.min_scale, w.window, w.hysteresis, 0, 1)
+    if w.ragged:
+        buckets = [(b.start, b.size) for b in FlatLayout(ragged_numels()).buckets]
+    else:
+        buckets = [(0, n)]
+
+    # resident gradient buffers: one per (step, micro-batch) if they fit, else cycled
+    total_mb = (args.steps + args.warmup) * K
+    free = torch.cuda.mem_get_info(dev)[0]
+    fit = max(1, int((free - (4 << 30)) // (2 * n)))
+    nbuf = max(1, min(total_mb, fit, args.max_grad_buffers))
+    grads = []
+    for b in range(nbuf):
+        g = torch.empty(n, dtype=torch.int16, device=dev)
+        s, k = divmod(b, K)
+        synth.device_fill_grad16(torch, tabs, g, w.grad_key(s + 1, k), w.grad_spec)
+        grads.append(g)
+    torch.cuda.synchronize()
+    log(f"workload {w.name}: psi={n} K={K} grad buffers={nbuf} (of {total_mb} micro-batches)")
+
+    hp = (LR, BETA1, BETA2, EPS, WD)
+    ev = []
+
+    def one_step(i, timed):
+        base = i * K
+        if K == 1:
+            g = grads[base % nbuf]
+            _lib.ds_check_overflow(st, g, _lib.DS_FP16, n, stream)
+            gptr, dt = g, _lib.DS_FP16
+        else:
+            for k in range(K):
+                g = grads[(base + k) % nbuf]
+                for start, size in buckets:
+                    _lib.ds_accumulate(acc.data_ptr() + 4 * start, g.data_ptr() + 2 * start, size,
+                                       k == 0, st if k == K - 1 else None, stream)
+            gptr, dt = acc, _lib.DS_FP32
+        if timed:
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+        _lib.ds_adam_step(st, master, m, v, p16, gptr, dt, n, *hp, K, stream)
+        if timed:
+            b.record(stream)
+            ev.append((a, b))
+        _lib.ds_update_loss_scale(st, stream)
+
+    for i in range(args.warmup):
+        one_step(i, False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.warmup, args.warmup + args.steps):
+        one_step(i, True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    sc = _lib.ds_state_read(st, stream)
+    adam_ms = [a.elapsed_time(b) for a, b in ev]
+    adam_avg_s = sum(adam_ms) / len(adam_ms) / 1e3
+    bytes_per_elem = 28 if K == 1 else 30
+    achieved = bytes_per_elem * n / adam_avg_s / 1e9
+    step_bytes = (2 + 28) if K == 1 else (6 + 10 * (K - 1) + 30)
+    traffic = load_traffic(w.name)
+    out = {
+        "metric": METRIC,
+        "value": round(n * args.steps / wall / 1e9, 3),
+        "unit": "Gparams/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": w.name,
+            "psi": n,
+            "micro_batches": K,
+            "grad": "fp16 N(0,%g) x %g" % (w.sigma, w.mult) + (" heavy tail" if w.heavy_tail else ""),
+            "state": "fp32 master/m/v, fp16 params",
+            "adam": {"lr": LR, "betas": [BETA1, BETA2], "eps": EPS, "weight_decay": WD},
+            "parallelism": "one GPU's ZeRO partition",
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "adam_kernel",
+            "achieved": round(achieved, 1),
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / PEAK_HBM_GBS, 4),
+            "traffic": traffic,
+            "alg_bytes_per_launch": bytes_per_elem * n,
+            "avg_launch_ms": round(adam_avg_s * 1e3, 4),
+        },
+        "step_hbm_gbs": round(step_bytes * n * args.steps / wall / 1e9, 1),
+        "scaler_after": {"scale": sc.scale, "applied_steps": sc.step, "skipped": sc.skipped},
+    }
+    del grads, master, m, v, p16, acc
+    torch.cuda.empty_cache()
+    return out
+
+
+# ----------------------------------------------------------------------------
+# CPU baseline: the oracle on a bounded slice of the same workload
+# ----------------------------------------------------------------------------
+
+def cpu_baseline(workload: str, min_seconds: float, slice_elems: int):
+    from concurrent.futures import ThreadPoolExecutor
+
+    import numpy as np
+
+    import oracle
+    import synth
+    from synth.workloads import BETA1, BETA2, EPS, LR, MASTER_SIGMA, WD, WORKLOADS
+
+    w = WORKLOADS[workload]
+    n = min(slice_elems, w.psi)
+    threads = max(1, min(16, len(os.sched_getaffinity(0))))
+    idx = np.arange(n)
+    master = synth.host_master32(w.master_key(), idx, MASTER_SIGMA)
+    m = np.zeros(n, np.float32)
+    v = np.zeros(n, np.float32)
+    p16 = np.zeros(n, np.uint16)
+    grads = [synth.host_grad16(w.grad_key(s + 1), idx, w.grad_spec) for s in range(2)]
+    sc = oracle.Scaler(w.init_scale, w.min_scale, w.window, w.hysteresis)
+    cuts = np.linspace(0, n, threads + 1).astype(np.int64)
+    sl = [slice(int(a), int(b)) for a, b in zip(cuts[:-1], cuts[1:])]
+    pool = ThreadPoolExecutor(threads)
+
+    def step(g):
+        flags = list(pool.map(lambda s: oracle.any_nonfinite(g[s]), sl))
+        ov = any(flags)
+        if not ov:
+            t = sc.applied + 1
+
+            def upd(s):
+                oracle.adam(g[s], master[s], m[s], v[s], p16[s], scale=sc.scale, accum_steps=1, t=t,
+                            lr=LR, beta1=BETA1, beta2=BETA2, eps=EPS, weight_decay=WD)
+            list(pool.map(upd, sl))
+        sc.update(ov)
+
+    steps = 0
+    t0 = time.perf_counter()
+    while True:
+        step(grads[steps % 2])
+        steps += 1
+        if time.perf_counter() - t0 >= min_seconds:
+            break
+    el = time.perf_counter() - t0
+    pool.shutdown()
+    return {
+        "value": round(n * steps / el / 1e9, 4),
+        "unit": "Gparams/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"{n}-element slice of {workload} (K=1 steps: check + Adam + scaler update), "
+                  f"{steps} steps in {el:.1f} s on {threads} threads",
+    }
+
+
+# ----------------------------------------------------------------------------
+# data-movement references
+# ----------------------------------------------------------------------------
+
+def copy_mode(args):
+    import torch
+
+    import synth
+    dev = torch.device("cuda:0")
+    res = {}
+    nbytes = 4 << 30
+    src = torch.empty(nbytes // 4, dtype=torch.int32, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        synth.device_copy(torch, dst, src)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 10
+    a.record()
+    for _ in range(reps):
+        synth.device_copy(torch, dst, src)
+    b.record()
+    torch.cuda.synchronize()
+    t = a.elapsed_time(b) / reps / 1e3
+    res["copy"] = {"bytes_read": nbytes, "bytes_written": nbytes, "avg_ms": round(t * 1e3, 4),
+                   "GBps": round(2 * nbytes / t / 1e9, 1)}
+    del src, dst
+    n = 109_375_000
+    g = torch.zeros(n, dtype=torch.int16, device=dev)
+    h = torch.zeros(n, dtype=torch.int16, device=dev)
+    x, y, z = (torch.zeros(n, dtype=torch.float32, device=dev) for _ in range(3))
+    for _ in range(3):
+        synth.device_stream_mix(torch, g, x, y, z, h)
+    torch.cuda.synchronize()
+    a.record()
+    for _ in range(reps):
+        synth.device_stream_mix(torch, g, x, y, z, h)
+    b.record()
+    torch.cuda.synchronize()
+    t = a.elapsed_time(b) / reps / 1e3
+    res["step_shaped_mix"] = {"elements": n, "bytes_per_elem": 28, "avg_ms": round(t * 1e3, 4),
+                              "GBps": round(28 * n / t / 1e9, 1)}
+    print(json.dumps({"mode": "copy", **res}), flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="zero2_7b")
+    ap.add_argument("--mode", default="step", choices=["step", "copy"])
+    ap.add_argument("--max-grad-buffers", type=int, default=64)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--cpu-slice", type=int, default=1 << 24)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: --gpus {args.gpus} is not supported; the benchmark measures one GPU's "
+              "partition (ranks only exchange the 4-byte overflow flag, which needs a second GPU)",
+              file=sys.stderr)
+        sys.exit(2)
+    if int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py: launched with WORLD_SIZE > 1; the benchmark measures one GPU", file=sys.stderr)
+        sys.exit(2)
+    if args.mode == "copy":
+        copy_mode(args)
+        return
+    out = gpu_run(args)
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a bounded slice ...")
+        out["cpu_baseline"] = cpu_baseline(args.workload, args.cpu_seconds, args.cpu_slice)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,218 @@
+/*
+ * dszero.h -- C ABI of the MI355X (gfx950) ZeRO mixed-precision optimizer step.
+ *
+ * One GPU's share of ZeRO data-parallel training: the optimizer step that each
+ * rank runs on its own contiguous 1/N partition of the model state, gated by
+ * dynamic loss scaling and fed by fp16 gradient accumulation into an fp32
+ * buffer.
+ *
+ * Pages cited (by title and section):
+ *   [Guide]    "DeepSpeed complete guide" (youngju.dev, Japanese)
+ *   [Overview] "DeepSpeed" project overview (aibars.net, Japanese), core features
+ *
+ * Model state per element of a partition ([Guide] section 2, memory table):
+ * fp16 parameter copy (p16), fp16 gradient, fp32 master parameter, fp32 Adam
+ * first moment (m), fp32 Adam second moment (v).  With ZeRO-1/2 each rank owns
+ * a contiguous 1/N range of these arrays and updates only that range
+ * ([Guide] sections 2.1 and 2.2).
+ *
+ * Conventions shared by every entry point:
+ *  - Memory.  Array arguments are DEVICE pointers owned by the caller; the
+ *    library never allocates, frees or keeps them.  Work is enqueued
+ *    asynchronously on `stream` (a hipStream_t; NULL is the default stream)
+ *    and uses the buffers until the stream reaches it.
+ *  - Layout.  Arrays are flat and contiguous, element i of every array belongs
+ *    to the same parameter.  fp16 values are IEEE binary16 bit patterns
+ *    (uint16_t); fp32 values are IEEE binary32.
+ *  - Alignment.  Every array pointer must be 16-byte aligned; a ds_scaler
+ *    pointer must be 8-byte aligned.
+ *  - Errors.  Every call validates all arguments before any device work, so a
+ *    call that returns an error has had no effect.  n < 0 -> DS_ERR_SIZE;
+ *    n == 0 -> DS_OK and nothing is launched; a NULL array with n > 0 ->
+ *    DS_ERR_NULL; a misaligned pointer -> DS_ERR_ALIGN; overlapping arrays ->
+ *    DS_ERR_ALIAS; an unknown dtype -> DS_ERR_DTYPE; an out-of-range
+ *    hyperparameter -> DS_ERR_HPARAM; a failed HIP launch or copy ->
+ *    DS_ERR_HIP (the enqueue failed; earlier work is unaffected).
+ *  - Data is not an error: inf/NaN gradients set the overflow flag.
+ *  - Per-step order on one stream: all ds_accumulate calls, then any number of
+ *    ds_check_overflow calls (disjoint ranges), then any number of
+ *    ds_adam_step calls (disjoint ranges, all reading the same state), then
+ *    exactly one ds_update_loss_scale.  No host synchronisation is needed
+ *    inside a step: the skip decision is taken on the device.
+ *  - Thread safety: no mutable global state besides a per-device cache of the
+ *    compute-unit count.  Calls that share a ds_scaler must be ordered on one
+ *    stream.
+ */
+#ifndef DSZERO_H
+#define DSZERO_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum ds_status {
+    DS_OK = 0,
+    DS_ERR_NULL = 1,
+    DS_ERR_SIZE = 2,
+    DS_ERR_ALIGN = 3,
+    DS_ERR_DTYPE = 4,
+    DS_ERR_HPARAM = 5,
+    DS_ERR_ALIAS = 6,
+    DS_ERR_HIP = 7
+} ds_status;
+
+typedef enum ds_dtype { DS_FP16 = 1, DS_FP32 = 2 } ds_dtype;
+
+/*
+ * Dynamic loss-scaler state, 64 bytes, kept in caller-owned DEVICE memory so
+ * that the kernels read the scale and the overflow flag without a host sync.
+ * Fields follow the fp16 block of ds_config.json ([Guide] section 4.2:
+ * loss_scale 0 = dynamic, initial scale 2^initial_scale_power,
+ * loss_scale_window = successful steps before the scale grows, hysteresis =
+ * overflows before it shrinks, min_loss_scale = floor).
+ */
+typedef struct ds_scaler {
+    float scale;                    /* S: loss scale the next step unscales by        */
+    float min_scale;                /* floor of S (min_loss_scale)                    */
+    int32_t growth_window;          /* W: successful steps before S doubles           */
+    int32_t growth_count;           /* successful steps since last overflow or growth */
+    int32_t hysteresis;             /* H: overflows needed before S halves            */
+    int32_t hysteresis_left;        /* overflows still tolerated before S halves      */
+    int32_t dynamic;                /* 1: dynamic scaling; 0: static S                */
+    uint32_t overflow;              /* OR of non-finite findings of the current step  */
+    int64_t step;                   /* applied Adam steps (t of the last update)      */
+    int64_t iter;                   /* all steps, applied or skipped                  */
+    int64_t skipped;                /* skipped steps                                  */
+    int32_t consecutive_hysteresis; /* 1: a successful step refills hysteresis_left   */
+    uint32_t last_overflow;         /* overflow flag consumed by the last update      */
+} ds_scaler;
+
+/* sizeof(ds_scaler) as compiled into the library (64). */
+size_t ds_scaler_size(void);
+
+/*
+ * Initialise a scaler ([Guide] section 4.2).  init_scale = 2^initial_scale_power,
+ * min_scale = min_loss_scale, growth_window = loss_scale_window, hysteresis,
+ * consecutive_hysteresis, dynamic = (loss_scale == 0); for a static scale pass
+ * the fixed scale as init_scale and dynamic = 0.  Sets step = iter = skipped = 0
+ * and clears the flag.  Asynchronous (a one-thread kernel writes the struct).
+ * DS_ERR_HPARAM: init_scale or min_scale not finite or <= 0, growth_window < 1,
+ * hysteresis < 1.
+ */
+ds_status ds_state_init(ds_scaler* st, float init_scale, float min_scale, int32_t growth_window,
+                        int32_t hysteresis, int32_t consecutive_hysteresis, int32_t dynamic,
+                        void* stream);
+
+/* Copy the device state into *host_out (host memory) and synchronise `stream`. */
+ds_status ds_state_read(const ds_scaler* st, ds_scaler* host_out, void* stream);
+
+/* Overwrite the device state with *host_in (resume from a snapshot).  The
+ * struct is passed by value to a one-thread kernel, so host_in may be freed as
+ * soon as the call returns. */
+ds_status ds_state_write(ds_scaler* st, const ds_scaler* host_in, void* stream);
+
+/*
+ * Gradient accumulation ([Overview] core features: accumulating micro-batch
+ * gradients emulates a larger batch; [Guide] section 5.1: backward handles
+ * the accumulation; section 4.3: gradient_accumulation_steps).
+ *   overwrite != 0 : acc[i] = float(g16[i])            (first micro-batch)
+ *   overwrite == 0 : acc[i] = acc[i] + float(g16[i])   (later micro-batches, in order)
+ * acc: fp32[n], g16: fp16[n].  If st is not NULL the same pass ORs "acc[i] is
+ * not finite" into st->overflow (use it on the last micro-batch: the check of
+ * the step then costs no extra pass).  Errors: see the conventions; acc, g16
+ * and st must not overlap.
+ */
+ds_status ds_accumulate(float* acc, const uint16_t* g16, int64_t n, int32_t overwrite,
+                        ds_scaler* st_or_null, void* stream);
+
+/*
+ * Overflow check ([Overview] core features: dynamic loss scaling; [Guide]
+ * section 13.1, gradient overflow in fp16): ORs "some grad[i] is +-inf or NaN"
+ * into st->overflow.  grad: fp16[n] (dt = DS_FP16) or fp32[n] (dt = DS_FP32).
+ * The largest finite fp16 value (65504) is not an overflow.  Does nothing more
+ * once the flag is already set for this step.
+ */
+ds_status ds_check_overflow(ds_scaler* st, const void* grad, ds_dtype dt, int64_t n, void* stream);
+
+/*
+ * Fused mixed-precision Adam step over n elements ([Guide] section 2: fp32
+ * master, first and second moments, fp16 parameter copy; section 4.1:
+ * optimizer AdamW with lr, betas, eps, weight_decay; section 5.1: step()).
+ * If st->overflow is set the kernel writes nothing (the step is skipped).
+ * Otherwise, with S = st->scale, K = accum_steps and t = st->step + 1:
+ *   g      = grad[i] / (S*K)                     (unscale; grad fp16 or fp32)
+ *   m[i]   = beta1*m[i] + (1-beta1)*g
+ *   v[i]   = beta2*v[i] + (1-beta2)*g*g
+ *   master = master - lr*weight_decay*master     (only if weight_decay != 0)
+ *   master = master - lr/(1-beta1^t) * m[i] / (sqrt(v[i])/sqrt(1-beta2^t) + eps)
+ *   p16[i] = fp16(master[i])                     (round to nearest even)
+ * in IEEE fp32, one rounding per operation; the two bias-correction factors
+ * are evaluated in fp64 and rounded once.  master/m/v: fp32[n] in place;
+ * p16: fp16[n] out; grad: fp16[n] or fp32[n] in.  st is read only (t and S
+ * advance in ds_update_loss_scale).  DS_ERR_HPARAM: lr or weight_decay
+ * negative or not finite, beta1 or beta2 outside [0, 1), eps not finite or
+ * <= 0, accum_steps < 1.
+ */
+ds_status ds_adam_step(const ds_scaler* st, float* master, float* m, float* v, uint16_t* p16,
+                       const void* grad, ds_dtype dt, int64_t n, float lr, float beta1,
+                       float beta2, float eps, float weight_decay, int32_t accum_steps,
+                       void* stream);
+
+/*
+ * End of a step: advance the scaler by the step's overflow flag, then clear
+ * the flag ([Guide] section 4.2).  Overflow: skipped += 1, growth_count = 0;
+ * if dynamic, one more overflow is charged to the hysteresis and, when it is
+ * used up, S = max(S/2, min_scale) and the hysteresis restarts.  No overflow:
+ * step += 1; if dynamic, growth_count += 1 and at growth_window S doubles and
+ * growth_count restarts (consecutive_hysteresis refills the hysteresis).
+ * iter += 1 and last_overflow = flag in both cases.  Call exactly once per step.
+ */
+ds_status ds_update_loss_scale(ds_scaler* st, void* stream);
+
+/*
+ * The bias-correction scalars the next applied step will use, evaluated on
+ * the device exactly as ds_adam_step does (t = st->step + 1):
+ * out2[0] = fp32(lr / (1 - beta1^t)), out2[1] = fp32(1 / sqrt(1 - beta2^t)).
+ * out2: device float[2].  For diagnostics and tests.
+ */
+ds_status ds_adam_bias_scalars(const ds_scaler* st, float lr, float beta1, float beta2,
+                               float* out2, void* stream);
+
+/*
+ * Flat layout of ragged tensors in contiguous buffers with greedy buckets
+ * ([Guide] sections 2.2 and 4.1: contiguous_gradients, reduce_bucket_size and
+ * allgather_bucket_size of 2e8 elements).  Host-only, no device work.
+ * Tensors keep their order; tensor i starts at offsets[i], a multiple of
+ * `align` elements.  A tensor joins the open bucket if the bucket, padded to
+ * `align`, then holds at most `cap` elements; otherwise the bucket closes and
+ * the tensor opens the next one (a tensor larger than cap gets its own
+ * bucket).  Outputs (host arrays of `count` entries, caller-owned): offsets,
+ * bucket_of; bucket_start and bucket_size (first *n_buckets entries used);
+ * *total = padded length of the flat array.  DS_ERR_SIZE: count < 0, a
+ * negative size, cap < 1, align < 1.
+ */
+ds_status ds_layout_greedy(const int64_t* numels, int32_t count, int64_t cap, int64_t align,
+                           int64_t* offsets, int32_t* bucket_of, int64_t* bucket_start,
+                           int64_t* bucket_size, int32_t* n_buckets, int64_t* total);
+
+/*
+ * ZeRO partition of a flat array of `total` elements over `world` ranks
+ * ([Guide] sections 2.1 and 2.2: each rank owns a contiguous 1/N share):
+ * rank r gets [r*per, min((r+1)*per, total)) with per = ceil(total/world)
+ * rounded up to `align`.  Host-only.  DS_ERR_SIZE: total < 0, world < 1,
+ * rank outside [0, world), align < 1.
+ */
+ds_status ds_partition_range(int64_t total, int32_t world, int32_t rank, int64_t align,
+                             int64_t* start, int64_t* count);
+
+/* Static string naming a status code. */
+const char* ds_status_string(ds_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DSZERO_H */

@@ -1,0 +1,218 @@
+"""CPU tests of the C ABI: exported symbols, argument validation (every error
+is returned before any device work, so these calls never reach the GPU), the
+host-only layout/partition entry points against the packing oracle, and the
+ds_config keys."""
+import ctypes
+import json
+import os
+import re
+
+import numpy as np
+import pytest
+
+from oracle import packing
+from zero_mixed_precision_amd import _lib, ZeroMPConfig, FlatLayout
+from zero_mixed_precision_amd._lib import (DS_ERR_ALIAS, DS_ERR_ALIGN, DS_ERR_DTYPE, DS_ERR_HPARAM,
+                                           DS_ERR_NULL, DS_ERR_SIZE, DS_FP16, DS_FP32, DS_OK)
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+GOLDEN = os.path.join(ROOT, "tests", "golden")
+L = _lib.lib
+
+# fake, never-dereferenced device addresses (validation fails before any launch)
+A, B, C, D, E, ST = (0x10000000 * k for k in range(1, 7))
+STREAM = None
+HP = (1e-4, 0.9, 0.999, 1e-8, 0.0, 1)
+
+
+def declared_symbols():
+    text = open(os.path.join(ROOT, "include", "dszero.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ds_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    syms = declared_symbols()
+    assert len(syms) >= 12
+    lib = ctypes.CDLL(_lib.LIB_PATH)
+    for s in syms:
+        assert hasattr(lib, s), s
+    assert sorted(_lib.EXPORTED) == syms
+
+
+def test_scaler_layout():
+    assert L.ds_scaler_size() == 64 == ctypes.sizeof(_lib.DsScaler)
+    offs = {n: getattr(_lib.DsScaler, n).offset for n, _ in _lib.DsScaler._fields_}
+    assert offs["overflow"] == 28 and offs["step"] == 32 and offs["last_overflow"] == 60
+
+
+def test_status_strings():
+    for s in range(8):
+        assert _lib.status_string(s).startswith("DS_")
+    assert "unknown" in _lib.status_string(99)
+
+
+def test_accumulate_validation():
+    acc = L.ds_accumulate
+    assert acc(A, B, -1, 1, None, STREAM) == DS_ERR_SIZE
+    assert acc(A, B, 0, 1, None, STREAM) == DS_OK                      # n == 0: nothing launched
+    assert acc(None, B, 5, 1, None, STREAM) == DS_ERR_NULL
+    assert acc(A, None, 5, 1, None, STREAM) == DS_ERR_NULL
+    assert acc(A + 4, B, 5, 1, None, STREAM) == DS_ERR_ALIGN
+    assert acc(A, B + 2, 5, 1, None, STREAM) == DS_ERR_ALIGN
+    assert acc(A, B, 5, 1, ST + 4, STREAM) == DS_ERR_ALIGN
+    assert acc(A, A + 16, 8, 1, None, STREAM) == DS_ERR_ALIAS          # acc [A, A+32) vs g16
+    assert acc(A, B, 8, 0, A + 16, STREAM) == DS_ERR_ALIAS             # state inside acc
+
+
+def test_check_overflow_validation():
+    chk = L.ds_check_overflow
+    assert chk(ST, A, DS_FP16, -1, STREAM) == DS_ERR_SIZE
+    assert chk(ST, A, 3, 10, STREAM) == DS_ERR_DTYPE
+    assert chk(None, A, DS_FP16, 10, STREAM) == DS_ERR_NULL
+    assert chk(ST, A, DS_FP16, 0, STREAM) == DS_OK
+    assert chk(ST, None, DS_FP16, 10, STREAM) == DS_ERR_NULL
+    assert chk(ST, A + 8, DS_FP32, 10, STREAM) == DS_ERR_ALIGN
+    assert chk(ST + 4, A, DS_FP32, 10, STREAM) == DS_ERR_ALIGN
+    assert chk(A + 32, A, DS_FP32, 10, STREAM) == DS_ERR_ALIAS
+
+
+def _adam(*, st=ST, ptrs=(A, B, C, D, E), dt=DS_FP16, n=16, hp=HP):
+    return L.ds_adam_step(st, *ptrs, dt, n, *hp, STREAM)
+
+
+def test_adam_validation():
+    assert _adam(n=-3) == DS_ERR_SIZE
+    assert _adam(dt=0) == DS_ERR_DTYPE
+    assert _adam(n=0) == DS_OK
+    assert _adam(st=None) == DS_ERR_NULL
+    for k in range(5):
+        ptrs = [A, B, C, D, E]
+        ptrs[k] = None
+        assert _adam(ptrs=tuple(ptrs)) == DS_ERR_NULL
+        ptrs = [A, B, C, D, E]
+        ptrs[k] += 8
+        assert _adam(ptrs=tuple(ptrs)) == DS_ERR_ALIGN
+    assert _adam(st=ST + 2) == DS_ERR_ALIGN
+    assert _adam(ptrs=(A, A + 32, C, D, E)) == DS_ERR_ALIAS            # master [A, A+64) vs m
+    assert _adam(ptrs=(A, B, C, D, D + 16)) == DS_ERR_ALIAS            # p16 vs grad
+    assert _adam(st=E + 16) == DS_ERR_ALIAS                            # state inside grad
+
+
+@pytest.mark.parametrize("bad", [
+    (-1e-4, 0.9, 0.999, 1e-8, 0.0, 1), (float("nan"), 0.9, 0.999, 1e-8, 0.0, 1),
+    (float("inf"), 0.9, 0.999, 1e-8, 0.0, 1), (1e-4, 1.0, 0.999, 1e-8, 0.0, 1),
+    (1e-4, -0.1, 0.999, 1e-8, 0.0, 1), (1e-4, 0.9, 1.0, 1e-8, 0.0, 1),
+    (1e-4, 0.9, float("nan"), 1e-8, 0.0, 1), (1e-4, 0.9, 0.999, 0.0, 0.0, 1),
+    (1e-4, 0.9, 0.999, -1e-8, 0.0, 1), (1e-4, 0.9, 0.999, float("inf"), 0.0, 1),
+    (1e-4, 0.9, 0.999, 1e-8, -0.01, 1), (1e-4, 0.9, 0.999, 1e-8, float("nan"), 1),
+    (1e-4, 0.9, 0.999, 1e-8, 0.0, 0), (1e-4, 0.9, 0.999, 1e-8, 0.0, -2),
+])
+def test_adam_hyperparameter_validation(bad):
+    assert _adam(hp=bad) == DS_ERR_HPARAM
+
+
+def test_state_and_scalar_validation():
+    init = L.ds_state_init
+    assert init(None, 65536.0, 1.0, 1000, 1, 0, 1, STREAM) == DS_ERR_NULL
+    assert init(ST + 4, 65536.0, 1.0, 1000, 1, 0, 1, STREAM) == DS_ERR_ALIGN
+    for args in [(0.0, 1.0, 1000, 1), (-1.0, 1.0, 1000, 1), (float("inf"), 1.0, 1000, 1),
+                 (65536.0, 0.0, 1000, 1), (65536.0, float("nan"), 1000, 1), (65536.0, 1.0, 0, 1),
+                 (65536.0, 1.0, 1000, 0)]:
+        assert init(ST, *args, 0, 1, STREAM) == DS_ERR_HPARAM, args
+    out = _lib.DsScaler()
+    assert L.ds_state_read(None, ctypes.byref(out), STREAM) == DS_ERR_NULL
+    assert L.ds_state_read(ST, None, STREAM) == DS_ERR_NULL
+    assert L.ds_state_write(None, ctypes.byref(out), STREAM) == DS_ERR_NULL
+    assert L.ds_state_write(ST + 1, ctypes.byref(out), STREAM) == DS_ERR_ALIGN
+    assert L.ds_update_loss_scale(None, STREAM) == DS_ERR_NULL
+    assert L.ds_update_loss_scale(ST + 4, STREAM) == DS_ERR_ALIGN
+    assert L.ds_adam_bias_scalars(None, 1e-4, 0.9, 0.999, A, STREAM) == DS_ERR_NULL
+    assert L.ds_adam_bias_scalars(ST, 1e-4, 0.9, 0.999, None, STREAM) == DS_ERR_NULL
+    assert L.ds_adam_bias_scalars(ST, 1e-4, 1.5, 0.999, A, STREAM) == DS_ERR_HPARAM
+    assert L.ds_adam_bias_scalars(ST, 1e-4, 0.9, 0.999, ST + 8, STREAM) == DS_ERR_ALIAS
+
+
+# -- host-only entry points against the packing oracle --------------------------
+
+def test_layout_matches_packing_oracle_on_the_ragged_layout():
+    numels = packing.llama_like_numels()
+    assert _lib.ds_layout_greedy(numels, int(2e8), 64) == tuple(packing.greedy_buckets(numels, int(2e8), 64))
+    lay = FlatLayout(numels)
+    assert lay.total == 6_476_267_520 and len(lay.buckets) == 38
+
+
+def test_layout_matches_packing_oracle_on_random_layouts():
+    rng = np.random.default_rng(3)
+    for _ in range(500):
+        k = int(rng.integers(0, 30))
+        numels = [int(x) for x in rng.integers(0, 3000, k)]
+        if k and rng.random() < 0.3:
+            numels[int(rng.integers(0, k))] = int(rng.integers(3000, 9000))
+        cap, align = int(rng.integers(1, 6000)), int(rng.choice([1, 2, 8, 64]))
+        assert _lib.ds_layout_greedy(numels, cap, align) == tuple(packing.greedy_buckets(numels, cap, align))
+
+
+def test_layout_validation():
+    with pytest.raises(_lib.DsError):
+        _lib.ds_layout_greedy([3, -1], 10, 1)
+    with pytest.raises(_lib.DsError):
+        _lib.ds_layout_greedy([3], 0, 1)
+    with pytest.raises(_lib.DsError):
+        _lib.ds_layout_greedy([3], 10, 0)
+
+
+def test_partition_matches_packing_oracle():
+    rng = np.random.default_rng(4)
+    for _ in range(2000):
+        total = int(rng.integers(0, 1 << 40))
+        world = int(rng.integers(1, 1024))
+        rank = int(rng.integers(0, world))
+        align = int(rng.choice([1, 8, 64]))
+        assert _lib.ds_partition_range(total, world, rank, align) == \
+            packing.partition_range(total, world, rank, align)
+    for bad in [(-1, 2, 0, 1), (10, 0, 0, 1), (10, 2, 2, 1), (10, 2, -1, 1), (10, 2, 0, 0)]:
+        with pytest.raises(_lib.DsError):
+            _lib.ds_partition_range(*bad)
+
+
+def test_partition_buckets_clip():
+    lay = FlatLayout([100, 100, 100], bucket_cap=150, align=4)
+    start, count = 50, 200
+    clipped = lay.buckets_in(start, count)
+    assert sum(b.size for b in clipped) == count and clipped[0].start == 0
+
+
+# -- ds_config keys ("DeepSpeed complete guide" sections 4.1-4.3) ------------------
+
+def test_config_from_the_pages_fp16_block():
+    g = json.load(open(os.path.join(GOLDEN, "fp16_config.json")))
+    cfg = ZeroMPConfig.from_dict({"fp16": g["fp16_section_4_2"],
+                                  "optimizer": {"type": "AdamW", "params": {"lr": 1e-4, "eps": 1e-8}},
+                                  "zero_optimization": g["zero_optimization_section_4_1"]})
+    assert cfg.dynamic and cfg.init_scale == 65536.0
+    assert cfg.loss_scale_window == 1000 and cfg.hysteresis == 2 and cfg.min_loss_scale == 1
+    assert cfg.reduce_bucket_size == 200_000_000 and cfg.stage == 2 and cfg.eps == 1e-8
+    dbg = ZeroMPConfig.from_dict({"fp16": g["fp16_section_13_1"]})
+    assert dbg.init_scale == 4096.0 and dbg.loss_scale_window == 500 and dbg.min_loss_scale == 1e-8
+    static = ZeroMPConfig.from_dict({"fp16": {"enabled": True, "loss_scale": 128}})
+    assert not static.dynamic and static.init_scale == 128.0
+
+
+def test_config_rejects_auto_and_other_optimizers():
+    with pytest.raises(ValueError):
+        ZeroMPConfig.from_dict({"optimizer": {"type": "AdamW", "params": {"lr": "auto"}}})
+    with pytest.raises(ValueError):
+        ZeroMPConfig.from_dict({"optimizer": {"type": "SGD"}})
+    with pytest.raises(ValueError):
+        ZeroMPConfig.from_dict({"fp16": {"enabled": False}})
+
+
+def test_batch_relation_from_the_pages():
+    g = json.load(open(os.path.join(GOLDEN, "batch_relation.json")))
+    cfg = ZeroMPConfig.from_dict({k: g[k] for k in ("train_micro_batch_size_per_gpu",
+                                                    "gradient_accumulation_steps")})
+    assert cfg.train_batch_size(g["world_size"]) == g["train_batch_size"] == 2048
+    with pytest.raises(ValueError):
+        ZeroMPConfig.from_dict({"train_batch_size": 1000, "world_size": 8,
+                                "train_micro_batch_size_per_gpu": 4, "gradient_accumulation_steps": 64})

@@ -1,0 +1,130 @@
+"""GPU parity at the workloads' full sizes, on sampled elements.
+
+The device runs the whole partition (one rank's ZeRO-2 share of 7B at N=64,
+a full 7B state, the ragged Llama-like layout with 8 micro-batches, one
+rank's ZeRO-1 share of 70B at N=8) in the default launch configuration.  The
+oracle runs the same steps on a sample of element indices: 2^20 seeded
+uniform indices, the first and last 4096 elements of the partition and of
+every bucket, and every injected index.
+
+Every element's update depends only on its own inputs and on the step's
+overflow flag, so sampling is exact provided the oracle's flag is the global
+one.  It is: the generator only emits entries of finite lookup tables (pinned
+on the CPU), so the only non-finite gradients are the injected ones, and all of
+those are in the sample.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from synth.workloads import BETA1, BETA2, EPS, LR, MASTER_SIGMA, WORKLOADS, ragged_numels
+from tests import gpu_util as gu
+
+pytestmark = pytest.mark.gpu
+
+HP = dict(lr=LR, beta1=BETA1, beta2=BETA2, eps=EPS)
+
+
+@pytest.fixture(scope="module")
+def torch():
+    t = gu.torch_mod()
+    import zero_mixed_precision_amd  # noqa: F401
+    return t
+
+
+def sample_indices(w, buckets):
+    rng = np.random.default_rng(20261202 + w.cid)
+    parts = [rng.integers(0, w.psi, 1 << 20), np.arange(4096), w.psi - 4096 + np.arange(4096)]
+    for start, size in buckets:
+        parts += [start + np.arange(min(4096, size)), start + size - np.arange(1, min(4096, size) + 1)]
+    for s in w.inject_steps:
+        parts.append(np.array([w.injection(s)[1]]))
+    return np.unique(np.concatenate(parts).astype(np.int64))
+
+
+def run_sampled(torch, name):
+    from zero_mixed_precision_amd import _lib, FlatLayout
+
+    w = WORKLOADS[name]
+    n, K = w.psi, w.K
+    spec = w.grad_spec
+    if w.ragged:
+        lay = FlatLayout(ragged_numels())
+        assert lay.total == n
+        buckets = [(b.start, b.size) for b in lay.buckets]
+    else:
+        buckets = [(0, n)]
+    I = sample_indices(w, buckets)
+    gu.say(f"[{name}] psi={n} K={K} steps={w.steps} sample={I.size}")
+
+    # oracle state on the sample
+    o = oracle.State(synth.host_master32(w.master_key(), I, MASTER_SIGMA), np.zeros(I.size, np.float32),
+                     np.zeros(I.size, np.float32), synth.host_grad16(w.p16_key(), I, synth.GradSpec(0.02, 1.0)),
+                     oracle.Scaler(w.init_scale, w.min_scale, w.window, w.hysteresis))
+
+    # device state over the whole partition
+    tabs = synth.DeviceTables(torch, "cuda:0")
+    master = torch.empty(n, dtype=torch.float32, device="cuda:0")
+    synth.device_fill_master32(torch, tabs, master, w.master_key(), MASTER_SIGMA)
+    m = torch.zeros(n, dtype=torch.float32, device="cuda:0")
+    v = torch.zeros(n, dtype=torch.float32, device="cuda:0")
+    p16 = torch.empty(n, dtype=torch.int16, device="cuda:0")
+    synth.device_fill_grad16(torch, tabs, p16, w.p16_key(), synth.GradSpec(0.02, 1.0))
+    g16 = torch.empty(n, dtype=torch.int16, device="cuda:0")
+    acc = torch.empty(n, dtype=torch.float32, device="cuda:0") if K > 1 else None
+    st = torch.zeros(64, dtype=torch.uint8, device="cuda:0")
+    _lib.ds_state_init(st, w.init_scale, w.min_scale, w.window, w.hysteresis, 0, 1)
+    Id = torch.from_numpy(I).to("cuda:0")
+
+    for s in range(1, w.steps + 1):
+        inj = w.injection(s)
+        gs_host = []
+        for k in range(K):
+            synth.device_fill_grad16(torch, tabs, g16, w.grad_key(s, k), spec)
+            gh = synth.host_grad16(w.grad_key(s, k), I, spec)
+            if inj is not None and inj[0] == k:
+                g16[inj[1]] = torch.tensor(0x7C00, dtype=torch.int32).to(torch.int16)
+                gh[np.searchsorted(I, inj[1])] = 0x7C00
+            gs_host.append(gh)
+            if K > 1:
+                for start, size in buckets:
+                    _lib.ds_accumulate(acc.data_ptr() + 4 * start, g16.data_ptr() + 2 * start, size,
+                                       k == 0, st if k == K - 1 else None)
+        if K == 1:
+            _lib.ds_check_overflow(st, g16, _lib.DS_FP16, n)
+            _lib.ds_adam_step(st, master, m, v, p16, g16, _lib.DS_FP16, n, LR, BETA1, BETA2, EPS, 0.0, 1)
+        else:
+            _lib.ds_adam_step(st, master, m, v, p16, acc, _lib.DS_FP32, n, LR, BETA1, BETA2, EPS, 0.0, K)
+        _lib.ds_update_loss_scale(st)
+        ov = oracle.step(o, gs_host if K > 1 else gs_host[0], **HP)
+        assert ov == (inj is not None), f"[{name}] step {s}: oracle flag"
+        gu.check_scaler(_lib.ds_state_read(st), o.scaler, ov, f"[{name}] step {s}")
+        if s in (1, w.steps // 2, w.steps):
+            du = gu.compare_arrays(f"[{name}] step {s}", gu.host_f32(master[Id]), gu.host_f32(m[Id]),
+                                   gu.host_f32(v[Id]), gu.host_u16(p16[Id]), o.master, o.m, o.v, o.p16)
+            gu.say(f"[{name}] step {s}: scale 2^{int(np.log2(o.scaler.scale))} applied {o.scaler.applied} "
+                   f"max ulp {du}")
+    del master, m, v, p16, g16, acc, st
+    torch.cuda.empty_cache()
+    return o.scaler
+
+
+def test_zero2_shard_of_7b(torch):
+    sc = run_sampled(torch, "zero2_7b")
+    assert sc.applied == 50 and sc.scale == 2.0 ** 16
+
+
+def test_full_7b_state(torch):
+    sc = run_sampled(torch, "full_7b")
+    assert sc.applied == 20 and sc.scale == 2.0 ** 16
+
+
+def test_ragged_layout_with_accumulation(torch):
+    sc = run_sampled(torch, "ragged")
+    assert sc.applied == 27 and sc.scale == 2.0 ** 14
+
+
+def test_zero1_shard_of_70b_heavy_tail(torch):
+    sc = run_sampled(torch, "zero1_70b")
+    assert sc.applied == 10 and sc.scale == 2.0 ** 18

@@ -1,0 +1,179 @@
+"""ctypes binding of libdszero.so (include/dszero.h), same names as the C ABI.
+
+Argument marshalling only: every entry point forwards to the native library,
+which enqueues HIP kernels.  Pointers may be passed as integers or as torch
+tensors (their ``data_ptr()``); ``stream`` defaults to torch's current HIP
+stream.  A non-OK status raises ``DsError``.  If the library has not been
+built, importing the binding raises -- there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libdszero.so")
+
+DS_OK, DS_ERR_NULL, DS_ERR_SIZE, DS_ERR_ALIGN, DS_ERR_DTYPE, DS_ERR_HPARAM, DS_ERR_ALIAS, DS_ERR_HIP = range(8)
+DS_FP16, DS_FP32 = 1, 2
+
+EXPORTED = (
+    "ds_scaler_size", "ds_state_init", "ds_state_read", "ds_state_write", "ds_accumulate",
+    "ds_check_overflow", "ds_adam_step", "ds_update_loss_scale", "ds_adam_bias_scalars",
+    "ds_layout_greedy", "ds_partition_range", "ds_status_string",
+)
+
+
+class DsScaler(ctypes.Structure):
+    """Mirror of ``ds_scaler`` (64 bytes)."""
+    _fields_ = [
+        ("scale", ctypes.c_float),
+        ("min_scale", ctypes.c_float),
+        ("growth_window", ctypes.c_int32),
+        ("growth_count", ctypes.c_int32),
+        ("hysteresis", ctypes.c_int32),
+        ("hysteresis_left", ctypes.c_int32),
+        ("dynamic", ctypes.c_int32),
+        ("overflow", ctypes.c_uint32),
+        ("step", ctypes.c_int64),
+        ("iter", ctypes.c_int64),
+        ("skipped", ctypes.c_int64),
+        ("consecutive_hysteresis", ctypes.c_int32),
+        ("last_overflow", ctypes.c_uint32),
+    ]
+
+    def as_dict(self) -> dict:
+        return {name: getattr(self, name) for name, _ in self._fields_}
+
+
+class DsError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = int(status)
+        super().__init__(f"{where}: {status_string(status)}")
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() "
+                          "(python -m zero_mixed_precision_amd.build)")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i64, i32, f32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_float
+    sig = {
+        "ds_scaler_size": ([], ctypes.c_size_t),
+        "ds_state_init": ([vp, f32, f32, i32, i32, i32, i32, vp], ctypes.c_int),
+        "ds_state_read": ([vp, ctypes.POINTER(DsScaler), vp], ctypes.c_int),
+        "ds_state_write": ([vp, ctypes.POINTER(DsScaler), vp], ctypes.c_int),
+        "ds_accumulate": ([vp, vp, i64, i32, vp, vp], ctypes.c_int),
+        "ds_check_overflow": ([vp, vp, ctypes.c_int, i64, vp], ctypes.c_int),
+        "ds_adam_step": ([vp, vp, vp, vp, vp, vp, ctypes.c_int, i64, f32, f32, f32, f32, f32, i32, vp],
+                         ctypes.c_int),
+        "ds_update_loss_scale": ([vp, vp], ctypes.c_int),
+        "ds_adam_bias_scalars": ([vp, f32, f32, f32, vp, vp], ctypes.c_int),
+        "ds_layout_greedy": ([vp, i32, i64, i64, vp, vp, vp, vp, ctypes.POINTER(i32),
+                              ctypes.POINTER(i64)], ctypes.c_int),
+        "ds_partition_range": ([i64, i32, i32, i64, ctypes.POINTER(i64), ctypes.POINTER(i64)],
+                               ctypes.c_int),
+        "ds_status_string": ([ctypes.c_int], ctypes.c_char_p),
+    }
+    for name, (args, res) in sig.items():
+        fn = getattr(L, name)
+        fn.argtypes, fn.restype = args, res
+    if L.ds_scaler_size() != ctypes.sizeof(DsScaler):
+        raise ImportError("ds_scaler layout mismatch between libdszero.so and the binding")
+    return L
+
+
+lib = _load()
+
+
+def status_string(status: int) -> str:
+    return lib.ds_status_string(int(status)).decode()
+
+
+def _p(x):
+    """Pointer argument: int, None, or a tensor-like with data_ptr()."""
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _s(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _ok(rc: int, where: str) -> None:
+    if rc != DS_OK:
+        raise DsError(rc, where)
+
+
+def ds_scaler_size() -> int:
+    return lib.ds_scaler_size()
+
+
+def ds_state_init(st, init_scale, min_scale, growth_window, hysteresis, consecutive_hysteresis=0,
+                  dynamic=1, stream=None) -> None:
+    _ok(lib.ds_state_init(_p(st), init_scale, min_scale, int(growth_window), int(hysteresis),
+                          int(consecutive_hysteresis), int(dynamic), _s(stream)), "ds_state_init")
+
+
+def ds_state_read(st, stream=None) -> DsScaler:
+    out = DsScaler()
+    _ok(lib.ds_state_read(_p(st), ctypes.byref(out), _s(stream)), "ds_state_read")
+    return out
+
+
+def ds_state_write(st, value: DsScaler, stream=None) -> None:
+    _ok(lib.ds_state_write(_p(st), ctypes.byref(value), _s(stream)), "ds_state_write")
+
+
+def ds_accumulate(acc, g16, n, overwrite, st_or_null=None, stream=None) -> None:
+    _ok(lib.ds_accumulate(_p(acc), _p(g16), int(n), int(bool(overwrite)), _p(st_or_null), _s(stream)),
+        "ds_accumulate")
+
+
+def ds_check_overflow(st, grad, dtype, n, stream=None) -> None:
+    _ok(lib.ds_check_overflow(_p(st), _p(grad), int(dtype), int(n), _s(stream)), "ds_check_overflow")
+
+
+def ds_adam_step(st, master, m, v, p16, grad, dtype, n, lr, beta1, beta2, eps, weight_decay,
+                 accum_steps, stream=None) -> None:
+    _ok(lib.ds_adam_step(_p(st), _p(master), _p(m), _p(v), _p(p16), _p(grad), int(dtype), int(n),
+                         lr, beta1, beta2, eps, weight_decay, int(accum_steps), _s(stream)),
+        "ds_adam_step")
+
+
+def ds_update_loss_scale(st, stream=None) -> None:
+    _ok(lib.ds_update_loss_scale(_p(st), _s(stream)), "ds_update_loss_scale")
+
+
+def ds_adam_bias_scalars(st, lr, beta1, beta2, out2, stream=None) -> None:
+    _ok(lib.ds_adam_bias_scalars(_p(st), lr, beta1, beta2, _p(out2), _s(stream)), "ds_adam_bias_scalars")
+
+
+def ds_layout_greedy(numels, cap, align):
+    """Host-only greedy packing; returns (offsets, bucket_of, bucket_starts, bucket_sizes, total)."""
+    n = len(numels)
+    c_num = (ctypes.c_int64 * max(n, 1))(*[int(x) for x in numels])
+    offs = (ctypes.c_int64 * max(n, 1))()
+    bof = (ctypes.c_int32 * max(n, 1))()
+    bst = (ctypes.c_int64 * max(n, 1))()
+    bsz = (ctypes.c_int64 * max(n, 1))()
+    nb, total = ctypes.c_int32(), ctypes.c_int64()
+    _ok(lib.ds_layout_greedy(c_num, n, int(cap), int(align), offs, bof, bst, bsz, ctypes.byref(nb),
+                             ctypes.byref(total)), "ds_layout_greedy")
+    k = nb.value
+    return list(offs[:n]), list(bof[:n]), list(bst[:k]), list(bsz[:k]), total.value
+
+
+def ds_partition_range(total, world, rank, align):
+    start, count = ctypes.c_int64(), ctypes.c_int64()
+    _ok(lib.ds_partition_range(int(total), int(world), int(rank), int(align), ctypes.byref(start),
+                               ctypes.byref(count)), "ds_partition_range")
+    return start.value, count.value

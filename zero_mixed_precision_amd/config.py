@@ -1,0 +1,88 @@
+"""The ds_config.json keys the optimizer step consumes.
+
+"DeepSpeed complete guide" section 4.1 (base structure: gradient_accumulation_steps,
+fp16, optimizer, zero_optimization), section 4.2 (fp16 block: loss_scale 0 is
+dynamic, initial scale 2^initial_scale_power, loss_scale_window,
+hysteresis, consecutive_hysteresis, min_loss_scale), section 4.3
+(train_batch_size = micro batch x gradient_accumulation_steps x world size).
+"auto" values are resolved by a trainer integration, which this library does
+not have: they are rejected.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+
+def _val(d: dict, key: str, default):
+    v = d.get(key, default)
+    if v == "auto":
+        raise ValueError(f"'{key}': \"auto\" needs a trainer integration; give a number")
+    return v
+
+
+@dataclass
+class ZeroMPConfig:
+    # fp16 block
+    loss_scale: float = 0.0
+    initial_scale_power: int = 16
+    loss_scale_window: int = 1000
+    hysteresis: int = 2
+    consecutive_hysteresis: bool = False
+    min_loss_scale: float = 1.0
+    # optimizer block
+    optimizer: str = "AdamW"
+    lr: float = 1e-4
+    betas: tuple = (0.9, 0.999)
+    eps: float = 1e-8
+    weight_decay: float = 0.0
+    # batch / ZeRO
+    gradient_accumulation_steps: int = 1
+    train_micro_batch_size_per_gpu: int = 1
+    reduce_bucket_size: int = int(2e8)
+    stage: int = 2
+
+    @property
+    def dynamic(self) -> bool:
+        return self.loss_scale == 0
+
+    @property
+    def init_scale(self) -> float:
+        return 2.0 ** self.initial_scale_power if self.dynamic else float(self.loss_scale)
+
+    def train_batch_size(self, world_size: int) -> int:
+        return self.train_micro_batch_size_per_gpu * self.gradient_accumulation_steps * world_size
+
+    @classmethod
+    def from_dict(cls, cfg: dict) -> "ZeroMPConfig":
+        fp16 = cfg.get("fp16", {})
+        if fp16 and not _val(fp16, "enabled", True):
+            raise ValueError("fp16.enabled is false: this step is the fp16 mixed-precision path")
+        opt = cfg.get("optimizer", {})
+        params = opt.get("params", {})
+        zero = cfg.get("zero_optimization", {})
+        kind = _val(opt, "type", "AdamW")
+        if kind not in ("Adam", "AdamW"):
+            raise ValueError(f"optimizer type {kind!r} is not Adam/AdamW")
+        betas = tuple(float(b) for b in _val(params, "betas", (0.9, 0.999)))
+        out = cls(
+            loss_scale=float(_val(fp16, "loss_scale", 0.0)),
+            initial_scale_power=int(_val(fp16, "initial_scale_power", 16)),
+            loss_scale_window=int(_val(fp16, "loss_scale_window", 1000)),
+            hysteresis=int(_val(fp16, "hysteresis", 2)),
+            consecutive_hysteresis=bool(_val(fp16, "consecutive_hysteresis", False)),
+            min_loss_scale=float(_val(fp16, "min_loss_scale", 1.0)),
+            optimizer=kind,
+            lr=float(_val(params, "lr", 1e-4)),
+            betas=betas,
+            eps=float(_val(params, "eps", 1e-8)),
+            weight_decay=float(_val(params, "weight_decay", 0.0)),
+            gradient_accumulation_steps=int(_val(cfg, "gradient_accumulation_steps", 1)),
+            train_micro_batch_size_per_gpu=int(_val(cfg, "train_micro_batch_size_per_gpu", 1)),
+            reduce_bucket_size=int(float(_val(zero, "reduce_bucket_size", 2e8))),
+            stage=int(_val(zero, "stage", 2)),
+        )
+        if "train_batch_size" in cfg and cfg["train_batch_size"] != "auto":
+            world = cfg.get("world_size")
+            if world is not None and out.train_batch_size(int(world)) != int(cfg["train_batch_size"]):
+                raise ValueError("train_batch_size != micro batch x accumulation steps x world size")
+        return out

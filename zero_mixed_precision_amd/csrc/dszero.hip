@@ -1,0 +1,806 @@
+// dszero.hip -- gfx950 (MI355X) kernels and C ABI of the ZeRO mixed-precision
+// optimizer step.  Declarations, argument meaning and error behaviour are in
+// include/dszero.h.
+//
+// Pages cited (by title and section):
+//   [Guide]    "DeepSpeed complete guide" (youngju.dev, Japanese)
+//   [Overview] "DeepSpeed" project overview (aibars.net, Japanese), core features
+//
+// Every kernel here is a single streaming pass over HBM: the step moves
+// 28 bytes per element (fp16 gradient + fp32 master/m/v in, fp32 master/m/v +
+// fp16 copy out) for a handful of fp32 operations, so the design goals are
+// full-width coalesced accesses and enough bytes in flight per CU, not ALU
+// throughput.  Elements are handled in quads of four: each lane moves one
+// 16-byte vector per fp32 array (8 bytes per fp16 array) per quad, so every
+// wave-wide load or store covers one contiguous 1 KiB (fp32) or 512 B (fp16)
+// span.  Grids are grid-stride over quads; each lane keeps U quads in flight.
+//
+// Numerics: IEEE fp32, round to nearest even, one rounding per operation in
+// the written order (built with -ffp-contract=off; fp32 division and square
+// root are the correctly rounded forms); the bias-correction factors are
+// evaluated in fp64 and rounded once; fp16 <-> fp32 conversions are the
+// hardware's exact widening and round-to-nearest-even narrowing.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cmath>
+#include <cstdint>
+#include <cstdlib>
+#include <cstring>
+
+#include "dszero.h"
+
+#pragma clang fp contract(off)
+
+static_assert(sizeof(ds_scaler) == 64, "ds_scaler must stay 64 bytes");
+
+namespace {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kBlock = 256;  // 4 waves of 64
+
+// ---------------------------------------------------------------------------
+// memory helpers
+// ---------------------------------------------------------------------------
+
+template <bool NT, typename T>
+__device__ __forceinline__ T load(const T* p)
+{
+    if constexpr (NT)
+        return __builtin_nontemporal_load(p);
+    else
+        return *p;
+}
+
+template <bool NT, typename T>
+__device__ __forceinline__ void store(T* p, T v)
+{
+    if constexpr (NT)
+        __builtin_nontemporal_store(v, p);
+    else
+        *p = v;
+}
+
+__device__ __forceinline__ float h2f(uint32_t bits)
+{
+    return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(bits)));
+}
+
+__device__ __forceinline__ uint32_t f2h(float x)
+{
+    return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<_Float16>(x)));
+}
+
+__device__ __forceinline__ f32x4 widen4(u32x2 w)
+{
+    return f32x4{h2f(w.x & 0xFFFFu), h2f(w.x >> 16), h2f(w.y & 0xFFFFu), h2f(w.y >> 16)};
+}
+
+__device__ __forceinline__ u32x2 narrow4(f32x4 p)
+{
+    return u32x2{f2h(p.x) | (f2h(p.y) << 16), f2h(p.z) | (f2h(p.w) << 16)};
+}
+
+// Non-finite tests on raw bits: an exponent field of all ones is +-inf or NaN.
+// Adding one unit to an all-ones exponent carries into the sign position, and
+// into nothing else, so one add and one mask test both halves of a word.
+__device__ __forceinline__ uint32_t nonfinite_f16x2(uint32_t w)
+{
+    return ((w & 0x7C007C00u) + 0x04000400u) & 0x80008000u;
+}
+
+__device__ __forceinline__ uint32_t nonfinite_f32(uint32_t w)
+{
+    return ((w & 0x7F800000u) + 0x00800000u) & 0x80000000u;
+}
+
+__device__ __forceinline__ uint32_t nonfinite_f32x4(f32x4 x)
+{
+    return nonfinite_f32(__float_as_uint(x.x)) | nonfinite_f32(__float_as_uint(x.y)) |
+           nonfinite_f32(__float_as_uint(x.z)) | nonfinite_f32(__float_as_uint(x.w));
+}
+
+// One atomic OR per wave that saw a non-finite value, issued by the lowest
+// lane that saw one.
+__device__ __forceinline__ void raise_flag(ds_scaler* st, uint32_t bad)
+{
+    const uint64_t mask = __ballot(bad != 0u);
+    if (mask != 0ull && __lane_id() == static_cast<unsigned>(__ffsll(static_cast<long long>(mask)) - 1))
+        atomicOr(&st->overflow, 1u);
+}
+
+// ---------------------------------------------------------------------------
+// Adam
+// ---------------------------------------------------------------------------
+
+struct AdamHyper {
+    float lr, beta1, beta2, eps, weight_decay;
+    int32_t accum_steps;
+};
+
+struct AdamConsts {
+    float inv;        // 1 / (S * K)
+    float b1, b2;     // beta1, beta2
+    float omb1, omb2; // 1 - beta1, 1 - beta2
+    float lrwd;       // lr * weight_decay
+    float step_size;  // lr / (1 - beta1^t)
+    float rbc2;       // 1 / sqrt(1 - beta2^t)
+    float eps;
+};
+
+// beta1^t and beta2^t by binary exponentiation over the bits of t, least
+// significant first (fp64 multiplies only), then the two bias-correction
+// factors in fp64, each rounded once to fp32.
+__device__ __forceinline__ void bias_scalars(int64_t t, float lr, float beta1, float beta2,
+                                             float* step_size, float* rbc2)
+{
+    double r1 = 1.0, r2 = 1.0, x1 = static_cast<double>(beta1), x2 = static_cast<double>(beta2);
+    for (int64_t e = t; e > 0; e >>= 1) {
+        if (e & 1) {
+            r1 = r1 * x1;
+            r2 = r2 * x2;
+        }
+        x1 = x1 * x1;
+        x2 = x2 * x2;
+    }
+    *step_size = static_cast<float>(static_cast<double>(lr) / (1.0 - r1));
+    *rbc2 = static_cast<float>(1.0 / sqrt(1.0 - r2));
+}
+
+__device__ __forceinline__ AdamConsts make_consts(float scale, int64_t t, const AdamHyper& h)
+{
+    AdamConsts c;
+    c.inv = 1.0f / (scale * static_cast<float>(h.accum_steps));
+    c.b1 = h.beta1;
+    c.b2 = h.beta2;
+    c.omb1 = 1.0f - h.beta1;
+    c.omb2 = 1.0f - h.beta2;
+    c.lrwd = h.lr * h.weight_decay;
+    c.eps = h.eps;
+    bias_scalars(t, h.lr, h.beta1, h.beta2, &c.step_size, &c.rbc2);
+    return c;
+}
+
+// One element, [Guide] section 2 state: fp32 master p, moments m and v.
+template <bool WD>
+__device__ __forceinline__ void adam1(float graw, float& p, float& m, float& v, const AdamConsts& c)
+{
+    const float g = graw * c.inv;
+    const float m1 = c.b1 * m;
+    const float m2 = c.omb1 * g;
+    m = m1 + m2;
+    const float gg = g * g;
+    const float v1 = c.b2 * v;
+    const float v2 = c.omb2 * gg;
+    v = v1 + v2;
+    if constexpr (WD) {
+        const float decay = c.lrwd * p;
+        p = p - decay;
+    }
+    const float root = sqrtf(v);
+    const float den0 = root * c.rbc2;
+    const float den = den0 + c.eps;
+    const float ratio = m / den;
+    const float delta = c.step_size * ratio;
+    p = p - delta;
+}
+
+template <bool WD>
+__device__ __forceinline__ void adam4(const f32x4& g, f32x4& p, f32x4& m, f32x4& v, const AdamConsts& c)
+{
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        float pk = p[k], mk = m[k], vk = v[k];
+        adam1<WD>(g[k], pk, mk, vk, c);
+        p[k] = pk;
+        m[k] = mk;
+        v[k] = vk;
+    }
+}
+
+template <bool F32G, bool NT>
+__device__ __forceinline__ f32x4 load_grad4(const void* grad, int64_t q)
+{
+    if constexpr (F32G)
+        return load<NT>(static_cast<const f32x4*>(grad) + q);
+    else
+        return widen4(load<NT>(static_cast<const u32x2*>(grad) + q));
+}
+
+template <bool F32G>
+__device__ __forceinline__ float load_grad1(const void* grad, int64_t i)
+{
+    if constexpr (F32G)
+        return static_cast<const float*>(grad)[i];
+    else
+        return h2f(static_cast<const uint16_t*>(grad)[i]);
+}
+
+// Gated fused step: if the step's overflow flag is set, return before any
+// write; else update every element of [0, n) once.
+template <bool F32G, bool WD, bool NT, int U>
+__global__ __launch_bounds__(kBlock) void adam_kernel(const ds_scaler* __restrict__ st,
+                                                      float* __restrict__ master,
+                                                      float* __restrict__ mom1,
+                                                      float* __restrict__ mom2,
+                                                      uint16_t* __restrict__ p16,
+                                                      const void* __restrict__ grad, int64_t n,
+                                                      AdamHyper hp)
+{
+    if (st->overflow != 0u)
+        return;
+    const AdamConsts c = make_consts(st->scale, st->step + 1, hp);
+
+    f32x4* P = reinterpret_cast<f32x4*>(master);
+    f32x4* M = reinterpret_cast<f32x4*>(mom1);
+    f32x4* V = reinterpret_cast<f32x4*>(mom2);
+    u32x2* H = reinterpret_cast<u32x2*>(p16);
+
+    const int64_t nq = n >> 2;
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * kBlock;
+    int64_t q = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x;
+
+    for (; q + (U - 1) * stride < nq; q += U * stride) {
+        f32x4 g[U], p[U], m[U], v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t i = q + u * stride;
+            g[u] = load_grad4<F32G, NT>(grad, i);
+            p[u] = load<NT>(P + i);
+            m[u] = load<NT>(M + i);
+            v[u] = load<NT>(V + i);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t i = q + u * stride;
+            adam4<WD>(g[u], p[u], m[u], v[u], c);
+            store<NT>(P + i, p[u]);
+            store<NT>(M + i, m[u]);
+            store<NT>(V + i, v[u]);
+            store<NT>(H + i, narrow4(p[u]));
+        }
+    }
+    for (; q < nq; q += stride) {
+        f32x4 g = load_grad4<F32G, NT>(grad, q);
+        f32x4 p = load<NT>(P + q), m = load<NT>(M + q), v = load<NT>(V + q);
+        adam4<WD>(g, p, m, v, c);
+        store<NT>(P + q, p);
+        store<NT>(M + q, m);
+        store<NT>(V + q, v);
+        store<NT>(H + q, narrow4(p));
+    }
+    // the last n % 4 elements
+    if (blockIdx.x == 0 && static_cast<int64_t>(threadIdx.x) < (n & 3)) {
+        const int64_t i = (nq << 2) + threadIdx.x;
+        float p = master[i], m = mom1[i], v = mom2[i];
+        adam1<WD>(load_grad1<F32G>(grad, i), p, m, v, c);
+        master[i] = p;
+        mom1[i] = m;
+        mom2[i] = v;
+        p16[i] = static_cast<uint16_t>(f2h(p));
+    }
+}
+
+__global__ void bias_scalars_kernel(const ds_scaler* st, float lr, float beta1, float beta2, float* out2)
+{
+    float a, b;
+    bias_scalars(st->step + 1, lr, beta1, beta2, &a, &b);
+    out2[0] = a;
+    out2[1] = b;
+}
+
+// ---------------------------------------------------------------------------
+// overflow check
+// ---------------------------------------------------------------------------
+
+// fp16: 8 elements per 16-byte vector; fp32: 4.
+template <bool F32, bool NT, int U>
+__global__ __launch_bounds__(kBlock) void check_kernel(ds_scaler* __restrict__ st,
+                                                       const void* __restrict__ grad, int64_t n)
+{
+    if (st->overflow != 0u)
+        return;  // already decided for this step
+    constexpr int kPer = F32 ? 4 : 8;
+    const u32x4* G = static_cast<const u32x4*>(grad);
+    const int64_t nv = n / kPer;
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * kBlock;
+    int64_t q = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x;
+    uint32_t bad = 0u;
+    for (; q + (U - 1) * stride < nv; q += U * stride) {
+        u32x4 w[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            w[u] = load<NT>(G + q + u * stride);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if constexpr (F32)
+                bad |= nonfinite_f32(w[u].x) | nonfinite_f32(w[u].y) | nonfinite_f32(w[u].z) |
+                       nonfinite_f32(w[u].w);
+            else
+                bad |= nonfinite_f16x2(w[u].x) | nonfinite_f16x2(w[u].y) | nonfinite_f16x2(w[u].z) |
+                       nonfinite_f16x2(w[u].w);
+        }
+    }
+    for (; q < nv; q += stride) {
+        const u32x4 w = load<NT>(G + q);
+        if constexpr (F32)
+            bad |= nonfinite_f32(w.x) | nonfinite_f32(w.y) | nonfinite_f32(w.z) | nonfinite_f32(w.w);
+        else
+            bad |= nonfinite_f16x2(w.x) | nonfinite_f16x2(w.y) | nonfinite_f16x2(w.z) |
+                   nonfinite_f16x2(w.w);
+    }
+    if (blockIdx.x == 0 && static_cast<int64_t>(threadIdx.x) < n - nv * kPer) {
+        const int64_t i = nv * kPer + threadIdx.x;
+        if constexpr (F32)
+            bad |= nonfinite_f32(static_cast<const uint32_t*>(grad)[i]);
+        else
+            bad |= nonfinite_f16x2(static_cast<const uint16_t*>(grad)[i]);
+    }
+    raise_flag(st, bad);
+}
+
+// ---------------------------------------------------------------------------
+// gradient accumulation
+// ---------------------------------------------------------------------------
+
+template <bool OVERWRITE, bool CHECK, bool NT, int U>
+__global__ __launch_bounds__(kBlock) void accumulate_kernel(float* __restrict__ acc,
+                                                            const uint16_t* __restrict__ g16,
+                                                            int64_t n, ds_scaler* __restrict__ st)
+{
+    f32x4* A = reinterpret_cast<f32x4*>(acc);
+    const u32x2* G = reinterpret_cast<const u32x2*>(g16);
+    const int64_t nq = n >> 2;
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * kBlock;
+    int64_t q = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x;
+    uint32_t bad = 0u;
+    for (; q + (U - 1) * stride < nq; q += U * stride) {
+        f32x4 g[U], a[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            g[u] = widen4(load<NT>(G + q + u * stride));
+            if constexpr (!OVERWRITE)
+                a[u] = load<NT>(A + q + u * stride);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            f32x4 r;
+            if constexpr (OVERWRITE)
+                r = g[u];
+            else
+                r = a[u] + g[u];
+            if constexpr (CHECK)
+                bad |= nonfinite_f32x4(r);
+            store<NT>(A + q + u * stride, r);
+        }
+    }
+    for (; q < nq; q += stride) {
+        const f32x4 g = widen4(load<NT>(G + q));
+        f32x4 r;
+        if constexpr (OVERWRITE)
+            r = g;
+        else
+            r = load<NT>(A + q) + g;
+        if constexpr (CHECK)
+            bad |= nonfinite_f32x4(r);
+        store<NT>(A + q, r);
+    }
+    if (blockIdx.x == 0 && static_cast<int64_t>(threadIdx.x) < (n & 3)) {
+        const int64_t i = (nq << 2) + threadIdx.x;
+        const float g = h2f(g16[i]);
+        const float r = OVERWRITE ? g : acc[i] + g;
+        if constexpr (CHECK)
+            bad |= nonfinite_f32(__float_as_uint(r));
+        acc[i] = r;
+    }
+    if constexpr (CHECK)
+        raise_flag(st, bad);
+}
+
+// ---------------------------------------------------------------------------
+// loss-scaler state machine ([Guide] section 4.2), one work-item
+// ---------------------------------------------------------------------------
+
+__global__ void update_scale_kernel(ds_scaler* st)
+{
+    ds_scaler s = *st;
+    const uint32_t ov = s.overflow != 0u ? 1u : 0u;
+    s.iter += 1;
+    if (ov) {
+        s.skipped += 1;
+        s.growth_count = 0;
+        if (s.dynamic) {
+            if (s.hysteresis_left <= 1) {
+                const float half = s.scale * 0.5f;
+                s.scale = half > s.min_scale ? half : s.min_scale;
+                s.hysteresis_left = s.hysteresis;
+            } else {
+                s.hysteresis_left -= 1;
+            }
+        }
+    } else {
+        s.step += 1;
+        if (s.dynamic) {
+            if (s.consecutive_hysteresis)
+                s.hysteresis_left = s.hysteresis;
+            s.growth_count += 1;
+            if (s.growth_count == s.growth_window) {
+                s.scale = s.scale * 2.0f;
+                s.growth_count = 0;
+            }
+        }
+    }
+    s.last_overflow = ov;
+    s.overflow = 0u;
+    *st = s;
+}
+
+__global__ void write_state_kernel(ds_scaler* st, ds_scaler value) { *st = value; }
+
+// ---------------------------------------------------------------------------
+// host helpers
+// ---------------------------------------------------------------------------
+
+int cu_count()
+{
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0)
+        return 256;
+    if (dev < 64) {
+        int c = cache[dev].load(std::memory_order_relaxed);
+        if (c > 0)
+            return c;
+    }
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+        cus = 256;
+    if (dev < 64)
+        cache[dev].store(cus, std::memory_order_relaxed);
+    return cus;
+}
+
+long env_long(const char* name, long dflt)
+{
+    const char* s = std::getenv(name);
+    if (s == nullptr || *s == '\0')
+        return dflt;
+    char* end = nullptr;
+    long v = std::strtol(s, &end, 10);
+    return (end != s) ? v : dflt;
+}
+
+// Blocks for a grid-stride launch over `items` per-lane work items:
+// enough to cover the work once, capped at blocks_per_cu per compute unit.
+// DSZERO_GRID pins the block count (grid-size invariance tests, sweeps);
+// DSZERO_BLOCKS_PER_CU changes the cap.
+unsigned grid_blocks(int64_t items)
+{
+    const long forced = env_long("DSZERO_GRID", 0);
+    if (forced > 0)
+        return static_cast<unsigned>(forced > 1048576 ? 1048576 : forced);
+    const long per_cu = env_long("DSZERO_BLOCKS_PER_CU", 8);
+    int64_t need = (items + kBlock - 1) / kBlock;
+    int64_t cap = static_cast<int64_t>(cu_count()) * (per_cu > 0 ? per_cu : 8);
+    if (need > cap)
+        need = cap;
+    if (need < 1)
+        need = 1;
+    return static_cast<unsigned>(need);
+}
+
+int variant_unroll() { return static_cast<int>(env_long("DSZERO_UNROLL", 2)); }
+bool variant_nt() { return env_long("DSZERO_NT", 0) != 0; }
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+bool overlap(const void* a, uint64_t abytes, const void* b, uint64_t bbytes)
+{
+    if (a == nullptr || b == nullptr || abytes == 0 || bbytes == 0)
+        return false;
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+    return a0 < b0 + bbytes && b0 < a0 + abytes;
+}
+
+bool finite_ge0(float x) { return std::isfinite(x) && x >= 0.0f; }
+bool beta_ok(float b) { return std::isfinite(b) && b >= 0.0f && b < 1.0f; }
+
+ds_status launched()
+{
+    return hipGetLastError() == hipSuccess ? DS_OK : DS_ERR_HIP;
+}
+
+template <bool F32G, bool WD, bool NT>
+void launch_adam_u(int unroll, unsigned blocks, hipStream_t s, const ds_scaler* st, float* master,
+                   float* m, float* v, uint16_t* p16, const void* grad, int64_t n, const AdamHyper& hp)
+{
+    switch (unroll) {
+    case 1: adam_kernel<F32G, WD, NT, 1><<<blocks, kBlock, 0, s>>>(st, master, m, v, p16, grad, n, hp); break;
+    case 4: adam_kernel<F32G, WD, NT, 4><<<blocks, kBlock, 0, s>>>(st, master, m, v, p16, grad, n, hp); break;
+    default: adam_kernel<F32G, WD, NT, 2><<<blocks, kBlock, 0, s>>>(st, master, m, v, p16, grad, n, hp); break;
+    }
+}
+
+template <bool F32G, bool WD>
+void launch_adam_nt(bool nt, int unroll, unsigned blocks, hipStream_t s, const ds_scaler* st,
+                    float* master, float* m, float* v, uint16_t* p16, const void* grad, int64_t n,
+                    const AdamHyper& hp)
+{
+    if (nt)
+        launch_adam_u<F32G, WD, true>(unroll, blocks, s, st, master, m, v, p16, grad, n, hp);
+    else
+        launch_adam_u<F32G, WD, false>(unroll, blocks, s, st, master, m, v, p16, grad, n, hp);
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// C ABI
+// ---------------------------------------------------------------------------
+
+extern "C" {
+
+size_t ds_scaler_size(void) { return sizeof(ds_scaler); }
+
+const char* ds_status_string(ds_status s)
+{
+    switch (s) {
+    case DS_OK: return "DS_OK";
+    case DS_ERR_NULL: return "DS_ERR_NULL: null pointer";
+    case DS_ERR_SIZE: return "DS_ERR_SIZE: invalid size";
+    case DS_ERR_ALIGN: return "DS_ERR_ALIGN: pointer not aligned";
+    case DS_ERR_DTYPE: return "DS_ERR_DTYPE: unknown dtype";
+    case DS_ERR_HPARAM: return "DS_ERR_HPARAM: hyperparameter out of range";
+    case DS_ERR_ALIAS: return "DS_ERR_ALIAS: arrays overlap";
+    case DS_ERR_HIP: return "DS_ERR_HIP: HIP launch or copy failed";
+    }
+    return "unknown ds_status";
+}
+
+ds_status ds_state_init(ds_scaler* st, float init_scale, float min_scale, int32_t growth_window,
+                        int32_t hysteresis, int32_t consecutive_hysteresis, int32_t dynamic,
+                        void* stream)
+{
+    if (st == nullptr)
+        return DS_ERR_NULL;
+    if (!aligned(st, 8))
+        return DS_ERR_ALIGN;
+    if (!std::isfinite(init_scale) || init_scale <= 0.0f || !std::isfinite(min_scale) ||
+        min_scale <= 0.0f || growth_window < 1 || hysteresis < 1)
+        return DS_ERR_HPARAM;
+    ds_scaler s;
+    std::memset(&s, 0, sizeof s);
+    s.scale = init_scale;
+    s.min_scale = min_scale;
+    s.growth_window = growth_window;
+    s.hysteresis = hysteresis;
+    s.hysteresis_left = hysteresis;
+    s.dynamic = dynamic ? 1 : 0;
+    s.consecutive_hysteresis = consecutive_hysteresis ? 1 : 0;
+    write_state_kernel<<<1, 1, 0, static_cast<hipStream_t>(stream)>>>(st, s);
+    return launched();
+}
+
+ds_status ds_state_read(const ds_scaler* st, ds_scaler* host_out, void* stream)
+{
+    if (st == nullptr || host_out == nullptr)
+        return DS_ERR_NULL;
+    if (!aligned(st, 8))
+        return DS_ERR_ALIGN;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (hipMemcpyAsync(host_out, st, sizeof(ds_scaler), hipMemcpyDeviceToHost, s) != hipSuccess)
+        return DS_ERR_HIP;
+    return hipStreamSynchronize(s) == hipSuccess ? DS_OK : DS_ERR_HIP;
+}
+
+ds_status ds_state_write(ds_scaler* st, const ds_scaler* host_in, void* stream)
+{
+    if (st == nullptr || host_in == nullptr)
+        return DS_ERR_NULL;
+    if (!aligned(st, 8))
+        return DS_ERR_ALIGN;
+    write_state_kernel<<<1, 1, 0, static_cast<hipStream_t>(stream)>>>(st, *host_in);
+    return launched();
+}
+
+ds_status ds_accumulate(float* acc, const uint16_t* g16, int64_t n, int32_t overwrite,
+                        ds_scaler* st_or_null, void* stream)
+{
+    if (n < 0)
+        return DS_ERR_SIZE;
+    if (n == 0)
+        return DS_OK;
+    if (acc == nullptr || g16 == nullptr)
+        return DS_ERR_NULL;
+    if (!aligned(acc, 16) || !aligned(g16, 16) || (st_or_null != nullptr && !aligned(st_or_null, 8)))
+        return DS_ERR_ALIGN;
+    const uint64_t un = static_cast<uint64_t>(n);
+    if (overlap(acc, 4 * un, g16, 2 * un) || overlap(acc, 4 * un, st_or_null, sizeof(ds_scaler)) ||
+        overlap(g16, 2 * un, st_or_null, sizeof(ds_scaler)))
+        return DS_ERR_ALIAS;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const unsigned blocks = grid_blocks((n >> 2) > 0 ? (n >> 2) : 1);
+    const bool nt = variant_nt();
+    const bool ow = overwrite != 0, ck = st_or_null != nullptr;
+#define DS_ACC(OW, CK, NT) accumulate_kernel<OW, CK, NT, 4><<<blocks, kBlock, 0, s>>>(acc, g16, n, st_or_null)
+    if (nt) {
+        if (ow) { if (ck) DS_ACC(true, true, true); else DS_ACC(true, false, true); }
+        else    { if (ck) DS_ACC(false, true, true); else DS_ACC(false, false, true); }
+    } else {
+        if (ow) { if (ck) DS_ACC(true, true, false); else DS_ACC(true, false, false); }
+        else    { if (ck) DS_ACC(false, true, false); else DS_ACC(false, false, false); }
+    }
+#undef DS_ACC
+    return launched();
+}
+
+ds_status ds_check_overflow(ds_scaler* st, const void* grad, ds_dtype dt, int64_t n, void* stream)
+{
+    if (n < 0)
+        return DS_ERR_SIZE;
+    if (dt != DS_FP16 && dt != DS_FP32)
+        return DS_ERR_DTYPE;
+    if (st == nullptr)
+        return DS_ERR_NULL;
+    if (n == 0)
+        return DS_OK;
+    if (grad == nullptr)
+        return DS_ERR_NULL;
+    if (!aligned(grad, 16) || !aligned(st, 8))
+        return DS_ERR_ALIGN;
+    const uint64_t es = dt == DS_FP16 ? 2 : 4;
+    if (overlap(grad, es * static_cast<uint64_t>(n), st, sizeof(ds_scaler)))
+        return DS_ERR_ALIAS;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int64_t vecs = n / (dt == DS_FP16 ? 8 : 4);
+    const unsigned blocks = grid_blocks(vecs > 0 ? vecs : 1);
+    const bool nt = variant_nt();
+    if (dt == DS_FP16) {
+        if (nt) check_kernel<false, true, 4><<<blocks, kBlock, 0, s>>>(st, grad, n);
+        else    check_kernel<false, false, 4><<<blocks, kBlock, 0, s>>>(st, grad, n);
+    } else {
+        if (nt) check_kernel<true, true, 4><<<blocks, kBlock, 0, s>>>(st, grad, n);
+        else    check_kernel<true, false, 4><<<blocks, kBlock, 0, s>>>(st, grad, n);
+    }
+    return launched();
+}
+
+ds_status ds_adam_step(const ds_scaler* st, float* master, float* m, float* v, uint16_t* p16,
+                       const void* grad, ds_dtype dt, int64_t n, float lr, float beta1,
+                       float beta2, float eps, float weight_decay, int32_t accum_steps,
+                       void* stream)
+{
+    if (n < 0)
+        return DS_ERR_SIZE;
+    if (dt != DS_FP16 && dt != DS_FP32)
+        return DS_ERR_DTYPE;
+    if (!finite_ge0(lr) || !beta_ok(beta1) || !beta_ok(beta2) || !std::isfinite(eps) || eps <= 0.0f ||
+        !finite_ge0(weight_decay) || accum_steps < 1)
+        return DS_ERR_HPARAM;
+    if (st == nullptr)
+        return DS_ERR_NULL;
+    if (n == 0)
+        return DS_OK;
+    if (master == nullptr || m == nullptr || v == nullptr || p16 == nullptr || grad == nullptr)
+        return DS_ERR_NULL;
+    if (!aligned(master, 16) || !aligned(m, 16) || !aligned(v, 16) || !aligned(p16, 16) ||
+        !aligned(grad, 16) || !aligned(st, 8))
+        return DS_ERR_ALIGN;
+    const uint64_t un = static_cast<uint64_t>(n);
+    const void* ptrs[6] = {master, m, v, p16, grad, st};
+    const uint64_t sizes[6] = {4 * un, 4 * un, 4 * un, 2 * un, (dt == DS_FP16 ? 2 : 4) * un,
+                               sizeof(ds_scaler)};
+    for (int i = 0; i < 6; ++i)
+        for (int j = i + 1; j < 6; ++j)
+            if (overlap(ptrs[i], sizes[i], ptrs[j], sizes[j]))
+                return DS_ERR_ALIAS;
+
+    const AdamHyper hp{lr, beta1, beta2, eps, weight_decay, accum_steps};
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int unroll = variant_unroll();
+    const unsigned blocks = grid_blocks((n >> 2) > 0 ? (n >> 2) : 1);
+    const bool nt = variant_nt();
+    const bool wd = weight_decay != 0.0f;
+    if (dt == DS_FP16) {
+        if (wd) launch_adam_nt<false, true>(nt, unroll, blocks, s, st, master, m, v, p16, grad, n, hp);
+        else    launch_adam_nt<false, false>(nt, unroll, blocks, s, st, master, m, v, p16, grad, n, hp);
+    } else {
+        if (wd) launch_adam_nt<true, true>(nt, unroll, blocks, s, st, master, m, v, p16, grad, n, hp);
+        else    launch_adam_nt<true, false>(nt, unroll, blocks, s, st, master, m, v, p16, grad, n, hp);
+    }
+    return launched();
+}
+
+ds_status ds_update_loss_scale(ds_scaler* st, void* stream)
+{
+    if (st == nullptr)
+        return DS_ERR_NULL;
+    if (!aligned(st, 8))
+        return DS_ERR_ALIGN;
+    update_scale_kernel<<<1, 1, 0, static_cast<hipStream_t>(stream)>>>(st);
+    return launched();
+}
+
+ds_status ds_adam_bias_scalars(const ds_scaler* st, float lr, float beta1, float beta2, float* out2,
+                               void* stream)
+{
+    if (st == nullptr || out2 == nullptr)
+        return DS_ERR_NULL;
+    if (!aligned(st, 8) || !aligned(out2, 8))
+        return DS_ERR_ALIGN;
+    if (!finite_ge0(lr) || !beta_ok(beta1) || !beta_ok(beta2))
+        return DS_ERR_HPARAM;
+    if (overlap(st, sizeof(ds_scaler), out2, 2 * sizeof(float)))
+        return DS_ERR_ALIAS;
+    bias_scalars_kernel<<<1, 1, 0, static_cast<hipStream_t>(stream)>>>(st, lr, beta1, beta2, out2);
+    return launched();
+}
+
+ds_status ds_layout_greedy(const int64_t* numels, int32_t count, int64_t cap, int64_t align,
+                           int64_t* offsets, int32_t* bucket_of, int64_t* bucket_start,
+                           int64_t* bucket_size, int32_t* n_buckets, int64_t* total)
+{
+    if (count < 0 || cap < 1 || align < 1)
+        return DS_ERR_SIZE;
+    if (n_buckets == nullptr || total == nullptr)
+        return DS_ERR_NULL;
+    if (count > 0 && (numels == nullptr || offsets == nullptr || bucket_of == nullptr ||
+                      bucket_start == nullptr || bucket_size == nullptr))
+        return DS_ERR_NULL;
+    for (int32_t i = 0; i < count; ++i)
+        if (numels[i] < 0)
+            return DS_ERR_SIZE;
+    auto up = [align](int64_t x) { return (x + align - 1) / align * align; };
+    int32_t nb = 0;
+    int64_t start = 0;     // first element of the open bucket
+    int64_t end = 0;       // end of the last tensor placed (unpadded)
+    int32_t members = 0;   // tensors in the open bucket
+    for (int32_t i = 0; i < count; ++i) {
+        int64_t off = up(end);
+        if (members > 0 && up(off + numels[i]) - start > cap) {
+            bucket_start[nb] = start;
+            bucket_size[nb] = up(end) - start;
+            ++nb;
+            start = up(end);
+            off = start;
+            members = 0;
+        }
+        offsets[i] = off;
+        bucket_of[i] = nb;
+        end = off + numels[i];
+        ++members;
+    }
+    if (members > 0) {
+        bucket_start[nb] = start;
+        bucket_size[nb] = up(end) - start;
+        ++nb;
+    }
+    *n_buckets = nb;
+    *total = up(end);
+    return DS_OK;
+}
+
+ds_status ds_partition_range(int64_t total, int32_t world, int32_t rank, int64_t align, int64_t* start,
+                             int64_t* count)
+{
+    if (total < 0 || world < 1 || rank < 0 || rank >= world || align < 1)
+        return DS_ERR_SIZE;
+    if (start == nullptr || count == nullptr)
+        return DS_ERR_NULL;
+    int64_t per = (total + world - 1) / world;
+    per = (per + align - 1) / align * align;
+    int64_t s0 = static_cast<int64_t>(rank) * per;
+    if (s0 > total)
+        s0 = total;
+    int64_t c = total - s0;
+    if (c > per)
+        c = per;
+    *start = s0;
+    *count = c;
+    return DS_OK;
+}
+
+}  // extern "C"

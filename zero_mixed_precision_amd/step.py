@@ -1,0 +1,69 @@
+"""ShardStep: one rank's ZeRO optimizer step over its flat partition.
+
+Owns the partition's device arrays (torch tensors used as memory only) and the
+device-resident loss-scaler state, and issues the per-step call sequence of
+the C ABI on one HIP stream ("DeepSpeed complete guide" section 5.1: backward
+scales and accumulates, step() updates):
+
+    K > 1:  ds_accumulate per bucket for micro-batches 1..K (the last one also
+            checks for inf/NaN), then ds_adam_step on the fp32 buffer
+    K = 1:  ds_check_overflow on the fp16 gradient, then ds_adam_step on it
+    then    ds_update_loss_scale (once)
+
+No call synchronises the host; ``scaler()`` reads the state back (one copy).
+"""
+from __future__ import annotations
+
+from . import _lib
+from .config import ZeroMPConfig
+
+
+class ShardStep:
+    def __init__(self, n: int, cfg: ZeroMPConfig, device="cuda", buckets=None, stream=None):
+        import torch
+
+        self.torch, self.n, self.cfg = torch, int(n), cfg
+        self.K = int(cfg.gradient_accumulation_steps)
+        self.stream = stream
+        f32 = dict(dtype=torch.float32, device=device)
+        self.master = torch.empty(self.n, **f32)
+        self.m = torch.zeros(self.n, **f32)
+        self.v = torch.zeros(self.n, **f32)
+        self.p16 = torch.empty(self.n, dtype=torch.float16, device=device)
+        self.acc = torch.empty(self.n, **f32) if self.K > 1 else None
+        self.state = torch.zeros(64, dtype=torch.uint8, device=device)
+        # accumulation granularity: the reduce buckets inside this partition
+        self.buckets = [(b.start, b.size) for b in buckets] if buckets else [(0, self.n)]
+        self._micro = 0
+        _lib.ds_state_init(self.state, cfg.init_scale, cfg.min_loss_scale, cfg.loss_scale_window,
+                           cfg.hysteresis, int(cfg.consecutive_hysteresis), int(cfg.dynamic),
+                           self.stream)
+
+    def accumulate(self, g16) -> None:
+        """Add one fp16 micro-batch gradient (K > 1); the K-th call also checks it."""
+        assert self.K > 1 and g16.numel() == self.n
+        k = self._micro
+        last = k == self.K - 1
+        for start, size in self.buckets:
+            _lib.ds_accumulate(self.acc.data_ptr() + 4 * start, g16.data_ptr() + 2 * start, size,
+                               overwrite=(k == 0), st_or_null=self.state if last else None,
+                               stream=self.stream)
+        self._micro = k + 1
+
+    def step(self, g16=None) -> None:
+        """Finish the step: check (K = 1), gated Adam, scaler update."""
+        c = self.cfg
+        if self.K == 1:
+            assert g16 is not None and g16.numel() == self.n
+            _lib.ds_check_overflow(self.state, g16, _lib.DS_FP16, self.n, self.stream)
+            grad, dt = g16, _lib.DS_FP16
+        else:
+            assert self._micro == self.K, "accumulate() must be called K times before step()"
+            grad, dt = self.acc, _lib.DS_FP32
+        _lib.ds_adam_step(self.state, self.master, self.m, self.v, self.p16, grad, dt, self.n, c.lr,
+                          c.betas[0], c.betas[1], c.eps, c.weight_decay, self.K, self.stream)
+        _lib.ds_update_loss_scale(self.state, self.stream)
+        self._micro = 0
+
+    def scaler(self) -> _lib.DsScaler:
+        return _lib.ds_state_read(self.state, self.stream)
