@@ -91,7 +91,8 @@ def gpu_run(args):
     else:
         buckets = [(0, n)]
 
-    # resident gradient buffers: one per (step, micro-batch) if they fit, else cycled
+    # resident gradient buffers, a ring of distinct draws (a real step rewrites one
+    # contiguous gradient buffer; the ring is larger than the 256 MB Infinity Cache)
     total_mb = (args.steps + args.warmup) * K
     free = torch.cuda.mem_get_info(dev)[0]
     fit = max(1, int((free - (4 << 30)) // (2 * n)))
@@ -297,7 +298,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="zero2_7b")
     ap.add_argument("--mode", default="step", choices=["step", "copy"])
-    ap.add_argument("--max-grad-buffers", type=int, default=64)
+    ap.add_argument("--max-grad-buffers", type=int, default=8)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--cpu-slice", type=int, default=1 << 24)
     ap.add_argument("--no-cpu-baseline", action="store_true")

@@ -39,9 +39,13 @@
  *    ds_adam_step calls (disjoint ranges, all reading the same state), then
  *    exactly one ds_update_loss_scale.  No host synchronisation is needed
  *    inside a step: the skip decision is taken on the device.
- *  - Thread safety: no mutable global state besides a per-device cache of the
- *    compute-unit count.  Calls that share a ds_scaler must be ordered on one
- *    stream.
+ *  - Thread safety: the library keeps no mutable global state.  Calls that
+ *    share a ds_scaler must be ordered on one stream.
+ *  - Launch-shape knobs, read from the environment at each call (for tests
+ *    and tuning; results are bit-identical under every setting):
+ *    DSZERO_GRID=<blocks> pins the block count, DSZERO_UNROLL=2|4 sets the
+ *    quads per lane of the read/write kernels, DSZERO_NT=0 turns off the
+ *    non-temporal load/store hints.
  */
 #ifndef DSZERO_H
 #define DSZERO_H

@@ -241,8 +241,8 @@ def test_grid_size_and_variant_invariance(torch):
     n = (1 << 20) + 3
     ref = _run_variant(torch, n, {})
     for env in [{"DSZERO_GRID": "1"}, {"DSZERO_GRID": "7"}, {"DSZERO_GRID": "100000"},
-                {"DSZERO_UNROLL": "1"}, {"DSZERO_UNROLL": "4"}, {"DSZERO_NT": "1"},
-                {"DSZERO_BLOCKS_PER_CU": "1"}, {}]:
+                {"DSZERO_UNROLL": "2"}, {"DSZERO_NT": "0"}, {"DSZERO_UNROLL": "2", "DSZERO_GRID": "3"},
+                {}]:
         got = _run_variant(torch, n, env)
         for a, b in zip(ref, got):
             assert np.array_equal(a.view(np.uint8), b.view(np.uint8)), env

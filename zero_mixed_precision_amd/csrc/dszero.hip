@@ -9,11 +9,18 @@
 // Every kernel here is a single streaming pass over HBM: the step moves
 // 28 bytes per element (fp16 gradient + fp32 master/m/v in, fp32 master/m/v +
 // fp16 copy out) for a handful of fp32 operations, so the design goals are
-// full-width coalesced accesses and enough bytes in flight per CU, not ALU
-// throughput.  Elements are handled in quads of four: each lane moves one
-// 16-byte vector per fp32 array (8 bytes per fp16 array) per quad, so every
-// wave-wide load or store covers one contiguous 1 KiB (fp32) or 512 B (fp16)
-// span.  Grids are grid-stride over quads; each lane keeps U quads in flight.
+// full-width coalesced accesses and the right amount of traffic in flight,
+// not ALU throughput.  Elements are handled in quads of four: each lane moves
+// one 16-byte vector per fp32 array (8 bytes per fp16 array) per quad, so
+// every wave-wide load or store covers one contiguous 1 KiB (fp32) or 512 B
+// (fp16) span.  The read/write kernels (Adam, accumulation) give each
+// 256-lane block one tile of U x 256 consecutive quads (U = 4: 4096
+// elements), issue all of the tile's loads before any arithmetic, and mark
+// loads and stores non-temporal (streamed data is touched once); the grid has
+// one block per tile.  Measured on MI355X with a 109M-element partition this
+// beats persistent grid-stride launches, whose extra waves per CU congest the
+// memory system under a 50/50 read/write mix.  The read-only overflow check
+// uses 1024-lane blocks, one 16-byte vector per lane.
 //
 // Numerics: IEEE fp32, round to nearest even, one rounding per operation in
 // the written order (built with -ffp-contract=off; fp32 division and square
@@ -22,7 +29,6 @@
 // hardware's exact widening and round-to-nearest-even narrowing.
 #include <hip/hip_runtime.h>
 
-#include <atomic>
 #include <cmath>
 #include <cstdint>
 #include <cstdlib>
@@ -40,7 +46,9 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kBlock = 256;  // 4 waves of 64
+constexpr int kStepBlock = 256;    // lanes per block of the read/write kernels
+constexpr int kCheckBlock = 1024;  // lanes per block of the read-only check
+constexpr int64_t kMaxBlocks = int64_t(1) << 22;
 
 // ---------------------------------------------------------------------------
 // memory helpers
@@ -220,15 +228,17 @@ __device__ __forceinline__ float load_grad1(const void* grad, int64_t i)
 }
 
 // Gated fused step: if the step's overflow flag is set, return before any
-// write; else update every element of [0, n) once.
-template <bool F32G, bool WD, bool NT, int U>
-__global__ __launch_bounds__(kBlock) void adam_kernel(const ds_scaler* __restrict__ st,
-                                                      float* __restrict__ master,
-                                                      float* __restrict__ mom1,
-                                                      float* __restrict__ mom2,
-                                                      uint16_t* __restrict__ p16,
-                                                      const void* __restrict__ grad, int64_t n,
-                                                      AdamHyper hp)
+// write; else update every element of [0, n) once.  Tiles of U x TPB quads are
+// dealt to blocks round-robin; block 0 also takes the quads of the last,
+// partial tile and the final n % 4 elements.
+template <bool F32G, bool WD, bool NT, int TPB, int U>
+__global__ __launch_bounds__(TPB) void adam_kernel(const ds_scaler* __restrict__ st,
+                                                   float* __restrict__ master,
+                                                   float* __restrict__ mom1,
+                                                   float* __restrict__ mom2,
+                                                   uint16_t* __restrict__ p16,
+                                                   const void* __restrict__ grad, int64_t n,
+                                                   AdamHyper hp)
 {
     if (st->overflow != 0u)
         return;
@@ -239,15 +249,15 @@ __global__ __launch_bounds__(kBlock) void adam_kernel(const ds_scaler* __restric
     f32x4* V = reinterpret_cast<f32x4*>(mom2);
     u32x2* H = reinterpret_cast<u32x2*>(p16);
 
+    constexpr int T = U * TPB;  // quads per tile
     const int64_t nq = n >> 2;
-    const int64_t stride = static_cast<int64_t>(gridDim.x) * kBlock;
-    int64_t q = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x;
-
-    for (; q + (U - 1) * stride < nq; q += U * stride) {
+    const int64_t ntiles = nq / T;
+    for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
+        const int64_t q0 = tile * T + threadIdx.x;
         f32x4 g[U], p[U], m[U], v[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int64_t i = q + u * stride;
+            const int64_t i = q0 + u * TPB;
             g[u] = load_grad4<F32G, NT>(grad, i);
             p[u] = load<NT>(P + i);
             m[u] = load<NT>(M + i);
@@ -255,7 +265,7 @@ __global__ __launch_bounds__(kBlock) void adam_kernel(const ds_scaler* __restric
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int64_t i = q + u * stride;
+            const int64_t i = q0 + u * TPB;
             adam4<WD>(g[u], p[u], m[u], v[u], c);
             store<NT>(P + i, p[u]);
             store<NT>(M + i, m[u]);
@@ -263,7 +273,9 @@ __global__ __launch_bounds__(kBlock) void adam_kernel(const ds_scaler* __restric
             store<NT>(H + i, narrow4(p[u]));
         }
     }
-    for (; q < nq; q += stride) {
+    if (blockIdx.x != 0)
+        return;
+    for (int64_t q = ntiles * T + threadIdx.x; q < nq; q += TPB) {
         f32x4 g = load_grad4<F32G, NT>(grad, q);
         f32x4 p = load<NT>(P + q), m = load<NT>(M + q), v = load<NT>(V + q);
         adam4<WD>(g, p, m, v, c);
@@ -272,8 +284,7 @@ __global__ __launch_bounds__(kBlock) void adam_kernel(const ds_scaler* __restric
         store<NT>(V + q, v);
         store<NT>(H + q, narrow4(p));
     }
-    // the last n % 4 elements
-    if (blockIdx.x == 0 && static_cast<int64_t>(threadIdx.x) < (n & 3)) {
+    if (static_cast<int64_t>(threadIdx.x) < (n & 3)) {
         const int64_t i = (nq << 2) + threadIdx.x;
         float p = master[i], m = mom1[i], v = mom2[i];
         adam1<WD>(load_grad1<F32G>(grad, i), p, m, v, c);
@@ -296,35 +307,20 @@ __global__ void bias_scalars_kernel(const ds_scaler* st, float lr, float beta1, 
 // overflow check
 // ---------------------------------------------------------------------------
 
-// fp16: 8 elements per 16-byte vector; fp32: 4.
-template <bool F32, bool NT, int U>
-__global__ __launch_bounds__(kBlock) void check_kernel(ds_scaler* __restrict__ st,
-                                                       const void* __restrict__ grad, int64_t n)
+// fp16: 8 elements per 16-byte vector; fp32: 4.  One vector per lane per
+// grid-stride step; block 0 also tests the elements after the last vector.
+template <bool F32, bool NT, int TPB>
+__global__ __launch_bounds__(TPB) void check_kernel(ds_scaler* __restrict__ st,
+                                                    const void* __restrict__ grad, int64_t n)
 {
     if (st->overflow != 0u)
         return;  // already decided for this step
     constexpr int kPer = F32 ? 4 : 8;
     const u32x4* G = static_cast<const u32x4*>(grad);
     const int64_t nv = n / kPer;
-    const int64_t stride = static_cast<int64_t>(gridDim.x) * kBlock;
-    int64_t q = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x;
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * TPB;
     uint32_t bad = 0u;
-    for (; q + (U - 1) * stride < nv; q += U * stride) {
-        u32x4 w[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u)
-            w[u] = load<NT>(G + q + u * stride);
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            if constexpr (F32)
-                bad |= nonfinite_f32(w[u].x) | nonfinite_f32(w[u].y) | nonfinite_f32(w[u].z) |
-                       nonfinite_f32(w[u].w);
-            else
-                bad |= nonfinite_f16x2(w[u].x) | nonfinite_f16x2(w[u].y) | nonfinite_f16x2(w[u].z) |
-                       nonfinite_f16x2(w[u].w);
-        }
-    }
-    for (; q < nv; q += stride) {
+    for (int64_t q = static_cast<int64_t>(blockIdx.x) * TPB + threadIdx.x; q < nv; q += stride) {
         const u32x4 w = load<NT>(G + q);
         if constexpr (F32)
             bad |= nonfinite_f32(w.x) | nonfinite_f32(w.y) | nonfinite_f32(w.z) | nonfinite_f32(w.w);
@@ -346,24 +342,26 @@ __global__ __launch_bounds__(kBlock) void check_kernel(ds_scaler* __restrict__ s
 // gradient accumulation
 // ---------------------------------------------------------------------------
 
-template <bool OVERWRITE, bool CHECK, bool NT, int U>
-__global__ __launch_bounds__(kBlock) void accumulate_kernel(float* __restrict__ acc,
-                                                            const uint16_t* __restrict__ g16,
-                                                            int64_t n, ds_scaler* __restrict__ st)
+// Same tiling as the Adam kernel.
+template <bool OVERWRITE, bool CHECK, bool NT, int TPB, int U>
+__global__ __launch_bounds__(TPB) void accumulate_kernel(float* __restrict__ acc,
+                                                         const uint16_t* __restrict__ g16,
+                                                         int64_t n, ds_scaler* __restrict__ st)
 {
     f32x4* A = reinterpret_cast<f32x4*>(acc);
     const u32x2* G = reinterpret_cast<const u32x2*>(g16);
+    constexpr int T = U * TPB;
     const int64_t nq = n >> 2;
-    const int64_t stride = static_cast<int64_t>(gridDim.x) * kBlock;
-    int64_t q = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x;
+    const int64_t ntiles = nq / T;
     uint32_t bad = 0u;
-    for (; q + (U - 1) * stride < nq; q += U * stride) {
+    for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
+        const int64_t q0 = tile * T + threadIdx.x;
         f32x4 g[U], a[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            g[u] = widen4(load<NT>(G + q + u * stride));
+            g[u] = widen4(load<NT>(G + q0 + u * TPB));
             if constexpr (!OVERWRITE)
-                a[u] = load<NT>(A + q + u * stride);
+                a[u] = load<NT>(A + q0 + u * TPB);
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
@@ -374,27 +372,29 @@ __global__ __launch_bounds__(kBlock) void accumulate_kernel(float* __restrict__ 
                 r = a[u] + g[u];
             if constexpr (CHECK)
                 bad |= nonfinite_f32x4(r);
-            store<NT>(A + q + u * stride, r);
+            store<NT>(A + q0 + u * TPB, r);
         }
     }
-    for (; q < nq; q += stride) {
-        const f32x4 g = widen4(load<NT>(G + q));
-        f32x4 r;
-        if constexpr (OVERWRITE)
-            r = g;
-        else
-            r = load<NT>(A + q) + g;
-        if constexpr (CHECK)
-            bad |= nonfinite_f32x4(r);
-        store<NT>(A + q, r);
-    }
-    if (blockIdx.x == 0 && static_cast<int64_t>(threadIdx.x) < (n & 3)) {
-        const int64_t i = (nq << 2) + threadIdx.x;
-        const float g = h2f(g16[i]);
-        const float r = OVERWRITE ? g : acc[i] + g;
-        if constexpr (CHECK)
-            bad |= nonfinite_f32(__float_as_uint(r));
-        acc[i] = r;
+    if (blockIdx.x == 0) {
+        for (int64_t q = ntiles * T + threadIdx.x; q < nq; q += TPB) {
+            const f32x4 g = widen4(load<NT>(G + q));
+            f32x4 r;
+            if constexpr (OVERWRITE)
+                r = g;
+            else
+                r = load<NT>(A + q) + g;
+            if constexpr (CHECK)
+                bad |= nonfinite_f32x4(r);
+            store<NT>(A + q, r);
+        }
+        if (static_cast<int64_t>(threadIdx.x) < (n & 3)) {
+            const int64_t i = (nq << 2) + threadIdx.x;
+            const float g = h2f(g16[i]);
+            const float r = OVERWRITE ? g : acc[i] + g;
+            if constexpr (CHECK)
+                bad |= nonfinite_f32(__float_as_uint(r));
+            acc[i] = r;
+        }
     }
     if constexpr (CHECK)
         raise_flag(st, bad);
@@ -444,25 +444,6 @@ __global__ void write_state_kernel(ds_scaler* st, ds_scaler value) { *st = value
 // host helpers
 // ---------------------------------------------------------------------------
 
-int cu_count()
-{
-    static std::atomic<int> cache[64];
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0)
-        return 256;
-    if (dev < 64) {
-        int c = cache[dev].load(std::memory_order_relaxed);
-        if (c > 0)
-            return c;
-    }
-    int cus = 0;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
-        cus = 256;
-    if (dev < 64)
-        cache[dev].store(cus, std::memory_order_relaxed);
-    return cus;
-}
-
 long env_long(const char* name, long dflt)
 {
     const char* s = std::getenv(name);
@@ -473,27 +454,28 @@ long env_long(const char* name, long dflt)
     return (end != s) ? v : dflt;
 }
 
-// Blocks for a grid-stride launch over `items` per-lane work items:
-// enough to cover the work once, capped at blocks_per_cu per compute unit.
-// DSZERO_GRID pins the block count (grid-size invariance tests, sweeps);
-// DSZERO_BLOCKS_PER_CU changes the cap.
-unsigned grid_blocks(int64_t items)
+// Blocks for `units` units of work (tiles, or vectors of the check): one
+// block per unit, at least one, at most kMaxBlocks (the kernels loop past
+// that).  DSZERO_GRID pins the block count (launch-shape invariance tests,
+// sweeps).
+unsigned grid_blocks(int64_t units)
 {
     const long forced = env_long("DSZERO_GRID", 0);
     if (forced > 0)
-        return static_cast<unsigned>(forced > 1048576 ? 1048576 : forced);
-    const long per_cu = env_long("DSZERO_BLOCKS_PER_CU", 8);
-    int64_t need = (items + kBlock - 1) / kBlock;
-    int64_t cap = static_cast<int64_t>(cu_count()) * (per_cu > 0 ? per_cu : 8);
-    if (need > cap)
-        need = cap;
-    if (need < 1)
-        need = 1;
-    return static_cast<unsigned>(need);
+        return static_cast<unsigned>(forced > kMaxBlocks ? kMaxBlocks : forced);
+    int64_t b = units;
+    if (b > kMaxBlocks)
+        b = kMaxBlocks;
+    if (b < 1)
+        b = 1;
+    return static_cast<unsigned>(b);
 }
 
-int variant_unroll() { return static_cast<int>(env_long("DSZERO_UNROLL", 2)); }
-bool variant_nt() { return env_long("DSZERO_NT", 0) != 0; }
+// Variant knobs (default: quads per lane U = 4, non-temporal accesses on).
+int variant_unroll() { return env_long("DSZERO_UNROLL", 4) == 2 ? 2 : 4; }
+bool variant_nt() { return env_long("DSZERO_NT", 1) != 0; }
+
+int64_t tiles_of(int64_t n, int unroll) { return (n >> 2) / (static_cast<int64_t>(unroll) * kStepBlock); }
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
@@ -517,11 +499,10 @@ template <bool F32G, bool WD, bool NT>
 void launch_adam_u(int unroll, unsigned blocks, hipStream_t s, const ds_scaler* st, float* master,
                    float* m, float* v, uint16_t* p16, const void* grad, int64_t n, const AdamHyper& hp)
 {
-    switch (unroll) {
-    case 1: adam_kernel<F32G, WD, NT, 1><<<blocks, kBlock, 0, s>>>(st, master, m, v, p16, grad, n, hp); break;
-    case 4: adam_kernel<F32G, WD, NT, 4><<<blocks, kBlock, 0, s>>>(st, master, m, v, p16, grad, n, hp); break;
-    default: adam_kernel<F32G, WD, NT, 2><<<blocks, kBlock, 0, s>>>(st, master, m, v, p16, grad, n, hp); break;
-    }
+    if (unroll == 2)
+        adam_kernel<F32G, WD, NT, kStepBlock, 2><<<blocks, kStepBlock, 0, s>>>(st, master, m, v, p16, grad, n, hp);
+    else
+        adam_kernel<F32G, WD, NT, kStepBlock, 4><<<blocks, kStepBlock, 0, s>>>(st, master, m, v, p16, grad, n, hp);
 }
 
 template <bool F32G, bool WD>
@@ -533,6 +514,16 @@ void launch_adam_nt(bool nt, int unroll, unsigned blocks, hipStream_t s, const d
         launch_adam_u<F32G, WD, true>(unroll, blocks, s, st, master, m, v, p16, grad, n, hp);
     else
         launch_adam_u<F32G, WD, false>(unroll, blocks, s, st, master, m, v, p16, grad, n, hp);
+}
+
+template <bool OW, bool CK, bool NT>
+void launch_acc_u(int unroll, unsigned blocks, hipStream_t s, float* acc, const uint16_t* g16, int64_t n,
+                  ds_scaler* st)
+{
+    if (unroll == 2)
+        accumulate_kernel<OW, CK, NT, kStepBlock, 2><<<blocks, kStepBlock, 0, s>>>(acc, g16, n, st);
+    else
+        accumulate_kernel<OW, CK, NT, kStepBlock, 4><<<blocks, kStepBlock, 0, s>>>(acc, g16, n, st);
 }
 
 }  // namespace
@@ -622,10 +613,11 @@ ds_status ds_accumulate(float* acc, const uint16_t* g16, int64_t n, int32_t over
         overlap(g16, 2 * un, st_or_null, sizeof(ds_scaler)))
         return DS_ERR_ALIAS;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    const unsigned blocks = grid_blocks((n >> 2) > 0 ? (n >> 2) : 1);
+    const int unroll = variant_unroll();
+    const unsigned blocks = grid_blocks(tiles_of(n, unroll));
     const bool nt = variant_nt();
     const bool ow = overwrite != 0, ck = st_or_null != nullptr;
-#define DS_ACC(OW, CK, NT) accumulate_kernel<OW, CK, NT, 4><<<blocks, kBlock, 0, s>>>(acc, g16, n, st_or_null)
+#define DS_ACC(OW, CK, NT) launch_acc_u<OW, CK, NT>(unroll, blocks, s, acc, g16, n, st_or_null)
     if (nt) {
         if (ow) { if (ck) DS_ACC(true, true, true); else DS_ACC(true, false, true); }
         else    { if (ck) DS_ACC(false, true, true); else DS_ACC(false, false, true); }
@@ -656,14 +648,14 @@ ds_status ds_check_overflow(ds_scaler* st, const void* grad, ds_dtype dt, int64_
         return DS_ERR_ALIAS;
     hipStream_t s = static_cast<hipStream_t>(stream);
     const int64_t vecs = n / (dt == DS_FP16 ? 8 : 4);
-    const unsigned blocks = grid_blocks(vecs > 0 ? vecs : 1);
+    const unsigned blocks = grid_blocks((vecs + kCheckBlock - 1) / kCheckBlock);
     const bool nt = variant_nt();
     if (dt == DS_FP16) {
-        if (nt) check_kernel<false, true, 4><<<blocks, kBlock, 0, s>>>(st, grad, n);
-        else    check_kernel<false, false, 4><<<blocks, kBlock, 0, s>>>(st, grad, n);
+        if (nt) check_kernel<false, true, kCheckBlock><<<blocks, kCheckBlock, 0, s>>>(st, grad, n);
+        else    check_kernel<false, false, kCheckBlock><<<blocks, kCheckBlock, 0, s>>>(st, grad, n);
     } else {
-        if (nt) check_kernel<true, true, 4><<<blocks, kBlock, 0, s>>>(st, grad, n);
-        else    check_kernel<true, false, 4><<<blocks, kBlock, 0, s>>>(st, grad, n);
+        if (nt) check_kernel<true, true, kCheckBlock><<<blocks, kCheckBlock, 0, s>>>(st, grad, n);
+        else    check_kernel<true, false, kCheckBlock><<<blocks, kCheckBlock, 0, s>>>(st, grad, n);
     }
     return launched();
 }
@@ -701,7 +693,7 @@ ds_status ds_adam_step(const ds_scaler* st, float* master, float* m, float* v, u
     const AdamHyper hp{lr, beta1, beta2, eps, weight_decay, accum_steps};
     hipStream_t s = static_cast<hipStream_t>(stream);
     const int unroll = variant_unroll();
-    const unsigned blocks = grid_blocks((n >> 2) > 0 ? (n >> 2) : 1);
+    const unsigned blocks = grid_blocks(tiles_of(n, unroll));
     const bool nt = variant_nt();
     const bool wd = weight_decay != 0.0f;
     if (dt == DS_FP16) {
