@@ -44,7 +44,7 @@
  *  - Launch-shape knobs, read from the environment at each call (for tests
  *    and tuning; results are bit-identical under every setting):
  *    DSZERO_GRID=<blocks> pins the block count, DSZERO_UNROLL=2|4 sets the
- *    quads per lane of the read/write kernels, DSZERO_NT=0 turns off the
+ *    quads per lane of the read/write kernels, DSZERO_NT=0 turns off their
  *    non-temporal load/store hints.
  */
 #ifndef DSZERO_H
