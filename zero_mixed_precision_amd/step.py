@@ -11,6 +11,9 @@ scales and accumulates, step() updates):
     then    ds_update_loss_scale (once)
 
 No call synchronises the host; ``scaler()`` reads the state back (one copy).
+``graph(grads)`` records the whole sequence for fixed gradient buffers into a
+HIP graph, so a step costs one graph launch; it contains kernels only (no
+memset or copy nodes).
 """
 from __future__ import annotations
 
@@ -64,6 +67,36 @@ class ShardStep:
                           c.betas[0], c.betas[1], c.eps, c.weight_decay, self.K, self.stream)
         _lib.ds_update_loss_scale(self.state, self.stream)
         self._micro = 0
+
+    def full_step(self, grads) -> None:
+        """One whole step from K fp16 micro-batch gradients (a tensor when K = 1)."""
+        if self.K == 1:
+            self.step(grads[0] if isinstance(grads, (list, tuple)) else grads)
+            return
+        assert len(grads) == self.K
+        for g in grads:
+            self.accumulate(g)
+        self.step()
+
+    def graph(self, grads):
+        """Record ``full_step(grads)`` into a HIP graph (torch.cuda.CUDAGraph).
+
+        The gradient buffers are baked in by address: write the next step's
+        gradients into the same tensors, then ``replay()``.  Replays read the
+        learning rate and other hyperparameters as recorded.
+        """
+        torch = self.torch
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        saved, self.stream = self.stream, None      # launch on the capturing (current) stream
+        try:
+            with torch.cuda.graph(g, stream=side):
+                self.full_step(grads)
+        finally:
+            self.stream = saved
+        torch.cuda.current_stream().wait_stream(side)
+        return g
 
     def scaler(self) -> _lib.DsScaler:
         return _lib.ds_state_read(self.state, self.stream)
