@@ -84,7 +84,7 @@ def gpu_run(args):
     p16 = torch.empty(n, dtype=torch.int16, device=dev)
     synth.device_fill_grad16(torch, tabs, p16, w.p16_key(), synth.GradSpec(0.02, 1.0))
     acc = torch.empty(n, dtype=torch.float32, device=dev) if K > 1 else None
-    st = torch.zeros(64, dtype=torch.uint8, device=dev)
+    st = torch.zeros(_lib.ds_scaler_size(), dtype=torch.uint8, device=dev)
     _lib.ds_state_init(st, w.init_scale, w.min_scale, w.window, w.hysteresis, 0, 1)
     if w.ragged:
         buckets = [(b.start, b.size) for b in FlatLayout(ragged_numels()).buckets]
@@ -106,21 +106,30 @@ def gpu_run(args):
     torch.cuda.synchronize()
     log(f"workload {w.name}: psi={n} K={K} grad buffers={nbuf} (of {total_mb} micro-batches)")
 
-    hp = (LR, BETA1, BETA2, EPS, WD)
+    hp = (LR, BETA1, BETA2, EPS, WD, args.clip)
+    ws = None
+    if args.clip > 0:   # global-norm clipping: the check passes also gather the sum of squares
+        ws = torch.zeros((_lib.ds_sumsq_workspace_bytes(n) + 7) // 8, dtype=torch.float64, device=dev)
     ev = []
 
     def one_step(i, timed):
         base = i * K
         if K == 1:
             g = grads[base % nbuf]
-            _lib.ds_check_overflow(st, g, _lib.DS_FP16, n, stream)
+            if ws is None:
+                _lib.ds_check_overflow(st, g, _lib.DS_FP16, n, stream)
+            else:
+                _lib.ds_check_overflow_sumsq(st, g, _lib.DS_FP16, n, ws, stream=stream)
             gptr, dt = g, _lib.DS_FP16
         else:
             for k in range(K):
                 g = grads[(base + k) % nbuf]
                 for start, size in buckets:
-                    _lib.ds_accumulate(acc.data_ptr() + 4 * start, g.data_ptr() + 2 * start, size,
-                                       k == 0, st if k == K - 1 else None, stream)
+                    a, gp = acc.data_ptr() + 4 * start, g.data_ptr() + 2 * start
+                    if k == K - 1 and ws is not None:
+                        _lib.ds_accumulate_sumsq(a, gp, size, k == 0, st, ws, stream=stream)
+                    else:
+                        _lib.ds_accumulate(a, gp, size, k == 0, st if k == K - 1 else None, stream)
             gptr, dt = acc, _lib.DS_FP32
         if timed:
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -167,6 +176,7 @@ def gpu_run(args):
             "grad": "fp16 N(0,%g) x %g" % (w.sigma, w.mult) + (" heavy tail" if w.heavy_tail else ""),
             "state": "fp32 master/m/v, fp16 params",
             "adam": {"lr": LR, "betas": [BETA1, BETA2], "eps": EPS, "weight_decay": WD},
+            "gradient_clipping": args.clip,
             "parallelism": "one GPU's ZeRO partition",
         },
         "roofline": {
@@ -299,6 +309,8 @@ def main():
     ap.add_argument("--workload", default="zero2_7b")
     ap.add_argument("--mode", default="step", choices=["step", "copy"])
     ap.add_argument("--max-grad-buffers", type=int, default=8)
+    ap.add_argument("--clip", type=float, default=0.0,
+                    help="gradient_clipping max norm (0: the workloads' setting, no clipping)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--cpu-slice", type=int, default=1 << 24)
     ap.add_argument("--no-cpu-baseline", action="store_true")

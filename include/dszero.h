@@ -71,12 +71,14 @@ typedef enum ds_status {
 typedef enum ds_dtype { DS_FP16 = 1, DS_FP32 = 2 } ds_dtype;
 
 /*
- * Dynamic loss-scaler state, 64 bytes, kept in caller-owned DEVICE memory so
- * that the kernels read the scale and the overflow flag without a host sync.
- * Fields follow the fp16 block of ds_config.json ([Guide] section 4.2:
- * loss_scale 0 = dynamic, initial scale 2^initial_scale_power,
- * loss_scale_window = successful steps before the scale grows, hysteresis =
- * overflows before it shrinks, min_loss_scale = floor).
+ * Per-step device state, 128 bytes, kept in caller-owned DEVICE memory so that
+ * the kernels read the scale, the overflow flag and the gradient norm without
+ * a host sync.  The loss-scaler fields follow the fp16 block of ds_config.json
+ * ([Guide] section 4.2: loss_scale 0 = dynamic, initial scale
+ * 2^initial_scale_power, loss_scale_window = successful steps before the scale
+ * grows, hysteresis = overflows before it shrinks, min_loss_scale = floor).
+ * grad_sumsq accumulates the sum of squares of the step's (still scaled)
+ * gradient for global-norm clipping ([Guide] section 4.1 gradient_clipping).
  */
 typedef struct ds_scaler {
     float scale;                    /* S: loss scale the next step unscales by        */
@@ -92,9 +94,12 @@ typedef struct ds_scaler {
     int64_t skipped;                /* skipped steps                                  */
     int32_t consecutive_hysteresis; /* 1: a successful step refills hysteresis_left   */
     uint32_t last_overflow;         /* overflow flag consumed by the last update      */
+    double grad_sumsq;              /* sum of squares of the step's gradient so far   */
+    double last_grad_sumsq;         /* grad_sumsq consumed by the last update         */
+    uint8_t reserved[48];           /* zero                                           */
 } ds_scaler;
 
-/* sizeof(ds_scaler) as compiled into the library (64). */
+/* sizeof(ds_scaler) as compiled into the library (128). */
 size_t ds_scaler_size(void);
 
 /*
@@ -102,7 +107,8 @@ size_t ds_scaler_size(void);
  * min_scale = min_loss_scale, growth_window = loss_scale_window, hysteresis,
  * consecutive_hysteresis, dynamic = (loss_scale == 0); for a static scale pass
  * the fixed scale as init_scale and dynamic = 0.  Sets step = iter = skipped = 0
- * and clears the flag.  Asynchronous (a one-thread kernel writes the struct).
+ * and clears the flag and the gradient sum of squares.  Asynchronous (a
+ * one-thread kernel writes the struct).
  * DS_ERR_HPARAM: init_scale or min_scale not finite or <= 0, growth_window < 1,
  * hysteresis < 1.
  */
@@ -148,6 +154,8 @@ ds_status ds_check_overflow(ds_scaler* st, const void* grad, ds_dtype dt, int64_
  * If st->overflow is set the kernel writes nothing (the step is skipped).
  * Otherwise, with S = st->scale, K = accum_steps and t = st->step + 1:
  *   g      = grad[i] / (S*K)                     (unscale; grad fp16 or fp32)
+ *            (with max_grad_norm > 0 the multiplier 1/(S*K) is scaled by the
+ *             global-norm clipping coefficient below)
  *   m[i]   = beta1*m[i] + (1-beta1)*g
  *   v[i]   = beta2*v[i] + (1-beta2)*g*g
  *   master = master - lr*weight_decay*master     (only if weight_decay != 0)
@@ -156,14 +164,22 @@ ds_status ds_check_overflow(ds_scaler* st, const void* grad, ds_dtype dt, int64_
  * in IEEE fp32, one rounding per operation; the two bias-correction factors
  * are evaluated in fp64 and rounded once.  master/m/v: fp32[n] in place;
  * p16: fp16[n] out; grad: fp16[n] or fp32[n] in.  st is read only (t and S
- * advance in ds_update_loss_scale).  DS_ERR_HPARAM: lr or weight_decay
- * negative or not finite, beta1 or beta2 outside [0, 1), eps not finite or
- * <= 0, accum_steps < 1.
+ * advance in ds_update_loss_scale).
+ * Global-norm clipping ([Guide] sections 4.1 and 5.4 gradient_clipping,
+ * section 5.1 step() includes clipping): with max_grad_norm > 0, using the
+ * step's st->grad_sumsq (filled by ds_check_overflow_sumsq or
+ * ds_accumulate_sumsq over the whole partition) and inv = fp32(1/(S*K)):
+ *   norm = sqrt(grad_sumsq) * inv                         (fp64)
+ *   coef = min(1, max_grad_norm / (norm + 1e-6))          (fp64)
+ *   the multiplier of the gradient becomes fp32(inv * coef)
+ * max_grad_norm = 0 disables clipping (the multiplier is inv).
+ * DS_ERR_HPARAM: lr, weight_decay or max_grad_norm negative or not finite,
+ * beta1 or beta2 outside [0, 1), eps not finite or <= 0, accum_steps < 1.
  */
 ds_status ds_adam_step(const ds_scaler* st, float* master, float* m, float* v, uint16_t* p16,
                        const void* grad, ds_dtype dt, int64_t n, float lr, float beta1,
-                       float beta2, float eps, float weight_decay, int32_t accum_steps,
-                       void* stream);
+                       float beta2, float eps, float weight_decay, float max_grad_norm,
+                       int32_t accum_steps, void* stream);
 
 /*
  * End of a step: advance the scaler by the step's overflow flag, then clear
@@ -172,9 +188,41 @@ ds_status ds_adam_step(const ds_scaler* st, float* master, float* m, float* v, u
  * used up, S = max(S/2, min_scale) and the hysteresis restarts.  No overflow:
  * step += 1; if dynamic, growth_count += 1 and at growth_window S doubles and
  * growth_count restarts (consecutive_hysteresis refills the hysteresis).
- * iter += 1 and last_overflow = flag in both cases.  Call exactly once per step.
+ * iter += 1, last_overflow = flag and last_grad_sumsq = grad_sumsq in both
+ * cases; grad_sumsq restarts at 0.  Call exactly once per step.
  */
 ds_status ds_update_loss_scale(ds_scaler* st, void* stream);
+
+/*
+ * Gradient sum of squares for global-norm clipping, fused into the passes
+ * that already read the gradient.  Both add sum(x_i^2) over their n values
+ * (the stored, still loss-scaled gradient: fp16 values, or the fp32
+ * accumulation) into st->grad_sumsq, in fp64.  The sum is taken over fixed
+ * chunks of consecutive elements (16,384 for the check, 4096 for the
+ * accumulation), each reduced in a fixed order, and the chunk sums in a fixed
+ * order, so the result does not depend on the launch shape.  Several calls per step (disjoint ranges, e.g. buckets) add up in
+ * call order.
+ *
+ * workspace: caller-owned DEVICE scratch of at least
+ * ds_sumsq_workspace_bytes(n) bytes (one fp64 partial sum per chunk), 8-byte
+ * aligned, no initial contents needed.  Each call is two kernels: the pass
+ * over the data writes the chunk sums, a one-block kernel adds them in order.
+ * One workspace serves every call on one stream (calls that may run at the
+ * same time need their own).
+ * Errors as for the plain entry points; DS_ERR_NULL / DS_ERR_SIZE /
+ * DS_ERR_ALIGN / DS_ERR_ALIAS also cover the workspace.
+ */
+size_t ds_sumsq_workspace_bytes(int64_t n);
+
+/* ds_check_overflow plus the sum of squares of grad (fp16 or fp32), one pass. */
+ds_status ds_check_overflow_sumsq(ds_scaler* st, const void* grad, ds_dtype dt, int64_t n,
+                                  void* workspace, size_t workspace_bytes, void* stream);
+
+/* ds_accumulate with the fused overflow check (st required) plus the sum of
+ * squares of the accumulated values, one pass: use it for the last
+ * micro-batch of a clipped step. */
+ds_status ds_accumulate_sumsq(float* acc, const uint16_t* g16, int64_t n, int32_t overwrite,
+                              ds_scaler* st, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * The bias-correction scalars the next applied step will use, evaluated on

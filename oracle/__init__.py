@@ -23,6 +23,7 @@ workload exercises them and the pages give only the keys' one-line meaning).
 from __future__ import annotations
 
 import ctypes
+import math
 import os
 import subprocess
 
@@ -86,6 +87,8 @@ def lib():
         L.zo_adam_scalars.restype = None
         L.zo_adam.argtypes = [vp, i32, i64, vp, vp, vp, vp, f32, i32, i64, f32, f32, f32, f32, f32]
         L.zo_adam.restype = None
+        L.zo_adam_mult.argtypes = [vp, i32, i64, vp, vp, vp, vp, f32, i64, f32, f32, f32, f32, f32]
+        L.zo_adam_mult.restype = None
         L.zo_scaler_init.argtypes = [ctypes.POINTER(ZoScaler), f32, f32, i32, i32, i32, i32]
         L.zo_scaler_init.restype = None
         L.zo_scaler_update.argtypes = [ctypes.POINTER(ZoScaler), i32]
@@ -151,6 +154,57 @@ def adam(grad, master, m, v, p16, *, scale, accum_steps, t, lr, beta1, beta2, ep
                   _ptr(p16), scale, int(accum_steps), int(t), lr, beta1, beta2, eps, weight_decay)
 
 
+def adam_mult(grad, master, m, v, p16, *, mult, t, lr, beta1, beta2, eps, weight_decay=0.0) -> None:
+    """One applied Adam step with an explicit gradient multiplier (fp32)."""
+    n = master.size
+    assert grad.size == n and grad.dtype in (np.uint16, np.float32)
+    lib().zo_adam_mult(_ptr(grad), int(grad.dtype == np.float32), n, _ptr(master), _ptr(m), _ptr(v),
+                       _ptr(p16), float(np.float32(mult)), int(t), lr, beta1, beta2, eps, weight_decay)
+
+
+# -- global-norm clipping ("DeepSpeed complete guide" section 4.1 and 5.4:
+#    gradient_clipping; section 5.1: step() includes clipping) ----------------
+
+def grad_sumsq(grad: np.ndarray) -> float:
+    """Sum of squares of the stored gradient values, exactly, rounded once to fp64.
+
+    fp16: each value is M * 2^E with integers M < 2^11, E in [-24, 5]; the
+    squares M^2 * 2^(2E) are summed exactly as integers per exponent (Python
+    integers), then divided by 2^48 with one correct rounding.  fp32: the
+    squares are exact in fp64 and math.fsum adds them with one rounding.
+    Non-finite gradients give inf or nan (their step is skipped anyway)."""
+    if grad.dtype == np.uint16:
+        h = grad.astype(np.int64)
+        e = (h >> 10) & 0x1F
+        if np.any(e == 31):
+            return float("inf")
+        f = h & 0x3FF
+        M = np.where(e == 0, f, f + 1024)
+        E = np.where(e == 0, -24, e - 25)
+        total = 0
+        for ex in np.unique(E):
+            total += int(np.sum(M[E == ex] ** 2)) << int(2 * ex + 48)
+        return total / (1 << 48)
+    assert grad.dtype == np.float32
+    if not np.all(np.isfinite(grad)):
+        return float("inf")
+    return math.fsum((grad.astype(np.float64) ** 2).tolist())
+
+
+def clip_multiplier(sumsq: float, scale: float, accum_steps: int, max_norm: float) -> np.float32:
+    """fp32 gradient multiplier: inv = fp32(1/(S*K)) without clipping; with a
+    positive max_norm, fp32(inv * min(1, max_norm / (norm + 1e-6))) where
+    norm = sqrt(sumsq) * inv is the L2 norm of the unscaled gradient (fp64)."""
+    inv = np.float32(1.0) / (np.float32(scale) * np.float32(accum_steps))
+    if max_norm <= 0:
+        return inv
+    inv64 = float(inv)
+    norm = math.sqrt(sumsq) * inv64
+    ratio = float(np.float32(max_norm)) / (norm + 1e-6)
+    coef = ratio if ratio < 1.0 else 1.0
+    return np.float32(inv64 * coef)
+
+
 class Scaler:
     """Dynamic loss scaler state machine (oracle.c ``zo_scaler``)."""
 
@@ -180,14 +234,17 @@ class State:
 
     def __init__(self, master, m, v, p16, scaler: Scaler):
         self.master, self.m, self.v, self.p16, self.scaler = master, m, v, p16, scaler
+        self.last_sumsq = 0.0
 
 
-def step(state: State, grads, *, lr, beta1, beta2, eps, weight_decay=0.0) -> bool:
+def step(state: State, grads, *, lr, beta1, beta2, eps, weight_decay=0.0, max_grad_norm=0.0) -> bool:
     """One full ZeRO optimizer step of the oracle; returns the overflow flag.
 
     ``grads`` is one uint16 array (K = 1: the fp16 gradient is consumed
     directly) or a list of K uint16 micro-batch gradients (K > 1: summed into
-    an fp32 buffer in micro-batch order first).
+    an fp32 buffer in micro-batch order first).  ``max_grad_norm`` > 0 clips
+    the unscaled gradient to that global L2 norm.  ``state.last_sumsq`` keeps
+    the step's gradient sum of squares when clipping.
     """
     if isinstance(grads, np.ndarray):
         grads = [grads]
@@ -200,8 +257,15 @@ def step(state: State, grads, *, lr, beta1, beta2, eps, weight_decay=0.0) -> boo
             accumulate(grad, np.ascontiguousarray(g, dtype=np.uint16), overwrite=(k == 0))
     overflow = any_nonfinite(grad)
     if not overflow:
-        adam(grad, state.master, state.m, state.v, state.p16,
-             scale=state.scaler.scale, accum_steps=K, t=state.scaler.applied + 1,
-             lr=lr, beta1=beta1, beta2=beta2, eps=eps, weight_decay=weight_decay)
+        if max_grad_norm > 0:
+            state.last_sumsq = grad_sumsq(grad)
+            mult = clip_multiplier(state.last_sumsq, state.scaler.scale, K, max_grad_norm)
+            adam_mult(grad, state.master, state.m, state.v, state.p16, mult=mult,
+                      t=state.scaler.applied + 1, lr=lr, beta1=beta1, beta2=beta2, eps=eps,
+                      weight_decay=weight_decay)
+        else:
+            adam(grad, state.master, state.m, state.v, state.p16,
+                 scale=state.scaler.scale, accum_steps=K, t=state.scaler.applied + 1,
+                 lr=lr, beta1=beta1, beta2=beta2, eps=eps, weight_decay=weight_decay)
     state.scaler.update(overflow)
     return overflow

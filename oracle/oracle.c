@@ -197,17 +197,18 @@ void zo_adam_scalars(int64_t t, float lr, float beta1, float beta2,
  * real arithmetic.  Each line below is one fp32 rounding, evaluated in the
  * written order.
  *
- * grad_is_f32 = 0: grad is fp16 bits (K = 1 path); 1: fp32 accumulation buffer. */
-void zo_adam(const void *grad, int32_t grad_is_f32, int64_t n,
-             float *master, float *m, float *v, uint16_t *p16,
-             float scale, int32_t accum_steps, int64_t t,
-             float lr, float beta1, float beta2, float eps, float weight_decay)
+ * grad_is_f32 = 0: grad is fp16 bits (K = 1 path); 1: fp32 accumulation buffer.
+ * zo_adam_mult takes the gradient multiplier (1/(S*K), or that times the
+ * clipping coefficient) as `inv`; zo_adam computes 1/(S*K) itself. */
+void zo_adam_mult(const void *grad, int32_t grad_is_f32, int64_t n,
+                  float *master, float *m, float *v, uint16_t *p16,
+                  float inv, int64_t t,
+                  float lr, float beta1, float beta2, float eps, float weight_decay)
 {
     float step_size, rbc2;
     zo_adam_scalars(t, lr, beta1, beta2, &step_size, &rbc2);
     float omb1 = 1.0f - beta1;
     float omb2 = 1.0f - beta2;
-    float inv = 1.0f / (scale * (float)accum_steps);
     float lrwd = lr * weight_decay;
 
     for (int64_t i = 0; i < n; ++i) {
@@ -241,6 +242,17 @@ void zo_adam(const void *grad, int32_t grad_is_f32, int64_t n,
         master[i] = p;
         p16[i] = zo_enc16(p);
     }
+}
+
+/* The unclipped step: the gradient multiplier is 1 / (S * K) in fp32. */
+void zo_adam(const void *grad, int32_t grad_is_f32, int64_t n,
+             float *master, float *m, float *v, uint16_t *p16,
+             float scale, int32_t accum_steps, int64_t t,
+             float lr, float beta1, float beta2, float eps, float weight_decay)
+{
+    float inv = 1.0f / (scale * (float)accum_steps);
+    zo_adam_mult(grad, grad_is_f32, n, master, m, v, p16, inv, t, lr, beta1, beta2, eps,
+                 weight_decay);
 }
 
 /* ------------------------------------------------------------------------ */

@@ -149,12 +149,27 @@ _LIB_PATH = os.path.join(_HERE, "libdssynth.so")
 _dlib = None
 
 
+def _bind_torch_hip_runtime() -> None:
+    """Make PyTorch's HIP runtime the global definition of the HIP symbols
+    before loading libdssynth.so, so its kernels launch on the runtime that
+    owns torch's streams and memory (a PyTorch-ROCm install carries its own
+    libamdhip64 besides the system one the library links against)."""
+    try:
+        import torch
+    except ImportError:
+        return
+    path = os.path.join(os.path.dirname(torch.__file__), "lib", "libamdhip64.so")
+    if os.path.exists(path):
+        ctypes.CDLL(path, mode=ctypes.RTLD_GLOBAL)
+
+
 def device_lib():
     """ctypes handle of libdssynth.so (device fill kernels); raises if not built."""
     global _dlib
     if _dlib is None:
         if not os.path.exists(_LIB_PATH):
             raise RuntimeError("libdssynth.so is not built: run __graft_entry__.build()")
+        _bind_torch_hip_runtime()
         L = ctypes.CDLL(_LIB_PATH)
         vp, i64, u64, u32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_uint64, ctypes.c_uint32
         L.synth_fill_grad16.argtypes = [vp, i64, i64, u64, vp, vp, u32, vp]

@@ -54,7 +54,7 @@ class DevState:
         self.n = master.size
         self.K = K
         self.acc = torch.empty(max(self.n, 1), dtype=torch.float32, device="cuda:0") if K > 1 else None
-        self.state = torch.zeros(64, dtype=torch.uint8, device="cuda:0")
+        self.state = torch.zeros(_lib.ds_scaler_size(), dtype=torch.uint8, device="cuda:0")
         _lib.ds_state_init(self.state, init_scale, min_scale, window, hysteresis, 0, dynamic)
 
     def step(self, grads, hp, buckets=None, fused_check=True):
@@ -82,7 +82,7 @@ class DevState:
                 L.ds_check_overflow(self.state, self.acc, L.DS_FP32, n)
             grad, dt = self.acc, L.DS_FP32
         L.ds_adam_step(self.state, self.master, self.m, self.v, self.p16, grad, dt, n, hp["lr"],
-                       hp["beta1"], hp["beta2"], hp["eps"], hp.get("weight_decay", 0.0), K)
+                       hp["beta1"], hp["beta2"], hp["eps"], hp.get("weight_decay", 0.0), 0.0, K)
         L.ds_update_loss_scale(self.state)
 
     def scaler(self):

@@ -22,7 +22,7 @@ L = _lib.lib
 # fake, never-dereferenced device addresses (validation fails before any launch)
 A, B, C, D, E, ST = (0x10000000 * k for k in range(1, 7))
 STREAM = None
-HP = (1e-4, 0.9, 0.999, 1e-8, 0.0, 1)
+HP = (1e-4, 0.9, 0.999, 1e-8, 0.0, 0.0, 1)
 
 
 def declared_symbols():
@@ -41,9 +41,10 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_scaler_layout():
-    assert L.ds_scaler_size() == 64 == ctypes.sizeof(_lib.DsScaler)
+    assert L.ds_scaler_size() == 128 == ctypes.sizeof(_lib.DsScaler)
     offs = {n: getattr(_lib.DsScaler, n).offset for n, _ in _lib.DsScaler._fields_}
     assert offs["overflow"] == 28 and offs["step"] == 32 and offs["last_overflow"] == 60
+    assert offs["grad_sumsq"] == 64 and offs["last_grad_sumsq"] == 72
 
 
 def test_status_strings():
@@ -99,17 +100,50 @@ def test_adam_validation():
     assert _adam(st=E + 16) == DS_ERR_ALIAS                            # state inside grad
 
 
+NAN, INF = float("nan"), float("inf")
+
+
 @pytest.mark.parametrize("bad", [
-    (-1e-4, 0.9, 0.999, 1e-8, 0.0, 1), (float("nan"), 0.9, 0.999, 1e-8, 0.0, 1),
-    (float("inf"), 0.9, 0.999, 1e-8, 0.0, 1), (1e-4, 1.0, 0.999, 1e-8, 0.0, 1),
-    (1e-4, -0.1, 0.999, 1e-8, 0.0, 1), (1e-4, 0.9, 1.0, 1e-8, 0.0, 1),
-    (1e-4, 0.9, float("nan"), 1e-8, 0.0, 1), (1e-4, 0.9, 0.999, 0.0, 0.0, 1),
-    (1e-4, 0.9, 0.999, -1e-8, 0.0, 1), (1e-4, 0.9, 0.999, float("inf"), 0.0, 1),
-    (1e-4, 0.9, 0.999, 1e-8, -0.01, 1), (1e-4, 0.9, 0.999, 1e-8, float("nan"), 1),
-    (1e-4, 0.9, 0.999, 1e-8, 0.0, 0), (1e-4, 0.9, 0.999, 1e-8, 0.0, -2),
+    # lr, beta1, beta2, eps, weight_decay, max_grad_norm, accum_steps
+    (-1e-4, 0.9, 0.999, 1e-8, 0.0, 0.0, 1), (NAN, 0.9, 0.999, 1e-8, 0.0, 0.0, 1),
+    (INF, 0.9, 0.999, 1e-8, 0.0, 0.0, 1), (1e-4, 1.0, 0.999, 1e-8, 0.0, 0.0, 1),
+    (1e-4, -0.1, 0.999, 1e-8, 0.0, 0.0, 1), (1e-4, 0.9, 1.0, 1e-8, 0.0, 0.0, 1),
+    (1e-4, 0.9, NAN, 1e-8, 0.0, 0.0, 1), (1e-4, 0.9, 0.999, 0.0, 0.0, 0.0, 1),
+    (1e-4, 0.9, 0.999, -1e-8, 0.0, 0.0, 1), (1e-4, 0.9, 0.999, INF, 0.0, 0.0, 1),
+    (1e-4, 0.9, 0.999, 1e-8, -0.01, 0.0, 1), (1e-4, 0.9, 0.999, 1e-8, NAN, 0.0, 1),
+    (1e-4, 0.9, 0.999, 1e-8, 0.0, 0.0, 0), (1e-4, 0.9, 0.999, 1e-8, 0.0, 0.0, -2),
+    (1e-4, 0.9, 0.999, 1e-8, 0.0, -1.0, 1), (1e-4, 0.9, 0.999, 1e-8, 0.0, NAN, 1),
+    (1e-4, 0.9, 0.999, 1e-8, 0.0, INF, 1),
 ])
 def test_adam_hyperparameter_validation(bad):
     assert _adam(hp=bad) == DS_ERR_HPARAM
+
+
+def test_sumsq_validation():
+    ws_need = L.ds_sumsq_workspace_bytes(10000)
+    assert ws_need == 8 * 3 and L.ds_sumsq_workspace_bytes(0) == 0
+    WS = 0x70000000
+    chk = L.ds_check_overflow_sumsq
+    assert chk(ST, A, DS_FP16, -1, WS, ws_need, STREAM) == DS_ERR_SIZE
+    assert chk(ST, A, 9, 10, WS, ws_need, STREAM) == DS_ERR_DTYPE
+    assert chk(None, A, DS_FP16, 10, WS, ws_need, STREAM) == DS_ERR_NULL
+    assert chk(ST, A, DS_FP16, 0, WS, ws_need, STREAM) == DS_OK
+    assert chk(ST, A, DS_FP16, 10000, None, ws_need, STREAM) == DS_ERR_NULL
+    assert chk(ST, A, DS_FP16, 10000, WS + 4, ws_need, STREAM) == DS_ERR_ALIGN
+    assert chk(ST, A, DS_FP16, 10000, WS, ws_need - 8, STREAM) == DS_ERR_SIZE
+    assert chk(ST, A + 8, DS_FP16, 10000, WS, ws_need, STREAM) == DS_ERR_ALIGN
+    assert chk(ST, A, DS_FP16, 10000, A + 64, ws_need, STREAM) == DS_ERR_ALIAS
+    assert chk(WS + 8, A, DS_FP16, 10000, WS, ws_need, STREAM) == DS_ERR_ALIAS   # state inside ws
+    acc = L.ds_accumulate_sumsq
+    assert acc(A, B, -1, 1, ST, WS, ws_need, STREAM) == DS_ERR_SIZE
+    assert acc(A, B, 10000, 1, None, WS, ws_need, STREAM) == DS_ERR_NULL
+    assert acc(A, B, 0, 1, ST, WS, ws_need, STREAM) == DS_OK
+    assert acc(None, B, 10000, 1, ST, WS, ws_need, STREAM) == DS_ERR_NULL
+    assert acc(A, B, 10000, 1, ST, None, ws_need, STREAM) == DS_ERR_NULL
+    assert acc(A, B + 4, 10000, 1, ST, WS, ws_need, STREAM) == DS_ERR_ALIGN
+    assert acc(A, B, 10000, 1, ST, WS, 8, STREAM) == DS_ERR_SIZE
+    assert acc(A, B, 10000, 1, ST, A + 1024, ws_need, STREAM) == DS_ERR_ALIAS
+    assert acc(A, A + 16, 10000, 1, ST, WS, ws_need, STREAM) == DS_ERR_ALIAS
 
 
 def test_state_and_scalar_validation():

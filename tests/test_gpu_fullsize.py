@@ -73,7 +73,7 @@ def run_sampled(torch, name):
     synth.device_fill_grad16(torch, tabs, p16, w.p16_key(), synth.GradSpec(0.02, 1.0))
     g16 = torch.empty(n, dtype=torch.int16, device="cuda:0")
     acc = torch.empty(n, dtype=torch.float32, device="cuda:0") if K > 1 else None
-    st = torch.zeros(64, dtype=torch.uint8, device="cuda:0")
+    st = torch.zeros(_lib.ds_scaler_size(), dtype=torch.uint8, device="cuda:0")
     _lib.ds_state_init(st, w.init_scale, w.min_scale, w.window, w.hysteresis, 0, 1)
     Id = torch.from_numpy(I).to("cuda:0")
 
@@ -93,9 +93,9 @@ def run_sampled(torch, name):
                                        k == 0, st if k == K - 1 else None)
         if K == 1:
             _lib.ds_check_overflow(st, g16, _lib.DS_FP16, n)
-            _lib.ds_adam_step(st, master, m, v, p16, g16, _lib.DS_FP16, n, LR, BETA1, BETA2, EPS, 0.0, 1)
+            _lib.ds_adam_step(st, master, m, v, p16, g16, _lib.DS_FP16, n, LR, BETA1, BETA2, EPS, 0.0, 0.0, 1)
         else:
-            _lib.ds_adam_step(st, master, m, v, p16, acc, _lib.DS_FP32, n, LR, BETA1, BETA2, EPS, 0.0, K)
+            _lib.ds_adam_step(st, master, m, v, p16, acc, _lib.DS_FP32, n, LR, BETA1, BETA2, EPS, 0.0, 0.0, K)
         _lib.ds_update_loss_scale(st)
         ov = oracle.step(o, gs_host if K > 1 else gs_host[0], **HP)
         assert ov == (inj is not None), f"[{name}] step {s}: oracle flag"

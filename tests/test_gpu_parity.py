@@ -124,7 +124,7 @@ def test_accumulate_buffer_bits_and_bucketed_calls(torch):
     for k, g in enumerate(gs):
         oracle.accumulate(acc_o, g, overwrite=(k == 0))
     acc = torch.full((n,), 7.0, device="cuda:0")
-    st = torch.zeros(64, dtype=torch.uint8, device="cuda:0")
+    st = torch.zeros(_lib.ds_scaler_size(), dtype=torch.uint8, device="cuda:0")
     _lib.ds_state_init(st, 1.0, 1.0, 1, 1, 0, 1)
     for k, g in enumerate(gs):
         gd = gu.dev_u16(torch, g)
@@ -182,7 +182,7 @@ def test_fp32_overflow_check(torch, n):
     from zero_mixed_precision_amd import _lib
     rng = np.random.default_rng(n)
     base = rng.normal(0, 1, n).astype(np.float32)
-    st = torch.zeros(64, dtype=torch.uint8, device="cuda:0")
+    st = torch.zeros(_lib.ds_scaler_size(), dtype=torch.uint8, device="cuda:0")
     for pos in (0, n // 2, n - 1):
         for bits in (0x7F800000, 0xFF800000, 0x7FC00000, 0x7F800001, 0x7F7FFFFF, 0x00000001):
             a = base.copy()
@@ -207,7 +207,7 @@ def test_fp16_overflow_check_all_patterns(torch):
         pos = (np.arange(chunk.size) * 97) % n
         a[np.arange(chunk.size), pos] = chunk
         da = gu.dev_u16(torch, a.reshape(-1))
-        states = torch.zeros((chunk.size, 64), dtype=torch.uint8, device="cuda:0")
+        states = torch.zeros((chunk.size, _lib.ds_scaler_size()), dtype=torch.uint8, device="cuda:0")
         for j in range(chunk.size):
             _lib.ds_check_overflow(states[j].data_ptr(), da.data_ptr() + 2 * stride * j, _lib.DS_FP16, n)
         got[c0:c0 + chunk.size] = states.cpu().numpy()[:, 28:32].copy().view(np.uint32)[:, 0] != 0
@@ -285,7 +285,7 @@ def test_bias_correction_scalars_bit_exact(torch):
     from zero_mixed_precision_amd import _lib
     ts = list(range(1, 3001)) + sorted({int(x) for x in np.logspace(3.5, 8, 150)})
     hps = [(1e-4, 0.9, 0.999), (3e-4, 0.95, 0.98), (1e-3, 0.5, 0.9999)]
-    st = torch.zeros(64, dtype=torch.uint8, device="cuda:0")
+    st = torch.zeros(_lib.ds_scaler_size(), dtype=torch.uint8, device="cuda:0")
     out = torch.zeros((len(hps), len(ts), 2), dtype=torch.float32, device="cuda:0")
     _lib.ds_state_init(st, 1.0, 1.0, 1, 1, 0, 1)
     base = _lib.ds_state_read(st)
@@ -359,7 +359,7 @@ def test_fp16_cast_of_every_fp32_pattern(torch):
     v = torch.zeros(chunk, dtype=torch.float32, device="cuda:0")
     p16 = torch.empty(chunk, dtype=torch.int16, device="cuda:0")
     g = torch.zeros(chunk, dtype=torch.int16, device="cuda:0")
-    st = torch.zeros(64, dtype=torch.uint8, device="cuda:0")
+    st = torch.zeros(_lib.ds_scaler_size(), dtype=torch.uint8, device="cuda:0")
     with ThreadPoolExecutor(8) as pool:
         for lo in range(0, 1 << 32, chunk):
             x = np.arange(lo, lo + chunk, dtype=np.uint32).view(np.float32)
@@ -368,7 +368,7 @@ def test_fp16_cast_of_every_fp32_pattern(torch):
             v.zero_()
             _lib.ds_state_init(st, 1.0, 1.0, 1000, 1, 0, 1)
             _lib.ds_adam_step(st, master, m, v, p16, g, _lib.DS_FP16, chunk, LR, BETA1, BETA2, EPS,
-                              0.0, 1)
+                              0.0, 0.0, 1)
             got = gu.host_u16(p16)
             want = _enc16_parallel(pool, x)
             nan_in = np.isnan(x)

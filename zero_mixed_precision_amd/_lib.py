@@ -20,12 +20,13 @@ DS_FP16, DS_FP32 = 1, 2
 EXPORTED = (
     "ds_scaler_size", "ds_state_init", "ds_state_read", "ds_state_write", "ds_accumulate",
     "ds_check_overflow", "ds_adam_step", "ds_update_loss_scale", "ds_adam_bias_scalars",
-    "ds_layout_greedy", "ds_partition_range", "ds_status_string",
+    "ds_layout_greedy", "ds_partition_range", "ds_status_string", "ds_sumsq_workspace_bytes",
+    "ds_check_overflow_sumsq", "ds_accumulate_sumsq",
 )
 
 
 class DsScaler(ctypes.Structure):
-    """Mirror of ``ds_scaler`` (64 bytes)."""
+    """Mirror of ``ds_scaler`` (128 bytes)."""
     _fields_ = [
         ("scale", ctypes.c_float),
         ("min_scale", ctypes.c_float),
@@ -40,10 +41,13 @@ class DsScaler(ctypes.Structure):
         ("skipped", ctypes.c_int64),
         ("consecutive_hysteresis", ctypes.c_int32),
         ("last_overflow", ctypes.c_uint32),
+        ("grad_sumsq", ctypes.c_double),
+        ("last_grad_sumsq", ctypes.c_double),
+        ("reserved", ctypes.c_uint8 * 48),
     ]
 
     def as_dict(self) -> dict:
-        return {name: getattr(self, name) for name, _ in self._fields_}
+        return {name: getattr(self, name) for name, _ in self._fields_ if name != "reserved"}
 
 
 class DsError(RuntimeError):
@@ -52,10 +56,33 @@ class DsError(RuntimeError):
         super().__init__(f"{where}: {status_string(status)}")
 
 
+def bind_torch_hip_runtime() -> None:
+    """Put the HIP runtime that PyTorch uses into the global symbol scope.
+
+    A PyTorch-ROCm install carries its own libamdhip64; the library is linked
+    against the system one.  The dynamic linker binds the library's HIP calls
+    (fatbinary registration, kernel launches) to the first definition in the
+    global scope, so without this step the binding depends on import order: if
+    libdszero.so loads before torch, its kernels go to a second runtime that
+    knows nothing of torch's streams (and a hipStream_t of one runtime is not a
+    stream of the other).  With torch's runtime global first, every launch uses
+    the runtime that owns the caller's memory and streams.  Without torch (a
+    plain C caller) the library uses the runtime it was linked against.
+    """
+    try:
+        import torch
+    except ImportError:
+        return
+    path = os.path.join(os.path.dirname(torch.__file__), "lib", "libamdhip64.so")
+    if os.path.exists(path):
+        ctypes.CDLL(path, mode=ctypes.RTLD_GLOBAL)
+
+
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() "
                           "(python -m zero_mixed_precision_amd.build)")
+    bind_torch_hip_runtime()
     L = ctypes.CDLL(LIB_PATH)
     vp, i64, i32, f32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_float
     sig = {
@@ -65,8 +92,11 @@ def _load():
         "ds_state_write": ([vp, ctypes.POINTER(DsScaler), vp], ctypes.c_int),
         "ds_accumulate": ([vp, vp, i64, i32, vp, vp], ctypes.c_int),
         "ds_check_overflow": ([vp, vp, ctypes.c_int, i64, vp], ctypes.c_int),
-        "ds_adam_step": ([vp, vp, vp, vp, vp, vp, ctypes.c_int, i64, f32, f32, f32, f32, f32, i32, vp],
-                         ctypes.c_int),
+        "ds_adam_step": ([vp, vp, vp, vp, vp, vp, ctypes.c_int, i64, f32, f32, f32, f32, f32, f32, i32,
+                          vp], ctypes.c_int),
+        "ds_sumsq_workspace_bytes": ([i64], ctypes.c_size_t),
+        "ds_check_overflow_sumsq": ([vp, vp, ctypes.c_int, i64, vp, ctypes.c_size_t, vp], ctypes.c_int),
+        "ds_accumulate_sumsq": ([vp, vp, i64, i32, vp, vp, ctypes.c_size_t, vp], ctypes.c_int),
         "ds_update_loss_scale": ([vp, vp], ctypes.c_int),
         "ds_adam_bias_scalars": ([vp, f32, f32, f32, vp, vp], ctypes.c_int),
         "ds_layout_greedy": ([vp, i32, i64, i64, vp, vp, vp, vp, ctypes.POINTER(i32),
@@ -143,10 +173,31 @@ def ds_check_overflow(st, grad, dtype, n, stream=None) -> None:
 
 
 def ds_adam_step(st, master, m, v, p16, grad, dtype, n, lr, beta1, beta2, eps, weight_decay,
-                 accum_steps, stream=None) -> None:
+                 max_grad_norm, accum_steps, stream=None) -> None:
     _ok(lib.ds_adam_step(_p(st), _p(master), _p(m), _p(v), _p(p16), _p(grad), int(dtype), int(n),
-                         lr, beta1, beta2, eps, weight_decay, int(accum_steps), _s(stream)),
-        "ds_adam_step")
+                         lr, beta1, beta2, eps, weight_decay, max_grad_norm, int(accum_steps),
+                         _s(stream)), "ds_adam_step")
+
+
+def ds_sumsq_workspace_bytes(n) -> int:
+    return lib.ds_sumsq_workspace_bytes(int(n))
+
+
+def _nbytes(ws, ws_bytes):
+    if ws_bytes is not None:
+        return int(ws_bytes)
+    return ws.numel() * ws.element_size()
+
+
+def ds_check_overflow_sumsq(st, grad, dtype, n, workspace, workspace_bytes=None, stream=None) -> None:
+    _ok(lib.ds_check_overflow_sumsq(_p(st), _p(grad), int(dtype), int(n), _p(workspace),
+                                    _nbytes(workspace, workspace_bytes), _s(stream)),
+        "ds_check_overflow_sumsq")
+
+
+def ds_accumulate_sumsq(acc, g16, n, overwrite, st, workspace, workspace_bytes=None, stream=None) -> None:
+    _ok(lib.ds_accumulate_sumsq(_p(acc), _p(g16), int(n), int(bool(overwrite)), _p(st), _p(workspace),
+                                _nbytes(workspace, workspace_bytes), _s(stream)), "ds_accumulate_sumsq")
 
 
 def ds_update_loss_scale(st, stream=None) -> None:

@@ -1,7 +1,7 @@
 """The ds_config.json keys the optimizer step consumes.
 
 "DeepSpeed complete guide" section 4.1 (base structure: gradient_accumulation_steps,
-fp16, optimizer, zero_optimization), section 4.2 (fp16 block: loss_scale 0 is
+gradient_clipping, fp16, optimizer, zero_optimization), section 4.2 (fp16 block: loss_scale 0 is
 dynamic, initial scale 2^initial_scale_power, loss_scale_window,
 hysteresis, consecutive_hysteresis, min_loss_scale), section 4.3
 (train_batch_size = micro batch x gradient_accumulation_steps x world size).
@@ -35,6 +35,8 @@ class ZeroMPConfig:
     betas: tuple = (0.9, 0.999)
     eps: float = 1e-8
     weight_decay: float = 0.0
+    # global-norm clipping of the unscaled gradient (0: off)
+    gradient_clipping: float = 0.0
     # batch / ZeRO
     gradient_accumulation_steps: int = 1
     train_micro_batch_size_per_gpu: int = 1
@@ -76,6 +78,7 @@ class ZeroMPConfig:
             betas=betas,
             eps=float(_val(params, "eps", 1e-8)),
             weight_decay=float(_val(params, "weight_decay", 0.0)),
+            gradient_clipping=float(_val(cfg, "gradient_clipping", 0.0)),
             gradient_accumulation_steps=int(_val(cfg, "gradient_accumulation_steps", 1)),
             train_micro_batch_size_per_gpu=int(_val(cfg, "train_micro_batch_size_per_gpu", 1)),
             reduce_bucket_size=int(float(_val(zero, "reduce_bucket_size", 2e8))),

@@ -42,7 +42,7 @@
 
 #pragma clang fp contract(off)
 
-static_assert(sizeof(ds_scaler) == 64, "ds_scaler must stay 64 bytes");
+static_assert(sizeof(ds_scaler) == 128, "ds_scaler must stay 128 bytes");
 
 namespace {
 
@@ -53,6 +53,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kStepBlock = 256;    // lanes per block of the read/write kernels
 constexpr int kCheckBlock = 1024;  // lanes per block of the read-only check
 constexpr int64_t kMaxBlocks = int64_t(1) << 22;
+constexpr int64_t kChunk = 4096;   // elements per chunk of the gradient sum of squares
 
 // ---------------------------------------------------------------------------
 // memory helpers
@@ -125,16 +126,69 @@ __device__ __forceinline__ void raise_flag(ds_scaler* st, uint32_t bad)
 }
 
 // ---------------------------------------------------------------------------
+// gradient sum of squares (global-norm clipping), deterministic
+// ---------------------------------------------------------------------------
+
+// Sum over a block in a fixed order: a fixed xor butterfly inside each wave
+// (lane 0's result is used), then the waves' sums in wave order.  The result
+// is meaningful in thread 0.  Every thread of the block must call it.
+template <int TPB>
+__device__ __forceinline__ double block_sum_fixed(double x, double* lds)
+{
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1)
+        x = x + __shfl_xor(x, off);
+    if ((threadIdx.x & 63) == 0)
+        lds[threadIdx.x >> 6] = x;
+    __syncthreads();
+    double total = 0.0;
+    if (threadIdx.x == 0)
+        for (int w = 0; w < TPB / 64; ++w)
+            total = total + lds[w];
+    __syncthreads();
+    return total;
+}
+
+__device__ __forceinline__ double sq(float x)
+{
+    const double d = static_cast<double>(x);
+    return d * d;  // exact: a 24-bit significand squared fits in 53 bits
+}
+
+__device__ __forceinline__ double sq4(const f32x4& x)
+{
+    return ((sq(x.x) + sq(x.y)) + sq(x.z)) + sq(x.w);
+}
+
+// Second pass of the sum of squares: one block adds the chunk sums in a fixed
+// order (lane j takes chunks j, j + TPB, ..., then the fixed block sum) into
+// st->grad_sumsq.  The chunking is fixed by n, so the result does not depend
+// on the grid of the first pass.
+template <int TPB>
+__global__ __launch_bounds__(TPB) void sumsq_finish_kernel(ds_scaler* __restrict__ st,
+                                                           const double* __restrict__ part,
+                                                           int64_t nchunks)
+{
+    __shared__ double lds[TPB / 64];
+    double s = 0.0;
+    for (int64_t i = threadIdx.x; i < nchunks; i += TPB)
+        s = s + part[i];
+    const double total = block_sum_fixed<TPB>(s, lds);
+    if (threadIdx.x == 0)
+        st->grad_sumsq = st->grad_sumsq + total;
+}
+
+// ---------------------------------------------------------------------------
 // Adam
 // ---------------------------------------------------------------------------
 
 struct AdamHyper {
-    float lr, beta1, beta2, eps, weight_decay;
+    float lr, beta1, beta2, eps, weight_decay, max_grad_norm;
     int32_t accum_steps;
 };
 
 struct AdamConsts {
-    float inv;        // 1 / (S * K)
+    float inv;        // 1 / (S * K), times the clipping coefficient when clipping
     float b1, b2;     // beta1, beta2
     float omb1, omb2; // 1 - beta1, 1 - beta2
     float lrwd;       // lr * weight_decay
@@ -162,17 +216,25 @@ __device__ __forceinline__ void bias_scalars(int64_t t, float lr, float beta1, f
     *rbc2 = static_cast<float>(1.0 / sqrt(1.0 - r2));
 }
 
-__device__ __forceinline__ AdamConsts make_consts(float scale, int64_t t, const AdamHyper& h)
+__device__ __forceinline__ AdamConsts make_consts(const ds_scaler* st, const AdamHyper& h)
 {
     AdamConsts c;
-    c.inv = 1.0f / (scale * static_cast<float>(h.accum_steps));
+    c.inv = 1.0f / (st->scale * static_cast<float>(h.accum_steps));
+    if (h.max_grad_norm > 0.0f) {
+        // global-norm clipping of the unscaled gradient
+        const double inv64 = static_cast<double>(c.inv);
+        const double norm = sqrt(st->grad_sumsq) * inv64;
+        const double ratio = static_cast<double>(h.max_grad_norm) / (norm + 1e-6);
+        const double coef = ratio < 1.0 ? ratio : 1.0;
+        c.inv = static_cast<float>(inv64 * coef);
+    }
     c.b1 = h.beta1;
     c.b2 = h.beta2;
     c.omb1 = 1.0f - h.beta1;
     c.omb2 = 1.0f - h.beta2;
     c.lrwd = h.lr * h.weight_decay;
     c.eps = h.eps;
-    bias_scalars(t, h.lr, h.beta1, h.beta2, &c.step_size, &c.rbc2);
+    bias_scalars(st->step + 1, h.lr, h.beta1, h.beta2, &c.step_size, &c.rbc2);
     return c;
 }
 
@@ -246,7 +308,7 @@ __global__ __launch_bounds__(TPB) void adam_kernel(const ds_scaler* __restrict__
 {
     if (st->overflow != 0u)
         return;
-    const AdamConsts c = make_consts(st->scale, st->step + 1, hp);
+    const AdamConsts c = make_consts(st, hp);
 
     f32x4* P = reinterpret_cast<f32x4*>(master);
     f32x4* M = reinterpret_cast<f32x4*>(mom1);
@@ -342,16 +404,90 @@ __global__ __launch_bounds__(TPB) void check_kernel(ds_scaler* __restrict__ st,
     raise_flag(st, bad);
 }
 
+// Overflow check plus the chunk sums of squares.  A chunk is TPB lanes x
+// kVecs 16-byte vectors (fp16: 512 x 4 x 8, fp32: 1024 x 4 x 4 = 16,384
+// elements); vector j of lane l is vector j * TPB + l of the chunk, so each
+// of the kVecs loads is one contiguous span across the block, and each lane
+// sums its elements in order.
+template <bool F32, int TPB>
+__global__ __launch_bounds__(TPB) void check_sumsq_kernel(ds_scaler* __restrict__ st,
+                                                          const void* __restrict__ grad, int64_t n,
+                                                          double* __restrict__ part)
+{
+    constexpr int kPer = F32 ? 4 : 8;
+    constexpr int kVecs = 4;
+    constexpr int64_t kCh = static_cast<int64_t>(TPB) * kVecs * kPer;
+    static_assert(kCh == 4 * kChunk, "four 4096-element units per chunk");
+    __shared__ double lds[TPB / 64];
+    const u32x4* G = static_cast<const u32x4*>(grad);
+    const int64_t nchunks = (n + kCh - 1) / kCh;
+    uint32_t bad = 0u;
+    for (int64_t c = blockIdx.x; c < nchunks; c += gridDim.x) {
+        const int64_t v0 = c * (kCh / kPer) + threadIdx.x;
+        u32x4 w[kVecs];
+        bool full[kVecs];
+#pragma unroll
+        for (int j = 0; j < kVecs; ++j) {
+            const int64_t v = v0 + static_cast<int64_t>(j) * TPB;
+            full[j] = (v + 1) * kPer <= n;
+            if (full[j])
+                w[j] = G[v];
+        }
+        double s = 0.0;
+#pragma unroll
+        for (int j = 0; j < kVecs; ++j) {
+            const int64_t e0 = (v0 + static_cast<int64_t>(j) * TPB) * kPer;
+            if (full[j]) {
+                if constexpr (F32) {
+                    bad |= nonfinite_f32(w[j].x) | nonfinite_f32(w[j].y) | nonfinite_f32(w[j].z) |
+                           nonfinite_f32(w[j].w);
+                    s = s + sq4(f32x4{__uint_as_float(w[j].x), __uint_as_float(w[j].y),
+                                      __uint_as_float(w[j].z), __uint_as_float(w[j].w)});
+                } else {
+                    bad |= nonfinite_f16x2(w[j].x) | nonfinite_f16x2(w[j].y) | nonfinite_f16x2(w[j].z) |
+                           nonfinite_f16x2(w[j].w);
+                    s = s + sq4(widen4(u32x2{w[j].x, w[j].y}));
+                    s = s + sq4(widen4(u32x2{w[j].z, w[j].w}));
+                }
+            } else {
+                for (int k = 0; k < kPer; ++k) {
+                    const int64_t i = e0 + k;
+                    if (i < n) {
+                        if constexpr (F32) {
+                            const uint32_t bits = static_cast<const uint32_t*>(grad)[i];
+                            bad |= nonfinite_f32(bits);
+                            s = s + sq(__uint_as_float(bits));
+                        } else {
+                            const uint32_t bits = static_cast<const uint16_t*>(grad)[i];
+                            bad |= nonfinite_f16x2(bits);
+                            s = s + sq(h2f(bits));
+                        }
+                    }
+                }
+            }
+        }
+        const double cs = block_sum_fixed<TPB>(s, lds);
+        if (threadIdx.x == 0)
+            part[c] = cs;
+    }
+    raise_flag(st, bad);
+}
+
 // ---------------------------------------------------------------------------
 // gradient accumulation
 // ---------------------------------------------------------------------------
 
-// Same tiling as the Adam kernel.
-template <bool OVERWRITE, bool CHECK, bool NT, int TPB, int U>
+// Same tiling as the Adam kernel.  With SUMSQ (which needs CHECK and U * TPB
+// * 4 == 4096) each tile is one chunk of the sum of squares of the result,
+// written to part[tile].
+template <bool OVERWRITE, bool CHECK, bool SUMSQ, bool NT, int TPB, int U>
 __global__ __launch_bounds__(TPB) void accumulate_kernel(float* __restrict__ acc,
                                                          const uint16_t* __restrict__ g16,
-                                                         int64_t n, ds_scaler* __restrict__ st)
+                                                         int64_t n, ds_scaler* __restrict__ st,
+                                                         double* __restrict__ part)
 {
+    static_assert(!SUMSQ || (CHECK && U * TPB * 4 == kChunk), "a tile is one chunk");
+    __shared__ double lds[SUMSQ ? TPB / 64 : 1];
     f32x4* A = reinterpret_cast<f32x4*>(acc);
     const u32x2* G = reinterpret_cast<const u32x2*>(g16);
     constexpr int T = U * TPB;
@@ -361,6 +497,7 @@ __global__ __launch_bounds__(TPB) void accumulate_kernel(float* __restrict__ acc
     for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
         const int64_t q0 = tile * T + threadIdx.x;
         f32x4 g[U], a[U];
+        double s = 0.0;
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             g[u] = widen4(load<NT>(G + q0 + u * TPB));
@@ -376,10 +513,18 @@ __global__ __launch_bounds__(TPB) void accumulate_kernel(float* __restrict__ acc
                 r = a[u] + g[u];
             if constexpr (CHECK)
                 bad |= nonfinite_f32x4(r);
+            if constexpr (SUMSQ)
+                s = s + sq4(r);
             store<NT>(A + q0 + u * TPB, r);
+        }
+        if constexpr (SUMSQ) {
+            const double cs = block_sum_fixed<TPB>(s, lds);
+            if (threadIdx.x == 0)
+                part[tile] = cs;
         }
     }
     if (blockIdx.x == 0) {
+        double s = 0.0;
         for (int64_t q = ntiles * T + threadIdx.x; q < nq; q += TPB) {
             const f32x4 g = widen4(load<NT>(G + q));
             f32x4 r;
@@ -389,6 +534,8 @@ __global__ __launch_bounds__(TPB) void accumulate_kernel(float* __restrict__ acc
                 r = load<NT>(A + q) + g;
             if constexpr (CHECK)
                 bad |= nonfinite_f32x4(r);
+            if constexpr (SUMSQ)
+                s = s + sq4(r);
             store<NT>(A + q, r);
         }
         if (static_cast<int64_t>(threadIdx.x) < (n & 3)) {
@@ -397,7 +544,16 @@ __global__ __launch_bounds__(TPB) void accumulate_kernel(float* __restrict__ acc
             const float r = OVERWRITE ? g : acc[i] + g;
             if constexpr (CHECK)
                 bad |= nonfinite_f32(__float_as_uint(r));
+            if constexpr (SUMSQ)
+                s = s + sq(r);
             acc[i] = r;
+        }
+        if constexpr (SUMSQ) {
+            if (ntiles * T * 4 < n) {          // a last, partial chunk exists
+                const double cs = block_sum_fixed<TPB>(s, lds);
+                if (threadIdx.x == 0)
+                    part[ntiles] = cs;
+            }
         }
     }
     if constexpr (CHECK)
@@ -439,6 +595,8 @@ __global__ void update_scale_kernel(ds_scaler* st)
     }
     s.last_overflow = ov;
     s.overflow = 0u;
+    s.last_grad_sumsq = s.grad_sumsq;
+    s.grad_sumsq = 0.0;
     *st = s;
 }
 
@@ -525,9 +683,24 @@ void launch_acc_u(int unroll, unsigned blocks, hipStream_t s, float* acc, const 
                   ds_scaler* st)
 {
     if (unroll == 2)
-        accumulate_kernel<OW, CK, NT, kStepBlock, 2><<<blocks, kStepBlock, 0, s>>>(acc, g16, n, st);
+        accumulate_kernel<OW, CK, false, NT, kStepBlock, 2><<<blocks, kStepBlock, 0, s>>>(acc, g16, n, st, nullptr);
     else
-        accumulate_kernel<OW, CK, NT, kStepBlock, 4><<<blocks, kStepBlock, 0, s>>>(acc, g16, n, st);
+        accumulate_kernel<OW, CK, false, NT, kStepBlock, 4><<<blocks, kStepBlock, 0, s>>>(acc, g16, n, st, nullptr);
+}
+
+int64_t sumsq_chunks(int64_t n) { return (n + kChunk - 1) / kChunk; }
+
+// validation shared by the two sum-of-squares entry points (one fp64 partial
+// sum per 4096-element chunk)
+ds_status check_workspace(const void* ws, size_t ws_bytes, int64_t n)
+{
+    if (ws == nullptr)
+        return DS_ERR_NULL;
+    if (!aligned(ws, 8))
+        return DS_ERR_ALIGN;
+    if (ws_bytes < 8 * static_cast<size_t>(sumsq_chunks(n)))
+        return DS_ERR_SIZE;
+    return DS_OK;
 }
 
 }  // namespace
@@ -663,15 +836,15 @@ ds_status ds_check_overflow(ds_scaler* st, const void* grad, ds_dtype dt, int64_
 
 ds_status ds_adam_step(const ds_scaler* st, float* master, float* m, float* v, uint16_t* p16,
                        const void* grad, ds_dtype dt, int64_t n, float lr, float beta1,
-                       float beta2, float eps, float weight_decay, int32_t accum_steps,
-                       void* stream)
+                       float beta2, float eps, float weight_decay, float max_grad_norm,
+                       int32_t accum_steps, void* stream)
 {
     if (n < 0)
         return DS_ERR_SIZE;
     if (dt != DS_FP16 && dt != DS_FP32)
         return DS_ERR_DTYPE;
     if (!finite_ge0(lr) || !beta_ok(beta1) || !beta_ok(beta2) || !std::isfinite(eps) || eps <= 0.0f ||
-        !finite_ge0(weight_decay) || accum_steps < 1)
+        !finite_ge0(weight_decay) || !finite_ge0(max_grad_norm) || accum_steps < 1)
         return DS_ERR_HPARAM;
     if (st == nullptr)
         return DS_ERR_NULL;
@@ -691,7 +864,7 @@ ds_status ds_adam_step(const ds_scaler* st, float* master, float* m, float* v, u
             if (overlap(ptrs[i], sizes[i], ptrs[j], sizes[j]))
                 return DS_ERR_ALIAS;
 
-    const AdamHyper hp{lr, beta1, beta2, eps, weight_decay, accum_steps};
+    const AdamHyper hp{lr, beta1, beta2, eps, weight_decay, max_grad_norm, accum_steps};
     hipStream_t s = static_cast<hipStream_t>(stream);
     const int unroll = variant_unroll();
     const unsigned blocks = grid_blocks(tiles_of(n, unroll));
@@ -704,6 +877,85 @@ ds_status ds_adam_step(const ds_scaler* st, float* master, float* m, float* v, u
         if (wd) launch_adam_nt<true, true>(nt, unroll, blocks, s, st, master, m, v, p16, grad, n, hp);
         else    launch_adam_nt<true, false>(nt, unroll, blocks, s, st, master, m, v, p16, grad, n, hp);
     }
+    return launched();
+}
+
+size_t ds_sumsq_workspace_bytes(int64_t n)
+{
+    return 8 * static_cast<size_t>(sumsq_chunks(n > 0 ? n : 0));
+}
+
+ds_status ds_check_overflow_sumsq(ds_scaler* st, const void* grad, ds_dtype dt, int64_t n,
+                                  void* workspace, size_t workspace_bytes, void* stream)
+{
+    if (n < 0)
+        return DS_ERR_SIZE;
+    if (dt != DS_FP16 && dt != DS_FP32)
+        return DS_ERR_DTYPE;
+    if (st == nullptr)
+        return DS_ERR_NULL;
+    if (n == 0)
+        return DS_OK;
+    if (grad == nullptr)
+        return DS_ERR_NULL;
+    if (!aligned(grad, 16) || !aligned(st, 8))
+        return DS_ERR_ALIGN;
+    if (const ds_status w = check_workspace(workspace, workspace_bytes, n); w != DS_OK)
+        return w;
+    const uint64_t gb = (dt == DS_FP16 ? 2 : 4) * static_cast<uint64_t>(n);
+    const uint64_t wb = 8 * static_cast<uint64_t>(sumsq_chunks(n));
+    if (overlap(grad, gb, st, sizeof(ds_scaler)) || overlap(grad, gb, workspace, wb) ||
+        overlap(st, sizeof(ds_scaler), workspace, wb))
+        return DS_ERR_ALIAS;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int64_t chunks = (n + 4 * kChunk - 1) / (4 * kChunk);   // 16,384-element chunks
+    const unsigned blocks = grid_blocks(chunks);
+    double* part = static_cast<double*>(workspace);
+    if (dt == DS_FP16)
+        check_sumsq_kernel<false, 512><<<blocks, 512, 0, s>>>(st, grad, n, part);
+    else
+        check_sumsq_kernel<true, 1024><<<blocks, 1024, 0, s>>>(st, grad, n, part);
+    if (launched() != DS_OK)
+        return DS_ERR_HIP;
+    sumsq_finish_kernel<1024><<<1, 1024, 0, s>>>(st, part, chunks);
+    return launched();
+}
+
+ds_status ds_accumulate_sumsq(float* acc, const uint16_t* g16, int64_t n, int32_t overwrite,
+                              ds_scaler* st, void* workspace, size_t workspace_bytes, void* stream)
+{
+    if (n < 0)
+        return DS_ERR_SIZE;
+    if (st == nullptr)
+        return DS_ERR_NULL;
+    if (n == 0)
+        return DS_OK;
+    if (acc == nullptr || g16 == nullptr)
+        return DS_ERR_NULL;
+    if (!aligned(acc, 16) || !aligned(g16, 16) || !aligned(st, 8))
+        return DS_ERR_ALIGN;
+    if (const ds_status w = check_workspace(workspace, workspace_bytes, n); w != DS_OK)
+        return w;
+    const uint64_t un = static_cast<uint64_t>(n);
+    const uint64_t wb = 8 * static_cast<uint64_t>(sumsq_chunks(n));
+    const void* ptrs[4] = {acc, g16, st, workspace};
+    const uint64_t sizes[4] = {4 * un, 2 * un, sizeof(ds_scaler), wb};
+    for (int i = 0; i < 4; ++i)
+        for (int j = i + 1; j < 4; ++j)
+            if (overlap(ptrs[i], sizes[i], ptrs[j], sizes[j]))
+                return DS_ERR_ALIAS;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    // the tile must be one 4096-element chunk: U = 4 whatever DSZERO_UNROLL says
+    const unsigned blocks = grid_blocks(tiles_of(n, 4));
+    double* part = static_cast<double*>(workspace);
+    const bool nt = variant_nt();
+#define DS_ACCS(OW, NT) accumulate_kernel<OW, true, true, NT, kStepBlock, 4><<<blocks, kStepBlock, 0, s>>>(acc, g16, n, st, part)
+    if (nt) { if (overwrite) DS_ACCS(true, true); else DS_ACCS(false, true); }
+    else    { if (overwrite) DS_ACCS(true, false); else DS_ACCS(false, false); }
+#undef DS_ACCS
+    if (launched() != DS_OK)
+        return DS_ERR_HIP;
+    sumsq_finish_kernel<1024><<<1, 1024, 0, s>>>(st, part, sumsq_chunks(n));
     return launched();
 }
 

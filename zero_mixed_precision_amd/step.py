@@ -10,6 +10,10 @@ scales and accumulates, step() updates):
     K = 1:  ds_check_overflow on the fp16 gradient, then ds_adam_step on it
     then    ds_update_loss_scale (once)
 
+With gradient clipping configured the check passes are the _sumsq variants
+(ds_accumulate_sumsq / ds_check_overflow_sumsq), which also gather the
+gradient's sum of squares for ds_adam_step's global-norm clipping.
+
 No call synchronises the host; ``scaler()`` reads the state back (one copy).
 ``graph(grads)`` records the whole sequence for fixed gradient buffers into a
 HIP graph, so a step costs one graph launch; it contains kernels only (no
@@ -19,6 +23,10 @@ from __future__ import annotations
 
 from . import _lib
 from .config import ZeroMPConfig
+
+
+def buckets_or_all(buckets, n):
+    return [(b.start, b.size) for b in buckets] if buckets else [(0, n)]
 
 
 class ShardStep:
@@ -34,9 +42,15 @@ class ShardStep:
         self.v = torch.zeros(self.n, **f32)
         self.p16 = torch.empty(self.n, dtype=torch.float16, device=device)
         self.acc = torch.empty(self.n, **f32) if self.K > 1 else None
-        self.state = torch.zeros(64, dtype=torch.uint8, device=device)
+        self.state = torch.zeros(_lib.ds_scaler_size(), dtype=torch.uint8, device=device)
+        self.clip = float(cfg.gradient_clipping)
+        self.ws = None
+        if self.clip > 0:
+            # chunk sums of the gradient's sum of squares (scratch, no initial contents)
+            nbytes = _lib.ds_sumsq_workspace_bytes(self.n)
+            self.ws = torch.zeros((nbytes + 7) // 8, dtype=torch.float64, device=device)
         # accumulation granularity: the reduce buckets inside this partition
-        self.buckets = [(b.start, b.size) for b in buckets] if buckets else [(0, self.n)]
+        self.buckets = buckets_or_all(buckets, self.n)
         self._micro = 0
         _lib.ds_state_init(self.state, cfg.init_scale, cfg.min_loss_scale, cfg.loss_scale_window,
                            cfg.hysteresis, int(cfg.consecutive_hysteresis), int(cfg.dynamic),
@@ -48,9 +62,12 @@ class ShardStep:
         k = self._micro
         last = k == self.K - 1
         for start, size in self.buckets:
-            _lib.ds_accumulate(self.acc.data_ptr() + 4 * start, g16.data_ptr() + 2 * start, size,
-                               overwrite=(k == 0), st_or_null=self.state if last else None,
-                               stream=self.stream)
+            a, g = self.acc.data_ptr() + 4 * start, g16.data_ptr() + 2 * start
+            if last and self.ws is not None:
+                _lib.ds_accumulate_sumsq(a, g, size, k == 0, self.state, self.ws, stream=self.stream)
+            else:
+                _lib.ds_accumulate(a, g, size, overwrite=(k == 0),
+                                   st_or_null=self.state if last else None, stream=self.stream)
         self._micro = k + 1
 
     def step(self, g16=None) -> None:
@@ -58,13 +75,18 @@ class ShardStep:
         c = self.cfg
         if self.K == 1:
             assert g16 is not None and g16.numel() == self.n
-            _lib.ds_check_overflow(self.state, g16, _lib.DS_FP16, self.n, self.stream)
+            if self.ws is not None:
+                _lib.ds_check_overflow_sumsq(self.state, g16, _lib.DS_FP16, self.n, self.ws,
+                                             stream=self.stream)
+            else:
+                _lib.ds_check_overflow(self.state, g16, _lib.DS_FP16, self.n, self.stream)
             grad, dt = g16, _lib.DS_FP16
         else:
             assert self._micro == self.K, "accumulate() must be called K times before step()"
             grad, dt = self.acc, _lib.DS_FP32
         _lib.ds_adam_step(self.state, self.master, self.m, self.v, self.p16, grad, dt, self.n, c.lr,
-                          c.betas[0], c.betas[1], c.eps, c.weight_decay, self.K, self.stream)
+                          c.betas[0], c.betas[1], c.eps, c.weight_decay, c.gradient_clipping, self.K,
+                          self.stream)
         _lib.ds_update_loss_scale(self.state, self.stream)
         self._micro = 0
 
