@@ -71,6 +71,9 @@ def gpu_run(args):
 
     w = WORKLOADS[args.workload]
     n, K = w.psi, w.K
+    # bf16 mode: bf16 gradients and parameter copy, no loss scaling (static scale 1)
+    gdt16 = _lib.DS_BF16 if args.bf16 else _lib.DS_FP16
+    gspec = synth.GradSpec(w.sigma, 1.0, w.heavy_tail, fmt="bf16") if args.bf16 else w.grad_spec
     dev = torch.device("cuda:0")
     props = torch.cuda.get_device_properties(dev)
     log(f"device: {props.name} CUs={props.multi_processor_count} mem={props.total_memory / 2**30:.0f} GiB")
@@ -85,7 +88,10 @@ def gpu_run(args):
     synth.device_fill_grad16(torch, tabs, p16, w.p16_key(), synth.GradSpec(0.02, 1.0))
     acc = torch.empty(n, dtype=torch.float32, device=dev) if K > 1 else None
     st = torch.zeros(_lib.ds_scaler_size(), dtype=torch.uint8, device=dev)
-    _lib.ds_state_init(st, w.init_scale, w.min_scale, w.window, w.hysteresis, 0, 1)
+    if args.bf16:
+        _lib.ds_state_init(st, 1.0, 1.0, w.window, w.hysteresis, 0, 0)
+    else:
+        _lib.ds_state_init(st, w.init_scale, w.min_scale, w.window, w.hysteresis, 0, 1)
     if w.ragged:
         buckets = [(b.start, b.size) for b in FlatLayout(ragged_numels()).buckets]
     else:
@@ -101,7 +107,7 @@ def gpu_run(args):
     for b in range(nbuf):
         g = torch.empty(n, dtype=torch.int16, device=dev)
         s, k = divmod(b, K)
-        synth.device_fill_grad16(torch, tabs, g, w.grad_key(s + 1, k), w.grad_spec)
+        synth.device_fill_grad16(torch, tabs, g, w.grad_key(s + 1, k), gspec)
         grads.append(g)
     torch.cuda.synchronize()
     log(f"workload {w.name}: psi={n} K={K} grad buffers={nbuf} (of {total_mb} micro-batches)")
@@ -117,24 +123,24 @@ def gpu_run(args):
         if K == 1:
             g = grads[base % nbuf]
             if ws is None:
-                _lib.ds_check_overflow(st, g, _lib.DS_FP16, n, stream)
+                _lib.ds_check_overflow(st, g, gdt16, n, stream)
             else:
-                _lib.ds_check_overflow_sumsq(st, g, _lib.DS_FP16, n, ws, stream=stream)
-            gptr, dt = g, _lib.DS_FP16
+                _lib.ds_check_overflow_sumsq(st, g, gdt16, n, ws, stream=stream)
+            gptr, dt = g, gdt16
         else:
             for k in range(K):
                 g = grads[(base + k) % nbuf]
                 for start, size in buckets:
                     a, gp = acc.data_ptr() + 4 * start, g.data_ptr() + 2 * start
                     if k == K - 1 and ws is not None:
-                        _lib.ds_accumulate_sumsq(a, gp, size, k == 0, st, ws, stream=stream)
+                        _lib.ds_accumulate_sumsq(a, gp, gdt16, size, k == 0, st, ws, stream=stream)
                     else:
-                        _lib.ds_accumulate(a, gp, size, k == 0, st if k == K - 1 else None, stream)
+                        _lib.ds_accumulate(a, gp, gdt16, size, k == 0, st if k == K - 1 else None, stream)
             gptr, dt = acc, _lib.DS_FP32
         if timed:
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a.record(stream)
-        _lib.ds_adam_step(st, master, m, v, p16, gptr, dt, n, *hp, K, stream)
+        _lib.ds_adam_step(st, master, m, v, p16, gdt16, gptr, dt, n, *hp, K, stream)
         if timed:
             b.record(stream)
             ev.append((a, b))
@@ -173,10 +179,12 @@ def gpu_run(args):
             "workload": w.name,
             "psi": n,
             "micro_batches": K,
-            "grad": "fp16 N(0,%g) x %g" % (w.sigma, w.mult) + (" heavy tail" if w.heavy_tail else ""),
-            "state": "fp32 master/m/v, fp16 params",
+            "grad": ("bf16 N(0,%g)" % w.sigma if args.bf16 else "fp16 N(0,%g) x %g" % (w.sigma, w.mult))
+                    + (" heavy tail" if w.heavy_tail else ""),
+            "state": "fp32 master/m/v, %s params" % ("bf16" if args.bf16 else "fp16"),
             "adam": {"lr": LR, "betas": [BETA1, BETA2], "eps": EPS, "weight_decay": WD},
             "gradient_clipping": args.clip,
+            "half": "bf16" if args.bf16 else "fp16",
             "parallelism": "one GPU's ZeRO partition",
         },
         "roofline": {
@@ -309,6 +317,8 @@ def main():
     ap.add_argument("--workload", default="zero2_7b")
     ap.add_argument("--mode", default="step", choices=["step", "copy"])
     ap.add_argument("--max-grad-buffers", type=int, default=8)
+    ap.add_argument("--bf16", action="store_true",
+                    help="bf16 gradients and parameter copy, no loss scaling")
     ap.add_argument("--clip", type=float, default=0.0,
                     help="gradient_clipping max norm (0: the workloads' setting, no clipping)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)

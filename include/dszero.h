@@ -12,7 +12,9 @@
  *
  * Model state per element of a partition ([Guide] section 2, memory table):
  * fp16 parameter copy (p16), fp16 gradient, fp32 master parameter, fp32 Adam
- * first moment (m), fp32 Adam second moment (v).  With ZeRO-1/2 each rank owns
+ * first moment (m), fp32 Adam second moment (v).  In bf16 mode ([Guide]
+ * section 4.2, bf16 settings) the 16-bit parameter copy and gradients are
+ * bf16 instead and no loss scaling is applied (a static scale of 1).  With ZeRO-1/2 each rank owns
  * a contiguous 1/N range of these arrays and updates only that range
  * ([Guide] sections 2.1 and 2.2).
  *
@@ -22,8 +24,9 @@
  *    asynchronously on `stream` (a hipStream_t; NULL is the default stream)
  *    and uses the buffers until the stream reaches it.
  *  - Layout.  Arrays are flat and contiguous, element i of every array belongs
- *    to the same parameter.  fp16 values are IEEE binary16 bit patterns
- *    (uint16_t); fp32 values are IEEE binary32.
+ *    to the same parameter.  16-bit values are bit patterns (uint16_t) of IEEE
+ *    binary16 (DS_FP16) or bf16 (DS_BF16: the upper half of an IEEE binary32);
+ *    fp32 values are IEEE binary32.
  *  - Alignment.  Every array pointer must be 16-byte aligned; a ds_scaler
  *    pointer must be 8-byte aligned.
  *  - Errors.  Every call validates all arguments before any device work, so a
@@ -68,7 +71,7 @@ typedef enum ds_status {
     DS_ERR_HIP = 7
 } ds_status;
 
-typedef enum ds_dtype { DS_FP16 = 1, DS_FP32 = 2 } ds_dtype;
+typedef enum ds_dtype { DS_FP16 = 1, DS_FP32 = 2, DS_BF16 = 3 } ds_dtype;
 
 /*
  * Per-step device state, 128 bytes, kept in caller-owned DEVICE memory so that
@@ -130,20 +133,21 @@ ds_status ds_state_write(ds_scaler* st, const ds_scaler* host_in, void* stream);
  * the accumulation; section 4.3: gradient_accumulation_steps).
  *   overwrite != 0 : acc[i] = float(g16[i])            (first micro-batch)
  *   overwrite == 0 : acc[i] = acc[i] + float(g16[i])   (later micro-batches, in order)
- * acc: fp32[n], g16: fp16[n].  If st is not NULL the same pass ORs "acc[i] is
- * not finite" into st->overflow (use it on the last micro-batch: the check of
- * the step then costs no extra pass).  Errors: see the conventions; acc, g16
- * and st must not overlap.
+ * acc: fp32[n], g16: 16-bit[n] of type gdt (DS_FP16 or DS_BF16; the widening
+ * is exact).  If st is not NULL the same pass ORs "acc[i] is not finite" into
+ * st->overflow (use it on the last micro-batch: the check of the step then
+ * costs no extra pass).  Errors: see the conventions; acc, g16 and st must not
+ * overlap; gdt other than DS_FP16/DS_BF16 -> DS_ERR_DTYPE.
  */
-ds_status ds_accumulate(float* acc, const uint16_t* g16, int64_t n, int32_t overwrite,
+ds_status ds_accumulate(float* acc, const uint16_t* g16, ds_dtype gdt, int64_t n, int32_t overwrite,
                         ds_scaler* st_or_null, void* stream);
 
 /*
  * Overflow check ([Overview] core features: dynamic loss scaling; [Guide]
  * section 13.1, gradient overflow in fp16): ORs "some grad[i] is +-inf or NaN"
- * into st->overflow.  grad: fp16[n] (dt = DS_FP16) or fp32[n] (dt = DS_FP32).
- * The largest finite fp16 value (65504) is not an overflow.  Does nothing more
- * once the flag is already set for this step.
+ * into st->overflow.  grad: fp16[n] (dt = DS_FP16), bf16[n] (DS_BF16) or
+ * fp32[n] (DS_FP32).  The largest finite value (65504 in fp16) is not an
+ * overflow.  Does nothing more once the flag is already set for this step.
  */
 ds_status ds_check_overflow(ds_scaler* st, const void* grad, ds_dtype dt, int64_t n, void* stream);
 
@@ -160,11 +164,12 @@ ds_status ds_check_overflow(ds_scaler* st, const void* grad, ds_dtype dt, int64_
  *   v[i]   = beta2*v[i] + (1-beta2)*g*g
  *   master = master - lr*weight_decay*master     (only if weight_decay != 0)
  *   master = master - lr/(1-beta1^t) * m[i] / (sqrt(v[i])/sqrt(1-beta2^t) + eps)
- *   p16[i] = fp16(master[i])                     (round to nearest even)
+ *   p16[i] = fp16(master[i]) or bf16(master[i])  (pdt; round to nearest even)
  * in IEEE fp32, one rounding per operation; the two bias-correction factors
  * are evaluated in fp64 and rounded once.  master/m/v: fp32[n] in place;
- * p16: fp16[n] out; grad: fp16[n] or fp32[n] in.  st is read only (t and S
- * advance in ds_update_loss_scale).
+ * p16: 16-bit[n] out, of type pdt (DS_FP16 or DS_BF16); grad: [n] in, of
+ * type dt (DS_FP16, DS_BF16, or DS_FP32 for the accumulation buffer).  st is
+ * read only (t and S advance in ds_update_loss_scale).
  * Global-norm clipping ([Guide] sections 4.1 and 5.4 gradient_clipping,
  * section 5.1 step() includes clipping): with max_grad_norm > 0, using the
  * step's st->grad_sumsq (filled by ds_check_overflow_sumsq or
@@ -177,7 +182,7 @@ ds_status ds_check_overflow(ds_scaler* st, const void* grad, ds_dtype dt, int64_
  * beta1 or beta2 outside [0, 1), eps not finite or <= 0, accum_steps < 1.
  */
 ds_status ds_adam_step(const ds_scaler* st, float* master, float* m, float* v, uint16_t* p16,
-                       const void* grad, ds_dtype dt, int64_t n, float lr, float beta1,
+                       ds_dtype pdt, const void* grad, ds_dtype dt, int64_t n, float lr, float beta1,
                        float beta2, float eps, float weight_decay, float max_grad_norm,
                        int32_t accum_steps, void* stream);
 
@@ -214,15 +219,16 @@ ds_status ds_update_loss_scale(ds_scaler* st, void* stream);
  */
 size_t ds_sumsq_workspace_bytes(int64_t n);
 
-/* ds_check_overflow plus the sum of squares of grad (fp16 or fp32), one pass. */
+/* ds_check_overflow plus the sum of squares of grad (fp16, bf16 or fp32), one pass. */
 ds_status ds_check_overflow_sumsq(ds_scaler* st, const void* grad, ds_dtype dt, int64_t n,
                                   void* workspace, size_t workspace_bytes, void* stream);
 
 /* ds_accumulate with the fused overflow check (st required) plus the sum of
  * squares of the accumulated values, one pass: use it for the last
  * micro-batch of a clipped step. */
-ds_status ds_accumulate_sumsq(float* acc, const uint16_t* g16, int64_t n, int32_t overwrite,
-                              ds_scaler* st, void* workspace, size_t workspace_bytes, void* stream);
+ds_status ds_accumulate_sumsq(float* acc, const uint16_t* g16, ds_dtype gdt, int64_t n,
+                              int32_t overwrite, ds_scaler* st, void* workspace,
+                              size_t workspace_bytes, void* stream);
 
 /*
  * The bias-correction scalars the next applied step will use, evaluated on

@@ -80,14 +80,18 @@ def lib():
         L.zo_enc16.argtypes, L.zo_enc16.restype = [f32], ctypes.c_uint16
         L.zo_dec16_array.argtypes, L.zo_dec16_array.restype = [vp, vp, i64], None
         L.zo_enc16_array.argtypes, L.zo_enc16_array.restype = [vp, vp, i64], None
-        L.zo_accumulate.argtypes, L.zo_accumulate.restype = [vp, vp, i64, i32], None
-        L.zo_any_nonfinite16.argtypes, L.zo_any_nonfinite16.restype = [vp, i64], i32
+        L.zo_decbf16.argtypes, L.zo_decbf16.restype = [ctypes.c_uint16], f32
+        L.zo_encbf16.argtypes, L.zo_encbf16.restype = [f32], ctypes.c_uint16
+        L.zo_decbf16_array.argtypes, L.zo_decbf16_array.restype = [vp, vp, i64], None
+        L.zo_encbf16_array.argtypes, L.zo_encbf16_array.restype = [vp, vp, i64], None
+        L.zo_accumulate.argtypes, L.zo_accumulate.restype = [vp, vp, i64, i32, i32], None
+        L.zo_any_nonfinite16.argtypes, L.zo_any_nonfinite16.restype = [vp, i64, i32], i32
         L.zo_any_nonfinite32.argtypes, L.zo_any_nonfinite32.restype = [vp, i64], i32
         L.zo_adam_scalars.argtypes = [i64, f32, f32, f32, ctypes.POINTER(f32), ctypes.POINTER(f32)]
         L.zo_adam_scalars.restype = None
-        L.zo_adam.argtypes = [vp, i32, i64, vp, vp, vp, vp, f32, i32, i64, f32, f32, f32, f32, f32]
+        L.zo_adam.argtypes = [vp, i32, i64, vp, vp, vp, vp, i32, f32, i32, i64, f32, f32, f32, f32, f32]
         L.zo_adam.restype = None
-        L.zo_adam_mult.argtypes = [vp, i32, i64, vp, vp, vp, vp, f32, i64, f32, f32, f32, f32, f32]
+        L.zo_adam_mult.argtypes = [vp, i32, i64, vp, vp, vp, vp, i32, f32, i64, f32, f32, f32, f32, f32]
         L.zo_adam_mult.restype = None
         L.zo_scaler_init.argtypes = [ctypes.POINTER(ZoScaler), f32, f32, i32, i32, i32, i32]
         L.zo_scaler_init.restype = None
@@ -122,16 +126,40 @@ def enc16(x: np.ndarray) -> np.ndarray:
     return out
 
 
+def decbf16(h: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns (uint16) -> float32 (exact)."""
+    h = np.ascontiguousarray(h, dtype=np.uint16)
+    out = np.empty(h.shape, np.float32)
+    lib().zo_decbf16_array(_ptr(h), _ptr(out), h.size)
+    return out
+
+
+def encbf16(x: np.ndarray) -> np.ndarray:
+    """float32 -> bf16 bit patterns (uint16), round to nearest even."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    out = np.empty(x.shape, np.uint16)
+    lib().zo_encbf16_array(_ptr(x), _ptr(out), x.size)
+    return out
+
+
+# 16-bit formats: "fp16" (IEEE binary16) or "bf16" (upper half of binary32)
+FMT = {"fp16": 0, "bf16": 1}
+
+
+def decode(h: np.ndarray, fmt: str = "fp16") -> np.ndarray:
+    return decbf16(h) if fmt == "bf16" else dec16(h)
+
+
 # -- the four steps ------------------------------------------------------------
 
-def accumulate(acc: np.ndarray, g16: np.ndarray, overwrite: bool) -> None:
+def accumulate(acc: np.ndarray, g16: np.ndarray, overwrite: bool, fmt: str = "fp16") -> None:
     assert acc.dtype == np.float32 and g16.dtype == np.uint16 and acc.size == g16.size
-    lib().zo_accumulate(_ptr(acc), _ptr(g16), acc.size, int(bool(overwrite)))
+    lib().zo_accumulate(_ptr(acc), _ptr(g16), acc.size, int(bool(overwrite)), FMT[fmt])
 
 
-def any_nonfinite(grad: np.ndarray) -> bool:
+def any_nonfinite(grad: np.ndarray, fmt: str = "fp16") -> bool:
     if grad.dtype == np.uint16:
-        return bool(lib().zo_any_nonfinite16(_ptr(grad), grad.size))
+        return bool(lib().zo_any_nonfinite16(_ptr(grad), grad.size, FMT[fmt]))
     assert grad.dtype == np.float32
     return bool(lib().zo_any_nonfinite32(_ptr(grad), grad.size))
 
@@ -143,36 +171,45 @@ def adam_scalars(t: int, lr: float, beta1: float, beta2: float) -> tuple[float, 
     return a.value, b.value
 
 
+def _gfmt(grad, fmt):
+    return 2 if grad.dtype == np.float32 else FMT[fmt]
+
+
 def adam(grad, master, m, v, p16, *, scale, accum_steps, t, lr, beta1, beta2, eps,
-         weight_decay=0.0) -> None:
-    """One applied Adam step, in place on master/m/v/p16 (see oracle.c)."""
+         weight_decay=0.0, fmt="fp16", param_fmt="fp16") -> None:
+    """One applied Adam step, in place on master/m/v/p16 (see oracle.c).  ``fmt`` is
+    the format of a 16-bit gradient, ``param_fmt`` that of the parameter copy."""
     n = master.size
     for a, dt in ((master, np.float32), (m, np.float32), (v, np.float32), (p16, np.uint16)):
         assert a.dtype == dt and a.size == n and a.flags["C_CONTIGUOUS"]
     assert grad.size == n and grad.dtype in (np.uint16, np.float32)
-    lib().zo_adam(_ptr(grad), int(grad.dtype == np.float32), n, _ptr(master), _ptr(m), _ptr(v),
-                  _ptr(p16), scale, int(accum_steps), int(t), lr, beta1, beta2, eps, weight_decay)
+    lib().zo_adam(_ptr(grad), _gfmt(grad, fmt), n, _ptr(master), _ptr(m), _ptr(v), _ptr(p16),
+                  FMT[param_fmt], scale, int(accum_steps), int(t), lr, beta1, beta2, eps, weight_decay)
 
 
-def adam_mult(grad, master, m, v, p16, *, mult, t, lr, beta1, beta2, eps, weight_decay=0.0) -> None:
+def adam_mult(grad, master, m, v, p16, *, mult, t, lr, beta1, beta2, eps, weight_decay=0.0,
+              fmt="fp16", param_fmt="fp16") -> None:
     """One applied Adam step with an explicit gradient multiplier (fp32)."""
     n = master.size
     assert grad.size == n and grad.dtype in (np.uint16, np.float32)
-    lib().zo_adam_mult(_ptr(grad), int(grad.dtype == np.float32), n, _ptr(master), _ptr(m), _ptr(v),
-                       _ptr(p16), float(np.float32(mult)), int(t), lr, beta1, beta2, eps, weight_decay)
+    lib().zo_adam_mult(_ptr(grad), _gfmt(grad, fmt), n, _ptr(master), _ptr(m), _ptr(v), _ptr(p16),
+                       FMT[param_fmt], float(np.float32(mult)), int(t), lr, beta1, beta2, eps,
+                       weight_decay)
 
 
 # -- global-norm clipping ("DeepSpeed complete guide" section 4.1 and 5.4:
 #    gradient_clipping; section 5.1: step() includes clipping) ----------------
 
-def grad_sumsq(grad: np.ndarray) -> float:
+def grad_sumsq(grad: np.ndarray, fmt: str = "fp16") -> float:
     """Sum of squares of the stored gradient values, exactly, rounded once to fp64.
 
     fp16: each value is M * 2^E with integers M < 2^11, E in [-24, 5]; the
     squares M^2 * 2^(2E) are summed exactly as integers per exponent (Python
-    integers), then divided by 2^48 with one correct rounding.  fp32: the
-    squares are exact in fp64 and math.fsum adds them with one rounding.
+    integers), then divided by 2^48 with one correct rounding.  bf16 and fp32:
+    the squares are exact in fp64 and math.fsum adds them with one rounding.
     Non-finite gradients give inf or nan (their step is skipped anyway)."""
+    if grad.dtype == np.uint16 and fmt == "bf16":
+        grad = decbf16(grad)
     if grad.dtype == np.uint16:
         h = grad.astype(np.int64)
         e = (h >> 10) & 0x1F
@@ -232,18 +269,21 @@ class Scaler:
 class State:
     """The flat partition's model state (fp16 params, fp32 master/m/v) plus the scaler."""
 
-    def __init__(self, master, m, v, p16, scaler: Scaler):
+    def __init__(self, master, m, v, p16, scaler: Scaler, param_fmt: str = "fp16"):
         self.master, self.m, self.v, self.p16, self.scaler = master, m, v, p16, scaler
+        self.param_fmt = param_fmt
         self.last_sumsq = 0.0
 
 
-def step(state: State, grads, *, lr, beta1, beta2, eps, weight_decay=0.0, max_grad_norm=0.0) -> bool:
+def step(state: State, grads, *, lr, beta1, beta2, eps, weight_decay=0.0, max_grad_norm=0.0,
+         fmt="fp16") -> bool:
     """One full ZeRO optimizer step of the oracle; returns the overflow flag.
 
     ``grads`` is one uint16 array (K = 1: the fp16 gradient is consumed
     directly) or a list of K uint16 micro-batch gradients (K > 1: summed into
-    an fp32 buffer in micro-batch order first).  ``max_grad_norm`` > 0 clips
-    the unscaled gradient to that global L2 norm.  ``state.last_sumsq`` keeps
+    an fp32 buffer in micro-batch order first); ``fmt`` is their 16-bit format
+    ("fp16" or "bf16").  ``max_grad_norm`` > 0 clips the unscaled gradient to
+    that global L2 norm.  ``state.last_sumsq`` keeps
     the step's gradient sum of squares when clipping.
     """
     if isinstance(grads, np.ndarray):
@@ -254,18 +294,17 @@ def step(state: State, grads, *, lr, beta1, beta2, eps, weight_decay=0.0, max_gr
     else:
         grad = np.empty(state.master.size, np.float32)
         for k, g in enumerate(grads):
-            accumulate(grad, np.ascontiguousarray(g, dtype=np.uint16), overwrite=(k == 0))
-    overflow = any_nonfinite(grad)
+            accumulate(grad, np.ascontiguousarray(g, dtype=np.uint16), overwrite=(k == 0), fmt=fmt)
+    overflow = any_nonfinite(grad, fmt)
     if not overflow:
+        kw = dict(t=state.scaler.applied + 1, lr=lr, beta1=beta1, beta2=beta2, eps=eps,
+                  weight_decay=weight_decay, fmt=fmt, param_fmt=state.param_fmt)
         if max_grad_norm > 0:
-            state.last_sumsq = grad_sumsq(grad)
+            state.last_sumsq = grad_sumsq(grad, fmt)
             mult = clip_multiplier(state.last_sumsq, state.scaler.scale, K, max_grad_norm)
-            adam_mult(grad, state.master, state.m, state.v, state.p16, mult=mult,
-                      t=state.scaler.applied + 1, lr=lr, beta1=beta1, beta2=beta2, eps=eps,
-                      weight_decay=weight_decay)
+            adam_mult(grad, state.master, state.m, state.v, state.p16, mult=mult, **kw)
         else:
-            adam(grad, state.master, state.m, state.v, state.p16,
-                 scale=state.scaler.scale, accum_steps=K, t=state.scaler.applied + 1,
-                 lr=lr, beta1=beta1, beta2=beta2, eps=eps, weight_decay=weight_decay)
+            adam(grad, state.master, state.m, state.v, state.p16, scale=state.scaler.scale,
+                 accum_steps=K, **kw)
     state.scaler.update(overflow)
     return overflow

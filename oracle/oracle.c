@@ -96,6 +96,54 @@ uint16_t zo_enc16(float x)
     return (uint16_t)(sign | bits);
 }
 
+/* bf16 ("brain float"): the upper 16 bits of an IEEE binary32 (sign, 8-bit
+ * exponent, 7 fraction bits).  Decoding appends 16 zero bits, exactly. */
+float zo_decbf16(uint16_t b)
+{
+    uint32_t bits = (uint32_t)b << 16;
+    float out;
+    memcpy(&out, &bits, sizeof out);
+    return out;
+}
+
+/* Encode binary32 as bf16, rounding to nearest, ties to even.  For values of
+ * one sign the binary32 encoding is monotonic in the bit pattern, and the bf16
+ * values are exactly the binary32 values whose low 16 bits are zero, so
+ * rounding the magnitude to the nearest multiple of 2^16 in the integer
+ * representation (ties to an even upper half) is rounding the value; a carry
+ * out of the fraction moves to the next binade, and past the largest finite
+ * value to infinity, as it should.  NaN encodes as the quiet NaN 0x7FC0 with
+ * the input's sign. */
+uint16_t zo_encbf16(float x)
+{
+    uint32_t u;
+    memcpy(&u, &x, sizeof u);
+    if (isnan(x))
+        return (uint16_t)(((u >> 16) & 0x8000u) | 0x7FC0u);
+    uint32_t upper = u >> 16, lower = u & 0xFFFFu;
+    if (lower > 0x8000u || (lower == 0x8000u && (upper & 1u)))
+        upper += 1u;
+    return (uint16_t)upper;
+}
+
+/* 16-bit formats of the gradient and of the parameter copy */
+enum { ZO_FP16 = 0, ZO_BF16 = 1, ZO_FP32 = 2 };
+
+static float dec_fmt(uint16_t h, int32_t fmt) { return fmt == ZO_BF16 ? zo_decbf16(h) : zo_dec16(h); }
+static uint16_t enc_fmt(float x, int32_t fmt) { return fmt == ZO_BF16 ? zo_encbf16(x) : zo_enc16(x); }
+
+void zo_decbf16_array(const uint16_t *h, float *out, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = zo_decbf16(h[i]);
+}
+
+void zo_encbf16_array(const float *x, uint16_t *out, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = zo_encbf16(x[i]);
+}
+
 void zo_dec16_array(const uint16_t *h, float *out, int64_t n)
 {
     for (int64_t i = 0; i < n; ++i)
@@ -114,12 +162,13 @@ void zo_enc16_array(const float *x, uint16_t *out, int64_t n)
 /* training loop, backward handles accumulation; section 4.3 batch relation).*/
 /* ------------------------------------------------------------------------ */
 
-/* acc[i] = dec16(g[i])            when overwrite != 0 (first micro-batch)
- * acc[i] = acc[i] + dec16(g[i])   otherwise (later micro-batches, in order)  */
-void zo_accumulate(float *acc, const uint16_t *g, int64_t n, int32_t overwrite)
+/* acc[i] = dec(g[i])            when overwrite != 0 (first micro-batch)
+ * acc[i] = acc[i] + dec(g[i])   otherwise (later micro-batches, in order)
+ * g is fp16 (fmt 0) or bf16 (fmt 1). */
+void zo_accumulate(float *acc, const uint16_t *g, int64_t n, int32_t overwrite, int32_t fmt)
 {
     for (int64_t i = 0; i < n; ++i) {
-        float gi = zo_dec16(g[i]);
+        float gi = dec_fmt(g[i], fmt);
         if (overwrite)
             acc[i] = gi;
         else
@@ -133,11 +182,11 @@ void zo_accumulate(float *acc, const uint16_t *g, int64_t n, int32_t overwrite)
 /* The step overflows when any gradient value is not finite (+-inf or NaN).  */
 /* ------------------------------------------------------------------------ */
 
-int32_t zo_any_nonfinite16(const uint16_t *g, int64_t n)
+int32_t zo_any_nonfinite16(const uint16_t *g, int64_t n, int32_t fmt)
 {
     int32_t flag = 0;
     for (int64_t i = 0; i < n; ++i)
-        if (!isfinite(zo_dec16(g[i])))
+        if (!isfinite(dec_fmt(g[i], fmt)))
             flag = 1;
     return flag;
 }
@@ -191,17 +240,18 @@ void zo_adam_scalars(int64_t t, float lr, float beta1, float beta2,
  *   v      = beta2 v + (1 - beta2) g^2
  *   p      = p - lr wd p                     (decoupled decay, AdamW; skipped when wd == 0)
  *   p      = p - lr/(1-beta1^t) * m / (sqrt(v)/sqrt(1-beta2^t) + eps)
- *   p16    = fp16(p)                         round to nearest even
+ *   p16    = fp16(p) or bf16(p)              round to nearest even
  * The textbook form m_hat / (sqrt(v_hat) + eps) is regrouped so that each
  * element takes one divide and one square root; the regrouping is exact in
  * real arithmetic.  Each line below is one fp32 rounding, evaluated in the
  * written order.
  *
- * grad_is_f32 = 0: grad is fp16 bits (K = 1 path); 1: fp32 accumulation buffer.
+ * gfmt: grad is fp16 bits (0), bf16 bits (1) or the fp32 accumulation buffer
+ * (2); pfmt: the parameter copy is fp16 (0) or bf16 (1).
  * zo_adam_mult takes the gradient multiplier (1/(S*K), or that times the
  * clipping coefficient) as `inv`; zo_adam computes 1/(S*K) itself. */
-void zo_adam_mult(const void *grad, int32_t grad_is_f32, int64_t n,
-                  float *master, float *m, float *v, uint16_t *p16,
+void zo_adam_mult(const void *grad, int32_t gfmt, int64_t n,
+                  float *master, float *m, float *v, uint16_t *p16, int32_t pfmt,
                   float inv, int64_t t,
                   float lr, float beta1, float beta2, float eps, float weight_decay)
 {
@@ -212,8 +262,8 @@ void zo_adam_mult(const void *grad, int32_t grad_is_f32, int64_t n,
     float lrwd = lr * weight_decay;
 
     for (int64_t i = 0; i < n; ++i) {
-        float graw = grad_is_f32 ? ((const float *)grad)[i]
-                                 : zo_dec16(((const uint16_t *)grad)[i]);
+        float graw = gfmt == ZO_FP32 ? ((const float *)grad)[i]
+                                     : dec_fmt(((const uint16_t *)grad)[i], gfmt);
         float g = graw * inv;
 
         float m1 = beta1 * m[i];
@@ -240,18 +290,18 @@ void zo_adam_mult(const void *grad, int32_t grad_is_f32, int64_t n,
         m[i] = mi;
         v[i] = vi;
         master[i] = p;
-        p16[i] = zo_enc16(p);
+        p16[i] = enc_fmt(p, pfmt);
     }
 }
 
 /* The unclipped step: the gradient multiplier is 1 / (S * K) in fp32. */
-void zo_adam(const void *grad, int32_t grad_is_f32, int64_t n,
-             float *master, float *m, float *v, uint16_t *p16,
+void zo_adam(const void *grad, int32_t gfmt, int64_t n,
+             float *master, float *m, float *v, uint16_t *p16, int32_t pfmt,
              float scale, int32_t accum_steps, int64_t t,
              float lr, float beta1, float beta2, float eps, float weight_decay)
 {
     float inv = 1.0f / (scale * (float)accum_steps);
-    zo_adam_mult(grad, grad_is_f32, n, master, m, v, p16, inv, t, lr, beta1, beta2, eps,
+    zo_adam_mult(grad, gfmt, n, master, m, v, p16, pfmt, inv, t, lr, beta1, beta2, eps,
                  weight_decay);
 }
 

@@ -89,6 +89,16 @@ def table16(scale: float) -> np.ndarray:
 
 
 @functools.lru_cache(maxsize=None)
+def tablebf16(scale: float) -> np.ndarray:
+    """uint16 bit patterns of bf16(q_j * scale) (drawn through torch's bf16 cast)."""
+    import torch
+    t = torch.from_numpy(_quantiles() * float(scale)).to(torch.float32).to(torch.bfloat16)
+    out = t.view(torch.int16).numpy().view(np.uint16).copy()
+    out.setflags(write=False)
+    return out
+
+
+@functools.lru_cache(maxsize=None)
 def table32(scale: float) -> np.ndarray:
     """uint32 bit patterns of fp32(q_j * scale), j = 0..65535."""
     t = (_quantiles() * float(scale)).astype(np.float32).view(np.uint32).copy()
@@ -97,18 +107,23 @@ def table32(scale: float) -> np.ndarray:
 
 
 class GradSpec:
-    """Distribution of an fp16 gradient: N(0, sigma) * mult, optional heavy tail."""
+    """Distribution of a 16-bit gradient: N(0, sigma) * mult, optional heavy tail,
+    stored as fp16 (``fmt="fp16"``) or bf16."""
 
-    def __init__(self, sigma: float, mult: float, heavy_tail: bool = False):
+    def __init__(self, sigma: float, mult: float, heavy_tail: bool = False, fmt: str = "fp16"):
         self.sigma, self.mult, self.heavy_tail = float(sigma), float(mult), bool(heavy_tail)
+        self.fmt = fmt
+
+    def _table(self, scale):
+        return tablebf16(scale) if self.fmt == "bf16" else table16(scale)
 
     @property
     def table(self) -> np.ndarray:
-        return table16(self.sigma * self.mult)
+        return self._table(self.sigma * self.mult)
 
     @property
     def tail_table(self) -> np.ndarray:
-        return table16(self.sigma * self.mult * 100.0) if self.heavy_tail else self.table
+        return self._table(self.sigma * self.mult * 100.0) if self.heavy_tail else self.table
 
     @property
     def tail_thresh(self) -> int:

@@ -46,9 +46,11 @@ class DevState:
     """Device copy of one partition's state plus a ds_scaler."""
 
     def __init__(self, torch, master, m, v, p16, *, init_scale, window, hysteresis=1, min_scale=1.0,
-                 dynamic=1, K=1):
+                 dynamic=1, K=1, fmt="fp16", param_fmt="fp16"):
         from zero_mixed_precision_amd import _lib
         self.torch, self.lib = torch, _lib
+        self.gdt = _lib.DS_BF16 if fmt == "bf16" else _lib.DS_FP16
+        self.pdt = _lib.DS_BF16 if param_fmt == "bf16" else _lib.DS_FP16
         self.master, self.m, self.v = dev_f32(torch, master), dev_f32(torch, m), dev_f32(torch, v)
         self.p16 = dev_u16(torch, p16)
         self.n = master.size
@@ -67,8 +69,8 @@ class DevState:
         for g in grads:
             assert g.numel() >= n
         if K == 1:
-            L.ds_check_overflow(self.state, grads[0], L.DS_FP16, n)
-            grad, dt = grads[0], L.DS_FP16
+            L.ds_check_overflow(self.state, grads[0], self.gdt, n)
+            grad, dt = grads[0], self.gdt
         else:
             spans = buckets or [(0, n)]
             assert sum(s for _, s in spans) == n
@@ -76,12 +78,12 @@ class DevState:
                 last = k == K - 1
                 for start, size in spans:
                     assert start % 8 == 0 and start + size <= n
-                    L.ds_accumulate(self.acc.data_ptr() + 4 * start, g.data_ptr() + 2 * start, size,
+                    L.ds_accumulate(self.acc.data_ptr() + 4 * start, g.data_ptr() + 2 * start, self.gdt, size,
                                     k == 0, self.state if (last and fused_check) else None)
             if not fused_check:
                 L.ds_check_overflow(self.state, self.acc, L.DS_FP32, n)
             grad, dt = self.acc, L.DS_FP32
-        L.ds_adam_step(self.state, self.master, self.m, self.v, self.p16, grad, dt, n, hp["lr"],
+        L.ds_adam_step(self.state, self.master, self.m, self.v, self.p16, self.pdt, grad, dt, n, hp["lr"],
                        hp["beta1"], hp["beta2"], hp["eps"], hp.get("weight_decay", 0.0), 0.0, K)
         L.ds_update_loss_scale(self.state)
 

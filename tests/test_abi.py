@@ -12,8 +12,8 @@ import pytest
 
 from oracle import packing
 from zero_mixed_precision_amd import _lib, ZeroMPConfig, FlatLayout
-from zero_mixed_precision_amd._lib import (DS_ERR_ALIAS, DS_ERR_ALIGN, DS_ERR_DTYPE, DS_ERR_HPARAM,
-                                           DS_ERR_NULL, DS_ERR_SIZE, DS_FP16, DS_FP32, DS_OK)
+from zero_mixed_precision_amd._lib import (DS_BF16, DS_ERR_ALIAS, DS_ERR_ALIGN, DS_ERR_DTYPE,
+                                           DS_ERR_HPARAM, DS_ERR_NULL, DS_ERR_SIZE, DS_FP16, DS_FP32, DS_OK)
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 GOLDEN = os.path.join(ROOT, "tests", "golden")
@@ -55,21 +55,24 @@ def test_status_strings():
 
 def test_accumulate_validation():
     acc = L.ds_accumulate
-    assert acc(A, B, -1, 1, None, STREAM) == DS_ERR_SIZE
-    assert acc(A, B, 0, 1, None, STREAM) == DS_OK                      # n == 0: nothing launched
-    assert acc(None, B, 5, 1, None, STREAM) == DS_ERR_NULL
-    assert acc(A, None, 5, 1, None, STREAM) == DS_ERR_NULL
-    assert acc(A + 4, B, 5, 1, None, STREAM) == DS_ERR_ALIGN
-    assert acc(A, B + 2, 5, 1, None, STREAM) == DS_ERR_ALIGN
-    assert acc(A, B, 5, 1, ST + 4, STREAM) == DS_ERR_ALIGN
-    assert acc(A, A + 16, 8, 1, None, STREAM) == DS_ERR_ALIAS          # acc [A, A+32) vs g16
-    assert acc(A, B, 8, 0, A + 16, STREAM) == DS_ERR_ALIAS             # state inside acc
+    assert acc(A, B, DS_FP16, -1, 1, None, STREAM) == DS_ERR_SIZE
+    assert acc(A, B, DS_FP16, 0, 1, None, STREAM) == DS_OK                      # n == 0: nothing launched
+    assert acc(None, B, DS_FP16, 5, 1, None, STREAM) == DS_ERR_NULL
+    assert acc(A, None, DS_FP16, 5, 1, None, STREAM) == DS_ERR_NULL
+    assert acc(A + 4, B, DS_FP16, 5, 1, None, STREAM) == DS_ERR_ALIGN
+    assert acc(A, B + 2, DS_FP16, 5, 1, None, STREAM) == DS_ERR_ALIGN
+    assert acc(A, B, DS_FP16, 5, 1, ST + 4, STREAM) == DS_ERR_ALIGN
+    assert acc(A, A + 16, DS_FP16, 8, 1, None, STREAM) == DS_ERR_ALIAS          # acc [A, A+32) vs g16
+    assert acc(A, B, DS_FP16, 8, 0, A + 16, STREAM) == DS_ERR_ALIAS             # state inside acc
+    assert acc(A, B, DS_FP32, 8, 0, None, STREAM) == DS_ERR_DTYPE             # 16-bit gradients only
+    assert acc(A, B, 9, 8, 0, None, STREAM) == DS_ERR_DTYPE
 
 
 def test_check_overflow_validation():
     chk = L.ds_check_overflow
     assert chk(ST, A, DS_FP16, -1, STREAM) == DS_ERR_SIZE
-    assert chk(ST, A, 3, 10, STREAM) == DS_ERR_DTYPE
+    assert chk(ST, A, 4, 10, STREAM) == DS_ERR_DTYPE
+    assert chk(ST, A, DS_BF16, -1, STREAM) == DS_ERR_SIZE
     assert chk(None, A, DS_FP16, 10, STREAM) == DS_ERR_NULL
     assert chk(ST, A, DS_FP16, 0, STREAM) == DS_OK
     assert chk(ST, None, DS_FP16, 10, STREAM) == DS_ERR_NULL
@@ -78,13 +81,16 @@ def test_check_overflow_validation():
     assert chk(A + 32, A, DS_FP32, 10, STREAM) == DS_ERR_ALIAS
 
 
-def _adam(*, st=ST, ptrs=(A, B, C, D, E), dt=DS_FP16, n=16, hp=HP):
-    return L.ds_adam_step(st, *ptrs, dt, n, *hp, STREAM)
+def _adam(*, st=ST, ptrs=(A, B, C, D, E), dt=DS_FP16, pdt=DS_FP16, n=16, hp=HP):
+    master, m, v, p16, grad = ptrs
+    return L.ds_adam_step(st, master, m, v, p16, pdt, grad, dt, n, *hp, STREAM)
 
 
 def test_adam_validation():
     assert _adam(n=-3) == DS_ERR_SIZE
     assert _adam(dt=0) == DS_ERR_DTYPE
+    assert _adam(pdt=DS_FP32) == DS_ERR_DTYPE                       # the copy is 16-bit
+    assert _adam(pdt=5) == DS_ERR_DTYPE
     assert _adam(n=0) == DS_OK
     assert _adam(st=None) == DS_ERR_NULL
     for k in range(5):
@@ -135,15 +141,16 @@ def test_sumsq_validation():
     assert chk(ST, A, DS_FP16, 10000, A + 64, ws_need, STREAM) == DS_ERR_ALIAS
     assert chk(WS + 8, A, DS_FP16, 10000, WS, ws_need, STREAM) == DS_ERR_ALIAS   # state inside ws
     acc = L.ds_accumulate_sumsq
-    assert acc(A, B, -1, 1, ST, WS, ws_need, STREAM) == DS_ERR_SIZE
-    assert acc(A, B, 10000, 1, None, WS, ws_need, STREAM) == DS_ERR_NULL
-    assert acc(A, B, 0, 1, ST, WS, ws_need, STREAM) == DS_OK
-    assert acc(None, B, 10000, 1, ST, WS, ws_need, STREAM) == DS_ERR_NULL
-    assert acc(A, B, 10000, 1, ST, None, ws_need, STREAM) == DS_ERR_NULL
-    assert acc(A, B + 4, 10000, 1, ST, WS, ws_need, STREAM) == DS_ERR_ALIGN
-    assert acc(A, B, 10000, 1, ST, WS, 8, STREAM) == DS_ERR_SIZE
-    assert acc(A, B, 10000, 1, ST, A + 1024, ws_need, STREAM) == DS_ERR_ALIAS
-    assert acc(A, A + 16, 10000, 1, ST, WS, ws_need, STREAM) == DS_ERR_ALIAS
+    assert acc(A, B, DS_FP16, -1, 1, ST, WS, ws_need, STREAM) == DS_ERR_SIZE
+    assert acc(A, B, DS_FP16, 10000, 1, None, WS, ws_need, STREAM) == DS_ERR_NULL
+    assert acc(A, B, DS_FP16, 0, 1, ST, WS, ws_need, STREAM) == DS_OK
+    assert acc(None, B, DS_FP16, 10000, 1, ST, WS, ws_need, STREAM) == DS_ERR_NULL
+    assert acc(A, B, DS_FP16, 10000, 1, ST, None, ws_need, STREAM) == DS_ERR_NULL
+    assert acc(A, B + 4, DS_FP16, 10000, 1, ST, WS, ws_need, STREAM) == DS_ERR_ALIGN
+    assert acc(A, B, DS_FP16, 10000, 1, ST, WS, 8, STREAM) == DS_ERR_SIZE
+    assert acc(A, B, DS_FP16, 10000, 1, ST, A + 1024, ws_need, STREAM) == DS_ERR_ALIAS
+    assert acc(A, A + 16, DS_FP16, 10000, 1, ST, WS, ws_need, STREAM) == DS_ERR_ALIAS
+    assert acc(A, B, DS_FP32, 10000, 1, ST, WS, ws_need, STREAM) == DS_ERR_DTYPE
 
 
 def test_state_and_scalar_validation():

@@ -59,11 +59,11 @@ class ClipDev:
                 for start, size in spans:
                     a, gp = self.acc.data_ptr() + 4 * start, g.data_ptr() + 2 * start
                     if k == self.K - 1:
-                        L.ds_accumulate_sumsq(a, gp, size, k == 0, self.st, self.ws)
+                        L.ds_accumulate_sumsq(a, gp, L.DS_FP16, size, k == 0, self.st, self.ws)
                     else:
-                        L.ds_accumulate(a, gp, size, k == 0)
+                        L.ds_accumulate(a, gp, L.DS_FP16, size, k == 0)
             grad, dt = self.acc, L.DS_FP32
-        L.ds_adam_step(self.st, self.master, self.m, self.v, self.p16, grad, dt, n, LR, BETA1, BETA2, EPS,
+        L.ds_adam_step(self.st, self.master, self.m, self.v, self.p16, L.DS_FP16, grad, dt, n, LR, BETA1, BETA2, EPS,
                        0.0, max_norm, self.K)
         L.ds_update_loss_scale(self.st)
         return L.ds_state_read(self.st)
@@ -130,7 +130,7 @@ def test_sum_of_squares_does_not_depend_on_launch_shape(torch):
                 out.append(_lib.ds_state_read(st).grad_sumsq)
             acc = torch.zeros(n, device="cuda:0")
             _lib.ds_state_init(st, 1.0, 1.0, 1, 1, 0, 1)
-            _lib.ds_accumulate_sumsq(acc, g, n, True, st, ws)
+            _lib.ds_accumulate_sumsq(acc, g, _lib.DS_FP16, n, True, st, ws)
             out.append(_lib.ds_state_read(st).grad_sumsq)
             results[str(env)] = out
         finally:

@@ -89,13 +89,13 @@ def run_sampled(torch, name):
             gs_host.append(gh)
             if K > 1:
                 for start, size in buckets:
-                    _lib.ds_accumulate(acc.data_ptr() + 4 * start, g16.data_ptr() + 2 * start, size,
+                    _lib.ds_accumulate(acc.data_ptr() + 4 * start, g16.data_ptr() + 2 * start, _lib.DS_FP16, size,
                                        k == 0, st if k == K - 1 else None)
         if K == 1:
             _lib.ds_check_overflow(st, g16, _lib.DS_FP16, n)
-            _lib.ds_adam_step(st, master, m, v, p16, g16, _lib.DS_FP16, n, LR, BETA1, BETA2, EPS, 0.0, 0.0, 1)
+            _lib.ds_adam_step(st, master, m, v, p16, _lib.DS_FP16, g16, _lib.DS_FP16, n, LR, BETA1, BETA2, EPS, 0.0, 0.0, 1)
         else:
-            _lib.ds_adam_step(st, master, m, v, p16, acc, _lib.DS_FP32, n, LR, BETA1, BETA2, EPS, 0.0, 0.0, K)
+            _lib.ds_adam_step(st, master, m, v, p16, _lib.DS_FP16, acc, _lib.DS_FP32, n, LR, BETA1, BETA2, EPS, 0.0, 0.0, K)
         _lib.ds_update_loss_scale(st)
         ov = oracle.step(o, gs_host if K > 1 else gs_host[0], **HP)
         assert ov == (inj is not None), f"[{name}] step {s}: oracle flag"

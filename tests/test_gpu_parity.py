@@ -129,7 +129,7 @@ def test_accumulate_buffer_bits_and_bucketed_calls(torch):
     for k, g in enumerate(gs):
         gd = gu.dev_u16(torch, g)
         for start, size in spans:
-            _lib.ds_accumulate(acc.data_ptr() + 4 * start, gd.data_ptr() + 2 * start, size, k == 0,
+            _lib.ds_accumulate(acc.data_ptr() + 4 * start, gd.data_ptr() + 2 * start, _lib.DS_FP16, size, k == 0,
                                st if k == K - 1 else None)
     got = gu.host_f32(acc)
     assert np.array_equal(f32_bits(got), f32_bits(acc_o))
@@ -367,7 +367,7 @@ def test_fp16_cast_of_every_fp32_pattern(torch):
             m.zero_()
             v.zero_()
             _lib.ds_state_init(st, 1.0, 1.0, 1000, 1, 0, 1)
-            _lib.ds_adam_step(st, master, m, v, p16, g, _lib.DS_FP16, chunk, LR, BETA1, BETA2, EPS,
+            _lib.ds_adam_step(st, master, m, v, p16, _lib.DS_FP16, g, _lib.DS_FP16, chunk, LR, BETA1, BETA2, EPS,
                               0.0, 0.0, 1)
             got = gu.host_u16(p16)
             want = _enc16_parallel(pool, x)

@@ -7,10 +7,10 @@ dynamic loss-scale update -- hand-written HIP kernels behind the C ABI in
 include/dszero.h.  PyTorch supplies device memory and streams only.
 """
 from . import _lib
-from ._lib import DS_FP16, DS_FP32, DsError, DsScaler
+from ._lib import DS_BF16, DS_FP16, DS_FP32, DsError, DsScaler
 from .config import ZeroMPConfig
 from .layout import FlatLayout
 from .step import ShardStep
 
-__all__ = ["_lib", "DS_FP16", "DS_FP32", "DsError", "DsScaler", "ZeroMPConfig", "FlatLayout",
+__all__ = ["_lib", "DS_BF16", "DS_FP16", "DS_FP32", "DsError", "DsScaler", "ZeroMPConfig", "FlatLayout",
            "ShardStep"]

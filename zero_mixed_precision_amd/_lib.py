@@ -15,7 +15,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libdszero.so")
 
 DS_OK, DS_ERR_NULL, DS_ERR_SIZE, DS_ERR_ALIGN, DS_ERR_DTYPE, DS_ERR_HPARAM, DS_ERR_ALIAS, DS_ERR_HIP = range(8)
-DS_FP16, DS_FP32 = 1, 2
+DS_FP16, DS_FP32, DS_BF16 = 1, 2, 3
 
 EXPORTED = (
     "ds_scaler_size", "ds_state_init", "ds_state_read", "ds_state_write", "ds_accumulate",
@@ -90,13 +90,13 @@ def _load():
         "ds_state_init": ([vp, f32, f32, i32, i32, i32, i32, vp], ctypes.c_int),
         "ds_state_read": ([vp, ctypes.POINTER(DsScaler), vp], ctypes.c_int),
         "ds_state_write": ([vp, ctypes.POINTER(DsScaler), vp], ctypes.c_int),
-        "ds_accumulate": ([vp, vp, i64, i32, vp, vp], ctypes.c_int),
+        "ds_accumulate": ([vp, vp, ctypes.c_int, i64, i32, vp, vp], ctypes.c_int),
         "ds_check_overflow": ([vp, vp, ctypes.c_int, i64, vp], ctypes.c_int),
-        "ds_adam_step": ([vp, vp, vp, vp, vp, vp, ctypes.c_int, i64, f32, f32, f32, f32, f32, f32, i32,
-                          vp], ctypes.c_int),
+        "ds_adam_step": ([vp, vp, vp, vp, vp, ctypes.c_int, vp, ctypes.c_int, i64, f32, f32, f32, f32, f32,
+                          f32, i32, vp], ctypes.c_int),
         "ds_sumsq_workspace_bytes": ([i64], ctypes.c_size_t),
         "ds_check_overflow_sumsq": ([vp, vp, ctypes.c_int, i64, vp, ctypes.c_size_t, vp], ctypes.c_int),
-        "ds_accumulate_sumsq": ([vp, vp, i64, i32, vp, vp, ctypes.c_size_t, vp], ctypes.c_int),
+        "ds_accumulate_sumsq": ([vp, vp, ctypes.c_int, i64, i32, vp, vp, ctypes.c_size_t, vp], ctypes.c_int),
         "ds_update_loss_scale": ([vp, vp], ctypes.c_int),
         "ds_adam_bias_scalars": ([vp, f32, f32, f32, vp, vp], ctypes.c_int),
         "ds_layout_greedy": ([vp, i32, i64, i64, vp, vp, vp, vp, ctypes.POINTER(i32),
@@ -163,19 +163,19 @@ def ds_state_write(st, value: DsScaler, stream=None) -> None:
     _ok(lib.ds_state_write(_p(st), ctypes.byref(value), _s(stream)), "ds_state_write")
 
 
-def ds_accumulate(acc, g16, n, overwrite, st_or_null=None, stream=None) -> None:
-    _ok(lib.ds_accumulate(_p(acc), _p(g16), int(n), int(bool(overwrite)), _p(st_or_null), _s(stream)),
-        "ds_accumulate")
+def ds_accumulate(acc, g16, gdt, n, overwrite, st_or_null=None, stream=None) -> None:
+    _ok(lib.ds_accumulate(_p(acc), _p(g16), int(gdt), int(n), int(bool(overwrite)), _p(st_or_null),
+                          _s(stream)), "ds_accumulate")
 
 
 def ds_check_overflow(st, grad, dtype, n, stream=None) -> None:
     _ok(lib.ds_check_overflow(_p(st), _p(grad), int(dtype), int(n), _s(stream)), "ds_check_overflow")
 
 
-def ds_adam_step(st, master, m, v, p16, grad, dtype, n, lr, beta1, beta2, eps, weight_decay,
+def ds_adam_step(st, master, m, v, p16, pdt, grad, dtype, n, lr, beta1, beta2, eps, weight_decay,
                  max_grad_norm, accum_steps, stream=None) -> None:
-    _ok(lib.ds_adam_step(_p(st), _p(master), _p(m), _p(v), _p(p16), _p(grad), int(dtype), int(n),
-                         lr, beta1, beta2, eps, weight_decay, max_grad_norm, int(accum_steps),
+    _ok(lib.ds_adam_step(_p(st), _p(master), _p(m), _p(v), _p(p16), int(pdt), _p(grad), int(dtype),
+                         int(n), lr, beta1, beta2, eps, weight_decay, max_grad_norm, int(accum_steps),
                          _s(stream)), "ds_adam_step")
 
 
@@ -195,9 +195,11 @@ def ds_check_overflow_sumsq(st, grad, dtype, n, workspace, workspace_bytes=None,
         "ds_check_overflow_sumsq")
 
 
-def ds_accumulate_sumsq(acc, g16, n, overwrite, st, workspace, workspace_bytes=None, stream=None) -> None:
-    _ok(lib.ds_accumulate_sumsq(_p(acc), _p(g16), int(n), int(bool(overwrite)), _p(st), _p(workspace),
-                                _nbytes(workspace, workspace_bytes), _s(stream)), "ds_accumulate_sumsq")
+def ds_accumulate_sumsq(acc, g16, gdt, n, overwrite, st, workspace, workspace_bytes=None,
+                        stream=None) -> None:
+    _ok(lib.ds_accumulate_sumsq(_p(acc), _p(g16), int(gdt), int(n), int(bool(overwrite)), _p(st),
+                                _p(workspace), _nbytes(workspace, workspace_bytes), _s(stream)),
+        "ds_accumulate_sumsq")
 
 
 def ds_update_loss_scale(st, stream=None) -> None:

@@ -1,9 +1,9 @@
 """The ds_config.json keys the optimizer step consumes.
 
 "DeepSpeed complete guide" section 4.1 (base structure: gradient_accumulation_steps,
-gradient_clipping, fp16, optimizer, zero_optimization), section 4.2 (fp16 block: loss_scale 0 is
+gradient_clipping, fp16, bf16, optimizer, zero_optimization), section 4.2 (fp16 block: loss_scale 0 is
 dynamic, initial scale 2^initial_scale_power, loss_scale_window,
-hysteresis, consecutive_hysteresis, min_loss_scale), section 4.3
+hysteresis, consecutive_hysteresis, min_loss_scale; bf16 block: no loss scaling), section 4.3
 (train_batch_size = micro batch x gradient_accumulation_steps x world size).
 "auto" values are resolved by a trainer integration, which this library does
 not have: they are rejected.
@@ -22,6 +22,9 @@ def _val(d: dict, key: str, default):
 
 @dataclass
 class ZeroMPConfig:
+    # bf16 block (section 4.2: bf16 needs no loss scaling): bf16 gradients and
+    # parameter copy, a static loss scale of 1 (a non-finite gradient still skips)
+    bf16: bool = False
     # fp16 block
     loss_scale: float = 0.0
     initial_scale_power: int = 16
@@ -45,10 +48,12 @@ class ZeroMPConfig:
 
     @property
     def dynamic(self) -> bool:
-        return self.loss_scale == 0
+        return self.loss_scale == 0 and not self.bf16
 
     @property
     def init_scale(self) -> float:
+        if self.bf16:
+            return 1.0
         return 2.0 ** self.initial_scale_power if self.dynamic else float(self.loss_scale)
 
     def train_batch_size(self, world_size: int) -> int:
@@ -57,8 +62,12 @@ class ZeroMPConfig:
     @classmethod
     def from_dict(cls, cfg: dict) -> "ZeroMPConfig":
         fp16 = cfg.get("fp16", {})
-        if fp16 and not _val(fp16, "enabled", True):
-            raise ValueError("fp16.enabled is false: this step is the fp16 mixed-precision path")
+        bf16 = bool(_val(cfg.get("bf16", {}), "enabled", False))
+        fp16_on = bool(_val(fp16, "enabled", True)) if fp16 else not bf16
+        if bf16 and fp16 and fp16_on:
+            raise ValueError("fp16 and bf16 are both enabled")
+        if not bf16 and not fp16_on:
+            raise ValueError("neither fp16 nor bf16 is enabled: this step is the mixed-precision path")
         opt = cfg.get("optimizer", {})
         params = opt.get("params", {})
         zero = cfg.get("zero_optimization", {})
@@ -67,6 +76,7 @@ class ZeroMPConfig:
             raise ValueError(f"optimizer type {kind!r} is not Adam/AdamW")
         betas = tuple(float(b) for b in _val(params, "betas", (0.9, 0.999)))
         out = cls(
+            bf16=bf16,
             loss_scale=float(_val(fp16, "loss_scale", 0.0)),
             initial_scale_power=int(_val(fp16, "initial_scale_power", 16)),
             loss_scale_window=int(_val(fp16, "loss_scale_window", 1000)),

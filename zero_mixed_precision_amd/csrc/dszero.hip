@@ -87,14 +87,49 @@ __device__ __forceinline__ uint32_t f2h(float x)
     return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<_Float16>(x)));
 }
 
-__device__ __forceinline__ f32x4 widen4(u32x2 w)
+// Element formats: 16-bit arrays are fp16 (IEEE binary16) or bf16 (the top
+// half of a binary32); gradients may also be fp32 (the accumulation buffer).
+constexpr int kF16 = 0, kBF16 = 1, kF32 = 2;
+
+// bf16 -> fp32 is exact (append 16 zero bits); fp32 -> bf16 rounds to nearest
+// even (hardware conversion).
+__device__ __forceinline__ uint32_t f2bf(float x)
 {
-    return f32x4{h2f(w.x & 0xFFFFu), h2f(w.x >> 16), h2f(w.y & 0xFFFFu), h2f(w.y >> 16)};
+    return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<__bf16>(x)));
 }
 
+template <int FMT>
+__device__ __forceinline__ float dec1(uint32_t bits)
+{
+    if constexpr (FMT == kBF16)
+        return __uint_as_float((bits & 0xFFFFu) << 16);
+    else
+        return h2f(bits);
+}
+
+template <int FMT>
+__device__ __forceinline__ uint32_t enc1(float x)
+{
+    if constexpr (FMT == kBF16)
+        return f2bf(x);
+    else
+        return f2h(x);
+}
+
+template <int FMT>
+__device__ __forceinline__ f32x4 widen4(u32x2 w)
+{
+    if constexpr (FMT == kBF16)
+        return f32x4{__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xFFFF0000u),
+                     __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xFFFF0000u)};
+    else
+        return f32x4{h2f(w.x & 0xFFFFu), h2f(w.x >> 16), h2f(w.y & 0xFFFFu), h2f(w.y >> 16)};
+}
+
+template <int FMT>
 __device__ __forceinline__ u32x2 narrow4(f32x4 p)
 {
-    return u32x2{f2h(p.x) | (f2h(p.y) << 16), f2h(p.z) | (f2h(p.w) << 16)};
+    return u32x2{enc1<FMT>(p.x) | (enc1<FMT>(p.y) << 16), enc1<FMT>(p.z) | (enc1<FMT>(p.w) << 16)};
 }
 
 // Non-finite tests on raw bits: an exponent field of all ones is +-inf or NaN.
@@ -103,6 +138,20 @@ __device__ __forceinline__ u32x2 narrow4(f32x4 p)
 __device__ __forceinline__ uint32_t nonfinite_f16x2(uint32_t w)
 {
     return ((w & 0x7C007C00u) + 0x04000400u) & 0x80008000u;
+}
+
+__device__ __forceinline__ uint32_t nonfinite_bf16x2(uint32_t w)
+{
+    return ((w & 0x7F807F80u) + 0x00800080u) & 0x80008000u;
+}
+
+template <int FMT>
+__device__ __forceinline__ uint32_t nonfinite16x2(uint32_t w)
+{
+    if constexpr (FMT == kBF16)
+        return nonfinite_bf16x2(w);
+    else
+        return nonfinite_f16x2(w);
 }
 
 __device__ __forceinline__ uint32_t nonfinite_f32(uint32_t w)
@@ -275,29 +324,29 @@ __device__ __forceinline__ void adam4(const f32x4& g, f32x4& p, f32x4& m, f32x4&
     }
 }
 
-template <bool F32G, bool NT>
+template <int GF, bool NT>
 __device__ __forceinline__ f32x4 load_grad4(const void* grad, int64_t q)
 {
-    if constexpr (F32G)
+    if constexpr (GF == kF32)
         return load<NT>(static_cast<const f32x4*>(grad) + q);
     else
-        return widen4(load<NT>(static_cast<const u32x2*>(grad) + q));
+        return widen4<GF>(load<NT>(static_cast<const u32x2*>(grad) + q));
 }
 
-template <bool F32G>
+template <int GF>
 __device__ __forceinline__ float load_grad1(const void* grad, int64_t i)
 {
-    if constexpr (F32G)
+    if constexpr (GF == kF32)
         return static_cast<const float*>(grad)[i];
     else
-        return h2f(static_cast<const uint16_t*>(grad)[i]);
+        return dec1<GF>(static_cast<const uint16_t*>(grad)[i]);
 }
 
 // Gated fused step: if the step's overflow flag is set, return before any
 // write; else update every element of [0, n) once.  Tiles of U x TPB quads are
 // dealt to blocks round-robin; block 0 also takes the quads of the last,
 // partial tile and the final n % 4 elements.
-template <bool F32G, bool WD, bool NT, int TPB, int U>
+template <int GF, int PF, bool WD, bool NT, int TPB, int U>
 __global__ __launch_bounds__(TPB) void adam_kernel(const ds_scaler* __restrict__ st,
                                                    float* __restrict__ master,
                                                    float* __restrict__ mom1,
@@ -324,7 +373,7 @@ __global__ __launch_bounds__(TPB) void adam_kernel(const ds_scaler* __restrict__
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int64_t i = q0 + u * TPB;
-            g[u] = load_grad4<F32G, NT>(grad, i);
+            g[u] = load_grad4<GF, NT>(grad, i);
             p[u] = load<NT>(P + i);
             m[u] = load<NT>(M + i);
             v[u] = load<NT>(V + i);
@@ -336,28 +385,28 @@ __global__ __launch_bounds__(TPB) void adam_kernel(const ds_scaler* __restrict__
             store<NT>(P + i, p[u]);
             store<NT>(M + i, m[u]);
             store<NT>(V + i, v[u]);
-            store<NT>(H + i, narrow4(p[u]));
+            store<NT>(H + i, narrow4<PF>(p[u]));
         }
     }
     if (blockIdx.x != 0)
         return;
     for (int64_t q = ntiles * T + threadIdx.x; q < nq; q += TPB) {
-        f32x4 g = load_grad4<F32G, NT>(grad, q);
+        f32x4 g = load_grad4<GF, NT>(grad, q);
         f32x4 p = load<NT>(P + q), m = load<NT>(M + q), v = load<NT>(V + q);
         adam4<WD>(g, p, m, v, c);
         store<NT>(P + q, p);
         store<NT>(M + q, m);
         store<NT>(V + q, v);
-        store<NT>(H + q, narrow4(p));
+        store<NT>(H + q, narrow4<PF>(p));
     }
     if (static_cast<int64_t>(threadIdx.x) < (n & 3)) {
         const int64_t i = (nq << 2) + threadIdx.x;
         float p = master[i], m = mom1[i], v = mom2[i];
-        adam1<WD>(load_grad1<F32G>(grad, i), p, m, v, c);
+        adam1<WD>(load_grad1<GF>(grad, i), p, m, v, c);
         master[i] = p;
         mom1[i] = m;
         mom2[i] = v;
-        p16[i] = static_cast<uint16_t>(f2h(p));
+        p16[i] = static_cast<uint16_t>(enc1<PF>(p));
     }
 }
 
@@ -373,14 +422,15 @@ __global__ void bias_scalars_kernel(const ds_scaler* st, float lr, float beta1, 
 // overflow check
 // ---------------------------------------------------------------------------
 
-// fp16: 8 elements per 16-byte vector; fp32: 4.  One vector per lane per
+// fp16/bf16: 8 elements per 16-byte vector; fp32: 4.  One vector per lane per
 // grid-stride step; block 0 also tests the elements after the last vector.
-template <bool F32, bool NT, int TPB>
+template <int GF, bool NT, int TPB>
 __global__ __launch_bounds__(TPB) void check_kernel(ds_scaler* __restrict__ st,
                                                     const void* __restrict__ grad, int64_t n)
 {
     if (st->overflow != 0u)
         return;  // already decided for this step
+    constexpr bool F32 = GF == kF32;
     constexpr int kPer = F32 ? 4 : 8;
     const u32x4* G = static_cast<const u32x4*>(grad);
     const int64_t nv = n / kPer;
@@ -391,15 +441,15 @@ __global__ __launch_bounds__(TPB) void check_kernel(ds_scaler* __restrict__ st,
         if constexpr (F32)
             bad |= nonfinite_f32(w.x) | nonfinite_f32(w.y) | nonfinite_f32(w.z) | nonfinite_f32(w.w);
         else
-            bad |= nonfinite_f16x2(w.x) | nonfinite_f16x2(w.y) | nonfinite_f16x2(w.z) |
-                   nonfinite_f16x2(w.w);
+            bad |= nonfinite16x2<GF>(w.x) | nonfinite16x2<GF>(w.y) | nonfinite16x2<GF>(w.z) |
+                   nonfinite16x2<GF>(w.w);
     }
     if (blockIdx.x == 0 && static_cast<int64_t>(threadIdx.x) < n - nv * kPer) {
         const int64_t i = nv * kPer + threadIdx.x;
         if constexpr (F32)
             bad |= nonfinite_f32(static_cast<const uint32_t*>(grad)[i]);
         else
-            bad |= nonfinite_f16x2(static_cast<const uint16_t*>(grad)[i]);
+            bad |= nonfinite16x2<GF>(static_cast<const uint16_t*>(grad)[i]);
     }
     raise_flag(st, bad);
 }
@@ -409,11 +459,12 @@ __global__ __launch_bounds__(TPB) void check_kernel(ds_scaler* __restrict__ st,
 // elements); vector j of lane l is vector j * TPB + l of the chunk, so each
 // of the kVecs loads is one contiguous span across the block, and each lane
 // sums its elements in order.
-template <bool F32, int TPB>
+template <int GF, int TPB>
 __global__ __launch_bounds__(TPB) void check_sumsq_kernel(ds_scaler* __restrict__ st,
                                                           const void* __restrict__ grad, int64_t n,
                                                           double* __restrict__ part)
 {
+    constexpr bool F32 = GF == kF32;
     constexpr int kPer = F32 ? 4 : 8;
     constexpr int kVecs = 4;
     constexpr int64_t kCh = static_cast<int64_t>(TPB) * kVecs * kPer;
@@ -444,10 +495,10 @@ __global__ __launch_bounds__(TPB) void check_sumsq_kernel(ds_scaler* __restrict_
                     s = s + sq4(f32x4{__uint_as_float(w[j].x), __uint_as_float(w[j].y),
                                       __uint_as_float(w[j].z), __uint_as_float(w[j].w)});
                 } else {
-                    bad |= nonfinite_f16x2(w[j].x) | nonfinite_f16x2(w[j].y) | nonfinite_f16x2(w[j].z) |
-                           nonfinite_f16x2(w[j].w);
-                    s = s + sq4(widen4(u32x2{w[j].x, w[j].y}));
-                    s = s + sq4(widen4(u32x2{w[j].z, w[j].w}));
+                    bad |= nonfinite16x2<GF>(w[j].x) | nonfinite16x2<GF>(w[j].y) |
+                           nonfinite16x2<GF>(w[j].z) | nonfinite16x2<GF>(w[j].w);
+                    s = s + sq4(widen4<GF>(u32x2{w[j].x, w[j].y}));
+                    s = s + sq4(widen4<GF>(u32x2{w[j].z, w[j].w}));
                 }
             } else {
                 for (int k = 0; k < kPer; ++k) {
@@ -459,8 +510,8 @@ __global__ __launch_bounds__(TPB) void check_sumsq_kernel(ds_scaler* __restrict_
                             s = s + sq(__uint_as_float(bits));
                         } else {
                             const uint32_t bits = static_cast<const uint16_t*>(grad)[i];
-                            bad |= nonfinite_f16x2(bits);
-                            s = s + sq(h2f(bits));
+                            bad |= nonfinite16x2<GF>(bits);
+                            s = s + sq(dec1<GF>(bits));
                         }
                     }
                 }
@@ -480,7 +531,7 @@ __global__ __launch_bounds__(TPB) void check_sumsq_kernel(ds_scaler* __restrict_
 // Same tiling as the Adam kernel.  With SUMSQ (which needs CHECK and U * TPB
 // * 4 == 4096) each tile is one chunk of the sum of squares of the result,
 // written to part[tile].
-template <bool OVERWRITE, bool CHECK, bool SUMSQ, bool NT, int TPB, int U>
+template <int GF, bool OVERWRITE, bool CHECK, bool SUMSQ, bool NT, int TPB, int U>
 __global__ __launch_bounds__(TPB) void accumulate_kernel(float* __restrict__ acc,
                                                          const uint16_t* __restrict__ g16,
                                                          int64_t n, ds_scaler* __restrict__ st,
@@ -500,7 +551,7 @@ __global__ __launch_bounds__(TPB) void accumulate_kernel(float* __restrict__ acc
         double s = 0.0;
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            g[u] = widen4(load<NT>(G + q0 + u * TPB));
+            g[u] = widen4<GF>(load<NT>(G + q0 + u * TPB));
             if constexpr (!OVERWRITE)
                 a[u] = load<NT>(A + q0 + u * TPB);
         }
@@ -526,7 +577,7 @@ __global__ __launch_bounds__(TPB) void accumulate_kernel(float* __restrict__ acc
     if (blockIdx.x == 0) {
         double s = 0.0;
         for (int64_t q = ntiles * T + threadIdx.x; q < nq; q += TPB) {
-            const f32x4 g = widen4(load<NT>(G + q));
+            const f32x4 g = widen4<GF>(load<NT>(G + q));
             f32x4 r;
             if constexpr (OVERWRITE)
                 r = g;
@@ -540,7 +591,7 @@ __global__ __launch_bounds__(TPB) void accumulate_kernel(float* __restrict__ acc
         }
         if (static_cast<int64_t>(threadIdx.x) < (n & 3)) {
             const int64_t i = (nq << 2) + threadIdx.x;
-            const float g = h2f(g16[i]);
+            const float g = dec1<GF>(g16[i]);
             const float r = OVERWRITE ? g : acc[i] + g;
             if constexpr (CHECK)
                 bad |= nonfinite_f32(__float_as_uint(r));
@@ -657,35 +708,94 @@ ds_status launched()
     return hipGetLastError() == hipSuccess ? DS_OK : DS_ERR_HIP;
 }
 
-template <bool F32G, bool WD, bool NT>
-void launch_adam_u(int unroll, unsigned blocks, hipStream_t s, const ds_scaler* st, float* master,
-                   float* m, float* v, uint16_t* p16, const void* grad, int64_t n, const AdamHyper& hp)
+// Kernel dispatch: runtime formats and switches -> template instances.
+
+int fmt_of(ds_dtype dt) { return dt == DS_BF16 ? kBF16 : (dt == DS_FP32 ? kF32 : kF16); }
+bool is16(ds_dtype dt) { return dt == DS_FP16 || dt == DS_BF16; }
+bool known(ds_dtype dt) { return dt == DS_FP16 || dt == DS_BF16 || dt == DS_FP32; }
+uint64_t esize(ds_dtype dt) { return dt == DS_FP32 ? 4 : 2; }
+
+struct AdamArgs {
+    const ds_scaler* st;
+    float *master, *m, *v;
+    uint16_t* p16;
+    const void* grad;
+    int64_t n;
+    AdamHyper hp;
+};
+
+template <int GF, int PF, bool WD, bool NT>
+void launch_adam4(int unroll, unsigned blocks, hipStream_t s, const AdamArgs& a)
 {
     if (unroll == 2)
-        adam_kernel<F32G, WD, NT, kStepBlock, 2><<<blocks, kStepBlock, 0, s>>>(st, master, m, v, p16, grad, n, hp);
+        adam_kernel<GF, PF, WD, NT, kStepBlock, 2><<<blocks, kStepBlock, 0, s>>>(a.st, a.master, a.m, a.v, a.p16, a.grad, a.n, a.hp);
     else
-        adam_kernel<F32G, WD, NT, kStepBlock, 4><<<blocks, kStepBlock, 0, s>>>(st, master, m, v, p16, grad, n, hp);
+        adam_kernel<GF, PF, WD, NT, kStepBlock, 4><<<blocks, kStepBlock, 0, s>>>(a.st, a.master, a.m, a.v, a.p16, a.grad, a.n, a.hp);
 }
 
-template <bool F32G, bool WD>
-void launch_adam_nt(bool nt, int unroll, unsigned blocks, hipStream_t s, const ds_scaler* st,
-                    float* master, float* m, float* v, uint16_t* p16, const void* grad, int64_t n,
-                    const AdamHyper& hp)
+template <int GF, int PF>
+void launch_adam2(bool wd, bool nt, int unroll, unsigned blocks, hipStream_t s, const AdamArgs& a)
 {
-    if (nt)
-        launch_adam_u<F32G, WD, true>(unroll, blocks, s, st, master, m, v, p16, grad, n, hp);
-    else
-        launch_adam_u<F32G, WD, false>(unroll, blocks, s, st, master, m, v, p16, grad, n, hp);
+    if (wd) {
+        if (nt) launch_adam4<GF, PF, true, true>(unroll, blocks, s, a);
+        else    launch_adam4<GF, PF, true, false>(unroll, blocks, s, a);
+    } else {
+        if (nt) launch_adam4<GF, PF, false, true>(unroll, blocks, s, a);
+        else    launch_adam4<GF, PF, false, false>(unroll, blocks, s, a);
+    }
 }
 
-template <bool OW, bool CK, bool NT>
-void launch_acc_u(int unroll, unsigned blocks, hipStream_t s, float* acc, const uint16_t* g16, int64_t n,
-                  ds_scaler* st)
+void launch_adam(int gf, int pf, bool wd, bool nt, int unroll, unsigned blocks, hipStream_t s, const AdamArgs& a)
+{
+    if (pf == kBF16) {
+        if (gf == kF16)       launch_adam2<kF16, kBF16>(wd, nt, unroll, blocks, s, a);
+        else if (gf == kBF16) launch_adam2<kBF16, kBF16>(wd, nt, unroll, blocks, s, a);
+        else                  launch_adam2<kF32, kBF16>(wd, nt, unroll, blocks, s, a);
+    } else {
+        if (gf == kF16)       launch_adam2<kF16, kF16>(wd, nt, unroll, blocks, s, a);
+        else if (gf == kBF16) launch_adam2<kBF16, kF16>(wd, nt, unroll, blocks, s, a);
+        else                  launch_adam2<kF32, kF16>(wd, nt, unroll, blocks, s, a);
+    }
+}
+
+template <int GF, bool OW, bool CK, bool NT>
+void launch_acc4(int unroll, unsigned blocks, hipStream_t s, float* acc, const uint16_t* g16, int64_t n,
+                 ds_scaler* st)
 {
     if (unroll == 2)
-        accumulate_kernel<OW, CK, false, NT, kStepBlock, 2><<<blocks, kStepBlock, 0, s>>>(acc, g16, n, st, nullptr);
+        accumulate_kernel<GF, OW, CK, false, NT, kStepBlock, 2><<<blocks, kStepBlock, 0, s>>>(acc, g16, n, st, nullptr);
     else
-        accumulate_kernel<OW, CK, false, NT, kStepBlock, 4><<<blocks, kStepBlock, 0, s>>>(acc, g16, n, st, nullptr);
+        accumulate_kernel<GF, OW, CK, false, NT, kStepBlock, 4><<<blocks, kStepBlock, 0, s>>>(acc, g16, n, st, nullptr);
+}
+
+template <int GF>
+void launch_acc(bool ow, bool ck, bool nt, int unroll, unsigned blocks, hipStream_t s, float* acc,
+                const uint16_t* g16, int64_t n, ds_scaler* st)
+{
+    if (nt) {
+        if (ow) { if (ck) launch_acc4<GF, true, true, true>(unroll, blocks, s, acc, g16, n, st);
+                  else    launch_acc4<GF, true, false, true>(unroll, blocks, s, acc, g16, n, st); }
+        else    { if (ck) launch_acc4<GF, false, true, true>(unroll, blocks, s, acc, g16, n, st);
+                  else    launch_acc4<GF, false, false, true>(unroll, blocks, s, acc, g16, n, st); }
+    } else {
+        if (ow) { if (ck) launch_acc4<GF, true, true, false>(unroll, blocks, s, acc, g16, n, st);
+                  else    launch_acc4<GF, true, false, false>(unroll, blocks, s, acc, g16, n, st); }
+        else    { if (ck) launch_acc4<GF, false, true, false>(unroll, blocks, s, acc, g16, n, st);
+                  else    launch_acc4<GF, false, false, false>(unroll, blocks, s, acc, g16, n, st); }
+    }
+}
+
+template <int GF>
+void launch_acc_sumsq(bool ow, bool nt, unsigned blocks, hipStream_t s, float* acc, const uint16_t* g16,
+                      int64_t n, ds_scaler* st, double* part)
+{
+    if (nt) {
+        if (ow) accumulate_kernel<GF, true, true, true, true, kStepBlock, 4><<<blocks, kStepBlock, 0, s>>>(acc, g16, n, st, part);
+        else    accumulate_kernel<GF, false, true, true, true, kStepBlock, 4><<<blocks, kStepBlock, 0, s>>>(acc, g16, n, st, part);
+    } else {
+        if (ow) accumulate_kernel<GF, true, true, true, false, kStepBlock, 4><<<blocks, kStepBlock, 0, s>>>(acc, g16, n, st, part);
+        else    accumulate_kernel<GF, false, true, true, false, kStepBlock, 4><<<blocks, kStepBlock, 0, s>>>(acc, g16, n, st, part);
+    }
 }
 
 int64_t sumsq_chunks(int64_t n) { return (n + kChunk - 1) / kChunk; }
@@ -774,11 +884,13 @@ ds_status ds_state_write(ds_scaler* st, const ds_scaler* host_in, void* stream)
     return launched();
 }
 
-ds_status ds_accumulate(float* acc, const uint16_t* g16, int64_t n, int32_t overwrite,
+ds_status ds_accumulate(float* acc, const uint16_t* g16, ds_dtype gdt, int64_t n, int32_t overwrite,
                         ds_scaler* st_or_null, void* stream)
 {
     if (n < 0)
         return DS_ERR_SIZE;
+    if (!is16(gdt))
+        return DS_ERR_DTYPE;
     if (n == 0)
         return DS_OK;
     if (acc == nullptr || g16 == nullptr)
@@ -794,15 +906,10 @@ ds_status ds_accumulate(float* acc, const uint16_t* g16, int64_t n, int32_t over
     const unsigned blocks = grid_blocks(tiles_of(n, unroll));
     const bool nt = variant_nt();
     const bool ow = overwrite != 0, ck = st_or_null != nullptr;
-#define DS_ACC(OW, CK, NT) launch_acc_u<OW, CK, NT>(unroll, blocks, s, acc, g16, n, st_or_null)
-    if (nt) {
-        if (ow) { if (ck) DS_ACC(true, true, true); else DS_ACC(true, false, true); }
-        else    { if (ck) DS_ACC(false, true, true); else DS_ACC(false, false, true); }
-    } else {
-        if (ow) { if (ck) DS_ACC(true, true, false); else DS_ACC(true, false, false); }
-        else    { if (ck) DS_ACC(false, true, false); else DS_ACC(false, false, false); }
-    }
-#undef DS_ACC
+    if (gdt == DS_BF16)
+        launch_acc<kBF16>(ow, ck, nt, unroll, blocks, s, acc, g16, n, st_or_null);
+    else
+        launch_acc<kF16>(ow, ck, nt, unroll, blocks, s, acc, g16, n, st_or_null);
     return launched();
 }
 
@@ -810,7 +917,7 @@ ds_status ds_check_overflow(ds_scaler* st, const void* grad, ds_dtype dt, int64_
 {
     if (n < 0)
         return DS_ERR_SIZE;
-    if (dt != DS_FP16 && dt != DS_FP32)
+    if (!known(dt))
         return DS_ERR_DTYPE;
     if (st == nullptr)
         return DS_ERR_NULL;
@@ -820,28 +927,29 @@ ds_status ds_check_overflow(ds_scaler* st, const void* grad, ds_dtype dt, int64_
         return DS_ERR_NULL;
     if (!aligned(grad, 16) || !aligned(st, 8))
         return DS_ERR_ALIGN;
-    const uint64_t es = dt == DS_FP16 ? 2 : 4;
-    if (overlap(grad, es * static_cast<uint64_t>(n), st, sizeof(ds_scaler)))
+    if (overlap(grad, esize(dt) * static_cast<uint64_t>(n), st, sizeof(ds_scaler)))
         return DS_ERR_ALIAS;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    const int64_t vecs = n / (dt == DS_FP16 ? 8 : 4);
+    const int64_t vecs = n / (dt == DS_FP32 ? 4 : 8);
     const unsigned blocks = grid_blocks((vecs + kCheckBlock - 1) / kCheckBlock);
     // ordinary loads: leave the gradient in the Infinity Cache for the Adam pass
     if (dt == DS_FP16)
-        check_kernel<false, false, kCheckBlock><<<blocks, kCheckBlock, 0, s>>>(st, grad, n);
+        check_kernel<kF16, false, kCheckBlock><<<blocks, kCheckBlock, 0, s>>>(st, grad, n);
+    else if (dt == DS_BF16)
+        check_kernel<kBF16, false, kCheckBlock><<<blocks, kCheckBlock, 0, s>>>(st, grad, n);
     else
-        check_kernel<true, false, kCheckBlock><<<blocks, kCheckBlock, 0, s>>>(st, grad, n);
+        check_kernel<kF32, false, kCheckBlock><<<blocks, kCheckBlock, 0, s>>>(st, grad, n);
     return launched();
 }
 
 ds_status ds_adam_step(const ds_scaler* st, float* master, float* m, float* v, uint16_t* p16,
-                       const void* grad, ds_dtype dt, int64_t n, float lr, float beta1,
+                       ds_dtype pdt, const void* grad, ds_dtype dt, int64_t n, float lr, float beta1,
                        float beta2, float eps, float weight_decay, float max_grad_norm,
                        int32_t accum_steps, void* stream)
 {
     if (n < 0)
         return DS_ERR_SIZE;
-    if (dt != DS_FP16 && dt != DS_FP32)
+    if (!known(dt) || !is16(pdt))
         return DS_ERR_DTYPE;
     if (!finite_ge0(lr) || !beta_ok(beta1) || !beta_ok(beta2) || !std::isfinite(eps) || eps <= 0.0f ||
         !finite_ge0(weight_decay) || !finite_ge0(max_grad_norm) || accum_steps < 1)
@@ -857,8 +965,7 @@ ds_status ds_adam_step(const ds_scaler* st, float* master, float* m, float* v, u
         return DS_ERR_ALIGN;
     const uint64_t un = static_cast<uint64_t>(n);
     const void* ptrs[6] = {master, m, v, p16, grad, st};
-    const uint64_t sizes[6] = {4 * un, 4 * un, 4 * un, 2 * un, (dt == DS_FP16 ? 2 : 4) * un,
-                               sizeof(ds_scaler)};
+    const uint64_t sizes[6] = {4 * un, 4 * un, 4 * un, 2 * un, esize(dt) * un, sizeof(ds_scaler)};
     for (int i = 0; i < 6; ++i)
         for (int j = i + 1; j < 6; ++j)
             if (overlap(ptrs[i], sizes[i], ptrs[j], sizes[j]))
@@ -870,13 +977,8 @@ ds_status ds_adam_step(const ds_scaler* st, float* master, float* m, float* v, u
     const unsigned blocks = grid_blocks(tiles_of(n, unroll));
     const bool nt = variant_nt();
     const bool wd = weight_decay != 0.0f;
-    if (dt == DS_FP16) {
-        if (wd) launch_adam_nt<false, true>(nt, unroll, blocks, s, st, master, m, v, p16, grad, n, hp);
-        else    launch_adam_nt<false, false>(nt, unroll, blocks, s, st, master, m, v, p16, grad, n, hp);
-    } else {
-        if (wd) launch_adam_nt<true, true>(nt, unroll, blocks, s, st, master, m, v, p16, grad, n, hp);
-        else    launch_adam_nt<true, false>(nt, unroll, blocks, s, st, master, m, v, p16, grad, n, hp);
-    }
+    const AdamArgs args{st, master, m, v, p16, grad, n, hp};
+    launch_adam(fmt_of(dt), fmt_of(pdt), wd, nt, unroll, blocks, s, args);
     return launched();
 }
 
@@ -890,7 +992,7 @@ ds_status ds_check_overflow_sumsq(ds_scaler* st, const void* grad, ds_dtype dt, 
 {
     if (n < 0)
         return DS_ERR_SIZE;
-    if (dt != DS_FP16 && dt != DS_FP32)
+    if (!known(dt))
         return DS_ERR_DTYPE;
     if (st == nullptr)
         return DS_ERR_NULL;
@@ -902,7 +1004,7 @@ ds_status ds_check_overflow_sumsq(ds_scaler* st, const void* grad, ds_dtype dt, 
         return DS_ERR_ALIGN;
     if (const ds_status w = check_workspace(workspace, workspace_bytes, n); w != DS_OK)
         return w;
-    const uint64_t gb = (dt == DS_FP16 ? 2 : 4) * static_cast<uint64_t>(n);
+    const uint64_t gb = esize(dt) * static_cast<uint64_t>(n);
     const uint64_t wb = 8 * static_cast<uint64_t>(sumsq_chunks(n));
     if (overlap(grad, gb, st, sizeof(ds_scaler)) || overlap(grad, gb, workspace, wb) ||
         overlap(st, sizeof(ds_scaler), workspace, wb))
@@ -912,20 +1014,24 @@ ds_status ds_check_overflow_sumsq(ds_scaler* st, const void* grad, ds_dtype dt, 
     const unsigned blocks = grid_blocks(chunks);
     double* part = static_cast<double*>(workspace);
     if (dt == DS_FP16)
-        check_sumsq_kernel<false, 512><<<blocks, 512, 0, s>>>(st, grad, n, part);
+        check_sumsq_kernel<kF16, 512><<<blocks, 512, 0, s>>>(st, grad, n, part);
+    else if (dt == DS_BF16)
+        check_sumsq_kernel<kBF16, 512><<<blocks, 512, 0, s>>>(st, grad, n, part);
     else
-        check_sumsq_kernel<true, 1024><<<blocks, 1024, 0, s>>>(st, grad, n, part);
+        check_sumsq_kernel<kF32, 1024><<<blocks, 1024, 0, s>>>(st, grad, n, part);
     if (launched() != DS_OK)
         return DS_ERR_HIP;
     sumsq_finish_kernel<1024><<<1, 1024, 0, s>>>(st, part, chunks);
     return launched();
 }
 
-ds_status ds_accumulate_sumsq(float* acc, const uint16_t* g16, int64_t n, int32_t overwrite,
+ds_status ds_accumulate_sumsq(float* acc, const uint16_t* g16, ds_dtype gdt, int64_t n, int32_t overwrite,
                               ds_scaler* st, void* workspace, size_t workspace_bytes, void* stream)
 {
     if (n < 0)
         return DS_ERR_SIZE;
+    if (!is16(gdt))
+        return DS_ERR_DTYPE;
     if (st == nullptr)
         return DS_ERR_NULL;
     if (n == 0)
@@ -949,10 +1055,10 @@ ds_status ds_accumulate_sumsq(float* acc, const uint16_t* g16, int64_t n, int32_
     const unsigned blocks = grid_blocks(tiles_of(n, 4));
     double* part = static_cast<double*>(workspace);
     const bool nt = variant_nt();
-#define DS_ACCS(OW, NT) accumulate_kernel<OW, true, true, NT, kStepBlock, 4><<<blocks, kStepBlock, 0, s>>>(acc, g16, n, st, part)
-    if (nt) { if (overwrite) DS_ACCS(true, true); else DS_ACCS(false, true); }
-    else    { if (overwrite) DS_ACCS(true, false); else DS_ACCS(false, false); }
-#undef DS_ACCS
+    if (gdt == DS_BF16)
+        launch_acc_sumsq<kBF16>(overwrite != 0, nt, blocks, s, acc, g16, n, st, part);
+    else
+        launch_acc_sumsq<kF16>(overwrite != 0, nt, blocks, s, acc, g16, n, st, part);
     if (launched() != DS_OK)
         return DS_ERR_HIP;
     sumsq_finish_kernel<1024><<<1, 1024, 0, s>>>(st, part, sumsq_chunks(n));

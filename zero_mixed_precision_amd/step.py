@@ -36,11 +36,13 @@ class ShardStep:
         self.torch, self.n, self.cfg = torch, int(n), cfg
         self.K = int(cfg.gradient_accumulation_steps)
         self.stream = stream
+        # 16-bit format of the gradients and of the parameter copy
+        self.gdt = self.pdt = _lib.DS_BF16 if cfg.bf16 else _lib.DS_FP16
         f32 = dict(dtype=torch.float32, device=device)
         self.master = torch.empty(self.n, **f32)
         self.m = torch.zeros(self.n, **f32)
         self.v = torch.zeros(self.n, **f32)
-        self.p16 = torch.empty(self.n, dtype=torch.float16, device=device)
+        self.p16 = torch.empty(self.n, dtype=torch.bfloat16 if cfg.bf16 else torch.float16, device=device)
         self.acc = torch.empty(self.n, **f32) if self.K > 1 else None
         self.state = torch.zeros(_lib.ds_scaler_size(), dtype=torch.uint8, device=device)
         self.clip = float(cfg.gradient_clipping)
@@ -64,9 +66,10 @@ class ShardStep:
         for start, size in self.buckets:
             a, g = self.acc.data_ptr() + 4 * start, g16.data_ptr() + 2 * start
             if last and self.ws is not None:
-                _lib.ds_accumulate_sumsq(a, g, size, k == 0, self.state, self.ws, stream=self.stream)
+                _lib.ds_accumulate_sumsq(a, g, self.gdt, size, k == 0, self.state, self.ws,
+                                         stream=self.stream)
             else:
-                _lib.ds_accumulate(a, g, size, overwrite=(k == 0),
+                _lib.ds_accumulate(a, g, self.gdt, size, overwrite=(k == 0),
                                    st_or_null=self.state if last else None, stream=self.stream)
         self._micro = k + 1
 
@@ -76,15 +79,15 @@ class ShardStep:
         if self.K == 1:
             assert g16 is not None and g16.numel() == self.n
             if self.ws is not None:
-                _lib.ds_check_overflow_sumsq(self.state, g16, _lib.DS_FP16, self.n, self.ws,
+                _lib.ds_check_overflow_sumsq(self.state, g16, self.gdt, self.n, self.ws,
                                              stream=self.stream)
             else:
-                _lib.ds_check_overflow(self.state, g16, _lib.DS_FP16, self.n, self.stream)
-            grad, dt = g16, _lib.DS_FP16
+                _lib.ds_check_overflow(self.state, g16, self.gdt, self.n, self.stream)
+            grad, dt = g16, self.gdt
         else:
             assert self._micro == self.K, "accumulate() must be called K times before step()"
             grad, dt = self.acc, _lib.DS_FP32
-        _lib.ds_adam_step(self.state, self.master, self.m, self.v, self.p16, grad, dt, self.n, c.lr,
+        _lib.ds_adam_step(self.state, self.master, self.m, self.v, self.p16, self.pdt, grad, dt, self.n, c.lr,
                           c.betas[0], c.betas[1], c.eps, c.weight_decay, c.gradient_clipping, self.K,
                           self.stream)
         _lib.ds_update_loss_scale(self.state, self.stream)
