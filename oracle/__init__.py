@@ -93,6 +93,8 @@ def lib():
         L.zo_adam.restype = None
         L.zo_adam_mult.argtypes = [vp, i32, i64, vp, vp, vp, vp, i32, f32, i64, f32, f32, f32, f32, f32]
         L.zo_adam_mult.restype = None
+        L.zo_lr_schedule.argtypes = [i32, i64, f32, f32, i64, i64]
+        L.zo_lr_schedule.restype = f32
         L.zo_scaler_init.argtypes = [ctypes.POINTER(ZoScaler), f32, f32, i32, i32, i32, i32]
         L.zo_scaler_init.restype = None
         L.zo_scaler_update.argtypes = [ctypes.POINTER(ZoScaler), i32]
@@ -266,6 +268,24 @@ class Scaler:
         return self.s.as_dict()
 
 
+LR_WARMUP, LR_WARMUP_DECAY = 1, 2
+
+
+class LrSchedule:
+    """Per-step learning rate of a WarmupLR (``kind=LR_WARMUP``) or WarmupDecayLR
+    (``kind=LR_WARMUP_DECAY``) schedule (oracle.c ``zo_lr_schedule``).  The
+    iteration is the number of applied Adam steps before the current one."""
+
+    def __init__(self, kind, warmup_min_lr, warmup_max_lr, warmup_num_steps, total_num_steps=0):
+        self.kind = int(kind)
+        self.min_lr, self.max_lr = float(warmup_min_lr), float(warmup_max_lr)
+        self.warmup, self.total = int(warmup_num_steps), int(total_num_steps)
+
+    def at(self, it: int) -> float:
+        return lib().zo_lr_schedule(self.kind, int(it), self.min_lr, self.max_lr, self.warmup,
+                                    self.total)
+
+
 class State:
     """The flat partition's model state (fp16 params, fp32 master/m/v) plus the scaler."""
 
@@ -282,7 +302,8 @@ def step(state: State, grads, *, lr, beta1, beta2, eps, weight_decay=0.0, max_gr
     ``grads`` is one uint16 array (K = 1: the fp16 gradient is consumed
     directly) or a list of K uint16 micro-batch gradients (K > 1: summed into
     an fp32 buffer in micro-batch order first); ``fmt`` is their 16-bit format
-    ("fp16" or "bf16").  ``max_grad_norm`` > 0 clips the unscaled gradient to
+    ("fp16" or "bf16").  ``lr`` is a number or an ``LrSchedule``, which is
+    read at the count of steps applied so far.  ``max_grad_norm`` > 0 clips the unscaled gradient to
     that global L2 norm.  ``state.last_sumsq`` keeps
     the step's gradient sum of squares when clipping.
     """
@@ -297,6 +318,8 @@ def step(state: State, grads, *, lr, beta1, beta2, eps, weight_decay=0.0, max_gr
             accumulate(grad, np.ascontiguousarray(g, dtype=np.uint16), overwrite=(k == 0), fmt=fmt)
     overflow = any_nonfinite(grad, fmt)
     if not overflow:
+        if isinstance(lr, LrSchedule):
+            lr = lr.at(state.scaler.applied)
         kw = dict(t=state.scaler.applied + 1, lr=lr, beta1=beta1, beta2=beta2, eps=eps,
                   weight_decay=weight_decay, fmt=fmt, param_fmt=state.param_fmt)
         if max_grad_norm > 0:

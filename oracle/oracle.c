@@ -306,6 +306,42 @@ void zo_adam(const void *grad, int32_t gfmt, int64_t n,
 }
 
 /* ------------------------------------------------------------------------ */
+/* Learning-rate schedules ([Guide] section 4.1, the "scheduler" block with  */
+/* WarmupLR; section 4.4, WarmupDecayLR with warmup_min_lr, warmup_max_lr,   */
+/* warmup_num_steps, total_num_steps and a linear warmup).  The pages give   */
+/* the parameters, not the formula; this is the plain reading of them.       */
+/* ------------------------------------------------------------------------ */
+
+enum { ZO_LR_WARMUP = 1, ZO_LR_WARMUP_DECAY = 2 };
+
+/* lr of schedule iteration `it`, the count of Adam steps applied before this
+ * one (a fresh run starts at 0; skipped steps do not count).  A fraction
+ * gamma in [0, 1] places lr between warmup_min_lr and warmup_max_lr:
+ *   while it < warmup:          gamma = it / warmup          (linear rise)
+ *   afterwards, WarmupLR:       gamma = 1                    (hold the peak)
+ *   afterwards, WarmupDecayLR:  gamma = (total - it) / (total - warmup),
+ *                               at least 0; the divisor at least 1
+ *   lr = min_lr + (max_lr - min_lr) * gamma
+ * all in fp64, rounded once to fp32. */
+float zo_lr_schedule(int32_t kind, int64_t it, float min_lr, float max_lr, int64_t warmup,
+                     int64_t total)
+{
+    double gamma = 1.0;
+    if (it < warmup) {
+        gamma = (double)it / (double)warmup;
+    } else if (kind == ZO_LR_WARMUP_DECAY) {
+        int64_t span = total - warmup;
+        double left = (double)(total - it);
+        gamma = left / (double)(span > 1 ? span : 1);
+        if (gamma < 0.0)
+            gamma = 0.0;
+    }
+    double lo = (double)min_lr;
+    double range = (double)max_lr - lo;
+    return (float)(lo + range * gamma);
+}
+
+/* ------------------------------------------------------------------------ */
 /* Dynamic loss scaler ([Guide] section 4.2 fp16 settings: loss_scale 0 means */
 /* dynamic, initial scale 2^initial_scale_power, loss_scale_window counts the */
 /* successful steps before an increase, hysteresis counts the overflows      */
