@@ -187,6 +187,50 @@ ds_status ds_adam_step(const ds_scaler* st, float* master, float* m, float* v, u
                        int32_t accum_steps, void* stream);
 
 /*
+ * Learning-rate schedules ([Guide] section 4.1: the scheduler block of the
+ * base ds_config.json, WarmupLR; section 4.4: WarmupDecayLR with
+ * warmup_min_lr, warmup_max_lr, warmup_num_steps, total_num_steps and a
+ * linear warmup).  The pages give the parameters, not the formula; the
+ * schedule read here: with it = st->step, the count of Adam steps applied
+ * before this one (a fresh run starts at 0; a skipped step does not advance
+ * it, so the schedule stays on the device and resumes with the state),
+ *   gamma = it / warmup_num_steps                    while it < warmup_num_steps
+ *         = 1                                        afterwards, DS_LR_WARMUP
+ *         = max(0, (total - it) / max(1, total - warmup_num_steps))
+ *                                                    afterwards, DS_LR_WARMUP_DECAY
+ *   lr    = warmup_min_lr + (warmup_max_lr - warmup_min_lr) * gamma
+ * in fp64, rounded once to fp32; that lr then enters the step like a
+ * constant lr.  A host struct, read during the call and not kept.
+ * Valid: kind one of the two below, both rates finite and >= 0,
+ * warmup_num_steps >= 0, and for DS_LR_WARMUP_DECAY total_num_steps >=
+ * warmup_num_steps; anything else is DS_ERR_HPARAM.
+ */
+typedef enum ds_lr_kind { DS_LR_WARMUP = 1, DS_LR_WARMUP_DECAY = 2 } ds_lr_kind;
+
+typedef struct ds_lr_schedule {
+    int32_t kind;             /* ds_lr_kind */
+    int32_t reserved;         /* set to 0 */
+    int64_t warmup_num_steps; /* applied steps of the linear rise */
+    int64_t total_num_steps;  /* DS_LR_WARMUP_DECAY: where the fall ends; else ignored */
+    float warmup_min_lr;      /* lr of the first step, and the end of the fall */
+    float warmup_max_lr;      /* the peak, reached after the warmup */
+} ds_lr_schedule;
+
+/*
+ * ds_adam_step with the learning rate taken from `sched` (a HOST pointer) at
+ * the device's applied-step count, so a whole step, schedule included, runs
+ * without a host round trip (and can be captured once into a graph and
+ * replayed).  Every other argument, the arithmetic and the errors are those
+ * of ds_adam_step; sched NULL is DS_ERR_NULL, an invalid schedule
+ * DS_ERR_HPARAM.
+ */
+ds_status ds_adam_step_sched(const ds_scaler* st, float* master, float* m, float* v, uint16_t* p16,
+                             ds_dtype pdt, const void* grad, ds_dtype dt, int64_t n,
+                             const ds_lr_schedule* sched, float beta1, float beta2, float eps,
+                             float weight_decay, float max_grad_norm, int32_t accum_steps,
+                             void* stream);
+
+/*
  * End of a step: advance the scaler by the step's overflow flag, then clear
  * the flag ([Guide] section 4.2).  Overflow: skipped += 1, growth_count = 0;
  * if dynamic, one more overflow is charged to the hysteresis and, when it is
@@ -238,6 +282,16 @@ ds_status ds_accumulate_sumsq(float* acc, const uint16_t* g16, ds_dtype gdt, int
  */
 ds_status ds_adam_bias_scalars(const ds_scaler* st, float lr, float beta1, float beta2,
                                float* out2, void* stream);
+
+/*
+ * The scheduled learning rate and bias-correction scalars the next applied
+ * step will use, evaluated on the device exactly as ds_adam_step_sched does:
+ * out3[0] = lr, out3[1] = fp32(lr / (1 - beta1^t)),
+ * out3[2] = fp32(1 / sqrt(1 - beta2^t)), t = st->step + 1.
+ * sched: host struct; out3: device float[3].  For diagnostics and tests.
+ */
+ds_status ds_lr_scalars(const ds_scaler* st, const ds_lr_schedule* sched, float beta1, float beta2,
+                        float* out3, void* stream);
 
 /*
  * Flat layout of ragged tensors in contiguous buffers with greedy buckets

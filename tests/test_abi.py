@@ -106,6 +106,38 @@ def test_adam_validation():
     assert _adam(st=E + 16) == DS_ERR_ALIAS                            # state inside grad
 
 
+def _sched_call(sched, st=ST, n=1024, hp=HP[1:]):
+    return L.ds_adam_step_sched(st, A, B, C, D, DS_FP16, E, DS_FP16, n,
+                                ctypes.byref(sched) if sched is not None else None, *hp, STREAM)
+
+
+def test_schedule_layout_and_validation():
+    assert ctypes.sizeof(_lib.DsLrSchedule) == 32
+    S = _lib.DsLrSchedule.make
+    good = S(_lib.DS_LR_WARMUP_DECAY, 0.0, 3e-4, 2000, 100000)
+    assert _sched_call(good, n=0) == DS_OK
+    assert _sched_call(good, n=-1) == DS_ERR_SIZE
+    assert _sched_call(None) == DS_ERR_NULL
+    assert _sched_call(good, st=None) == DS_ERR_NULL
+    for bad in [S(0, 0.0, 3e-4, 10, 20), S(3, 0.0, 3e-4, 10, 20), S(1, -1e-5, 3e-4, 10),
+                S(1, 0.0, float("nan"), 10), S(1, 0.0, float("inf"), 10), S(1, 0.0, 3e-4, -1),
+                S(2, 0.0, 3e-4, 10, 9)]:
+        assert _sched_call(bad) == DS_ERR_HPARAM
+    # total_num_steps is ignored by WarmupLR
+    assert _sched_call(S(1, 0.0, 3e-4, 10, 9), n=0) == DS_OK
+    # the other hyperparameters are checked as for the constant-lr step
+    assert _sched_call(good, hp=(1.0, 0.999, 1e-8, 0.0, 0.0, 1)) == DS_ERR_HPARAM
+    assert _sched_call(good, hp=(0.9, 0.999, 1e-8, 0.0, 0.0, 0)) == DS_ERR_HPARAM
+    sc = L.ds_lr_scalars
+    assert sc(None, ctypes.byref(good), 0.9, 0.999, A, STREAM) == DS_ERR_NULL
+    assert sc(ST, None, 0.9, 0.999, A, STREAM) == DS_ERR_NULL
+    assert sc(ST, ctypes.byref(good), 0.9, 0.999, None, STREAM) == DS_ERR_NULL
+    assert sc(ST, ctypes.byref(S(7, 0.0, 1e-3, 1)), 0.9, 0.999, A, STREAM) == DS_ERR_HPARAM
+    assert sc(ST, ctypes.byref(good), 0.9, 1.0, A, STREAM) == DS_ERR_HPARAM
+    assert sc(ST, ctypes.byref(good), 0.9, 0.999, A + 2, STREAM) == DS_ERR_ALIGN
+    assert sc(ST, ctypes.byref(good), 0.9, 0.999, ST + 120, STREAM) == DS_ERR_ALIAS
+
+
 NAN, INF = float("nan"), float("inf")
 
 

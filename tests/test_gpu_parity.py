@@ -334,6 +334,28 @@ def test_static_scale_and_hysteresis_two(torch):
         gu.compare_full(f"dyn={dynamic} H={hyst}", d, o)
 
 
+def test_loss_scale_floor_below_powers_of_two(torch):
+    """The guide's overflow-debugging floor (min_loss_scale 1e-8, hysteresis 2): after
+    enough overflows the scale is fp32(1e-8), not a power of two, so the unscale
+    multiplier 1/S is rounded; the device must round it as the oracle does."""
+    n = 4099
+    spec = synth.GradSpec(1e-3, 1.0)
+    for window in (500, 2):
+        master, m, v, p16 = _init_host(n, 8200)
+        o = oracle.State(master.copy(), m.copy(), v.copy(), p16.copy(), oracle.Scaler(4096.0, 1e-8, window, 2))
+        d = gu.DevState(torch, master, m, v, p16, init_scale=4096.0, window=window, hysteresis=2,
+                        min_scale=1e-8)
+        for s in range(86):
+            g = _mixed_grads(8300 + s, n, spec)
+            if s < 80:
+                g[(s * 31) % n] = 0x7C00 if s % 2 else 0xFE00
+            ov = oracle.step(o, g, **HP)
+            d.step(gu.dev_u16(torch, g), HP)
+            gu.check_scaler(d.scaler(), o.scaler, ov, f"floor W={window} step {s}")
+        assert o.scaler.scale == (float(np.float32(1e-8)) * (8 if window == 2 else 1))
+        gu.compare_full(f"floor W={window}", d, o)
+
+
 # -- the fp16 cast over every fp32 pattern ----------------------------------------------
 
 def _enc16_parallel(pool, x, parts=8):

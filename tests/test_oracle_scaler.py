@@ -92,6 +92,28 @@ def test_floor_holds_and_overflow_keeps_skipping(oracle_lib):
     assert sc.scale == 1.0 and sc.s.skipped == 5 and sc.applied == 0
 
 
+def test_floor_below_the_powers_of_two_from_pages(oracle_lib):
+    """The guide's gradient-overflow config (section 13.1: initial power 12, hysteresis 2,
+    min_loss_scale 1e-8): halving from 2^12 passes 2^-26 (1.49e-8); the next halving
+    (2^-27 = 7.45e-9) is below the floor, so the scale becomes fp32(1e-8) -- no longer a
+    power of two -- and stays there under further overflows; growth doubles it exactly."""
+    cfg = json.load(open(os.path.join(GOLDEN, "fp16_config.json")))["fp16_section_13_1"]
+    H, floor = cfg["hysteresis"], cfg["min_loss_scale"]
+    assert (cfg["initial_scale_power"], H, floor) == (12, 2, 1e-8)
+    sc = oracle.Scaler(2.0 ** cfg["initial_scale_power"], floor, 3, H)
+    scales = []
+    for _ in range(2 * 40):
+        sc.update(True)
+        scales.append(sc.scale)
+    # every second overflow halves (hysteresis 2)
+    assert scales[2 * 38 - 1] == 2.0 ** -26 and scales[2 * 38] == 2.0 ** -26
+    assert scales[2 * 39 - 1] == float(np.float32(1e-8))
+    assert scales[-1] == float(np.float32(1e-8)) and sc.s.skipped == 80
+    for _ in range(3):
+        sc.update(False)
+    assert sc.scale == 2 * float(np.float32(1e-8)) and sc.applied == 3
+
+
 def test_hysteresis_two_halves_every_second_overflow(oracle_lib):
     """hysteresis = 2 (the pages' default): two overflows per decrease.
     Parity unpinned: the pages give only the key's one-line meaning."""

@@ -21,8 +21,9 @@ EXPORTED = (
     "ds_scaler_size", "ds_state_init", "ds_state_read", "ds_state_write", "ds_accumulate",
     "ds_check_overflow", "ds_adam_step", "ds_update_loss_scale", "ds_adam_bias_scalars",
     "ds_layout_greedy", "ds_partition_range", "ds_status_string", "ds_sumsq_workspace_bytes",
-    "ds_check_overflow_sumsq", "ds_accumulate_sumsq",
+    "ds_check_overflow_sumsq", "ds_accumulate_sumsq", "ds_adam_step_sched", "ds_lr_scalars",
 )
+DS_LR_WARMUP, DS_LR_WARMUP_DECAY = 1, 2
 
 
 class DsScaler(ctypes.Structure):
@@ -48,6 +49,23 @@ class DsScaler(ctypes.Structure):
 
     def as_dict(self) -> dict:
         return {name: getattr(self, name) for name, _ in self._fields_ if name != "reserved"}
+
+
+class DsLrSchedule(ctypes.Structure):
+    """Mirror of ``ds_lr_schedule`` (32 bytes, host memory)."""
+    _fields_ = [
+        ("kind", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
+        ("warmup_num_steps", ctypes.c_int64),
+        ("total_num_steps", ctypes.c_int64),
+        ("warmup_min_lr", ctypes.c_float),
+        ("warmup_max_lr", ctypes.c_float),
+    ]
+
+    @classmethod
+    def make(cls, kind, warmup_min_lr, warmup_max_lr, warmup_num_steps, total_num_steps=0):
+        return cls(int(kind), 0, int(warmup_num_steps), int(total_num_steps), float(warmup_min_lr),
+                   float(warmup_max_lr))
 
 
 class DsError(RuntimeError):
@@ -99,6 +117,9 @@ def _load():
         "ds_accumulate_sumsq": ([vp, vp, ctypes.c_int, i64, i32, vp, vp, ctypes.c_size_t, vp], ctypes.c_int),
         "ds_update_loss_scale": ([vp, vp], ctypes.c_int),
         "ds_adam_bias_scalars": ([vp, f32, f32, f32, vp, vp], ctypes.c_int),
+        "ds_adam_step_sched": ([vp, vp, vp, vp, vp, ctypes.c_int, vp, ctypes.c_int, i64,
+                                ctypes.POINTER(DsLrSchedule), f32, f32, f32, f32, f32, i32, vp], ctypes.c_int),
+        "ds_lr_scalars": ([vp, ctypes.POINTER(DsLrSchedule), f32, f32, vp, vp], ctypes.c_int),
         "ds_layout_greedy": ([vp, i32, i64, i64, vp, vp, vp, vp, ctypes.POINTER(i32),
                               ctypes.POINTER(i64)], ctypes.c_int),
         "ds_partition_range": ([i64, i32, i32, i64, ctypes.POINTER(i64), ctypes.POINTER(i64)],
@@ -179,6 +200,13 @@ def ds_adam_step(st, master, m, v, p16, pdt, grad, dtype, n, lr, beta1, beta2, e
                          _s(stream)), "ds_adam_step")
 
 
+def ds_adam_step_sched(st, master, m, v, p16, pdt, grad, dtype, n, sched: DsLrSchedule, beta1, beta2, eps,
+                       weight_decay, max_grad_norm, accum_steps, stream=None) -> None:
+    _ok(lib.ds_adam_step_sched(_p(st), _p(master), _p(m), _p(v), _p(p16), int(pdt), _p(grad), int(dtype),
+                               int(n), ctypes.byref(sched), beta1, beta2, eps, weight_decay, max_grad_norm,
+                               int(accum_steps), _s(stream)), "ds_adam_step_sched")
+
+
 def ds_sumsq_workspace_bytes(n) -> int:
     return lib.ds_sumsq_workspace_bytes(int(n))
 
@@ -208,6 +236,10 @@ def ds_update_loss_scale(st, stream=None) -> None:
 
 def ds_adam_bias_scalars(st, lr, beta1, beta2, out2, stream=None) -> None:
     _ok(lib.ds_adam_bias_scalars(_p(st), lr, beta1, beta2, _p(out2), _s(stream)), "ds_adam_bias_scalars")
+
+
+def ds_lr_scalars(st, sched: DsLrSchedule, beta1, beta2, out3, stream=None) -> None:
+    _ok(lib.ds_lr_scalars(_p(st), ctypes.byref(sched), beta1, beta2, _p(out3), _s(stream)), "ds_lr_scalars")
 
 
 def ds_layout_greedy(numels, cap, align):

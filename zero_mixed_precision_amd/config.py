@@ -4,7 +4,9 @@
 gradient_clipping, fp16, bf16, optimizer, zero_optimization), section 4.2 (fp16 block: loss_scale 0 is
 dynamic, initial scale 2^initial_scale_power, loss_scale_window,
 hysteresis, consecutive_hysteresis, min_loss_scale; bf16 block: no loss scaling), section 4.3
-(train_batch_size = micro batch x gradient_accumulation_steps x world size).
+(train_batch_size = micro batch x gradient_accumulation_steps x world size), sections 4.1 and 4.4
+(scheduler block: WarmupLR, WarmupDecayLR with warmup_min_lr, warmup_max_lr, warmup_num_steps,
+total_num_steps, linear warmup).
 "auto" values are resolved by a trainer integration, which this library does
 not have: they are rejected.
 """
@@ -38,6 +40,12 @@ class ZeroMPConfig:
     betas: tuple = (0.9, 0.999)
     eps: float = 1e-8
     weight_decay: float = 0.0
+    # scheduler block: None (constant lr), "WarmupLR" or "WarmupDecayLR"
+    scheduler: str | None = None
+    warmup_min_lr: float = 0.0
+    warmup_max_lr: float = 0.0
+    warmup_num_steps: int = 0
+    total_num_steps: int = 0
     # global-norm clipping of the unscaled gradient (0: off)
     gradient_clipping: float = 0.0
     # batch / ZeRO
@@ -55,6 +63,16 @@ class ZeroMPConfig:
         if self.bf16:
             return 1.0
         return 2.0 ** self.initial_scale_power if self.dynamic else float(self.loss_scale)
+
+    def lr_schedule(self):
+        """The scheduler block as a ds_lr_schedule, or None for a constant lr."""
+        from ._lib import DS_LR_WARMUP, DS_LR_WARMUP_DECAY, DsLrSchedule
+
+        if self.scheduler is None:
+            return None
+        kind = DS_LR_WARMUP if self.scheduler == "WarmupLR" else DS_LR_WARMUP_DECAY
+        return DsLrSchedule.make(kind, self.warmup_min_lr, self.warmup_max_lr, self.warmup_num_steps,
+                                 self.total_num_steps)
 
     def train_batch_size(self, world_size: int) -> int:
         return self.train_micro_batch_size_per_gpu * self.gradient_accumulation_steps * world_size
@@ -94,8 +112,41 @@ class ZeroMPConfig:
             reduce_bucket_size=int(float(_val(zero, "reduce_bucket_size", 2e8))),
             stage=int(_val(zero, "stage", 2)),
         )
+        sched = cfg.get("scheduler")
+        if sched:
+            _parse_scheduler(out, sched)
         if "train_batch_size" in cfg and cfg["train_batch_size"] != "auto":
             world = cfg.get("world_size")
             if world is not None and out.train_batch_size(int(world)) != int(cfg["train_batch_size"]):
                 raise ValueError("train_batch_size != micro batch x accumulation steps x world size")
         return out
+
+
+_NAMED_WITHOUT_FORMULA = ("LRRangeTest", "OneCycle", "WarmupCosineLR")
+
+
+def _parse_scheduler(out: ZeroMPConfig, sched: dict) -> None:
+    kind = _val(sched, "type", None)
+    if kind in _NAMED_WITHOUT_FORMULA:
+        raise ValueError(f"scheduler {kind!r} is named by the guide without its parameters; "
+                         "WarmupLR and WarmupDecayLR are supported")
+    if kind not in ("WarmupLR", "WarmupDecayLR"):
+        raise ValueError(f"unknown scheduler type {kind!r}")
+    p = sched.get("params", {})
+    for key in ("warmup_max_lr", "warmup_num_steps") + (("total_num_steps",) if kind == "WarmupDecayLR" else ()):
+        if key not in p:
+            raise ValueError(f"scheduler {kind}: '{key}' is required")
+    if _val(p, "warmup_type", "linear") != "linear":
+        raise ValueError("only the linear warmup is supported")
+    if int(_val(p, "last_batch_iteration", -1)) != -1:
+        raise ValueError("last_batch_iteration must be -1: a resumed run takes its position from the "
+                         "restored optimizer state")
+    out.scheduler = kind
+    out.warmup_min_lr = float(_val(p, "warmup_min_lr", 0.0))
+    out.warmup_max_lr = float(_val(p, "warmup_max_lr", None))
+    out.warmup_num_steps = int(_val(p, "warmup_num_steps", None))
+    out.total_num_steps = int(_val(p, "total_num_steps", 0))
+    if out.warmup_num_steps < 0 or out.warmup_min_lr < 0 or out.warmup_max_lr < 0:
+        raise ValueError("scheduler rates and step counts must be >= 0")
+    if kind == "WarmupDecayLR" and out.total_num_steps < out.warmup_num_steps:
+        raise ValueError("total_num_steps must be >= warmup_num_steps")

@@ -43,6 +43,7 @@
 #pragma clang fp contract(off)
 
 static_assert(sizeof(ds_scaler) == 128, "ds_scaler must stay 128 bytes");
+static_assert(sizeof(ds_lr_schedule) == 32, "ds_lr_schedule is 32 bytes");
 
 namespace {
 
@@ -234,6 +235,11 @@ __global__ __launch_bounds__(TPB) void sumsq_finish_kernel(ds_scaler* __restrict
 struct AdamHyper {
     float lr, beta1, beta2, eps, weight_decay, max_grad_norm;
     int32_t accum_steps;
+    // learning-rate schedule (lr_kind 0: the constant lr above; else a
+    // ds_lr_kind, with lr playing warmup_max_lr)
+    int32_t lr_kind;
+    float lr_min;
+    int64_t lr_warmup, lr_total;
 };
 
 struct AdamConsts {
@@ -265,9 +271,36 @@ __device__ __forceinline__ void bias_scalars(int64_t t, float lr, float beta1, f
     *rbc2 = static_cast<float>(1.0 / sqrt(1.0 - r2));
 }
 
+// Learning rate of schedule iteration `it` (Adam steps applied before this
+// one): gamma in [0, 1] rises linearly over the warmup, then holds at 1
+// (WarmupLR) or falls linearly to 0 at lr_total (WarmupDecayLR);
+// lr = lr_min + (lr_max - lr_min) * gamma in fp64, rounded once.
+__device__ __forceinline__ float schedule_lr(int64_t it, const AdamHyper& h)
+{
+    double gamma = 1.0;
+    if (it < h.lr_warmup) {
+        gamma = static_cast<double>(it) / static_cast<double>(h.lr_warmup);
+    } else if (h.lr_kind == DS_LR_WARMUP_DECAY) {
+        const int64_t span = h.lr_total - h.lr_warmup;
+        const double left = static_cast<double>(h.lr_total - it);
+        gamma = left / static_cast<double>(span > 1 ? span : 1);
+        if (gamma < 0.0)
+            gamma = 0.0;
+    }
+    const double lo = static_cast<double>(h.lr_min);
+    const double range = static_cast<double>(h.lr) - lo;
+    return static_cast<float>(lo + range * gamma);
+}
+
+__device__ __forceinline__ float step_lr(const ds_scaler* st, const AdamHyper& h)
+{
+    return h.lr_kind == 0 ? h.lr : schedule_lr(st->step, h);
+}
+
 __device__ __forceinline__ AdamConsts make_consts(const ds_scaler* st, const AdamHyper& h)
 {
     AdamConsts c;
+    const float lr = step_lr(st, h);
     c.inv = 1.0f / (st->scale * static_cast<float>(h.accum_steps));
     if (h.max_grad_norm > 0.0f) {
         // global-norm clipping of the unscaled gradient
@@ -281,9 +314,9 @@ __device__ __forceinline__ AdamConsts make_consts(const ds_scaler* st, const Ada
     c.b2 = h.beta2;
     c.omb1 = 1.0f - h.beta1;
     c.omb2 = 1.0f - h.beta2;
-    c.lrwd = h.lr * h.weight_decay;
+    c.lrwd = lr * h.weight_decay;
     c.eps = h.eps;
-    bias_scalars(st->step + 1, h.lr, h.beta1, h.beta2, &c.step_size, &c.rbc2);
+    bias_scalars(st->step + 1, lr, h.beta1, h.beta2, &c.step_size, &c.rbc2);
     return c;
 }
 
@@ -416,6 +449,16 @@ __global__ void bias_scalars_kernel(const ds_scaler* st, float lr, float beta1, 
     bias_scalars(st->step + 1, lr, beta1, beta2, &a, &b);
     out2[0] = a;
     out2[1] = b;
+}
+
+__global__ void lr_scalars_kernel(const ds_scaler* st, AdamHyper hp, float* out3)
+{
+    const float lr = step_lr(st, hp);
+    float a, b;
+    bias_scalars(st->step + 1, lr, hp.beta1, hp.beta2, &a, &b);
+    out3[0] = lr;
+    out3[1] = a;
+    out3[2] = b;
 }
 
 // ---------------------------------------------------------------------------
@@ -819,6 +862,59 @@ ds_status check_workspace(const void* ws, size_t ws_bytes, int64_t n)
 // C ABI
 // ---------------------------------------------------------------------------
 
+bool schedule_ok(const ds_lr_schedule& q)
+{
+    if (q.kind != DS_LR_WARMUP && q.kind != DS_LR_WARMUP_DECAY)
+        return false;
+    if (!finite_ge0(q.warmup_min_lr) || !finite_ge0(q.warmup_max_lr) || q.warmup_num_steps < 0)
+        return false;
+    return q.kind != DS_LR_WARMUP_DECAY || q.total_num_steps >= q.warmup_num_steps;
+}
+
+// Validation and launch shared by the constant-lr and scheduled entry points
+// (a schedule is checked by its entry point; hp.lr is the constant lr or the
+// schedule's peak).
+ds_status adam_step(const ds_scaler* st, float* master, float* m, float* v, uint16_t* p16,
+                    ds_dtype pdt, const void* grad, ds_dtype dt, int64_t n, const AdamHyper& hp,
+                    void* stream)
+{
+    const float beta1 = hp.beta1, beta2 = hp.beta2, eps = hp.eps;
+    const float weight_decay = hp.weight_decay, max_grad_norm = hp.max_grad_norm;
+    const int32_t accum_steps = hp.accum_steps;
+    if (n < 0)
+        return DS_ERR_SIZE;
+    if (!known(dt) || !is16(pdt))
+        return DS_ERR_DTYPE;
+    if (!finite_ge0(hp.lr) || !beta_ok(beta1) || !beta_ok(beta2) || !std::isfinite(eps) ||
+        eps <= 0.0f || !finite_ge0(weight_decay) || !finite_ge0(max_grad_norm) || accum_steps < 1)
+        return DS_ERR_HPARAM;
+    if (st == nullptr)
+        return DS_ERR_NULL;
+    if (n == 0)
+        return DS_OK;
+    if (master == nullptr || m == nullptr || v == nullptr || p16 == nullptr || grad == nullptr)
+        return DS_ERR_NULL;
+    if (!aligned(master, 16) || !aligned(m, 16) || !aligned(v, 16) || !aligned(p16, 16) ||
+        !aligned(grad, 16) || !aligned(st, 8))
+        return DS_ERR_ALIGN;
+    const uint64_t un = static_cast<uint64_t>(n);
+    const void* ptrs[6] = {master, m, v, p16, grad, st};
+    const uint64_t sizes[6] = {4 * un, 4 * un, 4 * un, 2 * un, esize(dt) * un, sizeof(ds_scaler)};
+    for (int i = 0; i < 6; ++i)
+        for (int j = i + 1; j < 6; ++j)
+            if (overlap(ptrs[i], sizes[i], ptrs[j], sizes[j]))
+                return DS_ERR_ALIAS;
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int unroll = variant_unroll();
+    const unsigned blocks = grid_blocks(tiles_of(n, unroll));
+    const bool nt = variant_nt();
+    const bool wd = weight_decay != 0.0f;
+    const AdamArgs args{st, master, m, v, p16, grad, n, hp};
+    launch_adam(fmt_of(dt), fmt_of(pdt), wd, nt, unroll, blocks, s, args);
+    return launched();
+}
+
 extern "C" {
 
 size_t ds_scaler_size(void) { return sizeof(ds_scaler); }
@@ -947,39 +1043,23 @@ ds_status ds_adam_step(const ds_scaler* st, float* master, float* m, float* v, u
                        float beta2, float eps, float weight_decay, float max_grad_norm,
                        int32_t accum_steps, void* stream)
 {
-    if (n < 0)
-        return DS_ERR_SIZE;
-    if (!known(dt) || !is16(pdt))
-        return DS_ERR_DTYPE;
-    if (!finite_ge0(lr) || !beta_ok(beta1) || !beta_ok(beta2) || !std::isfinite(eps) || eps <= 0.0f ||
-        !finite_ge0(weight_decay) || !finite_ge0(max_grad_norm) || accum_steps < 1)
-        return DS_ERR_HPARAM;
-    if (st == nullptr)
-        return DS_ERR_NULL;
-    if (n == 0)
-        return DS_OK;
-    if (master == nullptr || m == nullptr || v == nullptr || p16 == nullptr || grad == nullptr)
-        return DS_ERR_NULL;
-    if (!aligned(master, 16) || !aligned(m, 16) || !aligned(v, 16) || !aligned(p16, 16) ||
-        !aligned(grad, 16) || !aligned(st, 8))
-        return DS_ERR_ALIGN;
-    const uint64_t un = static_cast<uint64_t>(n);
-    const void* ptrs[6] = {master, m, v, p16, grad, st};
-    const uint64_t sizes[6] = {4 * un, 4 * un, 4 * un, 2 * un, esize(dt) * un, sizeof(ds_scaler)};
-    for (int i = 0; i < 6; ++i)
-        for (int j = i + 1; j < 6; ++j)
-            if (overlap(ptrs[i], sizes[i], ptrs[j], sizes[j]))
-                return DS_ERR_ALIAS;
+    const AdamHyper hp{lr, beta1, beta2, eps, weight_decay, max_grad_norm, accum_steps, 0, 0.0f, 0, 0};
+    return adam_step(st, master, m, v, p16, pdt, grad, dt, n, hp, stream);
+}
 
-    const AdamHyper hp{lr, beta1, beta2, eps, weight_decay, max_grad_norm, accum_steps};
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    const int unroll = variant_unroll();
-    const unsigned blocks = grid_blocks(tiles_of(n, unroll));
-    const bool nt = variant_nt();
-    const bool wd = weight_decay != 0.0f;
-    const AdamArgs args{st, master, m, v, p16, grad, n, hp};
-    launch_adam(fmt_of(dt), fmt_of(pdt), wd, nt, unroll, blocks, s, args);
-    return launched();
+ds_status ds_adam_step_sched(const ds_scaler* st, float* master, float* m, float* v, uint16_t* p16,
+                             ds_dtype pdt, const void* grad, ds_dtype dt, int64_t n,
+                             const ds_lr_schedule* sched, float beta1, float beta2, float eps,
+                             float weight_decay, float max_grad_norm, int32_t accum_steps,
+                             void* stream)
+{
+    if (sched == nullptr)
+        return DS_ERR_NULL;
+    if (!schedule_ok(*sched))
+        return DS_ERR_HPARAM;
+    const AdamHyper hp{sched->warmup_max_lr, beta1, beta2, eps, weight_decay, max_grad_norm, accum_steps,
+                 sched->kind, sched->warmup_min_lr, sched->warmup_num_steps, sched->total_num_steps};
+    return adam_step(st, master, m, v, p16, pdt, grad, dt, n, hp, stream);
 }
 
 size_t ds_sumsq_workspace_bytes(int64_t n)
@@ -1087,6 +1167,24 @@ ds_status ds_adam_bias_scalars(const ds_scaler* st, float lr, float beta1, float
     if (overlap(st, sizeof(ds_scaler), out2, 2 * sizeof(float)))
         return DS_ERR_ALIAS;
     bias_scalars_kernel<<<1, 1, 0, static_cast<hipStream_t>(stream)>>>(st, lr, beta1, beta2, out2);
+    return launched();
+}
+
+ds_status ds_lr_scalars(const ds_scaler* st, const ds_lr_schedule* sched, float beta1, float beta2,
+                        float* out3, void* stream)
+{
+    if (st == nullptr || sched == nullptr || out3 == nullptr)
+        return DS_ERR_NULL;
+    if (!aligned(st, 8) || !aligned(out3, 4))
+        return DS_ERR_ALIGN;
+    if (!schedule_ok(*sched) || !beta_ok(beta1) || !beta_ok(beta2))
+        return DS_ERR_HPARAM;
+    if (overlap(st, sizeof(ds_scaler), out3, 3 * sizeof(float)))
+        return DS_ERR_ALIAS;
+    const AdamHyper hp{sched->warmup_max_lr, beta1, beta2, 1.0f, 0.0f, 0.0f, 1,
+                       sched->kind, sched->warmup_min_lr, sched->warmup_num_steps,
+                       sched->total_num_steps};
+    lr_scalars_kernel<<<1, 1, 0, static_cast<hipStream_t>(stream)>>>(st, hp, out3);
     return launched();
 }
 

@@ -12,7 +12,9 @@ scales and accumulates, step() updates):
 
 With gradient clipping configured the check passes are the _sumsq variants
 (ds_accumulate_sumsq / ds_check_overflow_sumsq), which also gather the
-gradient's sum of squares for ds_adam_step's global-norm clipping.
+gradient's sum of squares for ds_adam_step's global-norm clipping.  With a
+scheduler block the update is ds_adam_step_sched, which reads the learning
+rate of the schedule on the device.
 
 No call synchronises the host; ``scaler()`` reads the state back (one copy).
 ``graph(grads)`` records the whole sequence for fixed gradient buffers into a
@@ -45,6 +47,9 @@ class ShardStep:
         self.p16 = torch.empty(self.n, dtype=torch.bfloat16 if cfg.bf16 else torch.float16, device=device)
         self.acc = torch.empty(self.n, **f32) if self.K > 1 else None
         self.state = torch.zeros(_lib.ds_scaler_size(), dtype=torch.uint8, device=device)
+        # learning-rate schedule (None: the constant cfg.lr), read on the device
+        # at the applied-step count, so a skipped step does not advance it
+        self.sched = cfg.lr_schedule()
         self.clip = float(cfg.gradient_clipping)
         self.ws = None
         if self.clip > 0:
@@ -87,9 +92,14 @@ class ShardStep:
         else:
             assert self._micro == self.K, "accumulate() must be called K times before step()"
             grad, dt = self.acc, _lib.DS_FP32
-        _lib.ds_adam_step(self.state, self.master, self.m, self.v, self.p16, self.pdt, grad, dt, self.n, c.lr,
-                          c.betas[0], c.betas[1], c.eps, c.weight_decay, c.gradient_clipping, self.K,
-                          self.stream)
+        if self.sched is not None:
+            _lib.ds_adam_step_sched(self.state, self.master, self.m, self.v, self.p16, self.pdt, grad, dt,
+                                    self.n, self.sched, c.betas[0], c.betas[1], c.eps, c.weight_decay,
+                                    c.gradient_clipping, self.K, self.stream)
+        else:
+            _lib.ds_adam_step(self.state, self.master, self.m, self.v, self.p16, self.pdt, grad, dt, self.n,
+                              c.lr, c.betas[0], c.betas[1], c.eps, c.weight_decay, c.gradient_clipping,
+                              self.K, self.stream)
         _lib.ds_update_loss_scale(self.state, self.stream)
         self._micro = 0
 
@@ -107,8 +117,9 @@ class ShardStep:
         """Record ``full_step(grads)`` into a HIP graph (torch.cuda.CUDAGraph).
 
         The gradient buffers are baked in by address: write the next step's
-        gradients into the same tensors, then ``replay()``.  Replays read the
-        learning rate and other hyperparameters as recorded.
+        gradients into the same tensors, then ``replay()``.  Replays use the
+        hyperparameters as recorded; with a learning-rate schedule each replay
+        still takes the schedule's lr at the device's applied-step count.
         """
         torch = self.torch
         g = torch.cuda.CUDAGraph()
