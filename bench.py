@@ -14,7 +14,10 @@ over the timed steps; ``roofline`` is the Adam kernel's algorithmic HBM
 bandwidth (28 B/element with an fp16 gradient, 30 with the fp32 buffer) over
 its average duration, timed with HIP events on the launch stream, against
 the 8 TB/s HBM3E peak; ``traffic`` comes from the committed rocprofv3 counter
-summary when it was taken on the current kernel source.  ``cpu_baseline`` times
+summary when it was taken on the current kernel source; the median and minimum
+launch times and ``copy_mix_gbs`` (the same 14 B read + 14 B written per
+element with no arithmetic, on the same arrays, timed after the timed region)
+sit beside it.  ``cpu_baseline`` times
 the CPU oracle on a bounded slice of the same workload.
 
     python bench.py --mode copy    # plain-copy and step-shaped data-movement references
@@ -158,6 +161,25 @@ def gpu_run(args):
     sc = _lib.ds_state_read(st, stream)
     adam_ms = [a.elapsed_time(b) for a, b in ev]
     adam_avg_s = sum(adam_ms) / len(adam_ms) / 1e3
+    adam_sorted = sorted(adam_ms)
+
+    # achievable-bandwidth reference, after the timed region: the step's data
+    # movement (14 B read + 14 B written per element) with no arithmetic, on the
+    # same arrays (it scrambles them; the run is over)
+    nm = n - n % 4
+    mix_args = (grads[0][:nm], master[:nm], m[:nm], v[:nm], p16[:nm])
+    for _ in range(2):
+        synth.device_stream_mix(torch, *mix_args, stream=stream)
+    mix_ev = []
+    for _ in range(8):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        synth.device_stream_mix(torch, *mix_args, stream=stream)
+        b.record(stream)
+        mix_ev.append((a, b))
+    torch.cuda.synchronize()
+    mix_s = sum(a.elapsed_time(b) for a, b in mix_ev) / len(mix_ev) / 1e3
+    mix_gbs = 28 * nm / mix_s / 1e9
     bytes_per_elem = 28 if K == 1 else 30
     achieved = bytes_per_elem * n / adam_avg_s / 1e9
     step_bytes = (2 + 28) if K == 1 else (6 + 10 * (K - 1) + 30)
@@ -197,6 +219,9 @@ def gpu_run(args):
             "traffic": traffic,
             "alg_bytes_per_launch": bytes_per_elem * n,
             "avg_launch_ms": round(adam_avg_s * 1e3, 4),
+            "median_launch_ms": round(adam_sorted[len(adam_sorted) // 2], 4),
+            "min_launch_ms": round(adam_sorted[0], 4),
+            "copy_mix_gbs": round(mix_gbs, 1),
         },
         "step_hbm_gbs": round(step_bytes * n * args.steps / wall / 1e9, 1),
         "scaler_after": {"scale": sc.scale, "applied_steps": sc.step, "skipped": sc.skipped},
