@@ -80,23 +80,43 @@ __global__ __launch_bounds__(256) void copy_kernel(uint4* __restrict__ dst,
         dst[i] = src[i];
 }
 
-// Moves the bytes of one optimizer step without computing anything:
-// 4 elements per thread: reads fp16 x4 and three float4, writes three float4
-// (rotated) and fp16 x4.
-__global__ __launch_bounds__(256) void stream_mix_kernel(const uint2* __restrict__ g,
-                                                         float4* __restrict__ a,
-                                                         float4* __restrict__ b,
-                                                         float4* __restrict__ c,
-                                                         uint2* __restrict__ h, int64_t n4)
+// Moves the bytes of one optimizer step without computing anything: per
+// element it reads a 16-bit value and three fp32 values and writes three fp32
+// values (rotated) and the 16-bit value.  Laid out like a streaming optimizer
+// kernel: each 256-lane block owns one tile of 4 x 256 quads (4096 elements),
+// loads all of it, then stores all of it, with non-temporal hints.
+typedef float mix_f4 __attribute__((ext_vector_type(4)));
+typedef unsigned mix_u2 __attribute__((ext_vector_type(2)));
+constexpr int kMixLanes = 256, kMixQuads = 4;
+
+__global__ __launch_bounds__(kMixLanes) void stream_mix_kernel(const mix_u2* __restrict__ g,
+                                                               mix_f4* __restrict__ a,
+                                                               mix_f4* __restrict__ b,
+                                                               mix_f4* __restrict__ c,
+                                                               mix_u2* __restrict__ h, int64_t n4)
 {
-    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < n4; q += stride) {
-        uint2 gv = g[q];
-        float4 av = a[q], bv = b[q], cv = c[q];
-        a[q] = bv;
-        b[q] = cv;
-        c[q] = av;
-        h[q] = gv;
+    const int64_t first = (int64_t)blockIdx.x * (kMixLanes * kMixQuads) + threadIdx.x;
+    mix_u2 gv[kMixQuads];
+    mix_f4 av[kMixQuads], bv[kMixQuads], cv[kMixQuads];
+#pragma unroll
+    for (int u = 0; u < kMixQuads; ++u) {
+        const int64_t q = first + (int64_t)u * kMixLanes;
+        if (q < n4) {
+            gv[u] = __builtin_nontemporal_load(g + q);
+            av[u] = __builtin_nontemporal_load(a + q);
+            bv[u] = __builtin_nontemporal_load(b + q);
+            cv[u] = __builtin_nontemporal_load(c + q);
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < kMixQuads; ++u) {
+        const int64_t q = first + (int64_t)u * kMixLanes;
+        if (q < n4) {
+            __builtin_nontemporal_store(bv[u], a + q);
+            __builtin_nontemporal_store(cv[u], b + q);
+            __builtin_nontemporal_store(av[u], c + q);
+            __builtin_nontemporal_store(gv[u], h + q);
+        }
     }
 }
 
@@ -157,9 +177,12 @@ int synth_stream_mix(const void* g, void* a, void* b, void* c, void* h, int64_t 
           reinterpret_cast<uintptr_t>(c)) & 15u) != 0 ||
         ((reinterpret_cast<uintptr_t>(g) | reinterpret_cast<uintptr_t>(h)) & 7u) != 0)
         return (int)hipErrorInvalidValue;
-    stream_mix_kernel<<<grid_for(n / 4), 256, 0, static_cast<hipStream_t>(stream)>>>(
-        static_cast<const uint2*>(g), static_cast<float4*>(a), static_cast<float4*>(b),
-        static_cast<float4*>(c), static_cast<uint2*>(h), n / 4);
+    const int64_t n4 = n / 4;
+    const int64_t tiles = (n4 + kMixLanes * kMixQuads - 1) / (kMixLanes * kMixQuads);
+    if (tiles > 0x7FFFFFFF) return (int)hipErrorInvalidValue;
+    stream_mix_kernel<<<(unsigned)tiles, kMixLanes, 0, static_cast<hipStream_t>(stream)>>>(
+        static_cast<const mix_u2*>(g), static_cast<mix_f4*>(a), static_cast<mix_f4*>(b),
+        static_cast<mix_f4*>(c), static_cast<mix_u2*>(h), n4);
     return (int)hipGetLastError();
 }
 

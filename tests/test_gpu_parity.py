@@ -419,3 +419,21 @@ def test_device_generator_matches_host(torch):
     outm = torch.empty(n, dtype=torch.float32, device="cuda:0")
     synth.device_fill_master32(torch, tabs, outm, key, MASTER_SIGMA)
     assert np.array_equal(f32_bits(gu.host_f32(outm)), f32_bits(synth.host_master32(key, np.arange(n), MASTER_SIGMA)))
+
+
+def test_data_movement_reference_kernels(torch):
+    """The bandwidth references move the bytes they claim to: the copy, and the
+    step-shaped mix (a <- b, b <- c, c <- a, h <- g) over full tiles and a ragged last one."""
+    rng = np.random.default_rng(5)
+    n = 3 * 4096 + 1024 + 8
+    g = rng.integers(-2 ** 15, 2 ** 15, n).astype(np.int16)
+    a, b, c = (rng.standard_normal(n).astype(np.float32) for _ in range(3))
+    dg, da, db, dc = (torch.from_numpy(x.copy()).to("cuda:0") for x in (g, a, b, c))
+    dh = torch.zeros(n, dtype=torch.int16, device="cuda:0")
+    synth.device_stream_mix(torch, dg, da, db, dc, dh)
+    for dev, want in ((da, b), (db, c), (dc, a), (dh, g)):
+        assert np.array_equal(dev.cpu().numpy(), want)
+    src = torch.from_numpy(rng.integers(0, 2 ** 31, 4 * 1000 + 4).astype(np.int32)).to("cuda:0")
+    dst = torch.zeros_like(src)
+    synth.device_copy(torch, dst, src)
+    assert torch.equal(dst, src)
