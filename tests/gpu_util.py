@@ -46,7 +46,7 @@ class DevState:
     """Device copy of one partition's state plus a ds_scaler."""
 
     def __init__(self, torch, master, m, v, p16, *, init_scale, window, hysteresis=1, min_scale=1.0,
-                 dynamic=1, K=1, fmt="fp16", param_fmt="fp16"):
+                 dynamic=1, K=1, fmt="fp16", param_fmt="fp16", consecutive_hysteresis=0):
         from zero_mixed_precision_amd import _lib
         self.torch, self.lib = torch, _lib
         self.gdt = _lib.DS_BF16 if fmt == "bf16" else _lib.DS_FP16
@@ -57,7 +57,8 @@ class DevState:
         self.K = K
         self.acc = torch.empty(max(self.n, 1), dtype=torch.float32, device="cuda:0") if K > 1 else None
         self.state = torch.zeros(_lib.ds_scaler_size(), dtype=torch.uint8, device="cuda:0")
-        _lib.ds_state_init(self.state, init_scale, min_scale, window, hysteresis, 0, dynamic)
+        _lib.ds_state_init(self.state, init_scale, min_scale, window, hysteresis, int(consecutive_hysteresis),
+                           dynamic)
 
     def step(self, grads, hp, buckets=None, fused_check=True):
         """grads: one device fp16 tensor (K = 1) or a list of K of them."""

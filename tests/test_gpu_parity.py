@@ -356,6 +356,85 @@ def test_loss_scale_floor_below_powers_of_two(torch):
         gu.compare_full(f"floor W={window}", d, o)
 
 
+@pytest.mark.parametrize("dynamic,hyst,consec,window", [(1, 1, 0, 3), (1, 2, 0, 4), (1, 3, 1, 2), (1, 2, 1, 5),
+                                                         (0, 2, 0, 3)])
+def test_scaler_state_machine_random_overflows(torch, dynamic, hyst, consec, window):
+    """300 steps with random overflows (probability 0.3, runs of both kinds): the
+    device's scaler follows the oracle's after every step, in every mode."""
+    n = 40
+    rng = np.random.default_rng(100 * hyst + 10 * consec + window + dynamic)
+    master, m, v, p16 = _init_host(n, 8400)
+    o = oracle.State(master.copy(), m.copy(), v.copy(), p16.copy(),
+                     oracle.Scaler(2.0 ** 20, 4.0, window, hyst, dynamic=bool(dynamic),
+                                   consecutive_hysteresis=bool(consec)))
+    d = gu.DevState(torch, master, m, v, p16, init_scale=2.0 ** 20, window=window, hysteresis=hyst,
+                    min_scale=4.0, dynamic=dynamic, consecutive_hysteresis=consec)
+    spec = synth.GradSpec(1e-3, 2.0 ** 10)
+    scales = set()
+    for s in range(300):
+        g = _mixed_grads(8500 + s, n, spec)
+        if rng.random() < 0.3:
+            g[rng.integers(0, n)] = rng.choice([0x7C00, 0xFC00, 0x7E00, 0xFD55])
+        ov = oracle.step(o, g, **HP)
+        d.step(gu.dev_u16(torch, g), HP)
+        gu.check_scaler(d.scaler(), o.scaler, ov, f"dyn={dynamic} H={hyst} c={consec} W={window} step {s}")
+        scales.add(o.scaler.scale)
+    gu.compare_full(f"random overflows dyn={dynamic} H={hyst}", d, o)
+    assert len(scales) >= (3 if dynamic else 1)
+
+
+def _wild_f32(rng, n, nonneg=False):
+    """fp32 values from every class: raw random bit patterns (every exponent,
+    including inf and NaN), zeros and subnormals, values near the largest
+    finite, and ordinary N(0, 0.02) values."""
+    raw = rng.integers(0, 2 ** 32, n, dtype=np.uint64).astype(np.uint32)
+    cls = rng.integers(0, 16, n)
+    sign = raw & np.uint32(0x80000000)
+    bits = raw.copy()                                                                    # 0..3: raw
+    bits = np.where((cls >= 4) & (cls < 7), raw & np.uint32(0x807FFFFF), bits)            # 0 / subnormal
+    bits = np.where((cls >= 7) & (cls < 9), (raw & np.uint32(0x80FFFFFF)) | np.uint32(0x7E000000), bits)
+    bits = np.where(cls == 9, sign | np.uint32(0x7F800000), bits)                         # +-inf
+    bits = np.where(cls == 10, raw | np.uint32(0x7FC00000), bits)                         # NaN
+    normal = rng.normal(0, 0.02, n).astype(np.float32).view(np.uint32)
+    bits = np.where(cls >= 11, normal, bits)
+    if nonneg:
+        bits = bits & np.uint32(0x7FFFFFFF)
+    return bits.view(np.float32)
+
+
+@pytest.mark.parametrize("scale,K,wd,pfmt", [(2.0 ** 16, 1, 0.0, "fp16"), (3000.0, 1, 0.1, "bf16"),
+                                             (float(np.float32(1e-8)), 3, 0.0, "fp16"),
+                                             (12345.0, 2, 0.01, "fp16")])
+def test_adam_over_every_fp32_class(torch, scale, K, wd, pfmt):
+    """Adam on master/m/v drawn from every fp32 class, gradients from every finite 16-bit
+    class, scales that are not powers of two: the device's IEEE arithmetic (no flush to
+    zero, correctly rounded divide and square root, infinities and NaNs propagated)
+    matches the oracle's over the whole range (any NaN matches any NaN)."""
+    rng = np.random.default_rng(int(scale) + 7 * K)
+    n = 3 * 4096 + 77
+    master, m = _wild_f32(rng, n), _wild_f32(rng, n)
+    v = _wild_f32(rng, n, nonneg=True)
+    v[:64] = -v[:64]                                     # a few negative second moments: sqrt -> NaN
+    p16 = np.zeros(n, np.uint16)
+    o = oracle.State(master.copy(), m.copy(), v.copy(), p16.copy(),
+                     oracle.Scaler(scale, float(np.float32(1e-8)), 1000, 1), param_fmt=pfmt)
+    d = gu.DevState(torch, master, m, v, p16, init_scale=scale, window=1000, min_scale=float(np.float32(1e-8)),
+                    K=K, param_fmt=pfmt)
+    hp = dict(HP, weight_decay=wd)
+    for s in range(3):
+        gs = []
+        for k in range(K):
+            h = rng.integers(0, 65536, n).astype(np.uint16)
+            gs.append(np.where((h & 0x7C00) == 0x7C00, h & 0x83FF, h).astype(np.uint16))
+        ov = oracle.step(o, gs if K > 1 else gs[0], **hp)
+        assert not ov
+        d.step([gu.dev_u16(torch, g) for g in gs] if K > 1 else gu.dev_u16(torch, gs[0]), hp)
+        gu.check_scaler(d.scaler(), o.scaler, ov, f"wild step {s}")
+        du = gu.compare_full(f"wild scale={scale} K={K} wd={wd} {pfmt} step {s}", d, o)
+        gu.say(f"wild scale={scale} K={K} wd={wd} {pfmt} step {s}: max ulp {du}, "
+               f"nan share {np.isnan(o.master).mean():.3f}")
+
+
 # -- the fp16 cast over every fp32 pattern ----------------------------------------------
 
 def _enc16_parallel(pool, x, parts=8):
