@@ -17,7 +17,8 @@ the 8 TB/s HBM3E peak; ``traffic`` comes from the committed rocprofv3 counter
 summary when it was taken on the current kernel source; the median and minimum
 launch times and ``copy_mix_gbs`` (the same 14 B read + 14 B written per
 element with no arithmetic, on the same arrays, timed after the timed region)
-sit beside it.  ``cpu_baseline`` times
+sit beside it.  ``graph_replay`` times the same steps replayed from HIP
+graphs (one per position in the cycle of gradient buffers).  ``cpu_baseline`` times
 the CPU oracle on a bounded slice of the same workload.
 
     python bench.py --mode copy    # plain-copy and step-shaped data-movement references
@@ -27,6 +28,7 @@ from __future__ import annotations
 import argparse
 import hashlib
 import json
+import math
 import os
 import sys
 import time
@@ -121,14 +123,19 @@ def gpu_run(args):
         ws = torch.zeros((_lib.ds_sumsq_workspace_bytes(n) + 7) // 8, dtype=torch.float64, device=dev)
     ev = []
 
-    def one_step(i, timed):
+    step_ev = []
+
+    def one_step(i, timed, q=stream, whole=False):
+        if whole:
+            s0 = torch.cuda.Event(enable_timing=True)
+            s0.record(q)
         base = i * K
         if K == 1:
             g = grads[base % nbuf]
             if ws is None:
-                _lib.ds_check_overflow(st, g, gdt16, n, stream)
+                _lib.ds_check_overflow(st, g, gdt16, n, q)
             else:
-                _lib.ds_check_overflow_sumsq(st, g, gdt16, n, ws, stream=stream)
+                _lib.ds_check_overflow_sumsq(st, g, gdt16, n, ws, stream=q)
             gptr, dt = g, gdt16
         else:
             for k in range(K):
@@ -136,18 +143,22 @@ def gpu_run(args):
                 for start, size in buckets:
                     a, gp = acc.data_ptr() + 4 * start, g.data_ptr() + 2 * start
                     if k == K - 1 and ws is not None:
-                        _lib.ds_accumulate_sumsq(a, gp, gdt16, size, k == 0, st, ws, stream=stream)
+                        _lib.ds_accumulate_sumsq(a, gp, gdt16, size, k == 0, st, ws, stream=q)
                     else:
-                        _lib.ds_accumulate(a, gp, gdt16, size, k == 0, st if k == K - 1 else None, stream)
+                        _lib.ds_accumulate(a, gp, gdt16, size, k == 0, st if k == K - 1 else None, q)
             gptr, dt = acc, _lib.DS_FP32
         if timed:
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record(stream)
-        _lib.ds_adam_step(st, master, m, v, p16, gdt16, gptr, dt, n, *hp, K, stream)
+            a.record(q)
+        _lib.ds_adam_step(st, master, m, v, p16, gdt16, gptr, dt, n, *hp, K, q)
         if timed:
-            b.record(stream)
+            b.record(q)
             ev.append((a, b))
-        _lib.ds_update_loss_scale(st, stream)
+        _lib.ds_update_loss_scale(st, q)
+        if whole:
+            s1 = torch.cuda.Event(enable_timing=True)
+            s1.record(q)
+            step_ev.append((s0, s1))
 
     for i in range(args.warmup):
         one_step(i, False)
@@ -159,9 +170,40 @@ def gpu_run(args):
     wall = time.perf_counter() - t0
 
     sc = _lib.ds_state_read(st, stream)
+
+    # per-step device time (median, min) in a pass of its own, so that the
+    # extra events stay out of the timed region
+    for i in range(args.steps):
+        one_step(i, False, whole=True)
+    torch.cuda.synchronize()
+
+    # the same steps replayed from HIP graphs: one graph per position in the
+    # cycle of gradient buffers, each captured once (kernels only), replayed in
+    # order; this removes the host's per-launch cost, which bounds small shards
+    cycle = nbuf // math.gcd(nbuf, K)
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    graphs = []
+    for c in range(cycle):
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr, stream=side):
+            one_step(c, False, side)
+        graphs.append(gr)
+    stream.wait_stream(side)
+    for i in range(args.warmup):
+        graphs[i % cycle].replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        graphs[i % cycle].replay()
+    torch.cuda.synchronize()
+    gwall = time.perf_counter() - t0
+    del graphs
+
     adam_ms = [a.elapsed_time(b) for a, b in ev]
     adam_avg_s = sum(adam_ms) / len(adam_ms) / 1e3
     adam_sorted = sorted(adam_ms)
+    step_sorted = sorted(a.elapsed_time(b) for a, b in step_ev)
 
     # achievable-bandwidth reference, after the timed region: the step's data
     # movement (14 B read + 14 B written per element) with no arithmetic, on the
@@ -192,6 +234,8 @@ def gpu_run(args):
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(wall / args.steps * 1e3, 4),
+        "step_ms_median": round(step_sorted[len(step_sorted) // 2], 4),
+        "step_ms_min": round(step_sorted[0], 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -224,6 +268,11 @@ def gpu_run(args):
             "copy_mix_gbs": round(mix_gbs, 1),
         },
         "step_hbm_gbs": round(step_bytes * n * args.steps / wall / 1e9, 1),
+        "graph_replay": {"graphs": cycle, "ms_per_step": round(gwall / args.steps * 1e3, 4),
+                         "value": round(n * args.steps / gwall / 1e9, 3)},
+        "device": {"name": props.name, "arch": getattr(props, "gcnArchName", ""),
+                   "compute_units": props.multi_processor_count,
+                   "memory_gib": round(props.total_memory / 2 ** 30, 1)},
         "scaler_after": {"scale": sc.scale, "applied_steps": sc.step, "skipped": sc.skipped},
     }
     del grads, master, m, v, p16, acc
@@ -279,6 +328,25 @@ def cpu_baseline(workload: str, min_seconds: float, slice_elems: int):
             break
     el = time.perf_counter() - t0
     pool.shutdown()
+
+    # the same step on one thread, over a 1/16 slice, for a quarter of the time
+    n1 = max(1, n // 16)
+    g1 = [g[:n1].copy() for g in grads]
+    st1 = [master[:n1].copy(), np.zeros(n1, np.float32), np.zeros(n1, np.float32), np.zeros(n1, np.uint16)]
+    sc1 = oracle.Scaler(w.init_scale, w.min_scale, w.window, w.hysteresis)
+    steps1 = 0
+    t1 = time.perf_counter()
+    while True:
+        g = g1[steps1 % 2]
+        ov = oracle.any_nonfinite(g)
+        if not ov:
+            oracle.adam(g, *st1, scale=sc1.scale, accum_steps=1, t=sc1.applied + 1, lr=LR, beta1=BETA1,
+                        beta2=BETA2, eps=EPS, weight_decay=WD)
+        sc1.update(ov)
+        steps1 += 1
+        if time.perf_counter() - t1 >= min_seconds / 4:
+            break
+    el1 = time.perf_counter() - t1
     return {
         "value": round(n * steps / el / 1e9, 4),
         "unit": "Gparams/s",
@@ -286,7 +354,21 @@ def cpu_baseline(workload: str, min_seconds: float, slice_elems: int):
         "kind": "oracle",
         "sample": f"{n}-element slice of {workload} (K=1 steps: check + Adam + scaler update), "
                   f"{steps} steps in {el:.1f} s on {threads} threads",
+        "single_thread_value": round(n1 * steps1 / el1 / 1e9, 4),
+        "single_thread_sample": f"{n1}-element slice, {steps1} steps in {el1:.1f} s on 1 thread",
+        "cpu_model": cpu_model(),
     }
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 # ----------------------------------------------------------------------------

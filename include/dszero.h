@@ -47,8 +47,10 @@
  *  - Launch-shape knobs, read from the environment at each call (for tests
  *    and tuning; results are bit-identical under every setting):
  *    DSZERO_GRID=<blocks> pins the block count, DSZERO_UNROLL=2|4 sets the
- *    quads per lane of the read/write kernels, DSZERO_NT=0 turns off their
- *    non-temporal load/store hints.
+ *    quads per lane of the read/write kernels, DSZERO_NT=0|1 turns their
+ *    non-temporal load/store hints off or on (default: on above 2^24
+ *    elements, off at and below, where the state stays in the Infinity Cache
+ *    between steps).
  */
 #ifndef DSZERO_H
 #define DSZERO_H

@@ -241,7 +241,8 @@ def test_grid_size_and_variant_invariance(torch):
     n = (1 << 20) + 3
     ref = _run_variant(torch, n, {})
     for env in [{"DSZERO_GRID": "1"}, {"DSZERO_GRID": "7"}, {"DSZERO_GRID": "100000"},
-                {"DSZERO_UNROLL": "2"}, {"DSZERO_NT": "0"}, {"DSZERO_UNROLL": "2", "DSZERO_GRID": "3"},
+                {"DSZERO_UNROLL": "2"}, {"DSZERO_NT": "0"}, {"DSZERO_NT": "1"},
+                {"DSZERO_UNROLL": "2", "DSZERO_GRID": "3", "DSZERO_NT": "1"},
                 {}]:
         got = _run_variant(torch, n, env)
         for a, b in zip(ref, got):

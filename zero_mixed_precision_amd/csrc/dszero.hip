@@ -729,7 +729,19 @@ unsigned grid_blocks(int64_t units)
 
 // Variant knobs (default: quads per lane U = 4, non-temporal accesses on).
 int variant_unroll() { return env_long("DSZERO_UNROLL", 4) == 2 ? 2 : 4; }
-bool variant_nt() { return env_long("DSZERO_NT", 1) != 0; }
+// Non-temporal hints on the read/write kernels' streams: on by default above
+// kTemporalMaxElems elements, where a step's 28-30 B per element is more than
+// twice the 256 MB Infinity Cache and every array is streamed once; off
+// below, where a small partition's state stays in the cache between steps.
+// DSZERO_NT=0|1 forces either.
+constexpr int64_t kTemporalMaxElems = int64_t(1) << 24;
+bool variant_nt(int64_t n)
+{
+    const long forced = env_long("DSZERO_NT", -1);
+    if (forced >= 0)
+        return forced != 0;
+    return n > kTemporalMaxElems;
+}
 
 int64_t tiles_of(int64_t n, int unroll) { return (n >> 2) / (static_cast<int64_t>(unroll) * kStepBlock); }
 
@@ -908,7 +920,7 @@ ds_status adam_step(const ds_scaler* st, float* master, float* m, float* v, uint
     hipStream_t s = static_cast<hipStream_t>(stream);
     const int unroll = variant_unroll();
     const unsigned blocks = grid_blocks(tiles_of(n, unroll));
-    const bool nt = variant_nt();
+    const bool nt = variant_nt(n);
     const bool wd = weight_decay != 0.0f;
     const AdamArgs args{st, master, m, v, p16, grad, n, hp};
     launch_adam(fmt_of(dt), fmt_of(pdt), wd, nt, unroll, blocks, s, args);
@@ -1000,7 +1012,7 @@ ds_status ds_accumulate(float* acc, const uint16_t* g16, ds_dtype gdt, int64_t n
     hipStream_t s = static_cast<hipStream_t>(stream);
     const int unroll = variant_unroll();
     const unsigned blocks = grid_blocks(tiles_of(n, unroll));
-    const bool nt = variant_nt();
+    const bool nt = variant_nt(n);
     const bool ow = overwrite != 0, ck = st_or_null != nullptr;
     if (gdt == DS_BF16)
         launch_acc<kBF16>(ow, ck, nt, unroll, blocks, s, acc, g16, n, st_or_null);
@@ -1134,7 +1146,7 @@ ds_status ds_accumulate_sumsq(float* acc, const uint16_t* g16, ds_dtype gdt, int
     // the tile must be one 4096-element chunk: U = 4 whatever DSZERO_UNROLL says
     const unsigned blocks = grid_blocks(tiles_of(n, 4));
     double* part = static_cast<double*>(workspace);
-    const bool nt = variant_nt();
+    const bool nt = variant_nt(n);
     if (gdt == DS_BF16)
         launch_acc_sumsq<kBF16>(overwrite != 0, nt, blocks, s, acc, g16, n, st, part);
     else
