@@ -40,6 +40,18 @@ def test_every_declared_symbol_is_exported():
     assert sorted(_lib.EXPORTED) == syms
 
 
+def test_nothing_but_the_declared_abi_is_exported():
+    """The library's dynamic symbol table holds the declared entry points and no
+    C++ helper (the HIP compiler's own module id aside)."""
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    names = {line.split()[-1] for line in out.splitlines() if line.strip()}
+    extra = {s for s in names if not s.startswith("ds_") and not s.startswith("__hip_cuid_")}
+    assert not extra, sorted(extra)
+    assert {s for s in names if s.startswith("ds_")} == set(declared_symbols())
+
+
 def test_scaler_layout():
     assert L.ds_scaler_size() == 128 == ctypes.sizeof(_lib.DsScaler)
     offs = {n: getattr(_lib.DsScaler, n).offset for n, _ in _lib.DsScaler._fields_}

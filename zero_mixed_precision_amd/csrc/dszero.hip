@@ -16,8 +16,9 @@
 // (fp16) span.  The read/write kernels (Adam, accumulation) give each
 // 256-lane block one tile of U x 256 consecutive quads (U = 4: 4096
 // elements), issue all of the tile's loads before any arithmetic, and mark
-// loads and stores non-temporal (streamed data is touched once); the grid has
-// one block per tile.  Measured on MI355X with a 109M-element partition this
+// loads and stores non-temporal (streamed data is touched once) on partitions
+// larger than twice the Infinity Cache; the grid has one block per tile.
+// Measured on MI355X with a 109M-element partition this
 // beats persistent grid-stride launches, whose extra waves per CU congest the
 // memory system under a 50/50 read/write mix.  The read-only overflow check
 // uses 1024-lane blocks, one 16-byte vector per lane, and ordinary (cache-
@@ -710,8 +711,9 @@ long env_long(const char* name, long dflt)
     return (end != s) ? v : dflt;
 }
 
-// Blocks for `units` units of work (tiles, or vectors of the check): one
-// block per unit, at least one, at most kMaxBlocks (the kernels loop past
+// Blocks for `units` units of work (tiles, sum-of-squares chunks, or the
+// check's groups of kCheckBlock vectors): one block per unit, at least one,
+// at most kMaxBlocks (the kernels loop past
 // that).  DSZERO_GRID pins the block count (launch-shape invariance tests,
 // sweeps).
 unsigned grid_blocks(int64_t units)
@@ -727,7 +729,7 @@ unsigned grid_blocks(int64_t units)
     return static_cast<unsigned>(b);
 }
 
-// Variant knobs (default: quads per lane U = 4, non-temporal accesses on).
+// Variant knobs (default: quads per lane U = 4).
 int variant_unroll() { return env_long("DSZERO_UNROLL", 4) == 2 ? 2 : 4; }
 // Non-temporal hints on the read/write kernels' streams: on by default above
 // kTemporalMaxElems elements, where a step's 28-30 B per element is more than
@@ -868,12 +870,6 @@ ds_status check_workspace(const void* ws, size_t ws_bytes, int64_t n)
     return DS_OK;
 }
 
-}  // namespace
-
-// ---------------------------------------------------------------------------
-// C ABI
-// ---------------------------------------------------------------------------
-
 bool schedule_ok(const ds_lr_schedule& q)
 {
     if (q.kind != DS_LR_WARMUP && q.kind != DS_LR_WARMUP_DECAY)
@@ -926,6 +922,12 @@ ds_status adam_step(const ds_scaler* st, float* master, float* m, float* v, uint
     launch_adam(fmt_of(dt), fmt_of(pdt), wd, nt, unroll, blocks, s, args);
     return launched();
 }
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// C ABI
+// ---------------------------------------------------------------------------
 
 extern "C" {
 
