@@ -172,10 +172,22 @@ def gpu_run(args):
     sc = _lib.ds_state_read(st, stream)
 
     # per-step device time (median, min) in a pass of its own, so that the
-    # extra events stay out of the timed region
+    # extra events stay out of the timed region; with --step-log, one JSON line
+    # per step of that pass (reading the scaler synchronises every step)
+    log_f = open(args.step_log, "w") if args.step_log else None
     for i in range(args.steps):
+        if log_f is not None:
+            used = _lib.ds_state_read(st, stream).scale
         one_step(i, False, whole=True)
+        if log_f is not None:
+            after = _lib.ds_state_read(st, stream)
+            a, b = step_ev[-1]
+            log_f.write(json.dumps({"step": int(after.iter), "scale": used, "overflow": int(after.last_overflow),
+                                    "t": int(after.step), "growth_count": int(after.growth_count),
+                                    "skipped": int(after.skipped), "step_ms": round(a.elapsed_time(b), 4)}) + "\n")
     torch.cuda.synchronize()
+    if log_f is not None:
+        log_f.close()
 
     # the same steps replayed from HIP graphs: one graph per position in the
     # cycle of gradient buffers, each captured once (kernels only), replayed in
@@ -431,6 +443,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--cpu-slice", type=int, default=1 << 24)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--step-log", default=None,
+                    help="write one JSON line per step (scale used, overflow, t, growth count, device time) "
+                         "from an untimed pass")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: --gpus {args.gpus} is not supported; the benchmark measures one GPU's "

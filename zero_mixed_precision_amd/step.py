@@ -17,6 +17,8 @@ scheduler block the update is ds_adam_step_sched, which reads the learning
 rate of the schedule on the device.
 
 No call synchronises the host; ``scaler()`` reads the state back (one copy).
+``save_checkpoint``/``load_checkpoint`` write and restore the shard between
+steps (safetensors files, see checkpoint.py).
 ``graph(grads)`` records the whole sequence for fixed gradient buffers into a
 HIP graph, so a step costs one graph launch; it contains kernels only (no
 memset or copy nodes).
@@ -136,3 +138,13 @@ class ShardStep:
 
     def scaler(self) -> _lib.DsScaler:
         return _lib.ds_state_read(self.state, self.stream)
+
+    def save_checkpoint(self, save_dir, tag=None, client_state=None, rank=0) -> str:
+        """Save this shard between steps ("DeepSpeed complete guide" section 5.2); see checkpoint.py."""
+        from .checkpoint import save_checkpoint
+        return save_checkpoint(self, save_dir, tag, client_state, rank)
+
+    def load_checkpoint(self, load_dir, tag=None, rank=0):
+        """Restore this shard; returns (path, client_state)."""
+        from .checkpoint import load_checkpoint
+        return load_checkpoint(self, load_dir, tag, rank)
