@@ -4,8 +4,9 @@
 
 One step = the whole per-rank hot path over one synthetic batch: (K > 1:
 bucketed fp16 -> fp32 accumulation of every micro-batch, the last one with the
-fused inf/NaN check; K = 1: the inf/NaN check of the fp16 gradient), the gated
-fused Adam update with the fp16 copy, and the loss-scale update.  Inputs are
+fused inf/NaN check; K = 1: the inf/NaN check of the fp16 gradient), then the
+gated fused Adam update with the fp16 copy, whose kernel also performs the
+loss-scale update.  Inputs are
 resident in HBM before the timed region; gradients are drawn on the device
 (distinct buffers, reused cyclically when they do not all fit).
 
@@ -150,11 +151,11 @@ def gpu_run(args):
         if timed:
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a.record(q)
-        _lib.ds_adam_step(st, master, m, v, p16, gdt16, gptr, dt, n, *hp, K, q)
+        # the Adam kernel also advances the loss scaler (one launch for both)
+        _lib.ds_adam_step_fused(st, master, m, v, p16, gdt16, gptr, dt, n, hp[0], None, *hp[1:], K, q)
         if timed:
             b.record(q)
             ev.append((a, b))
-        _lib.ds_update_loss_scale(st, q)
         if whole:
             s1 = torch.cuda.Event(enable_timing=True)
             s1.record(q)

@@ -101,7 +101,8 @@ typedef struct ds_scaler {
     uint32_t last_overflow;         /* overflow flag consumed by the last update      */
     double grad_sumsq;              /* sum of squares of the step's gradient so far   */
     double last_grad_sumsq;         /* grad_sumsq consumed by the last update         */
-    uint8_t reserved[48];           /* zero                                           */
+    uint32_t blocks_done;           /* ds_adam_step_fused: blocks finished (0 between steps) */
+    uint8_t reserved[44];           /* zero                                           */
 } ds_scaler;
 
 /* sizeof(ds_scaler) as compiled into the library (128). */
@@ -231,6 +232,22 @@ ds_status ds_adam_step_sched(const ds_scaler* st, float* master, float* m, float
                              const ds_lr_schedule* sched, float beta1, float beta2, float eps,
                              float weight_decay, float max_grad_norm, int32_t accum_steps,
                              void* stream);
+
+/*
+ * ds_adam_step (sched_or_null NULL: constant lr) or ds_adam_step_sched
+ * (sched_or_null: a host ds_lr_schedule, lr ignored) followed by
+ * ds_update_loss_scale, in one kernel: for a partition updated by a single
+ * call per step, which then calls no ds_update_loss_scale of its own.  Each
+ * block of the kernel, when done, takes a ticket from st->blocks_done (one
+ * atomic add); the block with the last ticket advances the scaler exactly as
+ * ds_update_loss_scale does and sets the count back to 0.  Arithmetic,
+ * results and errors are those of the two calls it replaces; with n == 0
+ * only the scaler advances.  st is read and written.
+ */
+ds_status ds_adam_step_fused(ds_scaler* st, float* master, float* m, float* v, uint16_t* p16, ds_dtype pdt,
+                             const void* grad, ds_dtype dt, int64_t n, float lr,
+                             const ds_lr_schedule* sched_or_null, float beta1, float beta2, float eps,
+                             float weight_decay, float max_grad_norm, int32_t accum_steps, void* stream);
 
 /*
  * End of a step: advance the scaler by the step's overflow flag, then clear

@@ -436,6 +436,66 @@ def test_adam_over_every_fp32_class(torch, scale, K, wd, pfmt):
                f"nan share {np.isnan(o.master).mean():.3f}")
 
 
+@pytest.mark.parametrize("n,K,grid", [(1_000_003, 1, None), (1_000_003, 1, "1"), (300_001, 3, "7"),
+                                      (300_001, 1, "100000"), (4096 * 4, 2, None), (5, 1, None)])
+def test_fused_step_matches_separate_calls(torch, n, K, grid):
+    """ds_adam_step_fused (Adam plus the scaler update in one kernel, the last block
+    to finish advancing the scaler) against ds_adam_step + ds_update_loss_scale and the
+    oracle, bit for bit, through overflowed steps and forced grids (one block; more
+    blocks than tiles, so that blocks with no tile still count themselves)."""
+    from zero_mixed_precision_amd import _lib
+    env = {"DSZERO_GRID": grid} if grid else {}
+    master, m, v, p16 = _init_host(n, 8600)
+    o = oracle.State(master.copy(), m.copy(), v.copy(), p16.copy(), oracle.Scaler(4096.0, 1.0, 2, 1))
+    sep = gu.DevState(torch, master, m, v, p16, init_scale=4096.0, window=2, K=K)
+    fus = gu.DevState(torch, master, m, v, p16, init_scale=4096.0, window=2, K=K)
+    spec = synth.GradSpec(1e-3, 4096.0)
+    old = {k: os.environ.get(k) for k in env}
+    os.environ.update(env)
+    try:
+        for s in range(8):
+            gs = [_mixed_grads(8700 + 10 * s + k, n, spec) for k in range(K)]
+            if s in (2, 5):
+                gs[-1][(s * 131) % n] = 0x7C00
+            ov = oracle.step(o, gs if K > 1 else gs[0], **HP)
+            dg = [gu.dev_u16(torch, g) for g in gs]
+            sep.step(dg if K > 1 else dg[0], HP)
+            # the same sequence with the fused entry point
+            if K == 1:
+                _lib.ds_check_overflow(fus.state, dg[0], _lib.DS_FP16, n)
+                grad, dt = dg[0], _lib.DS_FP16
+            else:
+                for k, g in enumerate(dg):
+                    _lib.ds_accumulate(fus.acc, g, _lib.DS_FP16, n, k == 0, fus.state if k == K - 1 else None)
+                grad, dt = fus.acc, _lib.DS_FP32
+            _lib.ds_adam_step_fused(fus.state, fus.master, fus.m, fus.v, fus.p16, _lib.DS_FP16, grad, dt, n,
+                                    HP["lr"], None, HP["beta1"], HP["beta2"], HP["eps"], 0.0, 0.0, K)
+            sc = fus.scaler()
+            gu.check_scaler(sc, o.scaler, ov, f"fused n={n} K={K} grid={grid} step {s}")
+            assert sc.blocks_done == 0
+            assert sc.as_dict() == sep.scaler().as_dict()
+    finally:
+        for k, val in old.items():
+            if val is None:
+                os.environ.pop(k, None)
+            else:
+                os.environ[k] = val
+    for a, b in ((sep.master, fus.master), (sep.m, fus.m), (sep.v, fus.v), (sep.p16, fus.p16)):
+        assert np.array_equal(a.cpu().numpy().view(np.uint8), b.cpu().numpy().view(np.uint8))
+    gu.compare_full(f"fused n={n} K={K}", fus, o)
+
+
+def test_fused_step_on_an_empty_partition_advances_the_scaler(torch):
+    from zero_mixed_precision_amd import _lib
+    st = torch.zeros(_lib.ds_scaler_size(), dtype=torch.uint8, device="cuda:0")
+    _lib.ds_state_init(st, 1024.0, 1.0, 2, 1, 0, 1)
+    for _ in range(2):
+        _lib.ds_adam_step_fused(st, 0, 0, 0, 0, _lib.DS_FP16, 0, _lib.DS_FP16, 0, 1e-4, None, 0.9, 0.999, 1e-8,
+                                0.0, 0.0, 1)
+    sc = _lib.ds_state_read(st)
+    assert sc.step == 2 and sc.iter == 2 and sc.scale == 2048.0
+
+
 # -- the fp16 cast over every fp32 pattern ----------------------------------------------
 
 def _enc16_parallel(pool, x, parts=8):

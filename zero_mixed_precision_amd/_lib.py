@@ -22,6 +22,7 @@ EXPORTED = (
     "ds_check_overflow", "ds_adam_step", "ds_update_loss_scale", "ds_adam_bias_scalars",
     "ds_layout_greedy", "ds_partition_range", "ds_status_string", "ds_sumsq_workspace_bytes",
     "ds_check_overflow_sumsq", "ds_accumulate_sumsq", "ds_adam_step_sched", "ds_lr_scalars",
+    "ds_adam_step_fused",
 )
 DS_LR_WARMUP, DS_LR_WARMUP_DECAY = 1, 2
 
@@ -44,7 +45,8 @@ class DsScaler(ctypes.Structure):
         ("last_overflow", ctypes.c_uint32),
         ("grad_sumsq", ctypes.c_double),
         ("last_grad_sumsq", ctypes.c_double),
-        ("reserved", ctypes.c_uint8 * 48),
+        ("blocks_done", ctypes.c_uint32),
+        ("reserved", ctypes.c_uint8 * 44),
     ]
 
     def as_dict(self) -> dict:
@@ -99,7 +101,7 @@ def bind_torch_hip_runtime() -> None:
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() "
-                          "(python -m zero_mixed_precision_amd.build)")
+                          "(python zero_mixed_precision_amd/build.py)")
     bind_torch_hip_runtime()
     L = ctypes.CDLL(LIB_PATH)
     vp, i64, i32, f32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_float
@@ -120,6 +122,8 @@ def _load():
         "ds_adam_step_sched": ([vp, vp, vp, vp, vp, ctypes.c_int, vp, ctypes.c_int, i64,
                                 ctypes.POINTER(DsLrSchedule), f32, f32, f32, f32, f32, i32, vp], ctypes.c_int),
         "ds_lr_scalars": ([vp, ctypes.POINTER(DsLrSchedule), f32, f32, vp, vp], ctypes.c_int),
+        "ds_adam_step_fused": ([vp, vp, vp, vp, vp, ctypes.c_int, vp, ctypes.c_int, i64, f32,
+                                ctypes.POINTER(DsLrSchedule), f32, f32, f32, f32, f32, i32, vp], ctypes.c_int),
         "ds_layout_greedy": ([vp, i32, i64, i64, vp, vp, vp, vp, ctypes.POINTER(i32),
                               ctypes.POINTER(i64)], ctypes.c_int),
         "ds_partition_range": ([i64, i32, i32, i64, ctypes.POINTER(i64), ctypes.POINTER(i64)],
@@ -127,7 +131,11 @@ def _load():
         "ds_status_string": ([ctypes.c_int], ctypes.c_char_p),
     }
     for name, (args, res) in sig.items():
-        fn = getattr(L, name)
+        try:
+            fn = getattr(L, name)
+        except AttributeError:
+            raise ImportError(f"{LIB_PATH} does not export {name}: it is older than include/dszero.h; "
+                              "rebuild it (python zero_mixed_precision_amd/build.py)") from None
         fn.argtypes, fn.restype = args, res
     if L.ds_scaler_size() != ctypes.sizeof(DsScaler):
         raise ImportError("ds_scaler layout mismatch between libdszero.so and the binding")
@@ -205,6 +213,14 @@ def ds_adam_step_sched(st, master, m, v, p16, pdt, grad, dtype, n, sched: DsLrSc
     _ok(lib.ds_adam_step_sched(_p(st), _p(master), _p(m), _p(v), _p(p16), int(pdt), _p(grad), int(dtype),
                                int(n), ctypes.byref(sched), beta1, beta2, eps, weight_decay, max_grad_norm,
                                int(accum_steps), _s(stream)), "ds_adam_step_sched")
+
+
+def ds_adam_step_fused(st, master, m, v, p16, pdt, grad, dtype, n, lr, sched, beta1, beta2, eps, weight_decay,
+                       max_grad_norm, accum_steps, stream=None) -> None:
+    """ds_adam_step (sched None) or ds_adam_step_sched, then the scaler update, in one kernel."""
+    _ok(lib.ds_adam_step_fused(_p(st), _p(master), _p(m), _p(v), _p(p16), int(pdt), _p(grad), int(dtype), int(n),
+                               lr, ctypes.byref(sched) if sched is not None else None, beta1, beta2, eps,
+                               weight_decay, max_grad_norm, int(accum_steps), _s(stream)), "ds_adam_step_fused")
 
 
 def ds_sumsq_workspace_bytes(n) -> int:

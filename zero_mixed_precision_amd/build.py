@@ -1,7 +1,9 @@
 """Build the gfx950 shared libraries in place (hipcc cross-compiles without a GPU).
 
-    python -m zero_mixed_precision_amd.build
+    python zero_mixed_precision_amd/build.py
 
+(run as a script: importing the package first would load the library being
+rebuilt)
 Flags that carry meaning for the numerics:
   -ffp-contract=off                       no fused multiply-add contraction: one
                                           rounding per written operation

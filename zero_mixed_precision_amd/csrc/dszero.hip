@@ -230,6 +230,48 @@ __global__ __launch_bounds__(TPB) void sumsq_finish_kernel(ds_scaler* __restrict
 }
 
 // ---------------------------------------------------------------------------
+// loss-scaler state machine ([Guide] section 4.2), one work-item
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ void advance_scaler(ds_scaler* st)
+{
+    ds_scaler s = *st;
+    const uint32_t ov = s.overflow != 0u ? 1u : 0u;
+    s.iter += 1;
+    if (ov) {
+        s.skipped += 1;
+        s.growth_count = 0;
+        if (s.dynamic) {
+            if (s.hysteresis_left <= 1) {
+                const float half = s.scale * 0.5f;
+                s.scale = half > s.min_scale ? half : s.min_scale;
+                s.hysteresis_left = s.hysteresis;
+            } else {
+                s.hysteresis_left -= 1;
+            }
+        }
+    } else {
+        s.step += 1;
+        if (s.dynamic) {
+            if (s.consecutive_hysteresis)
+                s.hysteresis_left = s.hysteresis;
+            s.growth_count += 1;
+            if (s.growth_count == s.growth_window) {
+                s.scale = s.scale * 2.0f;
+                s.growth_count = 0;
+            }
+        }
+    }
+    s.last_overflow = ov;
+    s.overflow = 0u;
+    s.last_grad_sumsq = s.grad_sumsq;
+    s.grad_sumsq = 0.0;
+    *st = s;
+}
+
+__global__ void update_scale_kernel(ds_scaler* st) { advance_scaler(st); }
+
+// ---------------------------------------------------------------------------
 // Adam
 // ---------------------------------------------------------------------------
 
@@ -376,12 +418,17 @@ __device__ __forceinline__ float load_grad1(const void* grad, int64_t i)
         return dec1<GF>(static_cast<const uint16_t*>(grad)[i]);
 }
 
-// Gated fused step: if the step's overflow flag is set, return before any
-// write; else update every element of [0, n) once.  Tiles of U x TPB quads are
-// dealt to blocks round-robin; block 0 also takes the quads of the last,
-// partial tile and the final n % 4 elements.
-template <int GF, int PF, bool WD, bool NT, int TPB, int U>
-__global__ __launch_bounds__(TPB) void adam_kernel(const ds_scaler* __restrict__ st,
+// Gated fused step: if the step's overflow flag is set, write nothing; else
+// update every element of [0, n) once.  Tiles of U x TPB quads are dealt to
+// blocks round-robin; block 0 also takes the quads of the last, partial tile
+// and the final n % 4 elements.  With FUSE the kernel also ends the step:
+// every block, when done (whether or not the step is skipped), takes a ticket
+// from st->blocks_done with one atomic add, and the block that takes the last
+// ticket, after every other block has read the scaler state, advances the
+// scaler (as update_scale_kernel does) and resets the count.  No block waits
+// for another.
+template <int GF, int PF, bool WD, bool NT, int TPB, int U, bool FUSE>
+__global__ __launch_bounds__(TPB) void adam_kernel(ds_scaler* __restrict__ st,
                                                    float* __restrict__ master,
                                                    float* __restrict__ mom1,
                                                    float* __restrict__ mom2,
@@ -389,58 +436,66 @@ __global__ __launch_bounds__(TPB) void adam_kernel(const ds_scaler* __restrict__
                                                    const void* __restrict__ grad, int64_t n,
                                                    AdamHyper hp)
 {
-    if (st->overflow != 0u)
-        return;
-    const AdamConsts c = make_consts(st, hp);
+    if (st->overflow == 0u) {
+        const AdamConsts c = make_consts(st, hp);
 
-    f32x4* P = reinterpret_cast<f32x4*>(master);
-    f32x4* M = reinterpret_cast<f32x4*>(mom1);
-    f32x4* V = reinterpret_cast<f32x4*>(mom2);
-    u32x2* H = reinterpret_cast<u32x2*>(p16);
+        f32x4* P = reinterpret_cast<f32x4*>(master);
+        f32x4* M = reinterpret_cast<f32x4*>(mom1);
+        f32x4* V = reinterpret_cast<f32x4*>(mom2);
+        u32x2* H = reinterpret_cast<u32x2*>(p16);
 
-    constexpr int T = U * TPB;  // quads per tile
-    const int64_t nq = n >> 2;
-    const int64_t ntiles = nq / T;
-    for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
-        const int64_t q0 = tile * T + threadIdx.x;
-        f32x4 g[U], p[U], m[U], v[U];
+        constexpr int T = U * TPB;  // quads per tile
+        const int64_t nq = n >> 2;
+        const int64_t ntiles = nq / T;
+        for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
+            const int64_t q0 = tile * T + threadIdx.x;
+            f32x4 g[U], p[U], m[U], v[U];
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int64_t i = q0 + u * TPB;
-            g[u] = load_grad4<GF, NT>(grad, i);
-            p[u] = load<NT>(P + i);
-            m[u] = load<NT>(M + i);
-            v[u] = load<NT>(V + i);
+            for (int u = 0; u < U; ++u) {
+                const int64_t i = q0 + u * TPB;
+                g[u] = load_grad4<GF, NT>(grad, i);
+                p[u] = load<NT>(P + i);
+                m[u] = load<NT>(M + i);
+                v[u] = load<NT>(V + i);
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int64_t i = q0 + u * TPB;
+                adam4<WD>(g[u], p[u], m[u], v[u], c);
+                store<NT>(P + i, p[u]);
+                store<NT>(M + i, m[u]);
+                store<NT>(V + i, v[u]);
+                store<NT>(H + i, narrow4<PF>(p[u]));
+            }
         }
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int64_t i = q0 + u * TPB;
-            adam4<WD>(g[u], p[u], m[u], v[u], c);
-            store<NT>(P + i, p[u]);
-            store<NT>(M + i, m[u]);
-            store<NT>(V + i, v[u]);
-            store<NT>(H + i, narrow4<PF>(p[u]));
+        if (blockIdx.x == 0) {
+            for (int64_t q = ntiles * T + threadIdx.x; q < nq; q += TPB) {
+                f32x4 g = load_grad4<GF, NT>(grad, q);
+                f32x4 p = load<NT>(P + q), m = load<NT>(M + q), v = load<NT>(V + q);
+                adam4<WD>(g, p, m, v, c);
+                store<NT>(P + q, p);
+                store<NT>(M + q, m);
+                store<NT>(V + q, v);
+                store<NT>(H + q, narrow4<PF>(p));
+            }
+            if (static_cast<int64_t>(threadIdx.x) < (n & 3)) {
+                const int64_t i = (nq << 2) + threadIdx.x;
+                float p = master[i], m = mom1[i], v = mom2[i];
+                adam1<WD>(load_grad1<GF>(grad, i), p, m, v, c);
+                master[i] = p;
+                mom1[i] = m;
+                mom2[i] = v;
+                p16[i] = static_cast<uint16_t>(enc1<PF>(p));
+            }
         }
     }
-    if (blockIdx.x != 0)
-        return;
-    for (int64_t q = ntiles * T + threadIdx.x; q < nq; q += TPB) {
-        f32x4 g = load_grad4<GF, NT>(grad, q);
-        f32x4 p = load<NT>(P + q), m = load<NT>(M + q), v = load<NT>(V + q);
-        adam4<WD>(g, p, m, v, c);
-        store<NT>(P + q, p);
-        store<NT>(M + q, m);
-        store<NT>(V + q, v);
-        store<NT>(H + q, narrow4<PF>(p));
-    }
-    if (static_cast<int64_t>(threadIdx.x) < (n & 3)) {
-        const int64_t i = (nq << 2) + threadIdx.x;
-        float p = master[i], m = mom1[i], v = mom2[i];
-        adam1<WD>(load_grad1<GF>(grad, i), p, m, v, c);
-        master[i] = p;
-        mom1[i] = m;
-        mom2[i] = v;
-        p16[i] = static_cast<uint16_t>(enc1<PF>(p));
+    if constexpr (FUSE) {
+        // every lane of this block has read the scaler state (make_consts) by now
+        __syncthreads();
+        if (threadIdx.x == 0 && atomicAdd(&st->blocks_done, 1u) == gridDim.x - 1u) {
+            st->blocks_done = 0u;
+            advance_scaler(st);
+        }
     }
 }
 
@@ -655,46 +710,6 @@ __global__ __launch_bounds__(TPB) void accumulate_kernel(float* __restrict__ acc
         raise_flag(st, bad);
 }
 
-// ---------------------------------------------------------------------------
-// loss-scaler state machine ([Guide] section 4.2), one work-item
-// ---------------------------------------------------------------------------
-
-__global__ void update_scale_kernel(ds_scaler* st)
-{
-    ds_scaler s = *st;
-    const uint32_t ov = s.overflow != 0u ? 1u : 0u;
-    s.iter += 1;
-    if (ov) {
-        s.skipped += 1;
-        s.growth_count = 0;
-        if (s.dynamic) {
-            if (s.hysteresis_left <= 1) {
-                const float half = s.scale * 0.5f;
-                s.scale = half > s.min_scale ? half : s.min_scale;
-                s.hysteresis_left = s.hysteresis;
-            } else {
-                s.hysteresis_left -= 1;
-            }
-        }
-    } else {
-        s.step += 1;
-        if (s.dynamic) {
-            if (s.consecutive_hysteresis)
-                s.hysteresis_left = s.hysteresis;
-            s.growth_count += 1;
-            if (s.growth_count == s.growth_window) {
-                s.scale = s.scale * 2.0f;
-                s.growth_count = 0;
-            }
-        }
-    }
-    s.last_overflow = ov;
-    s.overflow = 0u;
-    s.last_grad_sumsq = s.grad_sumsq;
-    s.grad_sumsq = 0.0;
-    *st = s;
-}
-
 __global__ void write_state_kernel(ds_scaler* st, ds_scaler value) { *st = value; }
 
 // ---------------------------------------------------------------------------
@@ -773,7 +788,7 @@ bool known(ds_dtype dt) { return dt == DS_FP16 || dt == DS_BF16 || dt == DS_FP32
 uint64_t esize(ds_dtype dt) { return dt == DS_FP32 ? 4 : 2; }
 
 struct AdamArgs {
-    const ds_scaler* st;
+    ds_scaler* st;   // written only by the fused form
     float *master, *m, *v;
     uint16_t* p16;
     const void* grad;
@@ -782,36 +797,39 @@ struct AdamArgs {
 };
 
 template <int GF, int PF, bool WD, bool NT>
-void launch_adam4(int unroll, unsigned blocks, hipStream_t s, const AdamArgs& a)
+void launch_adam4(int unroll, bool fuse, unsigned blocks, hipStream_t s, const AdamArgs& a)
 {
-    if (unroll == 2)
-        adam_kernel<GF, PF, WD, NT, kStepBlock, 2><<<blocks, kStepBlock, 0, s>>>(a.st, a.master, a.m, a.v, a.p16, a.grad, a.n, a.hp);
+    if (fuse)   // the fused form is built for the default tile only
+        adam_kernel<GF, PF, WD, NT, kStepBlock, 4, true><<<blocks, kStepBlock, 0, s>>>(a.st, a.master, a.m, a.v, a.p16, a.grad, a.n, a.hp);
+    else if (unroll == 2)
+        adam_kernel<GF, PF, WD, NT, kStepBlock, 2, false><<<blocks, kStepBlock, 0, s>>>(a.st, a.master, a.m, a.v, a.p16, a.grad, a.n, a.hp);
     else
-        adam_kernel<GF, PF, WD, NT, kStepBlock, 4><<<blocks, kStepBlock, 0, s>>>(a.st, a.master, a.m, a.v, a.p16, a.grad, a.n, a.hp);
+        adam_kernel<GF, PF, WD, NT, kStepBlock, 4, false><<<blocks, kStepBlock, 0, s>>>(a.st, a.master, a.m, a.v, a.p16, a.grad, a.n, a.hp);
 }
 
 template <int GF, int PF>
-void launch_adam2(bool wd, bool nt, int unroll, unsigned blocks, hipStream_t s, const AdamArgs& a)
+void launch_adam2(bool wd, bool nt, int unroll, bool fuse, unsigned blocks, hipStream_t s, const AdamArgs& a)
 {
     if (wd) {
-        if (nt) launch_adam4<GF, PF, true, true>(unroll, blocks, s, a);
-        else    launch_adam4<GF, PF, true, false>(unroll, blocks, s, a);
+        if (nt) launch_adam4<GF, PF, true, true>(unroll, fuse, blocks, s, a);
+        else    launch_adam4<GF, PF, true, false>(unroll, fuse, blocks, s, a);
     } else {
-        if (nt) launch_adam4<GF, PF, false, true>(unroll, blocks, s, a);
-        else    launch_adam4<GF, PF, false, false>(unroll, blocks, s, a);
+        if (nt) launch_adam4<GF, PF, false, true>(unroll, fuse, blocks, s, a);
+        else    launch_adam4<GF, PF, false, false>(unroll, fuse, blocks, s, a);
     }
 }
 
-void launch_adam(int gf, int pf, bool wd, bool nt, int unroll, unsigned blocks, hipStream_t s, const AdamArgs& a)
+void launch_adam(int gf, int pf, bool wd, bool nt, int unroll, bool fuse, unsigned blocks, hipStream_t s,
+                 const AdamArgs& a)
 {
     if (pf == kBF16) {
-        if (gf == kF16)       launch_adam2<kF16, kBF16>(wd, nt, unroll, blocks, s, a);
-        else if (gf == kBF16) launch_adam2<kBF16, kBF16>(wd, nt, unroll, blocks, s, a);
-        else                  launch_adam2<kF32, kBF16>(wd, nt, unroll, blocks, s, a);
+        if (gf == kF16)       launch_adam2<kF16, kBF16>(wd, nt, unroll, fuse, blocks, s, a);
+        else if (gf == kBF16) launch_adam2<kBF16, kBF16>(wd, nt, unroll, fuse, blocks, s, a);
+        else                  launch_adam2<kF32, kBF16>(wd, nt, unroll, fuse, blocks, s, a);
     } else {
-        if (gf == kF16)       launch_adam2<kF16, kF16>(wd, nt, unroll, blocks, s, a);
-        else if (gf == kBF16) launch_adam2<kBF16, kF16>(wd, nt, unroll, blocks, s, a);
-        else                  launch_adam2<kF32, kF16>(wd, nt, unroll, blocks, s, a);
+        if (gf == kF16)       launch_adam2<kF16, kF16>(wd, nt, unroll, fuse, blocks, s, a);
+        else if (gf == kBF16) launch_adam2<kBF16, kF16>(wd, nt, unroll, fuse, blocks, s, a);
+        else                  launch_adam2<kF32, kF16>(wd, nt, unroll, fuse, blocks, s, a);
     }
 }
 
@@ -884,7 +902,7 @@ bool schedule_ok(const ds_lr_schedule& q)
 // schedule's peak).
 ds_status adam_step(const ds_scaler* st, float* master, float* m, float* v, uint16_t* p16,
                     ds_dtype pdt, const void* grad, ds_dtype dt, int64_t n, const AdamHyper& hp,
-                    void* stream)
+                    bool fuse, void* stream)
 {
     const float beta1 = hp.beta1, beta2 = hp.beta2, eps = hp.eps;
     const float weight_decay = hp.weight_decay, max_grad_norm = hp.max_grad_norm;
@@ -898,8 +916,14 @@ ds_status adam_step(const ds_scaler* st, float* master, float* m, float* v, uint
         return DS_ERR_HPARAM;
     if (st == nullptr)
         return DS_ERR_NULL;
-    if (n == 0)
-        return DS_OK;
+    if (n == 0) {
+        if (!fuse)
+            return DS_OK;
+        if (!aligned(st, 8))
+            return DS_ERR_ALIGN;
+        update_scale_kernel<<<1, 1, 0, static_cast<hipStream_t>(stream)>>>(const_cast<ds_scaler*>(st));
+        return launched();
+    }
     if (master == nullptr || m == nullptr || v == nullptr || p16 == nullptr || grad == nullptr)
         return DS_ERR_NULL;
     if (!aligned(master, 16) || !aligned(m, 16) || !aligned(v, 16) || !aligned(p16, 16) ||
@@ -914,12 +938,12 @@ ds_status adam_step(const ds_scaler* st, float* master, float* m, float* v, uint
                 return DS_ERR_ALIAS;
 
     hipStream_t s = static_cast<hipStream_t>(stream);
-    const int unroll = variant_unroll();
+    const int unroll = fuse ? 4 : variant_unroll();
     const unsigned blocks = grid_blocks(tiles_of(n, unroll));
     const bool nt = variant_nt(n);
     const bool wd = weight_decay != 0.0f;
-    const AdamArgs args{st, master, m, v, p16, grad, n, hp};
-    launch_adam(fmt_of(dt), fmt_of(pdt), wd, nt, unroll, blocks, s, args);
+    const AdamArgs args{const_cast<ds_scaler*>(st), master, m, v, p16, grad, n, hp};
+    launch_adam(fmt_of(dt), fmt_of(pdt), wd, nt, unroll, fuse, blocks, s, args);
     return launched();
 }
 
@@ -990,7 +1014,9 @@ ds_status ds_state_write(ds_scaler* st, const ds_scaler* host_in, void* stream)
         return DS_ERR_NULL;
     if (!aligned(st, 8))
         return DS_ERR_ALIGN;
-    write_state_kernel<<<1, 1, 0, static_cast<hipStream_t>(stream)>>>(st, *host_in);
+    ds_scaler value = *host_in;
+    value.blocks_done = 0u;   // between steps the fused form's block count is 0
+    write_state_kernel<<<1, 1, 0, static_cast<hipStream_t>(stream)>>>(st, value);
     return launched();
 }
 
@@ -1058,7 +1084,7 @@ ds_status ds_adam_step(const ds_scaler* st, float* master, float* m, float* v, u
                        int32_t accum_steps, void* stream)
 {
     const AdamHyper hp{lr, beta1, beta2, eps, weight_decay, max_grad_norm, accum_steps, 0, 0.0f, 0, 0};
-    return adam_step(st, master, m, v, p16, pdt, grad, dt, n, hp, stream);
+    return adam_step(st, master, m, v, p16, pdt, grad, dt, n, hp, false, stream);
 }
 
 ds_status ds_adam_step_sched(const ds_scaler* st, float* master, float* m, float* v, uint16_t* p16,
@@ -1073,7 +1099,24 @@ ds_status ds_adam_step_sched(const ds_scaler* st, float* master, float* m, float
         return DS_ERR_HPARAM;
     const AdamHyper hp{sched->warmup_max_lr, beta1, beta2, eps, weight_decay, max_grad_norm, accum_steps,
                  sched->kind, sched->warmup_min_lr, sched->warmup_num_steps, sched->total_num_steps};
-    return adam_step(st, master, m, v, p16, pdt, grad, dt, n, hp, stream);
+    return adam_step(st, master, m, v, p16, pdt, grad, dt, n, hp, false, stream);
+}
+
+ds_status ds_adam_step_fused(ds_scaler* st, float* master, float* m, float* v, uint16_t* p16, ds_dtype pdt,
+                             const void* grad, ds_dtype dt, int64_t n, float lr,
+                             const ds_lr_schedule* sched_or_null, float beta1, float beta2, float eps,
+                             float weight_decay, float max_grad_norm, int32_t accum_steps, void* stream)
+{
+    if (sched_or_null != nullptr) {
+        if (!schedule_ok(*sched_or_null))
+            return DS_ERR_HPARAM;
+        const ds_lr_schedule& q = *sched_or_null;
+        const AdamHyper hp{q.warmup_max_lr, beta1, beta2, eps, weight_decay, max_grad_norm, accum_steps,
+                           q.kind, q.warmup_min_lr, q.warmup_num_steps, q.total_num_steps};
+        return adam_step(st, master, m, v, p16, pdt, grad, dt, n, hp, true, stream);
+    }
+    const AdamHyper hp{lr, beta1, beta2, eps, weight_decay, max_grad_norm, accum_steps, 0, 0.0f, 0, 0};
+    return adam_step(st, master, m, v, p16, pdt, grad, dt, n, hp, true, stream);
 }
 
 size_t ds_sumsq_workspace_bytes(int64_t n)

@@ -6,15 +6,17 @@ the C ABI on one HIP stream ("DeepSpeed complete guide" section 5.1: backward
 scales and accumulates, step() updates):
 
     K > 1:  ds_accumulate per bucket for micro-batches 1..K (the last one also
-            checks for inf/NaN), then ds_adam_step on the fp32 buffer
-    K = 1:  ds_check_overflow on the fp16 gradient, then ds_adam_step on it
-    then    ds_update_loss_scale (once)
+            checks for inf/NaN), then the Adam step on the fp32 buffer
+    K = 1:  ds_check_overflow on the fp16 gradient, then the Adam step on it
+
+The Adam step covers the whole partition in one ds_adam_step_fused call,
+whose kernel also advances the loss scaler (ds_update_loss_scale's work).
 
 With gradient clipping configured the check passes are the _sumsq variants
 (ds_accumulate_sumsq / ds_check_overflow_sumsq), which also gather the
-gradient's sum of squares for ds_adam_step's global-norm clipping.  With a
-scheduler block the update is ds_adam_step_sched, which reads the learning
-rate of the schedule on the device.
+gradient's sum of squares for the Adam step's global-norm clipping.  With a
+scheduler block the Adam step reads the learning rate of the schedule on the
+device.
 
 No call synchronises the host; ``scaler()`` reads the state back (one copy).
 ``save_checkpoint``/``load_checkpoint`` write and restore the shard between
@@ -94,15 +96,10 @@ class ShardStep:
         else:
             assert self._micro == self.K, "accumulate() must be called K times before step()"
             grad, dt = self.acc, _lib.DS_FP32
-        if self.sched is not None:
-            _lib.ds_adam_step_sched(self.state, self.master, self.m, self.v, self.p16, self.pdt, grad, dt,
-                                    self.n, self.sched, c.betas[0], c.betas[1], c.eps, c.weight_decay,
-                                    c.gradient_clipping, self.K, self.stream)
-        else:
-            _lib.ds_adam_step(self.state, self.master, self.m, self.v, self.p16, self.pdt, grad, dt, self.n,
-                              c.lr, c.betas[0], c.betas[1], c.eps, c.weight_decay, c.gradient_clipping,
-                              self.K, self.stream)
-        _lib.ds_update_loss_scale(self.state, self.stream)
+        # the whole partition in one call: the Adam kernel also advances the scaler
+        _lib.ds_adam_step_fused(self.state, self.master, self.m, self.v, self.p16, self.pdt, grad, dt, self.n,
+                                c.lr, self.sched, c.betas[0], c.betas[1], c.eps, c.weight_decay,
+                                c.gradient_clipping, self.K, self.stream)
         self._micro = 0
 
     def full_step(self, grads) -> None:
