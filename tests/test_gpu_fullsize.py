@@ -43,7 +43,7 @@ def sample_indices(w, buckets):
     return np.unique(np.concatenate(parts).astype(np.int64))
 
 
-def run_sampled(torch, name):
+def run_sampled(torch, name, fused=False):
     from zero_mixed_precision_amd import _lib, FlatLayout
 
     w = WORKLOADS[name]
@@ -56,7 +56,7 @@ def run_sampled(torch, name):
     else:
         buckets = [(0, n)]
     I = sample_indices(w, buckets)
-    gu.say(f"[{name}] psi={n} K={K} steps={w.steps} sample={I.size}")
+    gu.say(f"[{name}] psi={n} K={K} steps={w.steps} sample={I.size} fused={fused}")
 
     # oracle state on the sample
     o = oracle.State(synth.host_master32(w.master_key(), I, MASTER_SIGMA), np.zeros(I.size, np.float32),
@@ -93,13 +93,18 @@ def run_sampled(torch, name):
                                        k == 0, st if k == K - 1 else None)
         if K == 1:
             _lib.ds_check_overflow(st, g16, _lib.DS_FP16, n)
-            _lib.ds_adam_step(st, master, m, v, p16, _lib.DS_FP16, g16, _lib.DS_FP16, n, LR, BETA1, BETA2, EPS, 0.0, 0.0, 1)
+        grad, dt = (g16, _lib.DS_FP16) if K == 1 else (acc, _lib.DS_FP32)
+        if fused:   # one kernel: Adam, then the last block to finish advances the scaler
+            _lib.ds_adam_step_fused(st, master, m, v, p16, _lib.DS_FP16, grad, dt, n, LR, None, BETA1, BETA2, EPS,
+                                    0.0, 0.0, K)
         else:
-            _lib.ds_adam_step(st, master, m, v, p16, _lib.DS_FP16, acc, _lib.DS_FP32, n, LR, BETA1, BETA2, EPS, 0.0, 0.0, K)
-        _lib.ds_update_loss_scale(st)
+            _lib.ds_adam_step(st, master, m, v, p16, _lib.DS_FP16, grad, dt, n, LR, BETA1, BETA2, EPS, 0.0, 0.0, K)
+            _lib.ds_update_loss_scale(st)
         ov = oracle.step(o, gs_host if K > 1 else gs_host[0], **HP)
         assert ov == (inj is not None), f"[{name}] step {s}: oracle flag"
-        gu.check_scaler(_lib.ds_state_read(st), o.scaler, ov, f"[{name}] step {s}")
+        got = _lib.ds_state_read(st)
+        gu.check_scaler(got, o.scaler, ov, f"[{name}] step {s}")
+        assert got.blocks_done == 0, f"[{name}] step {s}: block count not reset"
         if s in (1, w.steps // 2, w.steps):
             du = gu.compare_arrays(f"[{name}] step {s}", gu.host_f32(master[Id]), gu.host_f32(m[Id]),
                                    gu.host_f32(v[Id]), gu.host_u16(p16[Id]), o.master, o.m, o.v, o.p16)
@@ -128,3 +133,15 @@ def test_ragged_layout_with_accumulation(torch):
 def test_zero1_shard_of_70b_heavy_tail(torch):
     sc = run_sampled(torch, "zero1_70b")
     assert sc.applied == 10 and sc.scale == 2.0 ** 18
+
+
+def test_zero1_shard_of_70b_fused_scaler_update(torch):
+    """The fused Adam + scaler-update kernel at 8.75e9 elements (about 2.1 million
+    blocks, each taking one ticket)."""
+    sc = run_sampled(torch, "zero1_70b", fused=True)
+    assert sc.applied == 10 and sc.scale == 2.0 ** 18
+
+
+def test_ragged_layout_fused_scaler_update(torch):
+    sc = run_sampled(torch, "ragged", fused=True)
+    assert sc.applied == 27 and sc.scale == 2.0 ** 14
