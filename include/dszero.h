@@ -60,9 +60,16 @@
 
 #ifdef __cplusplus
 extern "C" {
+/* A C caller may pass any int where an enum is expected; giving the enums a
+ * fixed underlying type makes every such value representable in C++ (so the
+ * library can reject it as DS_ERR_DTYPE and the like) with the same 4-byte
+ * layout as the C enums. */
+#define DS_ENUM_BASE : int32_t
+#else
+#define DS_ENUM_BASE
 #endif
 
-typedef enum ds_status {
+typedef enum ds_status DS_ENUM_BASE {
     DS_OK = 0,
     DS_ERR_NULL = 1,
     DS_ERR_SIZE = 2,
@@ -73,7 +80,7 @@ typedef enum ds_status {
     DS_ERR_HIP = 7
 } ds_status;
 
-typedef enum ds_dtype { DS_FP16 = 1, DS_FP32 = 2, DS_BF16 = 3 } ds_dtype;
+typedef enum ds_dtype DS_ENUM_BASE { DS_FP16 = 1, DS_FP32 = 2, DS_BF16 = 3 } ds_dtype;
 
 /*
  * Per-step device state, 128 bytes, kept in caller-owned DEVICE memory so that
@@ -208,7 +215,7 @@ ds_status ds_adam_step(const ds_scaler* st, float* master, float* m, float* v, u
  * warmup_num_steps >= 0, and for DS_LR_WARMUP_DECAY total_num_steps >=
  * warmup_num_steps; anything else is DS_ERR_HPARAM.
  */
-typedef enum ds_lr_kind { DS_LR_WARMUP = 1, DS_LR_WARMUP_DECAY = 2 } ds_lr_kind;
+typedef enum ds_lr_kind DS_ENUM_BASE { DS_LR_WARMUP = 1, DS_LR_WARMUP_DECAY = 2 } ds_lr_kind;
 
 typedef struct ds_lr_schedule {
     int32_t kind;             /* ds_lr_kind */

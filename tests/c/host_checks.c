@@ -1,0 +1,177 @@
+/*
+ * host_checks.c -- every host-only path of libdszero.so, for a build with the
+ * host AddressSanitizer and UndefinedBehaviorSanitizer (device code is built
+ * as usual; no GPU is used): argument validation of every entry point (each
+ * call below fails before any device work), the layout and partition
+ * routines on the ragged Llama-like layout and on random layouts, and the
+ * status strings.  Exit status 0 when every expectation holds; the
+ * sanitizers abort on any memory or undefined-behaviour error.
+ */
+#include <stdint.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include "dszero.h"
+
+static int failures = 0;
+
+#define EXPECT(cond)                                                   \
+    do {                                                               \
+        if (!(cond)) {                                                 \
+            fprintf(stderr, "%s:%d: %s\n", __FILE__, __LINE__, #cond); \
+            ++failures;                                                \
+        }                                                              \
+    } while (0)
+
+/* fake device addresses: never dereferenced, every call below is rejected */
+#define A ((void*)(uintptr_t)0x10000000u)
+#define B ((void*)(uintptr_t)0x20000000u)
+#define C ((void*)(uintptr_t)0x30000000u)
+#define D ((void*)(uintptr_t)0x40000000u)
+#define E ((void*)(uintptr_t)0x50000000u)
+#define ST ((ds_scaler*)(uintptr_t)0x60000000u)
+
+static void validation(void)
+{
+    float* f = (float*)A;
+    EXPECT(ds_adam_step(ST, f, (float*)B, (float*)C, (uint16_t*)D, DS_FP16, E, DS_FP16, -1, 1e-4f, 0.9f, 0.999f,
+                        1e-8f, 0.0f, 0.0f, 1, NULL) == DS_ERR_SIZE);
+    EXPECT(ds_adam_step(ST, f, (float*)B, (float*)C, (uint16_t*)D, DS_FP32, E, DS_FP16, 8, 1e-4f, 0.9f, 0.999f,
+                        1e-8f, 0.0f, 0.0f, 1, NULL) == DS_ERR_DTYPE);
+    EXPECT(ds_adam_step(ST, f, (float*)B, (float*)C, (uint16_t*)D, DS_FP16, E, DS_FP16, 8, 1e-4f, 1.0f, 0.999f,
+                        1e-8f, 0.0f, 0.0f, 1, NULL) == DS_ERR_HPARAM);
+    EXPECT(ds_adam_step(NULL, f, (float*)B, (float*)C, (uint16_t*)D, DS_FP16, E, DS_FP16, 8, 1e-4f, 0.9f, 0.999f,
+                        1e-8f, 0.0f, 0.0f, 1, NULL) == DS_ERR_NULL);
+    EXPECT(ds_adam_step(ST, f + 1, (float*)B, (float*)C, (uint16_t*)D, DS_FP16, E, DS_FP16, 8, 1e-4f, 0.9f,
+                        0.999f, 1e-8f, 0.0f, 0.0f, 1, NULL) == DS_ERR_ALIGN);
+    EXPECT(ds_adam_step(ST, f, f + 4, (float*)C, (uint16_t*)D, DS_FP16, E, DS_FP16, 8, 1e-4f, 0.9f, 0.999f,
+                        1e-8f, 0.0f, 0.0f, 1, NULL) == DS_ERR_ALIAS);
+    EXPECT(ds_adam_step(ST, f, (float*)B, (float*)C, (uint16_t*)D, DS_FP16, E, DS_FP16, 0, 1e-4f, 0.9f, 0.999f,
+                        1e-8f, 0.0f, 0.0f, 1, NULL) == DS_OK);
+    EXPECT(ds_adam_step_fused(ST, f, (float*)B, (float*)C, (uint16_t*)D, DS_FP16, E, DS_FP16, -1, 1e-4f, NULL,
+                              0.9f, 0.999f, 1e-8f, 0.0f, 0.0f, 1, NULL) == DS_ERR_SIZE);
+    ds_lr_schedule bad = {7, 0, 10, 20, 0.0f, 1e-3f};
+    EXPECT(ds_adam_step_sched(ST, f, (float*)B, (float*)C, (uint16_t*)D, DS_FP16, E, DS_FP16, 8, &bad, 0.9f,
+                              0.999f, 1e-8f, 0.0f, 0.0f, 1, NULL) == DS_ERR_HPARAM);
+    EXPECT(ds_adam_step_sched(ST, f, (float*)B, (float*)C, (uint16_t*)D, DS_FP16, E, DS_FP16, 8, NULL, 0.9f,
+                              0.999f, 1e-8f, 0.0f, 0.0f, 1, NULL) == DS_ERR_NULL);
+    EXPECT(ds_accumulate(f, (uint16_t*)B, DS_FP32, 8, 1, NULL, NULL) == DS_ERR_DTYPE);
+    EXPECT(ds_accumulate(f, (uint16_t*)f + 2, DS_FP16, 8, 1, NULL, NULL) == DS_ERR_ALIGN);
+    EXPECT(ds_accumulate(f, (uint16_t*)(f + 4), DS_FP16, 64, 1, NULL, NULL) == DS_ERR_ALIAS);
+    EXPECT(ds_check_overflow(ST, E, (ds_dtype)9, 8, NULL) == DS_ERR_DTYPE);
+    EXPECT(ds_check_overflow(ST, (char*)E + 8, DS_FP16, 8, NULL) == DS_ERR_ALIGN);
+    const size_t ws = ds_sumsq_workspace_bytes(100000);
+    EXPECT(ws == 8 * 25);
+    EXPECT(ds_check_overflow_sumsq(ST, E, DS_FP16, 100000, A, ws - 8, NULL) == DS_ERR_SIZE);
+    EXPECT(ds_accumulate_sumsq(f, (uint16_t*)B, DS_FP16, 100000, 1, ST, NULL, ws, NULL) == DS_ERR_NULL);
+    EXPECT(ds_state_init(ST, 0.0f, 1.0f, 1000, 1, 0, 1, NULL) == DS_ERR_HPARAM);
+    EXPECT(ds_state_init((ds_scaler*)((char*)ST + 4), 65536.0f, 1.0f, 1000, 1, 0, 1, NULL) == DS_ERR_ALIGN);
+    EXPECT(ds_update_loss_scale(NULL, NULL) == DS_ERR_NULL);
+    EXPECT(ds_adam_bias_scalars(ST, 1e-4f, 0.9f, 1.5f, (float*)A, NULL) == DS_ERR_HPARAM);
+    ds_lr_schedule good = {DS_LR_WARMUP_DECAY, 0, 2000, 100000, 0.0f, 3e-4f};
+    EXPECT(ds_lr_scalars(ST, &good, 0.9f, 0.999f, (float*)((char*)ST + 8), NULL) == DS_ERR_ALIAS);
+    for (int s = -2; s < 10; ++s)
+        EXPECT(ds_status_string((ds_status)s) != NULL && strlen(ds_status_string((ds_status)s)) > 0);
+    EXPECT(ds_scaler_size() == 128);
+}
+
+/* The layout rule: tensors keep their order, each starts aligned, a bucket
+ * holds whole tensors, and the buckets tile [0, total). */
+static void check_layout(const int64_t* numels, int32_t count, int64_t cap, int64_t align)
+{
+    int64_t* offsets = malloc(sizeof(int64_t) * (size_t)(count > 0 ? count : 1));
+    int32_t* bucket_of = malloc(sizeof(int32_t) * (size_t)(count > 0 ? count : 1));
+    int64_t* bstart = malloc(sizeof(int64_t) * (size_t)(count > 0 ? count : 1));
+    int64_t* bsize = malloc(sizeof(int64_t) * (size_t)(count > 0 ? count : 1));
+    int32_t nb = -1;
+    int64_t total = -1;
+    EXPECT(ds_layout_greedy(numels, count, cap, align, offsets, bucket_of, bstart, bsize, &nb, &total) == DS_OK);
+    EXPECT(nb >= 0 && nb <= (count > 0 ? count : 0));
+    int64_t covered = 0;
+    for (int32_t b = 0; b < nb; ++b) {
+        EXPECT(bstart[b] == covered);
+        covered += bsize[b];
+    }
+    EXPECT(covered == total);
+    for (int32_t i = 0; i < count; ++i) {
+        EXPECT(offsets[i] % align == 0);
+        EXPECT(i == 0 || offsets[i] >= offsets[i - 1] + numels[i - 1]);
+        const int32_t b = bucket_of[i];
+        EXPECT(b >= 0 && b < nb);
+        if (b >= 0 && b < nb)
+            EXPECT(offsets[i] >= bstart[b] && offsets[i] + numels[i] <= bstart[b] + bsize[b]);
+    }
+    free(offsets);
+    free(bucket_of);
+    free(bstart);
+    free(bsize);
+}
+
+static uint64_t rng_state = 20261202u;
+static uint64_t next_u64(void)
+{
+    /* SplitMix64 */
+    uint64_t z = (rng_state += 0x9E3779B97F4A7C15ull);
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+    return z ^ (z >> 31);
+}
+
+static void layouts(void)
+{
+    /* the ragged Llama-like layout: 32 layers of q, k, v, o, gate, up, down, two norms */
+    int64_t ragged[32 * 9];
+    for (int l = 0; l < 32; ++l) {
+        const int64_t h = 4096, f = 11008;
+        const int64_t t[9] = {h * h, h * h, h * h, h * h, f * h, f * h, f * h, h, h};
+        memcpy(ragged + 9 * l, t, sizeof t);
+    }
+    check_layout(ragged, 32 * 9, 200000000, 64);
+    int32_t nb = 0;
+    int64_t total = 0;
+    int64_t offsets[32 * 9], bstart[32 * 9], bsize[32 * 9];
+    int32_t bof[32 * 9];
+    EXPECT(ds_layout_greedy(ragged, 32 * 9, 200000000, 64, offsets, bof, bstart, bsize, &nb, &total) == DS_OK);
+    EXPECT(nb == 38 && total == 6476267520ll);
+    for (int trial = 0; trial < 300; ++trial) {
+        const int32_t count = (int32_t)(next_u64() % 50);
+        int64_t numels[50];
+        for (int32_t i = 0; i < count; ++i)
+            numels[i] = (int64_t)(next_u64() % 5000);
+        check_layout(numels, count, 1 + (int64_t)(next_u64() % 9000), 1 + (int64_t)(next_u64() % 128));
+    }
+    int64_t neg[2] = {5, -1};
+    EXPECT(ds_layout_greedy(neg, 2, 100, 8, offsets, bof, bstart, bsize, &nb, &total) == DS_ERR_SIZE);
+    EXPECT(ds_layout_greedy(NULL, 0, 100, 8, NULL, NULL, NULL, NULL, &nb, &total) == DS_OK && nb == 0 && total == 0);
+    /* partitions tile [0, total) */
+    for (int trial = 0; trial < 300; ++trial) {
+        const int64_t tot = (int64_t)(next_u64() % 100000);
+        const int32_t world = 1 + (int32_t)(next_u64() % 70);
+        const int64_t align = 1 + (int64_t)(next_u64() % 64);
+        int64_t end = 0;
+        for (int32_t r = 0; r < world; ++r) {
+            int64_t start = -1, count = -1;
+            EXPECT(ds_partition_range(tot, world, r, align, &start, &count) == DS_OK);
+            EXPECT(count >= 0 && (count == 0 || start == end));
+            if (count > 0)
+                end = start + count;
+        }
+        EXPECT(end == tot);
+    }
+    int64_t s0, c0;
+    EXPECT(ds_partition_range(10, 0, 0, 8, &s0, &c0) == DS_ERR_SIZE);
+    EXPECT(ds_partition_range(10, 4, 4, 8, &s0, &c0) == DS_ERR_SIZE);
+}
+
+int main(void)
+{
+    validation();
+    layouts();
+    if (failures != 0) {
+        fprintf(stderr, "host_checks: %d expectation(s) failed\n", failures);
+        return 1;
+    }
+    printf("host_checks: all host paths ok\n");
+    return 0;
+}
