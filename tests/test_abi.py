@@ -293,6 +293,41 @@ def test_config_rejects_auto_and_other_optimizers():
         ZeroMPConfig.from_dict({"fp16": {"enabled": False}})
 
 
+def test_config_scheduler_block_from_the_pages():
+    g = json.load(open(os.path.join(GOLDEN, "scheduler_config.json")))
+    cfg = ZeroMPConfig.from_dict({"scheduler": g["scheduler_section_4_4"]})
+    assert (cfg.scheduler, cfg.warmup_min_lr, cfg.warmup_max_lr) == ("WarmupDecayLR", 0.0, 3e-4)
+    assert (cfg.warmup_num_steps, cfg.total_num_steps) == (2000, 100000)
+    sch = cfg.lr_schedule()
+    assert (sch.kind, sch.warmup_num_steps, sch.total_num_steps) == (_lib.DS_LR_WARMUP_DECAY, 2000, 100000)
+    assert abs(sch.warmup_max_lr - 3e-4) < 1e-10 and sch.warmup_min_lr == 0.0 and sch.reserved == 0
+    warm = ZeroMPConfig.from_dict({"scheduler": {"type": "WarmupLR", "params": {"warmup_max_lr": 1e-3,
+                                                                             "warmup_num_steps": 10}}})
+    assert warm.lr_schedule().kind == _lib.DS_LR_WARMUP and warm.warmup_min_lr == 0.0
+    assert ZeroMPConfig.from_dict({}).lr_schedule() is None
+    # the section 4.1 block resolves its values through a trainer ("auto"): rejected here
+    with pytest.raises(ValueError, match="auto"):
+        ZeroMPConfig.from_dict({"scheduler": g["scheduler_section_4_1"]})
+    # types the guide names without parameters or formula
+    for kind in g["supported_types_section_4_4"]:
+        if kind not in ("WarmupLR", "WarmupDecayLR"):
+            with pytest.raises(ValueError, match="without its parameters"):
+                ZeroMPConfig.from_dict({"scheduler": {"type": kind, "params": {}}})
+    bad_params = [
+        {"type": "Cosine", "params": {"warmup_max_lr": 1e-3, "warmup_num_steps": 1}},
+        {"type": "WarmupLR", "params": {"warmup_num_steps": 1}},
+        {"type": "WarmupDecayLR", "params": {"warmup_max_lr": 1e-3, "warmup_num_steps": 1}},
+        {"type": "WarmupLR", "params": {"warmup_max_lr": 1e-3, "warmup_num_steps": 1, "warmup_type": "log"}},
+        {"type": "WarmupLR", "params": {"warmup_max_lr": 1e-3, "warmup_num_steps": 1, "last_batch_iteration": 5}},
+        {"type": "WarmupDecayLR", "params": {"warmup_max_lr": 1e-3, "warmup_num_steps": 10,
+                                             "total_num_steps": 5}},
+        {"type": "WarmupLR", "params": {"warmup_max_lr": -1e-3, "warmup_num_steps": 1}},
+    ]
+    for blk in bad_params:
+        with pytest.raises(ValueError):
+            ZeroMPConfig.from_dict({"scheduler": blk})
+
+
 def test_batch_relation_from_the_pages():
     g = json.load(open(os.path.join(GOLDEN, "batch_relation.json")))
     cfg = ZeroMPConfig.from_dict({k: g[k] for k in ("train_micro_batch_size_per_gpu",
