@@ -13,6 +13,7 @@ moments), section 4.1 (optimizer AdamW, eps 1e-8), section 5.1 (step()
 updates the parameters after backward).
 """
 from decimal import Decimal, getcontext
+from fractions import Fraction
 
 import numpy as np
 import pytest
@@ -192,6 +193,114 @@ def test_sixteen_elements_match_per_operation_fp32(oracle_lib):
             assert f32_bits(pe) == f32_bits(po[i]) and f32_bits(me) == f32_bits(mo[i]) \
                 and f32_bits(ve) == f32_bits(vo[i]), (trial, i)
         assert np.array_equal(p16, po.astype(np.float16).view(np.uint16))
+
+
+# -- exact rational arithmetic, rounded by hand -----------------------------------
+
+def _round_binary(x: Fraction, mant_bits: int, emin: int, emax: int) -> Fraction:
+    """x rounded to nearest, ties to even, in a binary format with `mant_bits`
+    fraction bits and normal exponents emin..emax (subnormals kept; overflow is
+    not reached by these inputs and raises)."""
+    if x == 0:
+        return Fraction(0)
+    sign, a = (-1, -x) if x < 0 else (1, x)
+    e = a.numerator.bit_length() - a.denominator.bit_length()      # 2^e <= a < 2^(e+1) after the fix-up
+    if Fraction(2) ** e > a:
+        e -= 1
+    elif Fraction(2) ** (e + 1) <= a:
+        e += 1
+    quantum = Fraction(2) ** (max(e, emin) - mant_bits)             # spacing of representable values near a
+    scaled = a / quantum
+    n = scaled.numerator // scaled.denominator
+    rest = scaled - n
+    if rest > Fraction(1, 2) or (rest == Fraction(1, 2) and n % 2 == 1):
+        n += 1
+    v = n * quantum
+    if v >= Fraction(2) ** (emax + 1):
+        raise OverflowError("rounds to infinity")
+    return sign * v
+
+
+def _f32(x: Fraction) -> Fraction:
+    return _round_binary(x, 23, -126, 127)
+
+
+def _f16(x: Fraction) -> Fraction:
+    return _round_binary(x, 10, -14, 15)
+
+
+def _sqrt_f32(x: Fraction) -> Fraction:
+    """Correctly rounded fp32 square root of an fp32 value x >= 0, by integer square
+    roots: the exact root lies in [s, s + 1) * 2^-k, narrow enough that both ends
+    round alike unless the root is exact."""
+    from math import isqrt
+    if x == 0:
+        return Fraction(0)
+    k = 200
+    scaled = x * Fraction(2) ** (2 * k)
+    assert scaled.denominator == 1                                   # x is dyadic with < 400 fraction bits
+    s = isqrt(scaled.numerator)
+    lo, hi = Fraction(s, 2 ** k), Fraction(s + 1, 2 ** k)
+    if s * s == scaled.numerator:
+        return _f32(lo)
+    r = _f32(lo)
+    assert r == _f32(hi) or lo < r < hi, "rounding boundary inside the bracket"
+    return r
+
+
+def _exact_update(graw, p, m, v, *, inv, step_size, rbc2, omb1, omb2, b1, b2, eps, lrwd=None):
+    """One element of the bias-corrected Adam update, every operation exact then rounded
+    to fp32 (no shared rounding, no fused multiply-add), in the oracle's written order."""
+    g = _f32(graw * inv)
+    m = _f32(_f32(b1 * m) + _f32(omb1 * g))
+    v = _f32(_f32(b2 * v) + _f32(omb2 * _f32(g * g)))
+    if lrwd is not None:
+        p = _f32(p - _f32(lrwd * p))
+    den = _f32(_f32(_sqrt_f32(v) * rbc2) + eps)
+    p = _f32(p - _f32(step_size * _f32(m / den)))
+    return p, m, v
+
+
+@pytest.mark.parametrize("wd", [0.0, 0.01])
+def test_sixteen_elements_match_exact_rational_evaluation(oracle_lib, wd):
+    """The compiled oracle equals an exact rational re-evaluation of the update rounded
+    to fp32 by hand after every operation (binary16 for the parameter copy), bit for bit,
+    on 16-element inputs over three steps: no contraction, no extra precision, and the
+    IEEE rounding of divide and square root."""
+    rng = np.random.default_rng(15)
+    Q = lambda x: Fraction(float(x))                                 # exact value of a float
+    f = np.float32
+    for trial in range(12):
+        n = 16
+        p = rng.normal(0, 0.02, n).astype(np.float32)
+        m = rng.normal(0, 1e-4, n).astype(np.float32)
+        v = np.abs(rng.normal(0, 1e-7, n)).astype(np.float32)
+        scale = 2.0 ** int(rng.integers(0, 20)) * (1.0 if trial % 3 else 1.5)   # some scales not powers of two
+        K = int(rng.choice([1, 3, 8]))
+        state = oracle.State(p.copy(), m.copy(), v.copy(), np.zeros(n, np.uint16),
+                             oracle.Scaler(float(f(scale)), 1.0, 1000, 1))
+        ep, em, ev = [Q(x) for x in p], [Q(x) for x in m], [Q(x) for x in v]
+        for step in range(3):
+            grads = [(_all_finite_fp16_patterns(rng, n) if (trial + k) % 2 else _grads16(rng, n, scale=scale))
+                     for k in range(K)]
+            t = state.scaler.applied + 1
+            assert not oracle.step(state, grads if K > 1 else grads[0], lr=LR, beta1=B1, beta2=B2, eps=EPS,
+                                   weight_decay=wd)
+            step_size, rbc2 = oracle.adam_scalars(t, LR, B1, B2)
+            S = Q(f(scale))
+            kw = dict(inv=_f32(1 / _f32(S * K)), step_size=Q(step_size), rbc2=Q(rbc2),
+                      omb1=_f32(1 - Q(f(B1))), omb2=_f32(1 - Q(f(B2))), b1=Q(f(B1)), b2=Q(f(B2)), eps=Q(f(EPS)),
+                      lrwd=_f32(Q(f(LR)) * Q(f(wd))) if wd else None)
+            for i in range(n):
+                gsum = Fraction(0)
+                for k in range(K):                                   # the fp32 sum over micro-batches, in order
+                    gk = Q(grads[k].view(np.float16)[i])
+                    gsum = gk if k == 0 else _f32(gsum + gk)
+                ep[i], em[i], ev[i] = _exact_update(gsum, ep[i], em[i], ev[i], **kw)
+            got = [(Q(a), Q(b), Q(c)) for a, b, c in zip(state.master, state.m, state.v)]
+            assert got == list(zip(ep, em, ev)), (trial, step)
+            want16 = [_f16(x) for x in ep]
+            assert [Q(x) for x in state.p16.view(np.float16)] == want16, (trial, step)
 
 
 # -- skip invariant on 16-element inputs -----------------------------------------
