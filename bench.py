@@ -192,7 +192,8 @@ def gpu_run(args):
 
     # the same steps replayed from HIP graphs: one graph per position in the
     # cycle of gradient buffers, each captured once (kernels only), replayed in
-    # order; this removes the host's per-launch cost, which bounds small shards
+    # order, and reported beside the eager rate (on short steps a replay costs
+    # more than the launches it replaces; on long ones it changes nothing)
     cycle = nbuf // math.gcd(nbuf, K)
     side = torch.cuda.Stream()
     side.wait_stream(stream)
