@@ -43,12 +43,17 @@ def sample_indices(w, buckets):
     return np.unique(np.concatenate(parts).astype(np.int64))
 
 
-def run_sampled(torch, name, fused=False):
+def run_sampled(torch, name, fused=False, bf16=False):
     from zero_mixed_precision_amd import _lib, FlatLayout
 
     w = WORKLOADS[name]
     n, K = w.psi, w.K
-    spec = w.grad_spec
+    # bf16 mode: bf16 gradients N(0, sigma) and bf16 parameter copy, no loss scaling (a static scale of 1)
+    spec = synth.GradSpec(w.sigma, 1.0, w.heavy_tail, fmt="bf16") if bf16 else w.grad_spec
+    fmt = "bf16" if bf16 else "fp16"
+    dt16 = _lib.DS_BF16 if bf16 else _lib.DS_FP16
+    init_scale, dynamic = (1.0, False) if bf16 else (w.init_scale, True)
+    inf16 = 0x7F80 if bf16 else 0x7C00
     if w.ragged:
         lay = FlatLayout(ragged_numels())
         assert lay.total == n
@@ -56,12 +61,12 @@ def run_sampled(torch, name, fused=False):
     else:
         buckets = [(0, n)]
     I = sample_indices(w, buckets)
-    gu.say(f"[{name}] psi={n} K={K} steps={w.steps} sample={I.size} fused={fused}")
+    gu.say(f"[{name}] psi={n} K={K} steps={w.steps} sample={I.size} fused={fused} {fmt}")
 
     # oracle state on the sample
     o = oracle.State(synth.host_master32(w.master_key(), I, MASTER_SIGMA), np.zeros(I.size, np.float32),
                      np.zeros(I.size, np.float32), synth.host_grad16(w.p16_key(), I, synth.GradSpec(0.02, 1.0)),
-                     oracle.Scaler(w.init_scale, w.min_scale, w.window, w.hysteresis))
+                     oracle.Scaler(init_scale, w.min_scale, w.window, w.hysteresis, dynamic=dynamic), param_fmt=fmt)
 
     # device state over the whole partition
     tabs = synth.DeviceTables(torch, "cuda:0")
@@ -74,7 +79,7 @@ def run_sampled(torch, name, fused=False):
     g16 = torch.empty(n, dtype=torch.int16, device="cuda:0")
     acc = torch.empty(n, dtype=torch.float32, device="cuda:0") if K > 1 else None
     st = torch.zeros(_lib.ds_scaler_size(), dtype=torch.uint8, device="cuda:0")
-    _lib.ds_state_init(st, w.init_scale, w.min_scale, w.window, w.hysteresis, 0, 1)
+    _lib.ds_state_init(st, init_scale, w.min_scale, w.window, w.hysteresis, 0, int(dynamic))
     Id = torch.from_numpy(I).to("cuda:0")
 
     for s in range(1, w.steps + 1):
@@ -84,23 +89,23 @@ def run_sampled(torch, name, fused=False):
             synth.device_fill_grad16(torch, tabs, g16, w.grad_key(s, k), spec)
             gh = synth.host_grad16(w.grad_key(s, k), I, spec)
             if inj is not None and inj[0] == k:
-                g16[inj[1]] = torch.tensor(0x7C00, dtype=torch.int32).to(torch.int16)
-                gh[np.searchsorted(I, inj[1])] = 0x7C00
+                g16[inj[1]] = torch.tensor(inf16, dtype=torch.int32).to(torch.int16)
+                gh[np.searchsorted(I, inj[1])] = inf16
             gs_host.append(gh)
             if K > 1:
                 for start, size in buckets:
-                    _lib.ds_accumulate(acc.data_ptr() + 4 * start, g16.data_ptr() + 2 * start, _lib.DS_FP16, size,
+                    _lib.ds_accumulate(acc.data_ptr() + 4 * start, g16.data_ptr() + 2 * start, dt16, size,
                                        k == 0, st if k == K - 1 else None)
         if K == 1:
-            _lib.ds_check_overflow(st, g16, _lib.DS_FP16, n)
-        grad, dt = (g16, _lib.DS_FP16) if K == 1 else (acc, _lib.DS_FP32)
+            _lib.ds_check_overflow(st, g16, dt16, n)
+        grad, dt = (g16, dt16) if K == 1 else (acc, _lib.DS_FP32)
         if fused:   # one kernel: Adam, then the last block to finish advances the scaler
-            _lib.ds_adam_step_fused(st, master, m, v, p16, _lib.DS_FP16, grad, dt, n, LR, None, BETA1, BETA2, EPS,
+            _lib.ds_adam_step_fused(st, master, m, v, p16, dt16, grad, dt, n, LR, None, BETA1, BETA2, EPS,
                                     0.0, 0.0, K)
         else:
-            _lib.ds_adam_step(st, master, m, v, p16, _lib.DS_FP16, grad, dt, n, LR, BETA1, BETA2, EPS, 0.0, 0.0, K)
+            _lib.ds_adam_step(st, master, m, v, p16, dt16, grad, dt, n, LR, BETA1, BETA2, EPS, 0.0, 0.0, K)
             _lib.ds_update_loss_scale(st)
-        ov = oracle.step(o, gs_host if K > 1 else gs_host[0], **HP)
+        ov = oracle.step(o, gs_host if K > 1 else gs_host[0], fmt=fmt, **HP)
         assert ov == (inj is not None), f"[{name}] step {s}: oracle flag"
         got = _lib.ds_state_read(st)
         gu.check_scaler(got, o.scaler, ov, f"[{name}] step {s}")
@@ -108,7 +113,7 @@ def run_sampled(torch, name, fused=False):
         if s in (1, w.steps // 2, w.steps):
             du = gu.compare_arrays(f"[{name}] step {s}", gu.host_f32(master[Id]), gu.host_f32(m[Id]),
                                    gu.host_f32(v[Id]), gu.host_u16(p16[Id]), o.master, o.m, o.v, o.p16)
-            gu.say(f"[{name}] step {s}: scale 2^{int(np.log2(o.scaler.scale))} applied {o.scaler.applied} "
+            gu.say(f"[{name}] {fmt} step {s}: scale 2^{int(np.log2(o.scaler.scale))} applied {o.scaler.applied} "
                    f"max ulp {du}")
     del master, m, v, p16, g16, acc, st
     torch.cuda.empty_cache()
@@ -145,3 +150,69 @@ def test_zero1_shard_of_70b_fused_scaler_update(torch):
 def test_ragged_layout_fused_scaler_update(torch):
     sc = run_sampled(torch, "ragged", fused=True)
     assert sc.applied == 27 and sc.scale == 2.0 ** 14
+
+
+def test_zero2_shard_of_7b_bf16_fused(torch):
+    """bf16 mode at the shard's full size (the launch bench.py --bf16 times): bf16
+    gradients and parameter copy, a static scale of 1, the fused scaler update."""
+    sc = run_sampled(torch, "zero2_7b", fused=True, bf16=True)
+    assert sc.applied == 50 and sc.scale == 1.0
+
+
+def test_full_7b_bf16_fused(torch):
+    sc = run_sampled(torch, "full_7b", fused=True, bf16=True)
+    assert sc.applied == 20 and sc.scale == 1.0
+
+
+def test_zero2_shard_of_7b_clipped(torch):
+    """Global-norm clipping at the shard's full size (the launch bench.py --clip 1.0
+    times).  The clipping coefficient depends on the whole gradient, so the host
+    generates all 109,375,000 gradient values once and takes their exact sum of
+    squares (oracle.grad_sumsq); the sampled elements are then updated with the
+    oracle's multiplier.  The same gradient is applied in each of three steps (the
+    state still moves every step); clipping is active (norm about 10, limit 1)."""
+    from zero_mixed_precision_amd import _lib
+
+    w = WORKLOADS["zero2_7b"]
+    n, max_norm, steps = w.psi, 1.0, 3
+    spec = w.grad_spec
+    I = sample_indices(w, [(0, n)])
+    key = w.grad_key(1, 0)
+    g_full = synth.host_grad16(key, np.arange(n), spec)
+    sumsq = oracle.grad_sumsq(g_full, "fp16")
+    gs = g_full[I]
+    del g_full
+    gu.say(f"[zero2_7b clipped] sumsq {sumsq:.6g}, unscaled norm {np.sqrt(sumsq) / w.init_scale:.4g}")
+
+    master0 = synth.host_master32(w.master_key(), I, MASTER_SIGMA)
+    o = oracle.State(master0, np.zeros(I.size, np.float32), np.zeros(I.size, np.float32),
+                     np.zeros(I.size, np.uint16), oracle.Scaler(w.init_scale, w.min_scale, w.window, w.hysteresis))
+    tabs = synth.DeviceTables(torch, "cuda:0")
+    master = torch.empty(n, dtype=torch.float32, device="cuda:0")
+    synth.device_fill_master32(torch, tabs, master, w.master_key(), MASTER_SIGMA)
+    m = torch.zeros(n, dtype=torch.float32, device="cuda:0")
+    v = torch.zeros(n, dtype=torch.float32, device="cuda:0")
+    p16 = torch.zeros(n, dtype=torch.int16, device="cuda:0")
+    g16 = torch.empty(n, dtype=torch.int16, device="cuda:0")
+    synth.device_fill_grad16(torch, tabs, g16, key, spec)
+    ws = torch.zeros((_lib.ds_sumsq_workspace_bytes(n) + 7) // 8, dtype=torch.float64, device="cuda:0")
+    st = torch.zeros(_lib.ds_scaler_size(), dtype=torch.uint8, device="cuda:0")
+    _lib.ds_state_init(st, w.init_scale, w.min_scale, w.window, w.hysteresis, 0, 1)
+    Id = torch.from_numpy(I).to("cuda:0")
+    for s in range(steps):
+        _lib.ds_check_overflow_sumsq(st, g16, _lib.DS_FP16, n, ws)
+        _lib.ds_adam_step_fused(st, master, m, v, p16, _lib.DS_FP16, g16, _lib.DS_FP16, n, LR, None, BETA1, BETA2,
+                                EPS, 0.0, max_norm, 1)
+        got = _lib.ds_state_read(st)
+        assert abs(got.last_grad_sumsq - sumsq) <= 1e-13 * sumsq, (got.last_grad_sumsq, sumsq)
+        mult = oracle.clip_multiplier(sumsq, o.scaler.scale, 1, max_norm)
+        assert mult < np.float32(1.0) / np.float32(w.init_scale)          # clipping is active
+        oracle.adam_mult(gs, o.master, o.m, o.v, o.p16, mult=mult, t=o.scaler.applied + 1, lr=LR, beta1=BETA1,
+                         beta2=BETA2, eps=EPS)
+        o.scaler.update(False)
+        gu.check_scaler(got, o.scaler, False, f"[zero2_7b clipped] step {s}")
+        du = gu.compare_arrays(f"[zero2_7b clipped] step {s}", gu.host_f32(master[Id]), gu.host_f32(m[Id]),
+                               gu.host_f32(v[Id]), gu.host_u16(p16[Id]), o.master, o.m, o.v, o.p16)
+        gu.say(f"[zero2_7b clipped] step {s}: max ulp {du}")
+    del master, m, v, p16, g16, ws, st
+    torch.cuda.empty_cache()
