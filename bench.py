@@ -18,7 +18,9 @@ the 8 TB/s HBM3E peak; ``traffic`` comes from the committed rocprofv3 counter
 summary when it was taken on the current kernel source; the median and minimum
 launch times and ``copy_mix_gbs`` (the same 14 B read + 14 B written per
 element with no arithmetic, on the same arrays, timed after the timed region)
-sit beside it.  ``graph_replay`` times the same steps replayed from HIP
+sit beside it; ``step_ms_*`` and ``pre_adam_ms_*`` (the check, or the
+accumulation with its fused check) come from an untimed pass with events
+around each part.  ``graph_replay`` times the same steps replayed from HIP
 graphs (one per position in the cycle of gradient buffers).  ``cpu_baseline`` times
 the CPU oracle on a bounded slice of the same workload.
 
@@ -124,7 +126,7 @@ def gpu_run(args):
         ws = torch.zeros((_lib.ds_sumsq_workspace_bytes(n) + 7) // 8, dtype=torch.float64, device=dev)
     ev = []
 
-    step_ev = []
+    step_ev, pre_ev = [], []   # whole steps; their check (K = 1) or accumulation + check (K > 1) part
 
     def one_step(i, timed, q=stream, whole=False):
         if whole:
@@ -148,6 +150,9 @@ def gpu_run(args):
                     else:
                         _lib.ds_accumulate(a, gp, gdt16, size, k == 0, st if k == K - 1 else None, q)
             gptr, dt = acc, _lib.DS_FP32
+        if whole:
+            c1 = torch.cuda.Event(enable_timing=True)
+            c1.record(q)
         if timed:
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a.record(q)
@@ -160,6 +165,7 @@ def gpu_run(args):
             s1 = torch.cuda.Event(enable_timing=True)
             s1.record(q)
             step_ev.append((s0, s1))
+            pre_ev.append((s0, c1))
 
     for i in range(args.warmup):
         one_step(i, False)
@@ -218,6 +224,7 @@ def gpu_run(args):
     adam_avg_s = sum(adam_ms) / len(adam_ms) / 1e3
     adam_sorted = sorted(adam_ms)
     step_sorted = sorted(a.elapsed_time(b) for a, b in step_ev)
+    pre_sorted = sorted(a.elapsed_time(b) for a, b in pre_ev)
 
     # achievable-bandwidth reference, after the timed region: the step's data
     # movement (14 B read + 14 B written per element) with no arithmetic, on the
@@ -250,6 +257,8 @@ def gpu_run(args):
         "ms_per_step": round(wall / args.steps * 1e3, 4),
         "step_ms_median": round(step_sorted[len(step_sorted) // 2], 4),
         "step_ms_min": round(step_sorted[0], 4),
+        "pre_adam_ms_median": round(pre_sorted[len(pre_sorted) // 2], 4),
+        "pre_adam_ms_min": round(pre_sorted[0], 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
