@@ -40,14 +40,17 @@
  *  - Per-step order on one stream: all ds_accumulate calls, then any number of
  *    ds_check_overflow calls (disjoint ranges), then any number of
  *    ds_adam_step calls (disjoint ranges, all reading the same state), then
- *    exactly one ds_update_loss_scale.  No host synchronisation is needed
- *    inside a step: the skip decision is taken on the device.
+ *    exactly one ds_update_loss_scale; or, for a partition updated by a
+ *    single call, one ds_adam_step_fused in place of both.  No host
+ *    synchronisation is needed inside a step: the skip decision is taken on
+ *    the device.
  *  - Thread safety: the library keeps no mutable global state.  Calls that
  *    share a ds_scaler must be ordered on one stream.
  *  - Launch-shape knobs, read from the environment at each call (for tests
  *    and tuning; results are bit-identical under every setting):
  *    DSZERO_GRID=<blocks> pins the block count, DSZERO_UNROLL=2|4 sets the
- *    quads per lane of the read/write kernels, DSZERO_NT=0|1 turns their
+ *    quads per lane of the read/write kernels (ds_adam_step_fused and the
+ *    sum-of-squares accumulation always use 4), DSZERO_NT=0|1 turns their
  *    non-temporal load/store hints off or on (default: on above 2^24
  *    elements, off at and below, where the state stays in the Infinity Cache
  *    between steps).
