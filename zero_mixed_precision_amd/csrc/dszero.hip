@@ -211,6 +211,14 @@ __device__ __forceinline__ double sq4(const f32x4& x)
     return ((sq(x.x) + sq(x.y)) + sq(x.z)) + sq(x.w);
 }
 
+// sq4 for values whose squares are exact in fp32 (widened fp16): the same
+// result, with the squares taken in fp32.
+__device__ __forceinline__ double sq4_exact32(const f32x4& x)
+{
+    return ((static_cast<double>(x.x * x.x) + static_cast<double>(x.y * x.y)) + static_cast<double>(x.z * x.z)) +
+           static_cast<double>(x.w * x.w);
+}
+
 // Second pass of the sum of squares: one block adds the chunk sums in a fixed
 // order (lane j takes chunks j, j + TPB, ..., then the fixed block sum) into
 // st->grad_sumsq.  The chunking is fixed by n, so the result does not depend
@@ -554,10 +562,13 @@ __global__ __launch_bounds__(TPB) void check_kernel(ds_scaler* __restrict__ st,
 }
 
 // Overflow check plus the chunk sums of squares.  A chunk is TPB lanes x
-// kVecs 16-byte vectors (fp16: 512 x 4 x 8, fp32: 1024 x 4 x 4 = 16,384
-// elements); vector j of lane l is vector j * TPB + l of the chunk, so each
-// of the kVecs loads is one contiguous span across the block, and each lane
-// sums its elements in order.
+// kVecs 16-byte vectors (16-bit formats: 1024 x 2 x 8, fp32: 1024 x 4 x 4 =
+// 16,384 elements); vector j of lane l is vector j * TPB + l of the chunk, so
+// each of the kVecs loads is one contiguous span across the block, and each
+// lane sums its elements in order.  An fp16 value squared is exact in fp32
+// (at most 22 significant bits, between 2^-48 and 65504^2), so fp16 squares
+// are taken in fp32 and widened for the fp64 sum -- the same values as fp64
+// squares, for less fp64 work; bf16 and fp32 squares are taken in fp64.
 template <int GF, int TPB>
 __global__ __launch_bounds__(TPB) void check_sumsq_kernel(ds_scaler* __restrict__ st,
                                                           const void* __restrict__ grad, int64_t n,
@@ -565,7 +576,7 @@ __global__ __launch_bounds__(TPB) void check_sumsq_kernel(ds_scaler* __restrict_
 {
     constexpr bool F32 = GF == kF32;
     constexpr int kPer = F32 ? 4 : 8;
-    constexpr int kVecs = 4;
+    constexpr int kVecs = static_cast<int>((4 * kChunk) / (static_cast<int64_t>(TPB) * kPer));
     constexpr int64_t kCh = static_cast<int64_t>(TPB) * kVecs * kPer;
     static_assert(kCh == 4 * kChunk, "four 4096-element units per chunk");
     __shared__ double lds[TPB / 64];
@@ -596,8 +607,15 @@ __global__ __launch_bounds__(TPB) void check_sumsq_kernel(ds_scaler* __restrict_
                 } else {
                     bad |= nonfinite16x2<GF>(w[j].x) | nonfinite16x2<GF>(w[j].y) |
                            nonfinite16x2<GF>(w[j].z) | nonfinite16x2<GF>(w[j].w);
-                    s = s + sq4(widen4<GF>(u32x2{w[j].x, w[j].y}));
-                    s = s + sq4(widen4<GF>(u32x2{w[j].z, w[j].w}));
+                    const f32x4 a = widen4<GF>(u32x2{w[j].x, w[j].y});
+                    const f32x4 b = widen4<GF>(u32x2{w[j].z, w[j].w});
+                    if constexpr (GF == kF16) {
+                        s = s + sq4_exact32(a);
+                        s = s + sq4_exact32(b);
+                    } else {
+                        s = s + sq4(a);
+                        s = s + sq4(b);
+                    }
                 }
             } else {
                 for (int k = 0; k < kPer; ++k) {
@@ -1151,9 +1169,9 @@ ds_status ds_check_overflow_sumsq(ds_scaler* st, const void* grad, ds_dtype dt, 
     const unsigned blocks = grid_blocks(chunks);
     double* part = static_cast<double*>(workspace);
     if (dt == DS_FP16)
-        check_sumsq_kernel<kF16, 512><<<blocks, 512, 0, s>>>(st, grad, n, part);
+        check_sumsq_kernel<kF16, 1024><<<blocks, 1024, 0, s>>>(st, grad, n, part);
     else if (dt == DS_BF16)
-        check_sumsq_kernel<kBF16, 512><<<blocks, 512, 0, s>>>(st, grad, n, part);
+        check_sumsq_kernel<kBF16, 1024><<<blocks, 1024, 0, s>>>(st, grad, n, part);
     else
         check_sumsq_kernel<kF32, 1024><<<blocks, 1024, 0, s>>>(st, grad, n, part);
     if (launched() != DS_OK)
