@@ -217,8 +217,8 @@ class DeviceTables:
         key = (arr.dtype.str, arr.size, arr.ctypes.data)
         t = self._cache.get(key)
         if t is None:
-            host = self.torch.from_numpy(arr.view(np.int16) if arr.dtype == np.uint16
-                                         else arr.view(np.int32).copy())
+            # a private writable copy: the tables are read-only module constants
+            host = self.torch.from_numpy(arr.view(np.int16 if arr.dtype == np.uint16 else np.int32).copy())
             t = host.to(self.device)
             self._cache[key] = (t, arr)  # keep arr alive so its address stays unique
         else:

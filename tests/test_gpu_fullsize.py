@@ -120,13 +120,17 @@ def run_sampled(torch, name, fused=False, bf16=False):
     return o.scaler
 
 
-def test_zero2_shard_of_7b(torch):
-    sc = run_sampled(torch, "zero2_7b")
+@pytest.mark.parametrize("fused", [True, False], ids=["fused", "separate_update"])
+def test_zero2_shard_of_7b(torch, fused):
+    """fused=True is the launch bench.py times by default: the check kernel, then
+    the Adam kernel whose last block advances the scaler."""
+    sc = run_sampled(torch, "zero2_7b", fused=fused)
     assert sc.applied == 50 and sc.scale == 2.0 ** 16
 
 
-def test_full_7b_state(torch):
-    sc = run_sampled(torch, "full_7b")
+@pytest.mark.parametrize("fused", [True, False], ids=["fused", "separate_update"])
+def test_full_7b_state(torch, fused):
+    sc = run_sampled(torch, "full_7b", fused=fused)
     assert sc.applied == 20 and sc.scale == 2.0 ** 16
 
 
