@@ -315,6 +315,63 @@ def test_weight_decay(torch, wd):
         gu.compare_full(f"wd={wd} step {s}", d, o)
 
 
+# lr, beta1, beta2, eps, weight decay at the edges of what the boundary accepts
+DEGENERATE = {
+    "lr_zero": (0.0, 0.9, 0.999, 1e-8, 0.0),            # moments move, parameters stay
+    "lr_zero_with_decay": (0.0, 0.9, 0.999, 1e-8, 0.1),  # lr*wd = 0: the decay is an exact no-op
+    "no_moment_memory": (1e-4, 0.0, 0.0, 1e-8, 0.0),    # m = g, v = g*g, both factors exactly 1
+    "betas_one_half": (1e-4, 0.5, 0.5, 1e-8, 0.0),      # the Sterbenz edge of 1 - beta
+    "betas_near_one": (1e-4, 0.99999994, 0.99999994, 1e-8, 0.0),  # the largest fp32 below 1
+    "large_lr_and_eps": (1.0, 0.9, 0.999, 1.0, 0.0),
+    "tiny_eps": (1e-4, 0.9, 0.999, 1e-30, 0.0),
+    "subnormal_eps": (1e-4, 0.9, 0.999, 1e-40, 0.0),
+    "large_decay": (1e-2, 0.9, 0.999, 1e-8, 10.0),      # lr*wd = 0.1
+}
+
+
+@pytest.mark.parametrize("name", sorted(DEGENERATE))
+def test_degenerate_hyperparameters(torch, name):
+    lr, b1, b2, eps, wd = DEGENERATE[name]
+    n = 4096 * 3 + 5
+    o, d = _pair(torch, n, seed=7500)
+    spec = synth.GradSpec(1e-3, 2.0 ** 16)
+    hp = dict(lr=lr, beta1=b1, beta2=b2, eps=eps, weight_decay=wd)
+    for s in range(5):
+        g = _mixed_grads(7600 + s, n, spec)
+        if s == 2:
+            g[n - 1] = 0x7C00
+        ov = oracle.step(o, g, **hp)
+        d.step(gu.dev_u16(torch, g), hp)
+        gu.check_scaler(d.scaler(), o.scaler, ov, f"{name} step {s}")
+        du = gu.compare_full(f"{name} step {s}", d, o)
+        # both sides evaluate the same operations in the same order: no ulp apart
+        assert max(du.values()) == 0, f"{name} step {s}: {du}"
+    if lr == 0.0:
+        master, _, _, p16 = _init_host(n, 7500)
+        assert np.array_equal(f32_bits(o.master), f32_bits(master))
+
+
+@pytest.mark.parametrize("t0", [10 ** 4, 10 ** 7, 2 ** 40])
+def test_bias_correction_late_in_training(torch, t0):
+    """Resumed at a large applied-step count: beta^t underflows to 0 and both
+    factors become exactly lr and 1; the update is then plain lr*m/(sqrt(v)+eps)."""
+    n = 4096 + 3
+    o, d = _pair(torch, n, seed=7700)
+    sc = d.scaler()
+    sc.step = t0
+    d.lib.ds_state_write(d.state, sc)
+    o.scaler.s.applied = t0
+    spec = synth.GradSpec(1e-3, 2.0 ** 16)
+    for s in range(3):
+        g = _mixed_grads(7800 + s, n, spec)
+        ov = oracle.step(o, g, **HP)
+        d.step(gu.dev_u16(torch, g), HP)
+        gu.check_scaler(d.scaler(), o.scaler, ov, f"t0={t0} step {s}")
+        du = gu.compare_full(f"t0={t0} step {s}", d, o)
+        assert max(du.values()) == 0, f"t0={t0} step {s}: {du}"
+    assert d.scaler().step == t0 + 3
+
+
 def test_static_scale_and_hysteresis_two(torch):
     """Unexercised by the workloads; the device state machine still tracks the oracle's."""
     n = 1000
