@@ -336,3 +336,62 @@ def test_batch_relation_from_the_pages():
     with pytest.raises(ValueError):
         ZeroMPConfig.from_dict({"train_batch_size": 1000, "world_size": 8,
                                 "train_micro_batch_size_per_gpu": 4, "gradient_accumulation_steps": 64})
+
+
+class _FakeDeviceTensor:
+    """Stands in for a GPU tensor: the binding's checks read only these attributes,
+    and every call below is rejected before its address is used."""
+    is_cuda = True
+
+    def __init__(self, nbytes, esize=2, contiguous=True):
+        self._n, self._e, self._c = nbytes // esize, esize, contiguous
+
+    def numel(self):
+        return self._n
+
+    def element_size(self):
+        return self._e
+
+    def is_contiguous(self):
+        return self._c
+
+    def data_ptr(self):
+        return A
+
+
+def test_binding_rejects_host_short_and_strided_tensors():
+    """Python callers that pass tensors get an error, not a kernel reading an
+    address it may not touch: host tensors, non-contiguous tensors and tensors
+    shorter than the n elements the call covers are refused before the call."""
+    torch = pytest.importorskip("torch")
+    n = 1000
+    st = _FakeDeviceTensor(128, 1)
+    g = _FakeDeviceTensor(2 * n)
+    f32 = lambda k=n: _FakeDeviceTensor(4 * k, 4)
+    with pytest.raises(ValueError, match="GPU memory"):
+        _lib.ds_check_overflow(torch.zeros(128, dtype=torch.uint8), g, DS_FP16, n, stream=0)
+    with pytest.raises(ValueError, match="GPU memory"):
+        _lib.ds_check_overflow(st, torch.zeros(n, dtype=torch.float16), DS_FP16, n, stream=0)
+    with pytest.raises(ValueError, match="contiguous"):
+        _lib.ds_check_overflow(st, _FakeDeviceTensor(2 * n, contiguous=False), DS_FP16, n, stream=0)
+    with pytest.raises(ValueError, match="gradient"):
+        _lib.ds_check_overflow(st, g, DS_FP32, n, stream=0)      # 4 bytes per element of fp32
+    with pytest.raises(ValueError, match="ds_scaler"):
+        _lib.ds_check_overflow(_FakeDeviceTensor(64, 1), g, DS_FP16, n, stream=0)
+    with pytest.raises(ValueError, match="acc"):
+        _lib.ds_accumulate(f32(n - 1), g, DS_FP16, n, True, None, stream=0)
+    for short in range(5):
+        arrays = [f32(), f32(), f32(), _FakeDeviceTensor(2 * n), g]
+        arrays[short] = _FakeDeviceTensor(arrays[short].numel() * arrays[short].element_size() - 4,
+                                          arrays[short].element_size())
+        with pytest.raises(ValueError):
+            _lib.ds_adam_step_fused(st, *arrays[:4], DS_FP16, arrays[4], DS_FP16, n, 1e-4, None, 0.9, 0.999,
+                                    1e-8, 0.0, 0.0, 1, stream=0)
+    with pytest.raises(ValueError, match="workspace"):
+        _lib.ds_check_overflow_sumsq(st, _FakeDeviceTensor(200000), DS_FP16, 100000, _FakeDeviceTensor(8, 8),
+                                     stream=0)
+    with pytest.raises(ValueError, match="out2"):
+        _lib.ds_adam_bias_scalars(st, 1e-4, 0.9, 0.999, _FakeDeviceTensor(4, 4), stream=0)
+    # integers are raw addresses and pass through to the library's own validation
+    with pytest.raises(_lib.DsError, match="SIZE"):
+        _lib.ds_check_overflow(ST, A, DS_FP16, -1, stream=0)

@@ -57,3 +57,41 @@ def test_rank_share_of_a_ragged_layout(torch, rank):
         gu.compare_arrays(f"rank {rank} step {s}", gu.host_f32(d.master), gu.host_f32(d.m), gu.host_f32(d.v),
                           gu.host_u16(d.p16), o.master, o.m, o.v, o.p16)
     assert o.scaler.applied == 4
+
+
+def test_misuse_is_refused_before_any_device_work(torch):
+    """Host, short, wide or strided gradients and out-of-order calls raise, and
+    leave the device state as it was."""
+    from zero_mixed_precision_amd import ShardStep, ZeroMPConfig, _lib
+
+    n = 4099
+    one = ShardStep(n, ZeroMPConfig(lr=1e-4), device="cuda:0")
+    three = ShardStep(n, ZeroMPConfig(lr=1e-4, gradient_accumulation_steps=3), device="cuda:0")
+    g = torch.zeros(n, dtype=torch.float16, device="cuda:0")
+    bad = [torch.zeros(n, dtype=torch.float16),                      # host memory
+           torch.zeros(n - 1, dtype=torch.float16, device="cuda:0"),  # short
+           torch.zeros(n, dtype=torch.float32, device="cuda:0"),      # not 16-bit
+           torch.zeros(2 * n, dtype=torch.float16, device="cuda:0")[::2]]   # strided
+    for b in bad:
+        with pytest.raises(ValueError):
+            one.step(b)
+        with pytest.raises(ValueError):
+            three.accumulate(b)
+    with pytest.raises(RuntimeError):
+        one.accumulate(g)                 # K = 1 takes the gradient in step()
+    three.accumulate(g)
+    with pytest.raises(RuntimeError):
+        three.step()                      # one of three micro-batches
+    three.accumulate(g)
+    three.accumulate(g)
+    with pytest.raises(RuntimeError):
+        three.accumulate(g)               # a fourth
+    # the binding refuses host tensors and short tensors as well
+    with pytest.raises(ValueError):
+        _lib.ds_check_overflow(one.state, g.cpu(), _lib.DS_FP16, n)
+    with pytest.raises(ValueError):
+        _lib.ds_adam_step_fused(one.state, one.master, one.m, one.v, one.p16, _lib.DS_FP16, g[:-8], _lib.DS_FP16,
+                                n, 1e-4, None, 0.9, 0.999, 1e-8, 0.0, 0.0, 1)
+    assert one.scaler().iter == 0 and three.scaler().iter == 0
+    three.step()
+    assert three.scaler().iter == 1 and three.scaler().step == 1

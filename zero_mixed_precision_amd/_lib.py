@@ -149,13 +149,34 @@ def status_string(status: int) -> str:
     return lib.ds_status_string(int(status)).decode()
 
 
-def _p(x):
-    """Pointer argument: int, None, or a tensor-like with data_ptr()."""
+def _p(x, nbytes=0, what="pointer"):
+    """Pointer argument: int, None, or a torch tensor.
+
+    An int is passed through as it is (the caller vouches for it, as in C).  A
+    tensor must live on the GPU, be contiguous and hold at least ``nbytes``
+    bytes from its first element: a host tensor or a too-short one would
+    otherwise reach the kernels as an address they may not read or write.
+    """
     if x is None:
         return None
     if isinstance(x, int):
         return x
+    if not getattr(x, "is_cuda", False):
+        raise ValueError(f"{what}: expected a tensor in GPU memory, got one on {x.device}")
+    if not x.is_contiguous():
+        raise ValueError(f"{what}: expected a contiguous tensor")
+    have = x.numel() * x.element_size()
+    if nbytes > 0 and have < nbytes:
+        raise ValueError(f"{what}: tensor holds {have} bytes, the call reads or writes {nbytes}")
     return x.data_ptr()
+
+
+def _esize(dtype) -> int:
+    return 4 if int(dtype) == DS_FP32 else 2
+
+
+def _scaler(st):
+    return _p(st, ctypes.sizeof(DsScaler), "ds_scaler state")
 
 
 def _s(stream):
@@ -178,49 +199,61 @@ def ds_scaler_size() -> int:
 
 def ds_state_init(st, init_scale, min_scale, growth_window, hysteresis, consecutive_hysteresis=0,
                   dynamic=1, stream=None) -> None:
-    _ok(lib.ds_state_init(_p(st), init_scale, min_scale, int(growth_window), int(hysteresis),
+    _ok(lib.ds_state_init(_scaler(st), init_scale, min_scale, int(growth_window), int(hysteresis),
                           int(consecutive_hysteresis), int(dynamic), _s(stream)), "ds_state_init")
 
 
 def ds_state_read(st, stream=None) -> DsScaler:
     out = DsScaler()
-    _ok(lib.ds_state_read(_p(st), ctypes.byref(out), _s(stream)), "ds_state_read")
+    _ok(lib.ds_state_read(_scaler(st), ctypes.byref(out), _s(stream)), "ds_state_read")
     return out
 
 
 def ds_state_write(st, value: DsScaler, stream=None) -> None:
-    _ok(lib.ds_state_write(_p(st), ctypes.byref(value), _s(stream)), "ds_state_write")
+    _ok(lib.ds_state_write(_scaler(st), ctypes.byref(value), _s(stream)), "ds_state_write")
 
 
 def ds_accumulate(acc, g16, gdt, n, overwrite, st_or_null=None, stream=None) -> None:
-    _ok(lib.ds_accumulate(_p(acc), _p(g16), int(gdt), int(n), int(bool(overwrite)), _p(st_or_null),
-                          _s(stream)), "ds_accumulate")
+    n = int(n)
+    _ok(lib.ds_accumulate(_p(acc, 4 * n, "acc"), _p(g16, 2 * n, "gradient"), int(gdt), n, int(bool(overwrite)),
+                          _scaler(st_or_null), _s(stream)), "ds_accumulate")
 
 
 def ds_check_overflow(st, grad, dtype, n, stream=None) -> None:
-    _ok(lib.ds_check_overflow(_p(st), _p(grad), int(dtype), int(n), _s(stream)), "ds_check_overflow")
+    n = int(n)
+    _ok(lib.ds_check_overflow(_scaler(st), _p(grad, _esize(dtype) * n, "gradient"), int(dtype), n, _s(stream)),
+        "ds_check_overflow")
+
+
+def _adam_arrays(master, m, v, p16, pdt, grad, dtype, n):
+    """The five array arguments of the Adam entry points, checked for n elements."""
+    return (_p(master, 4 * n, "master"), _p(m, 4 * n, "m"), _p(v, 4 * n, "v"), _p(p16, 2 * n, "p16"), int(pdt),
+            _p(grad, _esize(dtype) * n, "gradient"), int(dtype), n)
 
 
 def ds_adam_step(st, master, m, v, p16, pdt, grad, dtype, n, lr, beta1, beta2, eps, weight_decay,
                  max_grad_norm, accum_steps, stream=None) -> None:
-    _ok(lib.ds_adam_step(_p(st), _p(master), _p(m), _p(v), _p(p16), int(pdt), _p(grad), int(dtype),
-                         int(n), lr, beta1, beta2, eps, weight_decay, max_grad_norm, int(accum_steps),
-                         _s(stream)), "ds_adam_step")
+    n = int(n)
+    _ok(lib.ds_adam_step(_scaler(st), *_adam_arrays(master, m, v, p16, pdt, grad, dtype, n), lr, beta1, beta2,
+                         eps, weight_decay, max_grad_norm, int(accum_steps), _s(stream)), "ds_adam_step")
 
 
 def ds_adam_step_sched(st, master, m, v, p16, pdt, grad, dtype, n, sched: DsLrSchedule, beta1, beta2, eps,
                        weight_decay, max_grad_norm, accum_steps, stream=None) -> None:
-    _ok(lib.ds_adam_step_sched(_p(st), _p(master), _p(m), _p(v), _p(p16), int(pdt), _p(grad), int(dtype),
-                               int(n), ctypes.byref(sched), beta1, beta2, eps, weight_decay, max_grad_norm,
+    n = int(n)
+    _ok(lib.ds_adam_step_sched(_scaler(st), *_adam_arrays(master, m, v, p16, pdt, grad, dtype, n),
+                               ctypes.byref(sched), beta1, beta2, eps, weight_decay, max_grad_norm,
                                int(accum_steps), _s(stream)), "ds_adam_step_sched")
 
 
 def ds_adam_step_fused(st, master, m, v, p16, pdt, grad, dtype, n, lr, sched, beta1, beta2, eps, weight_decay,
                        max_grad_norm, accum_steps, stream=None) -> None:
     """ds_adam_step (sched None) or ds_adam_step_sched, then the scaler update, in one kernel."""
-    _ok(lib.ds_adam_step_fused(_p(st), _p(master), _p(m), _p(v), _p(p16), int(pdt), _p(grad), int(dtype), int(n),
-                               lr, ctypes.byref(sched) if sched is not None else None, beta1, beta2, eps,
-                               weight_decay, max_grad_norm, int(accum_steps), _s(stream)), "ds_adam_step_fused")
+    n = int(n)
+    sched_p = ctypes.byref(sched) if sched is not None else None
+    _ok(lib.ds_adam_step_fused(_scaler(st), *_adam_arrays(master, m, v, p16, pdt, grad, dtype, n), lr, sched_p,
+                               beta1, beta2, eps, weight_decay, max_grad_norm, int(accum_steps), _s(stream)),
+        "ds_adam_step_fused")
 
 
 def ds_sumsq_workspace_bytes(n) -> int:
@@ -234,28 +267,35 @@ def _nbytes(ws, ws_bytes):
 
 
 def ds_check_overflow_sumsq(st, grad, dtype, n, workspace, workspace_bytes=None, stream=None) -> None:
-    _ok(lib.ds_check_overflow_sumsq(_p(st), _p(grad), int(dtype), int(n), _p(workspace),
+    n = int(n)
+    _ok(lib.ds_check_overflow_sumsq(_scaler(st), _p(grad, _esize(dtype) * n, "gradient"), int(dtype), n,
+                                    _p(workspace, ds_sumsq_workspace_bytes(max(n, 0)), "workspace"),
                                     _nbytes(workspace, workspace_bytes), _s(stream)),
         "ds_check_overflow_sumsq")
 
 
 def ds_accumulate_sumsq(acc, g16, gdt, n, overwrite, st, workspace, workspace_bytes=None,
                         stream=None) -> None:
-    _ok(lib.ds_accumulate_sumsq(_p(acc), _p(g16), int(gdt), int(n), int(bool(overwrite)), _p(st),
-                                _p(workspace), _nbytes(workspace, workspace_bytes), _s(stream)),
+    n = int(n)
+    _ok(lib.ds_accumulate_sumsq(_p(acc, 4 * n, "acc"), _p(g16, 2 * n, "gradient"), int(gdt), n,
+                                int(bool(overwrite)), _scaler(st),
+                                _p(workspace, ds_sumsq_workspace_bytes(max(n, 0)), "workspace"),
+                                _nbytes(workspace, workspace_bytes), _s(stream)),
         "ds_accumulate_sumsq")
 
 
 def ds_update_loss_scale(st, stream=None) -> None:
-    _ok(lib.ds_update_loss_scale(_p(st), _s(stream)), "ds_update_loss_scale")
+    _ok(lib.ds_update_loss_scale(_scaler(st), _s(stream)), "ds_update_loss_scale")
 
 
 def ds_adam_bias_scalars(st, lr, beta1, beta2, out2, stream=None) -> None:
-    _ok(lib.ds_adam_bias_scalars(_p(st), lr, beta1, beta2, _p(out2), _s(stream)), "ds_adam_bias_scalars")
+    _ok(lib.ds_adam_bias_scalars(_scaler(st), lr, beta1, beta2, _p(out2, 8, "out2"), _s(stream)),
+        "ds_adam_bias_scalars")
 
 
 def ds_lr_scalars(st, sched: DsLrSchedule, beta1, beta2, out3, stream=None) -> None:
-    _ok(lib.ds_lr_scalars(_p(st), ctypes.byref(sched), beta1, beta2, _p(out3), _s(stream)), "ds_lr_scalars")
+    _ok(lib.ds_lr_scalars(_scaler(st), ctypes.byref(sched), beta1, beta2, _p(out3, 12, "out3"), _s(stream)),
+        "ds_lr_scalars")
 
 
 def ds_layout_greedy(numels, cap, align):

@@ -67,9 +67,19 @@ class ShardStep:
                            cfg.hysteresis, int(cfg.consecutive_hysteresis), int(cfg.dynamic),
                            self.stream)
 
+    def _check_grad(self, g16) -> None:
+        if g16 is None or g16.numel() != self.n or g16.element_size() != 2:
+            raise ValueError(f"expected a 16-bit gradient of {self.n} elements")
+        if g16.device != self.master.device or not g16.is_contiguous():
+            raise ValueError(f"the gradient must be a contiguous tensor on {self.master.device}")
+
     def accumulate(self, g16) -> None:
         """Add one fp16 micro-batch gradient (K > 1); the K-th call also checks it."""
-        assert self.K > 1 and g16.numel() == self.n
+        if self.K == 1:
+            raise RuntimeError("accumulate() is for gradient_accumulation_steps > 1; pass the gradient to step()")
+        if self._micro >= self.K:
+            raise RuntimeError(f"accumulate() called more than {self.K} times before step()")
+        self._check_grad(g16)
         k = self._micro
         last = k == self.K - 1
         for start, size in self.buckets:
@@ -86,7 +96,7 @@ class ShardStep:
         """Finish the step: check (K = 1), gated Adam, scaler update."""
         c = self.cfg
         if self.K == 1:
-            assert g16 is not None and g16.numel() == self.n
+            self._check_grad(g16)
             if self.ws is not None:
                 _lib.ds_check_overflow_sumsq(self.state, g16, self.gdt, self.n, self.ws,
                                              stream=self.stream)
@@ -94,7 +104,9 @@ class ShardStep:
                 _lib.ds_check_overflow(self.state, g16, self.gdt, self.n, self.stream)
             grad, dt = g16, self.gdt
         else:
-            assert self._micro == self.K, "accumulate() must be called K times before step()"
+            if self._micro != self.K:
+                raise RuntimeError(f"accumulate() must be called {self.K} times before step() "
+                                   f"(called {self._micro} times)")
             grad, dt = self.acc, _lib.DS_FP32
         # the whole partition in one call: the Adam kernel also advances the scaler
         _lib.ds_adam_step_fused(self.state, self.master, self.m, self.v, self.p16, self.pdt, grad, dt, self.n,
@@ -107,7 +119,8 @@ class ShardStep:
         if self.K == 1:
             self.step(grads[0] if isinstance(grads, (list, tuple)) else grads)
             return
-        assert len(grads) == self.K
+        if len(grads) != self.K:
+            raise ValueError(f"expected {self.K} micro-batch gradients, got {len(grads)}")
         for g in grads:
             self.accumulate(g)
         self.step()
