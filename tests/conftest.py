@@ -10,7 +10,7 @@ if ROOT not in sys.path:
 
 
 def pytest_configure(config):
-    config.addinivalue_line("markers", "gpu: needs an MI355X (runs on the GPU box)")
+    config.addinivalue_line("markers", "gpu: needs an MI355X GPU")
     config.addinivalue_line("markers", "slow: long-running CPU test")
 
 
