@@ -50,7 +50,9 @@
  *    and tuning; results are bit-identical under every setting):
  *    DSZERO_GRID=<blocks> pins the block count, DSZERO_UNROLL=2|4 sets the
  *    quads per lane of the read/write kernels (ds_adam_step_fused and the
- *    sum-of-squares accumulation always use 4), DSZERO_NT=0|1 turns their
+ *    sum-of-squares accumulation ignore it: they always take 4096-element
+ *    tiles, ds_adam_step_fused as 256 lanes x 4 quads with non-temporal
+ *    hints and 512 lanes x 2 quads without), DSZERO_NT=0|1 turns their
  *    non-temporal load/store hints off or on (default: on above 2^24
  *    elements, off at and below, where the state stays in the Infinity Cache
  *    between steps).

@@ -60,6 +60,7 @@ class ShardStep:
             # chunk sums of the gradient's sum of squares (scratch, no initial contents)
             nbytes = _lib.ds_sumsq_workspace_bytes(self.n)
             self.ws = torch.zeros((nbytes + 7) // 8, dtype=torch.float64, device=device)
+        self._ws_bytes = self.ws.numel() * 8 if self.ws is not None else 0
         # accumulation granularity: the reduce buckets inside this partition
         self.buckets = buckets_or_all(buckets, self.n)
         self._micro = 0
@@ -82,34 +83,39 @@ class ShardStep:
         self._check_grad(g16)
         k = self._micro
         last = k == self.K - 1
+        st, acc, g0 = self.state.data_ptr(), self.acc.data_ptr(), g16.data_ptr()
         for start, size in self.buckets:
-            a, g = self.acc.data_ptr() + 4 * start, g16.data_ptr() + 2 * start
+            a, g = acc + 4 * start, g0 + 2 * start
             if last and self.ws is not None:
-                _lib.ds_accumulate_sumsq(a, g, self.gdt, size, k == 0, self.state, self.ws,
+                _lib.ds_accumulate_sumsq(a, g, self.gdt, size, k == 0, st, self.ws.data_ptr(), self._ws_bytes,
                                          stream=self.stream)
             else:
-                _lib.ds_accumulate(a, g, self.gdt, size, overwrite=(k == 0),
-                                   st_or_null=self.state if last else None, stream=self.stream)
+                _lib.ds_accumulate(a, g, self.gdt, size, overwrite=(k == 0), st_or_null=st if last else None,
+                                   stream=self.stream)
         self._micro = k + 1
 
     def step(self, g16=None) -> None:
         """Finish the step: check (K = 1), gated Adam, scaler update."""
         c = self.cfg
+        st = self.state.data_ptr()
         if self.K == 1:
             self._check_grad(g16)
+            grad, dt = g16.data_ptr(), self.gdt
             if self.ws is not None:
-                _lib.ds_check_overflow_sumsq(self.state, g16, self.gdt, self.n, self.ws,
+                _lib.ds_check_overflow_sumsq(st, grad, dt, self.n, self.ws.data_ptr(), self._ws_bytes,
                                              stream=self.stream)
             else:
-                _lib.ds_check_overflow(self.state, g16, self.gdt, self.n, self.stream)
-            grad, dt = g16, self.gdt
+                _lib.ds_check_overflow(st, grad, dt, self.n, self.stream)
         else:
             if self._micro != self.K:
                 raise RuntimeError(f"accumulate() must be called {self.K} times before step() "
                                    f"(called {self._micro} times)")
-            grad, dt = self.acc, _lib.DS_FP32
+            grad, dt = self.acc.data_ptr(), _lib.DS_FP32
         # the whole partition in one call: the Adam kernel also advances the scaler
-        _lib.ds_adam_step_fused(self.state, self.master, self.m, self.v, self.p16, self.pdt, grad, dt, self.n,
+        # (raw addresses: the arrays are this object's own, sized and placed at construction,
+        # and the gradient was checked above, so the binding's per-tensor checks are skipped)
+        _lib.ds_adam_step_fused(st, self.master.data_ptr(), self.m.data_ptr(), self.v.data_ptr(),
+                                self.p16.data_ptr(), self.pdt, grad, dt, self.n,
                                 c.lr, self.sched, c.betas[0], c.betas[1], c.eps, c.weight_decay,
                                 c.gradient_clipping, self.K, self.stream)
         self._micro = 0
