@@ -17,7 +17,10 @@
 // 256-lane block one tile of U x 256 consecutive quads (U = 4: 4096
 // elements), issue all of the tile's loads before any arithmetic, and mark
 // loads and stores non-temporal (streamed data is touched once) on partitions
-// larger than twice the Infinity Cache; the grid has one block per tile.
+// above 2^24 elements, whose step traffic is about twice the Infinity Cache or
+// more; the grid has one block per tile.  On the smaller, cache-resident
+// partitions the fused Adam kernel covers the same tile with 512 lanes x 2
+// quads.
 // Measured on MI355X with a 109M-element partition this
 // beats persistent grid-stride launches, whose extra waves per CU congest the
 // memory system under a 50/50 read/write mix.  The read-only overflow check
