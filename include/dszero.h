@@ -30,7 +30,8 @@
  *  - Alignment.  Every array pointer must be 16-byte aligned; a ds_scaler
  *    pointer must be 8-byte aligned.
  *  - Errors.  Every call validates all arguments before any device work, so a
- *    call that returns an error has had no effect.  n < 0 -> DS_ERR_SIZE;
+ *    call that returns an error has had no effect.  n < 0, or n > 2^40
+ *    (more elements than any device holds) -> DS_ERR_SIZE;
  *    n == 0 -> DS_OK and nothing is launched; a NULL array with n > 0 ->
  *    DS_ERR_NULL; a misaligned pointer -> DS_ERR_ALIGN; overlapping arrays ->
  *    DS_ERR_ALIAS; an unknown dtype -> DS_ERR_DTYPE; an out-of-range

@@ -51,6 +51,11 @@ static void validation(void)
                         1e-8f, 0.0f, 0.0f, 1, NULL) == DS_OK);
     EXPECT(ds_adam_step_fused(ST, f, (float*)B, (float*)C, (uint16_t*)D, DS_FP16, E, DS_FP16, -1, 1e-4f, NULL,
                               0.9f, 0.999f, 1e-8f, 0.0f, 0.0f, 1, NULL) == DS_ERR_SIZE);
+    /* beyond any device: refused before a byte count is formed from n */
+    EXPECT(ds_adam_step_fused(ST, f, (float*)B, (float*)C, (uint16_t*)D, DS_FP16, E, DS_FP16, INT64_MAX, 1e-4f,
+                              NULL, 0.9f, 0.999f, 1e-8f, 0.0f, 0.0f, 1, NULL) == DS_ERR_SIZE);
+    EXPECT(ds_accumulate(f, (uint16_t*)B, DS_FP16, ((int64_t)1 << 40) + 1, 1, NULL, NULL) == DS_ERR_SIZE);
+    EXPECT(ds_check_overflow(ST, E, DS_FP16, INT64_MAX, NULL) == DS_ERR_SIZE);
     ds_lr_schedule bad = {7, 0, 10, 20, 0.0f, 1e-3f};
     EXPECT(ds_adam_step_sched(ST, f, (float*)B, (float*)C, (uint16_t*)D, DS_FP16, E, DS_FP16, 8, &bad, 0.9f,
                               0.999f, 1e-8f, 0.0f, 0.0f, 1, NULL) == DS_ERR_HPARAM);

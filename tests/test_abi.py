@@ -93,6 +93,21 @@ def test_check_overflow_validation():
     assert chk(A + 32, A, DS_FP32, 10, STREAM) == DS_ERR_ALIAS
 
 
+def test_sizes_beyond_any_device_are_refused():
+    """n above 2^40 elements (more than any device holds) is DS_ERR_SIZE on every
+    entry point that takes n, before any byte count is formed from it."""
+    big = 2 ** 40 + 1
+    ws = L.ds_sumsq_workspace_bytes(big)
+    assert L.ds_accumulate(A, B, DS_FP16, big, 1, None, STREAM) == DS_ERR_SIZE
+    assert L.ds_check_overflow(ST, A, DS_FP16, big, STREAM) == DS_ERR_SIZE
+    assert L.ds_check_overflow_sumsq(ST, A, DS_FP16, big, B, ws, STREAM) == DS_ERR_SIZE
+    assert L.ds_accumulate_sumsq(A, B, DS_FP16, big, 1, ST, C, ws, STREAM) == DS_ERR_SIZE
+    for n in (big, 2 ** 62, 2 ** 63 - 1):
+        assert _adam(n=n) == DS_ERR_SIZE
+        assert L.ds_adam_step_fused(ST, A, B, C, D, DS_FP16, E, DS_FP16, n, 1e-4, None, *HP[1:], STREAM) \
+            == DS_ERR_SIZE
+
+
 def _adam(*, st=ST, ptrs=(A, B, C, D, E), dt=DS_FP16, pdt=DS_FP16, n=16, hp=HP):
     master, m, v, p16, grad = ptrs
     return L.ds_adam_step(st, master, m, v, p16, pdt, grad, dt, n, *hp, STREAM)

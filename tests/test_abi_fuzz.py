@@ -33,7 +33,8 @@ def _no_gpu():
 pytestmark = pytest.mark.skipif(not _no_gpu(), reason="fake device addresses: CPU-only test")
 
 # weighted toward valid values, so that the later rules are reached too
-sizes = st.sampled_from([-7, -1, 0, 0, 1, 5, 8, 4096, 10 ** 6, 10 ** 6])
+MAX_N = 2 ** 40      # the largest n the library accepts
+sizes = st.sampled_from([-7, -1, 0, 0, 1, 5, 8, 4096, 10 ** 6, 10 ** 6, MAX_N + 1, 2 ** 62])
 dtypes = st.sampled_from([FP16] * 4 + [FP32] * 2 + [BF16] * 2 + [0, 4, -1])
 
 
@@ -74,7 +75,7 @@ def _check(rc, broken, ctx):
        lr=lrs, b1=betas, b2=betas, eps=epss, wd=wds, clip=clips, K=ksteps)
 def test_adam_step_validation(n, dt, pdt, st_p, ptrs, lr, b1, b2, eps, wd, clip, K):
     broken = set()
-    if n < 0:
+    if n < 0 or n > MAX_N:
         broken.add(DS_ERR_SIZE)
     if dt not in ESIZE or pdt not in (FP16, BF16):
         broken.add(DS_ERR_DTYPE)
@@ -107,7 +108,7 @@ def test_adam_step_validation(n, dt, pdt, st_p, ptrs, lr, b1, b2, eps, wd, clip,
        ow=st.sampled_from([0, 1]))
 def test_accumulate_validation(n, gdt, st_p, acc, g, ow):
     broken = set()
-    if n < 0:
+    if n < 0 or n > MAX_N:
         broken.add(DS_ERR_SIZE)
     if gdt not in (FP16, BF16):
         broken.add(DS_ERR_DTYPE)
@@ -129,7 +130,7 @@ def test_accumulate_validation(n, gdt, st_p, acc, g, ow):
 def test_check_overflow_validation(n, dt, st_p, g, ws, ws_short):
     # the plain check
     broken = set()
-    if n < 0:
+    if n < 0 or n > MAX_N:
         broken.add(DS_ERR_SIZE)
     if dt not in ESIZE:
         broken.add(DS_ERR_DTYPE)
@@ -169,7 +170,7 @@ def test_check_overflow_validation(n, dt, st_p, g, ws, ws_short):
 def test_schedule_validation(kind, lo, hi, w, t, n):
     bad_ge0 = lambda x: not (x == x and x != float("inf") and x >= 0.0)
     broken = set()
-    if n < 0:
+    if n < 0 or n > MAX_N:
         broken.add(DS_ERR_SIZE)
     if kind not in (1, 2) or bad_ge0(lo) or bad_ge0(hi) or w < 0 or (kind == 2 and t < w):
         broken.add(DS_ERR_HPARAM)

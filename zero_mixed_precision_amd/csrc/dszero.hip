@@ -66,6 +66,10 @@ static_assert(2 * kSmallBlock == 4 * kStepBlock, "both shapes of the fused kerne
 constexpr int kCheckBlock = 1024;  // lanes per block of the read-only check
 constexpr int64_t kMaxBlocks = int64_t(1) << 22;
 constexpr int64_t kChunk = 4096;   // elements per chunk of the gradient sum of squares
+// Largest n any entry point accepts: 2^40 elements is far beyond one GPU's
+// memory (4 TiB of fp32), and keeps every byte count the validation computes
+// (at most 16 bytes per element) far from overflowing.
+constexpr int64_t kMaxElems = int64_t(1) << 40;
 
 // ---------------------------------------------------------------------------
 // memory helpers
@@ -790,6 +794,8 @@ bool variant_nt(int64_t n)
 
 int64_t tiles_of(int64_t n, int unroll) { return (n >> 2) / (static_cast<int64_t>(unroll) * kStepBlock); }
 
+bool size_ok(int64_t n) { return n >= 0 && n <= kMaxElems; }
+
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
 bool overlap(const void* a, uint64_t abytes, const void* b, uint64_t bbytes)
@@ -939,7 +945,7 @@ ds_status adam_step(const ds_scaler* st, float* master, float* m, float* v, uint
     const float beta1 = hp.beta1, beta2 = hp.beta2, eps = hp.eps;
     const float weight_decay = hp.weight_decay, max_grad_norm = hp.max_grad_norm;
     const int32_t accum_steps = hp.accum_steps;
-    if (n < 0)
+    if (!size_ok(n))
         return DS_ERR_SIZE;
     if (!known(dt) || !is16(pdt))
         return DS_ERR_DTYPE;
@@ -1055,7 +1061,7 @@ ds_status ds_state_write(ds_scaler* st, const ds_scaler* host_in, void* stream)
 ds_status ds_accumulate(float* acc, const uint16_t* g16, ds_dtype gdt, int64_t n, int32_t overwrite,
                         ds_scaler* st_or_null, void* stream)
 {
-    if (n < 0)
+    if (!size_ok(n))
         return DS_ERR_SIZE;
     if (!is16(gdt))
         return DS_ERR_DTYPE;
@@ -1083,7 +1089,7 @@ ds_status ds_accumulate(float* acc, const uint16_t* g16, ds_dtype gdt, int64_t n
 
 ds_status ds_check_overflow(ds_scaler* st, const void* grad, ds_dtype dt, int64_t n, void* stream)
 {
-    if (n < 0)
+    if (!size_ok(n))
         return DS_ERR_SIZE;
     if (!known(dt))
         return DS_ERR_DTYPE;
@@ -1159,7 +1165,7 @@ size_t ds_sumsq_workspace_bytes(int64_t n)
 ds_status ds_check_overflow_sumsq(ds_scaler* st, const void* grad, ds_dtype dt, int64_t n,
                                   void* workspace, size_t workspace_bytes, void* stream)
 {
-    if (n < 0)
+    if (!size_ok(n))
         return DS_ERR_SIZE;
     if (!known(dt))
         return DS_ERR_DTYPE;
@@ -1197,7 +1203,7 @@ ds_status ds_check_overflow_sumsq(ds_scaler* st, const void* grad, ds_dtype dt, 
 ds_status ds_accumulate_sumsq(float* acc, const uint16_t* g16, ds_dtype gdt, int64_t n, int32_t overwrite,
                               ds_scaler* st, void* workspace, size_t workspace_bytes, void* stream)
 {
-    if (n < 0)
+    if (!size_ok(n))
         return DS_ERR_SIZE;
     if (!is16(gdt))
         return DS_ERR_DTYPE;
