@@ -336,7 +336,8 @@ ds_status ds_lr_scalars(const ds_scaler* st, const ds_lr_schedule* sched, float 
  * bucket).  Outputs (host arrays of `count` entries, caller-owned): offsets,
  * bucket_of; bucket_start and bucket_size (first *n_buckets entries used);
  * *total = padded length of the flat array.  DS_ERR_SIZE: count < 0, a
- * negative size, cap < 1, align < 1.
+ * negative size, cap < 1, align < 1, cap or align above 2^40, or sizes whose
+ * sum plus count * (align - 1) exceeds 2^40 (nothing is written then).
  */
 ds_status ds_layout_greedy(const int64_t* numels, int32_t count, int64_t cap, int64_t align,
                            int64_t* offsets, int32_t* bucket_of, int64_t* bucket_start,
@@ -346,8 +347,8 @@ ds_status ds_layout_greedy(const int64_t* numels, int32_t count, int64_t cap, in
  * ZeRO partition of a flat array of `total` elements over `world` ranks
  * ([Guide] sections 2.1 and 2.2: each rank owns a contiguous 1/N share):
  * rank r gets [r*per, min((r+1)*per, total)) with per = ceil(total/world)
- * rounded up to `align`.  Host-only.  DS_ERR_SIZE: total < 0, world < 1,
- * rank outside [0, world), align < 1.
+ * rounded up to `align`.  Host-only.  DS_ERR_SIZE: total outside
+ * [0, 2^40], world < 1, rank outside [0, world), align outside [1, 2^40].
  */
 ds_status ds_partition_range(int64_t total, int32_t world, int32_t rank, int64_t align,
                              int64_t* start, int64_t* count);

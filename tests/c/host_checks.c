@@ -165,6 +165,16 @@ static void layouts(void)
         EXPECT(end == tot);
     }
     int64_t s0, c0;
+    /* the extremes the validation admits: no signed overflow (UBSan checks) */
+    const int64_t most = (int64_t)1 << 40;
+    EXPECT(ds_partition_range(most, INT32_MAX, INT32_MAX - 1, most, &s0, &c0) == DS_OK && s0 == most && c0 == 0);
+    EXPECT(ds_partition_range(most, INT32_MAX, 0, 8, &s0, &c0) == DS_OK && s0 == 0 && c0 > 0);
+    EXPECT(ds_partition_range(most + 1, 2, 0, 8, &s0, &c0) == DS_ERR_SIZE);
+    int64_t huge[2] = {INT64_MAX, INT64_MAX};
+    EXPECT(ds_layout_greedy(huge, 2, 100, 8, offsets, bof, bstart, bsize, &nb, &total) == DS_ERR_SIZE);
+    int64_t edge[2] = {most / 2 - 64, most / 2 - 64};
+    EXPECT(ds_layout_greedy(edge, 2, most, 64, offsets, bof, bstart, bsize, &nb, &total) == DS_OK &&
+           total == most - 128 && nb == 1);
     EXPECT(ds_partition_range(10, 0, 0, 8, &s0, &c0) == DS_ERR_SIZE);
     EXPECT(ds_partition_range(10, 4, 4, 8, &s0, &c0) == DS_ERR_SIZE);
 }

@@ -108,6 +108,26 @@ def test_sizes_beyond_any_device_are_refused():
             == DS_ERR_SIZE
 
 
+def test_layout_and_partition_refuse_sizes_beyond_any_device():
+    big = 2 ** 40
+    for numels, cap, align in (([big + 1], 10, 1), ([big // 2, big // 2, 5], 10, 1), ([5], big + 1, 1),
+                               ([5], 10, big + 1), ([2 ** 63 - 1, 2 ** 63 - 1], 10, 8)):
+        with pytest.raises(_lib.DsError, match="SIZE"):
+            _lib.ds_layout_greedy(numels, cap, align)
+    assert _lib.ds_layout_greedy([big // 2 - 64, big // 2 - 64], int(2e8), 64)[4] == big - 128
+    with pytest.raises(_lib.DsError, match="SIZE"):
+        _lib.ds_partition_range(big + 1, 8, 0, 8)
+    with pytest.raises(_lib.DsError, match="SIZE"):
+        _lib.ds_partition_range(100, 8, 0, big + 1)
+    # the largest total, the largest world: every rank's range is exact
+    world = 2 ** 31 - 1
+    per = -(-big // world)
+    per = -(-per // 8) * 8
+    for rank in (0, 1, big // per - 1, big // per, big // per + 1, world - 1):
+        start, count = _lib.ds_partition_range(big, world, rank, 8)
+        assert start == min(rank * per, big) and count == max(0, min(per, big - start))
+
+
 def _adam(*, st=ST, ptrs=(A, B, C, D, E), dt=DS_FP16, pdt=DS_FP16, n=16, hp=HP):
     master, m, v, p16, grad = ptrs
     return L.ds_adam_step(st, master, m, v, p16, pdt, grad, dt, n, *hp, STREAM)

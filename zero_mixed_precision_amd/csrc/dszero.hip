@@ -1294,9 +1294,18 @@ ds_status ds_layout_greedy(const int64_t* numels, int32_t count, int64_t cap, in
     if (count > 0 && (numels == nullptr || offsets == nullptr || bucket_of == nullptr ||
                       bucket_start == nullptr || bucket_size == nullptr))
         return DS_ERR_NULL;
-    for (int32_t i = 0; i < count; ++i)
-        if (numels[i] < 0)
+    if (cap > kMaxElems || align > kMaxElems)
+        return DS_ERR_SIZE;
+    // every tensor, padded, must fit in kMaxElems together: a bound on the
+    // flat length that keeps all of the arithmetic below in range
+    int64_t bound = 0;
+    for (int32_t i = 0; i < count; ++i) {
+        if (numels[i] < 0 || numels[i] > kMaxElems)
             return DS_ERR_SIZE;
+        bound += numels[i] + align - 1;
+        if (bound > kMaxElems)
+            return DS_ERR_SIZE;
+    }
     auto up = [align](int64_t x) { return (x + align - 1) / align * align; };
     int32_t nb = 0;
     int64_t start = 0;     // first element of the open bucket
@@ -1330,15 +1339,14 @@ ds_status ds_layout_greedy(const int64_t* numels, int32_t count, int64_t cap, in
 ds_status ds_partition_range(int64_t total, int32_t world, int32_t rank, int64_t align, int64_t* start,
                              int64_t* count)
 {
-    if (total < 0 || world < 1 || rank < 0 || rank >= world || align < 1)
+    if (!size_ok(total) || world < 1 || rank < 0 || rank >= world || align < 1 || align > kMaxElems)
         return DS_ERR_SIZE;
     if (start == nullptr || count == nullptr)
         return DS_ERR_NULL;
     int64_t per = (total + world - 1) / world;
     per = (per + align - 1) / align * align;
-    int64_t s0 = static_cast<int64_t>(rank) * per;
-    if (s0 > total)
-        s0 = total;
+    // rank * per, clamped to total without forming a product beyond it
+    const int64_t s0 = (per == 0 || rank > total / per) ? total : static_cast<int64_t>(rank) * per;
     int64_t c = total - s0;
     if (c > per)
         c = per;
