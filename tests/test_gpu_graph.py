@@ -21,12 +21,14 @@ def torch():
     return gu.torch_mod()
 
 
-@pytest.mark.parametrize("K", [1, 4])
-def test_graph_replays_match_eager_and_oracle(torch, K):
+@pytest.mark.parametrize("K,clip", [(1, 0.0), (4, 0.0), (1, 0.05), (4, 0.05)])
+def test_graph_replays_match_eager_and_oracle(torch, K, clip):
+    """clip > 0: the captured step also holds the sum-of-squares passes and their
+    workspace (the unscaled gradient's norm is about 0.45, so clipping is active)."""
     from zero_mixed_precision_amd import ShardStep, ZeroMPConfig
     n = 200_003
     cfg = ZeroMPConfig(lr=LR, betas=(BETA1, BETA2), eps=EPS, initial_scale_power=15, loss_scale_window=3,
-                       hysteresis=1, gradient_accumulation_steps=K)
+                       hysteresis=1, gradient_accumulation_steps=K, gradient_clipping=clip)
     idx = np.arange(n)
     master0 = synth.host_master32(synth.stream_key(77, synth.ARR_MASTER), idx, MASTER_SIGMA)
     eager, graphed = ShardStep(n, cfg), ShardStep(n, cfg)
@@ -48,7 +50,8 @@ def test_graph_replays_match_eager_and_oracle(torch, K):
             b.copy_(torch.from_numpy(h.view(np.int16)).view(torch.float16))
         g.replay()
         eager.full_step([b.clone() for b in bufs])
-        ov = oracle.step(o, host if K > 1 else host[0], lr=LR, beta1=BETA1, beta2=BETA2, eps=EPS)
+        ov = oracle.step(o, host if K > 1 else host[0], lr=LR, beta1=BETA1, beta2=BETA2, eps=EPS,
+                         max_grad_norm=clip)
         torch.cuda.synchronize()
         se, sg = eager.scaler(), graphed.scaler()
         assert se.as_dict() == sg.as_dict(), step
