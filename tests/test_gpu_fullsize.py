@@ -220,3 +220,68 @@ def test_zero2_shard_of_7b_clipped(torch):
         gu.say(f"[zero2_7b clipped] step {s}: max ulp {du}")
     del master, m, v, p16, g16, ws, st
     torch.cuda.empty_cache()
+
+
+def test_ragged_layout_clipped(torch):
+    """Clipping on the ragged layout with 8 micro-batches at full size (the launch
+    bench.py --workload ragged --clip 1.0 times): the last micro-batch's
+    accumulation also gathers the sum of squares of the fp32 sum, bucket by
+    bucket, into the state.  The whole sum cannot be formed on the host here, so
+    it is checked against torch's own fp64 sum of squares of the device's
+    accumulation buffer (a library routine, independent of these kernels) to
+    1e-12, and the sampled elements are updated by the oracle with the
+    multiplier of that sum; clipping is active (norm about 28, limit 1)."""
+    from zero_mixed_precision_amd import _lib, FlatLayout
+
+    w = WORKLOADS["ragged"]
+    n, K, max_norm, steps = w.psi, w.K, 1.0, 2
+    lay = FlatLayout(ragged_numels())
+    buckets = [(b.start, b.size) for b in lay.buckets]
+    I = sample_indices(w, buckets)
+    spec = w.grad_spec
+    master0 = synth.host_master32(w.master_key(), I, MASTER_SIGMA)
+    o = oracle.State(master0, np.zeros(I.size, np.float32), np.zeros(I.size, np.float32),
+                     np.zeros(I.size, np.uint16), oracle.Scaler(w.init_scale, w.min_scale, w.window, w.hysteresis))
+    tabs = synth.DeviceTables(torch, "cuda:0")
+    master = torch.empty(n, dtype=torch.float32, device="cuda:0")
+    synth.device_fill_master32(torch, tabs, master, w.master_key(), MASTER_SIGMA)
+    m = torch.zeros(n, dtype=torch.float32, device="cuda:0")
+    v = torch.zeros(n, dtype=torch.float32, device="cuda:0")
+    p16 = torch.zeros(n, dtype=torch.int16, device="cuda:0")
+    g16 = torch.empty(n, dtype=torch.int16, device="cuda:0")
+    acc = torch.empty(n, dtype=torch.float32, device="cuda:0")
+    ws = torch.zeros((_lib.ds_sumsq_workspace_bytes(n) + 7) // 8, dtype=torch.float64, device="cuda:0")
+    st = torch.zeros(_lib.ds_scaler_size(), dtype=torch.uint8, device="cuda:0")
+    _lib.ds_state_init(st, w.init_scale, w.min_scale, w.window, w.hysteresis, 0, 1)
+    Id = torch.from_numpy(I).to("cuda:0")
+    chunk = 1 << 28
+    for s in range(1, steps + 1):
+        acc_s = np.empty(I.size, np.float32)
+        for k in range(K):
+            key = w.grad_key(s, k)
+            synth.device_fill_grad16(torch, tabs, g16, key, spec)
+            oracle.accumulate(acc_s, synth.host_grad16(key, I, spec), overwrite=(k == 0))
+            for start, size in buckets:
+                a, gp = acc.data_ptr() + 4 * start, g16.data_ptr() + 2 * start
+                if k == K - 1:
+                    _lib.ds_accumulate_sumsq(a, gp, _lib.DS_FP16, size, k == 0, st, ws)
+                else:
+                    _lib.ds_accumulate(a, gp, _lib.DS_FP16, size, k == 0)
+        ref = sum(float(acc[i:i + chunk].double().square().sum()) for i in range(0, n, chunk))
+        got_pre = _lib.ds_state_read(st)
+        assert got_pre.overflow == 0
+        assert abs(got_pre.grad_sumsq - ref) <= 1e-12 * ref, (got_pre.grad_sumsq, ref)
+        _lib.ds_adam_step_fused(st, master, m, v, p16, _lib.DS_FP16, acc, _lib.DS_FP32, n, LR, None, BETA1, BETA2,
+                                EPS, 0.0, max_norm, K)
+        got = _lib.ds_state_read(st)
+        mult = oracle.clip_multiplier(ref, o.scaler.scale, K, max_norm)
+        assert mult < np.float32(1.0) / np.float32(w.init_scale * K)      # clipping is active
+        oracle.adam_mult(acc_s, o.master, o.m, o.v, o.p16, mult=mult, t=o.scaler.applied + 1, lr=LR, beta1=BETA1,
+                         beta2=BETA2, eps=EPS)
+        o.scaler.update(False)
+        gu.check_scaler(got, o.scaler, False, f"[ragged clipped] step {s}")
+        du = gu.compare_arrays(f"[ragged clipped] step {s}", gu.host_f32(master[Id]), gu.host_f32(m[Id]),
+                               gu.host_f32(v[Id]), gu.host_u16(p16[Id]), o.master, o.m, o.v, o.p16)
+        gu.say(f"[ragged clipped] step {s}: sumsq {ref:.6g}, max ulp {du}")
+    del master, m, v, p16, g16, acc, ws, st
+    torch.cuda.empty_cache()
