@@ -53,14 +53,16 @@ def kernel_source_hash() -> str:
     return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
 
 
-def load_traffic(workload: str):
+def load_traffic(workload: str, half: str):
     """Per-launch HBM bytes of the Adam kernel from the committed counter summary,
-    or None if it is missing or was taken on another kernel source."""
+    or None if it is missing, was taken on another kernel source, or on another
+    workload or 16-bit format (another instance of the kernel)."""
     try:
         rec = json.load(open(TRAFFIC_FILE))
     except (OSError, ValueError):
         return None
-    if rec.get("kernel_source_sha256_16") != kernel_source_hash() or rec.get("workload") != workload:
+    if (rec.get("kernel_source_sha256_16") != kernel_source_hash() or rec.get("workload") != workload
+            or rec.get("half") != half):
         return None
     return rec.get("traffic_bytes_per_launch")
 
@@ -255,7 +257,7 @@ def gpu_run(args):
     bytes_per_elem = 28 if K == 1 else 30
     achieved = bytes_per_elem * n / adam_avg_s / 1e9
     step_bytes = (2 + 28) if K == 1 else (6 + 10 * (K - 1) + 30)
-    traffic = load_traffic(w.name)
+    traffic = load_traffic(w.name, "bf16" if args.bf16 else "fp16")
     out = {
         "metric": METRIC,
         "value": round(n * args.steps / wall / 1e9, 3),
@@ -448,7 +450,7 @@ def copy_mode(args):
     print(json.dumps({"mode": "copy", **res}), flush=True)
 
 
-def main():
+def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
@@ -466,7 +468,7 @@ def main():
     ap.add_argument("--step-log", default=None,
                     help="write one JSON line per step (scale used, overflow, t, growth count, device time) "
                          "from an untimed pass")
-    args = ap.parse_args()
+    args = ap.parse_args(argv)
     if args.gpus != 1:
         print(f"bench.py: --gpus {args.gpus} is not supported; the benchmark measures one GPU's "
               "partition (ranks only exchange the 4-byte overflow flag, which needs a second GPU)",
