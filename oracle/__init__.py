@@ -17,10 +17,11 @@ oracle is in ``oracle.packing``.
 
 Parity pins: every function here is pinned by the ``-m "not gpu"`` tests in
 ``tests/test_oracle_*.py``.  Parts of the scaler are parity unpinned: what
-happens after a hysteresis >= 2 decrease, ``consecutive_hysteresis``, the
-static scale and the uncapped growth (no workload exercises them and the
-pages give only the keys' one-line meaning); the 1e-8 floor of the guide's
-section 13.1, where the scale stops being a power of two, is pinned.
+happens after a hysteresis >= 2 decrease, ``consecutive_hysteresis`` and the
+uncapped growth (no workload exercises them and the pages give only the keys'
+one-line meaning); the static scale is pinned against torch's loss scaler held
+at a fixed scale, and the 1e-8 floor of the guide's section 13.1, where the
+scale stops being a power of two, is pinned.
 """
 from __future__ import annotations
 

@@ -19,8 +19,8 @@
  * Pins (tests/test_oracle_*.py) fix every function against the pages' values,
  * closed forms, exhaustive library comparisons and brute force.  Parity
  * unpinned: in zo_scaler_update, the restart of the hysteresis count after a
- * decrease, consecutive_hysteresis, the static scale and the uncapped growth
- * (the pages give one-line meanings only and no workload exercises them).
+ * decrease, consecutive_hysteresis and the uncapped growth (the pages give
+ * one-line meanings only and no workload exercises them).
  *
  * Build: gcc -O2 -std=c11 -fPIC -shared -ffp-contract=off -fno-fast-math
  *            -o liboracle.so oracle.c -lm

@@ -13,7 +13,9 @@ optimizer untouched on an overflow), so these tests pin:
   * the whole step loop (unscale, check, skip, Adam, scale update): the scale
     sequence, which steps were applied, Adam's step count (a skipped step does
     not advance the bias correction) and the parameters and moments, against
-    ``GradScaler`` driving ``torch.optim.Adam`` on the CPU.
+    ``GradScaler`` driving ``torch.optim.Adam`` on the CPU;
+  * the static scale (``loss_scale`` > 0) against ``GradScaler`` held at a fixed
+    scale: overflows still skip, the scale never moves.
 """
 import numpy as np
 import pytest
@@ -109,3 +111,37 @@ def test_planted_skip_mistake_is_caught(oracle_lib):
     oracle.step(b, g, lr=lr, beta1=0.9, beta2=0.999, eps=1e-8)
     gap = np.abs(a.master.astype(np.float64) - b.master)
     assert np.median(gap) > 0.5 * lr > 1e-6 * 40 * lr + 4 * float(np.max(ulp32(a.master)))
+
+
+def test_static_scale_matches_gradscaler_with_a_fixed_scale(oracle_lib):
+    """loss_scale > 0 ("DeepSpeed complete guide" section 4.2: 0 selects dynamic
+    scaling, so a positive value is a fixed scale): torch's GradScaler pinned to
+    that scale after every step (update(new_scale=S)) still skips the optimizer on
+    inf/NaN.  The oracle's static mode matches it: the same skipped steps, the
+    same Adam step count, the scale never moves, parameters within the Adam bounds."""
+    rng = np.random.default_rng(13)
+    n, T, S = 4096, 24, 2.0 ** 10
+    lr, b1, b2, eps = 1e-4, 0.9, 0.999, 1e-8
+    p0 = rng.normal(0, 0.02, n).astype(np.float32)
+    st = oracle.State(p0.copy(), np.zeros(n, np.float32), np.zeros(n, np.float32), np.zeros(n, np.uint16),
+                      oracle.Scaler(S, 1.0, 2, 1, dynamic=False))
+    param = torch.nn.Parameter(torch.from_numpy(p0.copy()))
+    f = lambda x: float(np.float32(x))
+    opt = torch.optim.Adam([param], lr=f(lr), betas=(f(b1), f(b2)), eps=f(eps), foreach=False)
+    gs = torch.amp.GradScaler("cpu", init_scale=S, growth_interval=2)
+    gs.scale(torch.ones(()))
+    inject = {1: np.inf, 2: np.nan, 3: -np.inf, 9: np.inf}
+    for s in range(T):
+        g = (rng.normal(0, 1e-3, n) * S).astype(np.float16)
+        if s in inject:
+            g[rng.integers(0, n)] = inject[s]
+        ov = oracle.step(st, g.view(np.uint16), lr=lr, beta1=b1, beta2=b2, eps=eps)
+        param.grad = torch.from_numpy(g.astype(np.float32))
+        gs.step(opt)
+        gs.update(new_scale=S)
+        assert ov == (s in inject) and st.scaler.scale == S == gs.get_scale()
+        assert st.scaler.applied == int(opt.state[param]["step"].item())
+    assert st.scaler.applied == T - len(inject) and st.scaler.s.skipped == len(inject)
+    ref = param.detach().numpy()
+    assert np.all(np.abs((st.master.astype(np.float64) - p0) - (ref.astype(np.float64) - p0))
+                  <= 1e-6 * T * lr + 4 * ulp32(ref))
