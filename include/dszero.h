@@ -14,9 +14,9 @@
  * fp16 parameter copy (p16), fp16 gradient, fp32 master parameter, fp32 Adam
  * first moment (m), fp32 Adam second moment (v).  In bf16 mode ([Guide]
  * section 4.2, bf16 settings) the 16-bit parameter copy and gradients are
- * bf16 instead and no loss scaling is applied (a static scale of 1).  With ZeRO-1/2 each rank owns
- * a contiguous 1/N range of these arrays and updates only that range
- * ([Guide] sections 2.1 and 2.2).
+ * bf16 instead and no loss scaling is applied (a static scale of 1).  With
+ * ZeRO-1/2 each rank owns a contiguous 1/N range of these arrays and updates
+ * only that range ([Guide] sections 2.1 and 2.2).
  *
  * Conventions shared by every entry point:
  *  - Memory.  Array arguments are DEVICE pointers owned by the caller; the
@@ -281,8 +281,8 @@ ds_status ds_update_loss_scale(ds_scaler* st, void* stream);
  * accumulation) into st->grad_sumsq, in fp64.  The sum is taken over fixed
  * chunks of consecutive elements (16,384 for the check, 4096 for the
  * accumulation), each reduced in a fixed order, and the chunk sums in a fixed
- * order, so the result does not depend on the launch shape.  Several calls per step (disjoint ranges, e.g. buckets) add up in
- * call order.
+ * order, so the result does not depend on the launch shape.  Several calls
+ * per step (disjoint ranges, e.g. buckets) add up in call order.
  *
  * workspace: caller-owned DEVICE scratch of at least
  * ds_sumsq_workspace_bytes(n) bytes (one fp64 partial sum per chunk), 8-byte
