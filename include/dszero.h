@@ -307,6 +307,30 @@ ds_status ds_accumulate_sumsq(float* acc, const uint16_t* g16, ds_dtype gdt, int
                               size_t workspace_bytes, void* stream);
 
 /*
+ * Several micro-batch gradients folded into the accumulation buffer in one
+ * pass (gradient accumulation as for ds_accumulate: [Overview] core features;
+ * [Guide] sections 4.3 and 5.1):
+ *   acc[i] = (overwrite ? float(g_0[i]) : acc[i] + float(g_0[i]))
+ *            + float(g_1[i]) + ... + float(g_{count-1}[i])
+ * with every add an fp32 add in this order, so the result is bit for bit that
+ * of `count` consecutive ds_accumulate calls.  A caller that can hold `count`
+ * 16-bit micro-batch gradients at once (grads[k] is the k-th in micro-batch
+ * order) moves 2 * count + 8 bytes per element (2 * count + 4 when
+ * overwriting) instead of 10 bytes per micro-batch.
+ * grads: HOST array of `count` (1..8) DEVICE pointers to 16-bit[n] arrays of
+ * type gdt; they may repeat or overlap one another but not acc, st or the
+ * workspace.  st_or_null: as for ds_accumulate (the fused inf/NaN check of the
+ * result).  workspace_or_null: as for ds_accumulate_sumsq (requires st; adds
+ * the sum of squares of the result to st->grad_sumsq, same chunks, so the
+ * value equals that of a ds_accumulate_sumsq pass producing the same acc).
+ * Errors: count outside 1..8 -> DS_ERR_SIZE; otherwise as ds_accumulate and
+ * ds_accumulate_sumsq.
+ */
+ds_status ds_accumulate_multi(float* acc, const uint16_t* const* grads, int32_t count, ds_dtype gdt, int64_t n,
+                              int32_t overwrite, ds_scaler* st_or_null, void* workspace_or_null,
+                              size_t workspace_bytes, void* stream);
+
+/*
  * The bias-correction scalars the next applied step will use, evaluated on
  * the device exactly as ds_adam_step does (t = st->step + 1):
  * out2[0] = fp32(lr / (1 - beta1^t)), out2[1] = fp32(1 / sqrt(1 - beta2^t)).

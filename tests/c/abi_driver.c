@@ -150,6 +150,15 @@ int main(int argc, char** argv)
                 CHECK_DS(ds_check_overflow_sumsq((ds_scaler*)state, g16, DS_FP16, n, ws, ws_bytes, stream));
             else
                 CHECK_DS(ds_check_overflow((ds_scaler*)state, g16, DS_FP16, n, stream));
+        } else if (s % 2 == 1 && K <= 8) {
+            /* odd steps: the K micro-batches folded in one pass (same result) */
+            const uint16_t* list[8];
+            for (int32_t k = 0; k < K; ++k)
+                list[k] = g16 + (size_t)k * stride;
+            CHECK_DS(ds_accumulate_multi(acc, list, K, DS_FP16, n, 1, (ds_scaler*)state, clip > 0.0f ? ws : NULL,
+                                         clip > 0.0f ? ws_bytes : 0, stream));
+            grad = acc;
+            gdt = DS_FP32;
         } else {
             for (int32_t k = 0; k < K; ++k) {
                 const uint16_t* gk = g16 + (size_t)k * stride;

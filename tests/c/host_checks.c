@@ -62,6 +62,13 @@ static void validation(void)
     EXPECT(ds_adam_step_sched(ST, f, (float*)B, (float*)C, (uint16_t*)D, DS_FP16, E, DS_FP16, 8, NULL, 0.9f,
                               0.999f, 1e-8f, 0.0f, 0.0f, 1, NULL) == DS_ERR_NULL);
     EXPECT(ds_accumulate(f, (uint16_t*)B, DS_FP32, 8, 1, NULL, NULL) == DS_ERR_DTYPE);
+    const uint16_t* list[9] = {(uint16_t*)B, (uint16_t*)C, (uint16_t*)D, (uint16_t*)B, (uint16_t*)C,
+                               (uint16_t*)D, (uint16_t*)B, (uint16_t*)C, (uint16_t*)D};
+    EXPECT(ds_accumulate_multi(f, list, 9, DS_FP16, 8, 1, NULL, NULL, 0, NULL) == DS_ERR_SIZE);
+    EXPECT(ds_accumulate_multi(f, list, 0, DS_FP16, 8, 1, NULL, NULL, 0, NULL) == DS_ERR_SIZE);
+    EXPECT(ds_accumulate_multi(f, list, 3, DS_FP16, 8, 1, NULL, E, 8, NULL) == DS_ERR_NULL);
+    const uint16_t* inside[2] = {(uint16_t*)B, (uint16_t*)(f + 4)};
+    EXPECT(ds_accumulate_multi(f, inside, 2, DS_FP16, 64, 1, NULL, NULL, 0, NULL) == DS_ERR_ALIAS);
     EXPECT(ds_accumulate(f, (uint16_t*)f + 2, DS_FP16, 8, 1, NULL, NULL) == DS_ERR_ALIGN);
     EXPECT(ds_accumulate(f, (uint16_t*)(f + 4), DS_FP16, 64, 1, NULL, NULL) == DS_ERR_ALIAS);
     EXPECT(ds_check_overflow(ST, E, (ds_dtype)9, 8, NULL) == DS_ERR_DTYPE);

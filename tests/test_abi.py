@@ -80,6 +80,30 @@ def test_accumulate_validation():
     assert acc(A, B, 9, 8, 0, None, STREAM) == DS_ERR_DTYPE
 
 
+def test_accumulate_multi_validation():
+    f = L.ds_accumulate_multi
+    P = lambda *xs: (ctypes.c_void_p * len(xs))(*xs)
+    ws = L.ds_sumsq_workspace_bytes(100)
+    assert f(A, P(B, C), 2, DS_FP16, -1, 1, None, None, 0, STREAM) == DS_ERR_SIZE
+    assert f(A, P(B, C), 2, DS_FP16, 2 ** 40 + 1, 1, None, None, 0, STREAM) == DS_ERR_SIZE
+    assert f(A, P(B), 0, DS_FP16, 8, 1, None, None, 0, STREAM) == DS_ERR_SIZE            # count 1..8
+    assert f(A, P(*[B] * 9), 9, DS_FP16, 8, 1, None, None, 0, STREAM) == DS_ERR_SIZE
+    assert f(A, P(B, C), 2, DS_FP32, 8, 1, None, None, 0, STREAM) == DS_ERR_DTYPE        # 16-bit only
+    assert f(A, P(B, C), 2, DS_FP16, 8, 1, None, D, ws, STREAM) == DS_ERR_NULL           # workspace needs st
+    assert f(A, P(B, C), 2, DS_FP16, 0, 1, None, None, 0, STREAM) == DS_OK               # n == 0: nothing
+    assert f(None, P(B, C), 2, DS_FP16, 8, 1, None, None, 0, STREAM) == DS_ERR_NULL
+    assert f(A, None, 2, DS_FP16, 8, 1, None, None, 0, STREAM) == DS_ERR_NULL
+    assert f(A, P(B, None), 2, DS_FP16, 8, 1, None, None, 0, STREAM) == DS_ERR_NULL
+    assert f(A + 8, P(B, C), 2, DS_FP16, 8, 1, None, None, 0, STREAM) == DS_ERR_ALIGN
+    assert f(A, P(B, C + 2), 2, DS_FP16, 8, 1, None, None, 0, STREAM) == DS_ERR_ALIGN
+    assert f(A, P(B, C), 2, DS_FP16, 8, 1, ST + 4, None, 0, STREAM) == DS_ERR_ALIGN
+    assert f(A, P(B, C), 2, DS_FP16, 100, 1, ST, D + 4, ws, STREAM) == DS_ERR_ALIGN
+    assert f(A, P(B, C), 2, DS_FP16, 100, 1, ST, D, ws - 8, STREAM) == DS_ERR_SIZE     # short workspace
+    assert f(A, P(B, A + 16), 2, DS_FP16, 64, 1, None, None, 0, STREAM) == DS_ERR_ALIAS  # a gradient inside acc
+    assert f(A, P(B, C), 2, DS_FP16, 64, 0, A + 32, None, 0, STREAM) == DS_ERR_ALIAS     # state inside acc
+    assert f(A, P(B, C), 2, DS_FP16, 64, 0, ST, C + 16, 8, STREAM) == DS_ERR_ALIAS       # workspace on a gradient
+
+
 def test_check_overflow_validation():
     chk = L.ds_check_overflow
     assert chk(ST, A, DS_FP16, -1, STREAM) == DS_ERR_SIZE

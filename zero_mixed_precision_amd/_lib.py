@@ -22,7 +22,7 @@ EXPORTED = (
     "ds_check_overflow", "ds_adam_step", "ds_update_loss_scale", "ds_adam_bias_scalars",
     "ds_layout_greedy", "ds_partition_range", "ds_status_string", "ds_sumsq_workspace_bytes",
     "ds_check_overflow_sumsq", "ds_accumulate_sumsq", "ds_adam_step_sched", "ds_lr_scalars",
-    "ds_adam_step_fused",
+    "ds_adam_step_fused", "ds_accumulate_multi",
 )
 DS_LR_WARMUP, DS_LR_WARMUP_DECAY = 1, 2
 
@@ -117,6 +117,8 @@ def _load():
         "ds_sumsq_workspace_bytes": ([i64], ctypes.c_size_t),
         "ds_check_overflow_sumsq": ([vp, vp, ctypes.c_int, i64, vp, ctypes.c_size_t, vp], ctypes.c_int),
         "ds_accumulate_sumsq": ([vp, vp, ctypes.c_int, i64, i32, vp, vp, ctypes.c_size_t, vp], ctypes.c_int),
+        "ds_accumulate_multi": ([vp, ctypes.POINTER(vp), i32, ctypes.c_int, i64, i32, vp, vp, ctypes.c_size_t, vp],
+                                ctypes.c_int),
         "ds_update_loss_scale": ([vp, vp], ctypes.c_int),
         "ds_adam_bias_scalars": ([vp, f32, f32, f32, vp, vp], ctypes.c_int),
         "ds_adam_step_sched": ([vp, vp, vp, vp, vp, ctypes.c_int, vp, ctypes.c_int, i64,
@@ -282,6 +284,18 @@ def ds_accumulate_sumsq(acc, g16, gdt, n, overwrite, st, workspace, workspace_by
                                 _p(workspace, ds_sumsq_workspace_bytes(max(n, 0)), "workspace"),
                                 _nbytes(workspace, workspace_bytes), _s(stream)),
         "ds_accumulate_sumsq")
+
+
+def ds_accumulate_multi(acc, grads, gdt, n, overwrite, st_or_null=None, workspace=None, workspace_bytes=None,
+                        stream=None) -> None:
+    """``grads``: a sequence of 1..8 micro-batch gradients (tensors or device
+    addresses), folded into ``acc`` in one pass in this order."""
+    n = int(n)
+    ptrs = (ctypes.c_void_p * max(len(grads), 1))(*[_p(g, 2 * n, f"gradient {k}") for k, g in enumerate(grads)])
+    ws_bytes = 0 if workspace is None else _nbytes(workspace, workspace_bytes)
+    ws = None if workspace is None else _p(workspace, ds_sumsq_workspace_bytes(max(n, 0)), "workspace")
+    _ok(lib.ds_accumulate_multi(_p(acc, 4 * n, "acc"), ptrs, len(grads), int(gdt), n, int(bool(overwrite)),
+                                _scaler(st_or_null), ws, ws_bytes, _s(stream)), "ds_accumulate_multi")
 
 
 def ds_update_loss_scale(st, stream=None) -> None:

@@ -742,6 +742,122 @@ __global__ __launch_bounds__(TPB) void accumulate_kernel(float* __restrict__ acc
         raise_flag(st, bad);
 }
 
+// Several micro-batch gradients folded into the accumulation buffer in one
+// pass: acc = (OVERWRITE ? g_0 : acc + g_0) + g_1 + ... + g_{count-1}, every
+// add an fp32 add in this order, so the result is bit for bit that of count
+// consecutive single-gradient passes, for 2 * count + 8 (or + 4 when
+// overwriting) bytes per element instead of 10 * count.  Tiling, hints, the
+// fused check and the sum-of-squares chunks are those of accumulate_kernel
+// with 256 lanes x 4 quads; the gradient list is indexed with compile-time
+// indices only (no dynamic indexing of the argument).
+constexpr int kMaxFold = 8;
+struct GradList {
+    const uint16_t* p[kMaxFold];
+    int32_t count;
+};
+
+template <int GF, bool OVERWRITE, bool CHECK, bool SUMSQ, bool NT>
+__global__ __launch_bounds__(kStepBlock) void fold_kernel(float* __restrict__ acc, GradList gl, int64_t n,
+                                                          ds_scaler* __restrict__ st, double* __restrict__ part)
+{
+    constexpr int TPB = kStepBlock, U = 4, T = U * TPB;
+    static_assert(!SUMSQ || (CHECK && T * 4 == kChunk), "a tile is one chunk");
+    __shared__ double lds[SUMSQ ? TPB / 64 : 1];
+    f32x4* A = reinterpret_cast<f32x4*>(acc);
+    const int64_t nq = n >> 2;
+    const int64_t ntiles = nq / T;
+    uint32_t bad = 0u;
+    for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
+        const int64_t q0 = tile * T + threadIdx.x;
+        f32x4 r[U];
+        {
+            const u32x2* G = reinterpret_cast<const u32x2*>(gl.p[0]);
+            f32x4 g[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                g[u] = widen4<GF>(load<NT>(G + q0 + u * TPB));
+                if constexpr (!OVERWRITE)
+                    r[u] = load<NT>(A + q0 + u * TPB);
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                if constexpr (OVERWRITE)
+                    r[u] = g[u];
+                else
+                    r[u] = r[u] + g[u];
+            }
+        }
+#pragma unroll
+        for (int k = 1; k < kMaxFold; ++k) {
+            if (k < gl.count) {
+                const u32x2* G = reinterpret_cast<const u32x2*>(gl.p[k]);
+                f32x4 g[U];
+#pragma unroll
+                for (int u = 0; u < U; ++u)
+                    g[u] = widen4<GF>(load<NT>(G + q0 + u * TPB));
+#pragma unroll
+                for (int u = 0; u < U; ++u)
+                    r[u] = r[u] + g[u];
+            }
+        }
+        double s = 0.0;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if constexpr (CHECK)
+                bad |= nonfinite_f32x4(r[u]);
+            if constexpr (SUMSQ)
+                s = s + sq4(r[u]);
+            store<NT>(A + q0 + u * TPB, r[u]);
+        }
+        if constexpr (SUMSQ) {
+            const double cs = block_sum_fixed<TPB>(s, lds);
+            if (threadIdx.x == 0)
+                part[tile] = cs;
+        }
+    }
+    if (blockIdx.x == 0) {
+        double s = 0.0;
+        for (int64_t q = ntiles * T + threadIdx.x; q < nq; q += TPB) {
+            f32x4 r = widen4<GF>(load<NT>(reinterpret_cast<const u32x2*>(gl.p[0]) + q));
+            if constexpr (!OVERWRITE)
+                r = load<NT>(A + q) + r;
+#pragma unroll
+            for (int k = 1; k < kMaxFold; ++k)
+                if (k < gl.count)
+                    r = r + widen4<GF>(load<NT>(reinterpret_cast<const u32x2*>(gl.p[k]) + q));
+            if constexpr (CHECK)
+                bad |= nonfinite_f32x4(r);
+            if constexpr (SUMSQ)
+                s = s + sq4(r);
+            store<NT>(A + q, r);
+        }
+        if (static_cast<int64_t>(threadIdx.x) < (n & 3)) {
+            const int64_t i = (nq << 2) + threadIdx.x;
+            float r = dec1<GF>(gl.p[0][i]);
+            if constexpr (!OVERWRITE)
+                r = acc[i] + r;
+#pragma unroll
+            for (int k = 1; k < kMaxFold; ++k)
+                if (k < gl.count)
+                    r = r + dec1<GF>(gl.p[k][i]);
+            if constexpr (CHECK)
+                bad |= nonfinite_f32(__float_as_uint(r));
+            if constexpr (SUMSQ)
+                s = s + sq(r);
+            acc[i] = r;
+        }
+        if constexpr (SUMSQ) {
+            if (ntiles * T * 4 < n) {          // a last, partial chunk exists
+                const double cs = block_sum_fixed<TPB>(s, lds);
+                if (threadIdx.x == 0)
+                    part[ntiles] = cs;
+            }
+        }
+    }
+    if constexpr (CHECK)
+        raise_flag(st, bad);
+}
+
 __global__ void write_state_kernel(ds_scaler* st, ds_scaler value) { *st = value; }
 
 // ---------------------------------------------------------------------------
@@ -983,6 +1099,31 @@ ds_status adam_step(const ds_scaler* st, float* master, float* m, float* v, uint
     const AdamArgs args{const_cast<ds_scaler*>(st), master, m, v, p16, grad, n, hp};
     launch_adam(fmt_of(dt), fmt_of(pdt), wd, nt, unroll, fuse, blocks, s, args);
     return launched();
+}
+
+template <int GF, bool OW>
+void launch_fold2(bool ck, bool sumsq, bool nt, unsigned blocks, hipStream_t s, float* acc, const GradList& gl,
+                  int64_t n, ds_scaler* st, double* part)
+{
+    const unsigned b = blocks;
+    if (sumsq) {
+        if (nt) fold_kernel<GF, OW, true, true, true><<<b, kStepBlock, 0, s>>>(acc, gl, n, st, part);
+        else    fold_kernel<GF, OW, true, true, false><<<b, kStepBlock, 0, s>>>(acc, gl, n, st, part);
+    } else if (ck) {
+        if (nt) fold_kernel<GF, OW, true, false, true><<<b, kStepBlock, 0, s>>>(acc, gl, n, st, nullptr);
+        else    fold_kernel<GF, OW, true, false, false><<<b, kStepBlock, 0, s>>>(acc, gl, n, st, nullptr);
+    } else {
+        if (nt) fold_kernel<GF, OW, false, false, true><<<b, kStepBlock, 0, s>>>(acc, gl, n, nullptr, nullptr);
+        else    fold_kernel<GF, OW, false, false, false><<<b, kStepBlock, 0, s>>>(acc, gl, n, nullptr, nullptr);
+    }
+}
+
+template <int GF>
+void launch_fold(bool ow, bool ck, bool sumsq, bool nt, unsigned blocks, hipStream_t s, float* acc,
+                 const GradList& gl, int64_t n, ds_scaler* st, double* part)
+{
+    if (ow) launch_fold2<GF, true>(ck, sumsq, nt, blocks, s, acc, gl, n, st, part);
+    else    launch_fold2<GF, false>(ck, sumsq, nt, blocks, s, acc, gl, n, st, part);
 }
 
 }  // namespace
@@ -1237,6 +1378,68 @@ ds_status ds_accumulate_sumsq(float* acc, const uint16_t* g16, ds_dtype gdt, int
     if (launched() != DS_OK)
         return DS_ERR_HIP;
     sumsq_finish_kernel<1024><<<1, 1024, 0, s>>>(st, part, sumsq_chunks(n));
+    return launched();
+}
+
+ds_status ds_accumulate_multi(float* acc, const uint16_t* const* grads, int32_t count, ds_dtype gdt, int64_t n,
+                              int32_t overwrite, ds_scaler* st_or_null, void* workspace_or_null,
+                              size_t workspace_bytes, void* stream)
+{
+    if (!size_ok(n) || count < 1 || count > kMaxFold)
+        return DS_ERR_SIZE;
+    if (!is16(gdt))
+        return DS_ERR_DTYPE;
+    if (workspace_or_null != nullptr && st_or_null == nullptr)
+        return DS_ERR_NULL;
+    if (n == 0)
+        return DS_OK;
+    if (acc == nullptr || grads == nullptr)
+        return DS_ERR_NULL;
+    for (int32_t k = 0; k < count; ++k)
+        if (grads[k] == nullptr)
+            return DS_ERR_NULL;
+    if (!aligned(acc, 16) || (st_or_null != nullptr && !aligned(st_or_null, 8)))
+        return DS_ERR_ALIGN;
+    for (int32_t k = 0; k < count; ++k)
+        if (!aligned(grads[k], 16))
+            return DS_ERR_ALIGN;
+    const bool sumsq = workspace_or_null != nullptr;
+    if (sumsq) {
+        if (const ds_status w = check_workspace(workspace_or_null, workspace_bytes, n); w != DS_OK)
+            return w;
+    }
+    // written: acc, the state, the workspace; read: the gradients (which may
+    // repeat or overlap one another)
+    const uint64_t un = static_cast<uint64_t>(n);
+    const uint64_t wb = sumsq ? 8 * static_cast<uint64_t>(sumsq_chunks(n)) : 0;
+    const void* out[3] = {acc, st_or_null, workspace_or_null};
+    const uint64_t out_bytes[3] = {4 * un, st_or_null != nullptr ? sizeof(ds_scaler) : 0, wb};
+    for (int i = 0; i < 3; ++i) {
+        for (int j = i + 1; j < 3; ++j)
+            if (overlap(out[i], out_bytes[i], out[j], out_bytes[j]))
+                return DS_ERR_ALIAS;
+        for (int32_t k = 0; k < count; ++k)
+            if (overlap(out[i], out_bytes[i], grads[k], 2 * un))
+                return DS_ERR_ALIAS;
+    }
+    GradList gl{};
+    for (int32_t k = 0; k < count; ++k)
+        gl.p[k] = grads[k];
+    gl.count = count;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const unsigned blocks = grid_blocks(tiles_of(n, 4));
+    const bool nt = variant_nt(n);
+    const bool ck = st_or_null != nullptr;
+    double* part = static_cast<double*>(workspace_or_null);
+    if (gdt == DS_BF16)
+        launch_fold<kBF16>(overwrite != 0, ck, sumsq, nt, blocks, s, acc, gl, n, st_or_null, part);
+    else
+        launch_fold<kF16>(overwrite != 0, ck, sumsq, nt, blocks, s, acc, gl, n, st_or_null, part);
+    if (!sumsq)
+        return launched();
+    if (launched() != DS_OK)
+        return DS_ERR_HIP;
+    sumsq_finish_kernel<1024><<<1, 1024, 0, s>>>(st_or_null, part, sumsq_chunks(n));
     return launched();
 }
 
