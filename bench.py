@@ -113,6 +113,11 @@ def gpu_run(args):
     free = torch.cuda.mem_get_info(dev)[0]
     fit = max(1, int((free - (4 << 30)) // (2 * n)))
     nbuf = max(1, min(total_mb, fit, args.max_grad_buffers))
+    if not 1 <= args.fold <= 8:
+        sys.exit("bench.py: --fold takes 1..8")
+    fold = min(args.fold, K)
+    if fold > nbuf:
+        sys.exit(f"bench.py: --fold {fold} needs {fold} gradient buffers at once; {nbuf} fit")
     grads = []
     for b in range(nbuf):
         g = torch.empty(n, dtype=torch.int16, device=dev)
@@ -151,7 +156,7 @@ def gpu_run(args):
             else:
                 _lib.ds_check_overflow_sumsq(st_p, g, gdt16, n, ws_p, ws_bytes, stream=q)
             gptr, dt = g, gdt16
-        else:
+        elif fold == 1:
             for k in range(K):
                 g = grad_p[(base + k) % nbuf]
                 for start, size in buckets:
@@ -160,6 +165,15 @@ def gpu_run(args):
                         _lib.ds_accumulate_sumsq(a, gp, gdt16, size, k == 0, st_p, ws_p, ws_bytes, stream=q)
                     else:
                         _lib.ds_accumulate(a, gp, gdt16, size, k == 0, st_p if k == K - 1 else None, q)
+            gptr, dt = acc_p, _lib.DS_FP32
+        else:   # groups of `fold` micro-batches, each folded into the buffer in one pass
+            for g0 in range(0, K, fold):
+                grp = [grad_p[(base + k) % nbuf] for k in range(g0, min(g0 + fold, K))]
+                last = g0 + fold >= K
+                for start, size in buckets:
+                    _lib.ds_accumulate_multi(acc_p + 4 * start, [g + 2 * start for g in grp], gdt16, size, g0 == 0,
+                                             st_p if last else None, ws_p if (last and ws is not None) else None,
+                                             ws_bytes, stream=q)
             gptr, dt = acc_p, _lib.DS_FP32
         if whole:
             c1 = torch.cuda.Event(enable_timing=True)
@@ -256,7 +270,11 @@ def gpu_run(args):
     mix_gbs = 28 * nm / mix_s / 1e9
     bytes_per_elem = 28 if K == 1 else 30
     achieved = bytes_per_elem * n / adam_avg_s / 1e9
-    step_bytes = (2 + 28) if K == 1 else (6 + 10 * (K - 1) + 30)
+    if K == 1:
+        step_bytes = 2 + 28
+    else:   # each fold of f micro-batches: 2f + 4 bytes (the first, overwriting) or 2f + 8, then Adam's 30
+        sizes = [min(fold, K - g0) for g0 in range(0, K, fold)]
+        step_bytes = sum(2 * f + (4 if i == 0 else 8) for i, f in enumerate(sizes)) + 30
     traffic = load_traffic(w.name, "bf16" if args.bf16 else "fp16")
     out = {
         "metric": METRIC,
@@ -279,6 +297,7 @@ def gpu_run(args):
             "workload": w.name,
             "psi": n,
             "micro_batches": K,
+            "fold": fold,
             "grad": ("bf16 N(0,%g)" % w.sigma if args.bf16 else "fp16 N(0,%g) x %g" % (w.sigma, w.mult))
                     + (" heavy tail" if w.heavy_tail else ""),
             "state": "fp32 master/m/v, %s params" % ("bf16" if args.bf16 else "fp16"),
@@ -465,6 +484,9 @@ def main(argv=None):
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--cpu-slice", type=int, default=1 << 24)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--fold", type=int, default=1,
+                    help="micro-batches folded into the accumulation buffer per pass (1..8; K > 1 workloads; "
+                         "needs that many gradient buffers held at once)")
     ap.add_argument("--step-log", default=None,
                     help="write one JSON line per step (scale used, overflow, t, growth count, device time) "
                          "from an untimed pass")

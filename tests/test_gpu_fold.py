@@ -159,3 +159,42 @@ def test_whole_steps_with_folded_accumulation(torch):
         gu.check_scaler(d.scaler(), o.scaler, ov, f"fold step {s}")
         du = gu.compare_full(f"fold step {s}", d, o)
         assert max(du.values()) == 0, du
+
+
+@pytest.mark.parametrize("clip", [0.0, 0.05])
+def test_shard_step_folds_lists(torch, clip):
+    """ShardStep.accumulate with lists (folds of 2, 1 and 2 of K = 5) and
+    full_step (one fold of 5) give the oracle's steps; with clipping active the
+    fold's sum of squares feeds the multiplier (within the usual bar)."""
+    from zero_mixed_precision_amd import ShardStep, ZeroMPConfig
+    n, K = 30_011, 5
+    cfg = ZeroMPConfig(lr=LR, betas=(BETA1, BETA2), eps=EPS, initial_scale_power=14, loss_scale_window=2,
+                       hysteresis=1, gradient_accumulation_steps=K, gradient_clipping=clip)
+    master0 = synth.host_master32(synth.stream_key(4500, synth.ARR_MASTER), np.arange(n), MASTER_SIGMA)
+    a, b = ShardStep(n, cfg), ShardStep(n, cfg)
+    for sh in (a, b):
+        sh.master.copy_(torch.from_numpy(master0))
+        sh.p16.zero_()
+    o = oracle.State(master0.copy(), np.zeros(n, np.float32), np.zeros(n, np.float32), np.zeros(n, np.uint16),
+                     oracle.Scaler(2.0 ** 14, 1.0, 2, 1))
+    spec = synth.GradSpec(1e-3, 2.0 ** 14)
+    for s in range(4):
+        gs = [synth.host_grad16(synth.stream_key(4501, synth.ARR_GRAD, s, k), np.arange(n), spec) for k in range(K)]
+        if s == 1:
+            gs[3][5] = 0x7C00
+        dev = [gu.dev_u16(torch, g).view(torch.float16) for g in gs]
+        a.accumulate(dev[0:2])
+        a.accumulate(dev[2])
+        a.accumulate(dev[3:5])
+        a.step()
+        b.full_step(dev)
+        ov = oracle.step(o, gs, max_grad_norm=clip, **HP)
+        torch.cuda.synchronize()
+        assert a.scaler().as_dict() == b.scaler().as_dict()
+        gu.check_scaler(a.scaler(), o.scaler, ov, f"ShardStep fold step {s}")
+        for x, y in ((a.master, b.master), (a.m, b.m), (a.v, b.v)):
+            assert torch.equal(x.view(torch.int32), y.view(torch.int32))
+        du = gu.compare_arrays(f"ShardStep fold step {s}", gu.host_f32(a.master), gu.host_f32(a.m),
+                               gu.host_f32(a.v), gu.host_u16(a.p16.view(torch.int16)), o.master, o.m, o.v, o.p16)
+        if clip == 0.0:
+            assert max(du.values()) == 0, du

@@ -6,7 +6,10 @@ the C ABI on one HIP stream ("DeepSpeed complete guide" section 5.1: backward
 scales and accumulates, step() updates):
 
     K > 1:  ds_accumulate per bucket for micro-batches 1..K (the last one also
-            checks for inf/NaN), then the Adam step on the fp32 buffer
+            checks for inf/NaN), then the Adam step on the fp32 buffer;
+            micro-batches handed over together (a list to accumulate(), or
+            full_step()) are folded in one pass each (ds_accumulate_multi, up
+            to 8 at a time, the same result with less memory traffic)
     K = 1:  ds_check_overflow on the fp16 gradient, then the Adam step on it
 
 The Adam step covers the whole partition in one ds_adam_step_fused call,
@@ -75,9 +78,15 @@ class ShardStep:
             raise ValueError(f"the gradient must be a contiguous tensor on {self.master.device}")
 
     def accumulate(self, g16) -> None:
-        """Add one fp16 micro-batch gradient (K > 1); the K-th call also checks it."""
+        """Add one fp16 micro-batch gradient (K > 1), or a list of up to 8 of them
+        in micro-batch order, folded into the buffer in one pass (the same result
+        as one call each, with less memory traffic); the call that completes the
+        K micro-batches also checks the sum."""
         if self.K == 1:
             raise RuntimeError("accumulate() is for gradient_accumulation_steps > 1; pass the gradient to step()")
+        if isinstance(g16, (list, tuple)):
+            self._fold(list(g16))
+            return
         if self._micro >= self.K:
             raise RuntimeError(f"accumulate() called more than {self.K} times before step()")
         self._check_grad(g16)
@@ -93,6 +102,23 @@ class ShardStep:
                 _lib.ds_accumulate(a, g, self.gdt, size, overwrite=(k == 0), st_or_null=st if last else None,
                                    stream=self.stream)
         self._micro = k + 1
+
+    def _fold(self, grads) -> None:
+        count = len(grads)
+        if not 1 <= count <= 8:
+            raise ValueError("a fold takes 1 to 8 micro-batch gradients")
+        if self._micro + count > self.K:
+            raise RuntimeError(f"{self._micro} + {count} micro-batches exceed gradient_accumulation_steps={self.K}")
+        for g in grads:
+            self._check_grad(g)
+        first, last = self._micro == 0, self._micro + count == self.K
+        st, acc = self.state.data_ptr(), self.acc.data_ptr()
+        base = [g.data_ptr() for g in grads]
+        for start, size in self.buckets:
+            ws = self.ws.data_ptr() if (last and self.ws is not None) else None
+            _lib.ds_accumulate_multi(acc + 4 * start, [b + 2 * start for b in base], self.gdt, size, first,
+                                     st if last else None, ws, self._ws_bytes, stream=self.stream)
+        self._micro += count
 
     def step(self, g16=None) -> None:
         """Finish the step: check (K = 1), gated Adam, scaler update."""
@@ -127,8 +153,8 @@ class ShardStep:
             return
         if len(grads) != self.K:
             raise ValueError(f"expected {self.K} micro-batch gradients, got {len(grads)}")
-        for g in grads:
-            self.accumulate(g)
+        for i in range(0, self.K, 8):           # all K are at hand: fold up to 8 per pass
+            self.accumulate(list(grads[i:i + 8]))
         self.step()
 
     def graph(self, grads):
