@@ -787,17 +787,25 @@ __global__ __launch_bounds__(kStepBlock) void fold_kernel(float* __restrict__ ac
                     r[u] = r[u] + g[u];
             }
         }
+        // every gradient's loads issued before the first add (U x 8 B in flight
+        // per lane and gradient; measured 1-3 % faster than loading each
+        // gradient just before its add)
+        u32x2 raw[kMaxFold - 1][U];
 #pragma unroll
         for (int k = 1; k < kMaxFold; ++k) {
             if (k < gl.count) {
                 const u32x2* G = reinterpret_cast<const u32x2*>(gl.p[k]);
-                f32x4 g[U];
 #pragma unroll
                 for (int u = 0; u < U; ++u)
-                    g[u] = widen4<GF>(load<NT>(G + q0 + u * TPB));
+                    raw[k - 1][u] = load<NT>(G + q0 + u * TPB);
+            }
+        }
+#pragma unroll
+        for (int k = 1; k < kMaxFold; ++k) {
+            if (k < gl.count) {
 #pragma unroll
                 for (int u = 0; u < U; ++u)
-                    r[u] = r[u] + g[u];
+                    r[u] = r[u] + widen4<GF>(raw[k - 1][u]);
             }
         }
         double s = 0.0;
