@@ -6,8 +6,9 @@ a tile, or up to 70,000 elements), the micro-batch count and bucket cuts, the
 scaler settings (initial scale, window, hysteresis, consecutive hysteresis,
 floor), Adam's hyperparameters (including beta 0 and weight decay), a
 constant learning rate or a WarmupLR / WarmupDecayLR schedule, clipping (off,
-active or never reached), the fused or the separate scaler update, and
-non-finite values planted in random steps, micro-batches and positions.  The
+active or never reached), the fused or the separate scaler update, one
+accumulation pass per micro-batch or folds of several (ds_accumulate_multi),
+and non-finite values planted in random steps, micro-batches and positions.  The
 device runs the step through the C ABI; the oracle runs the same steps.
 
 Bar: scaler state exact after every step; without clipping every array
@@ -72,6 +73,14 @@ def draw_case(seed):
     edges = [0] + [x for x in cuts if x < c["n"]] + [c["n"]]
     c["spans"] = [(a, b - a) for a, b in zip(edges[:-1], edges[1:]) if b > a]
     c["sigma"] = float(r.choice([1e-3, 3e-2]))
+    # drawn apart, so that the cases above stay as they were: fold groups of
+    # the K micro-batches (ds_accumulate_multi) instead of one pass each
+    rf = np.random.default_rng(7_000_003 * seed + 5)
+    if c["K"] > 1 and rf.random() < 0.5:
+        cut = int(rf.integers(1, c["K"] + 1))
+        c["groups"] = [list(range(0, cut)), list(range(cut, c["K"]))] if cut < c["K"] else [list(range(c["K"]))]
+    else:
+        c["groups"] = None
     return c
 
 
@@ -125,6 +134,14 @@ def test_random_configuration(torch, seed):
             else:
                 _lib.ds_check_overflow(st, gs[0], dt16, n)
             grad, dt = gs[0], dt16
+        elif c["groups"] is not None:
+            for gi, grp in enumerate(c["groups"]):
+                last = gi == len(c["groups"]) - 1
+                for start, size in c["spans"]:
+                    _lib.ds_accumulate_multi(acc.data_ptr() + 4 * start, [gs[k].data_ptr() + 2 * start for k in grp],
+                                             dt16, size, gi == 0, st if last else None,
+                                             ws if (last and clip > 0) else None)
+            grad, dt = acc, _lib.DS_FP32
         else:
             for k, g in enumerate(gs):
                 last = k == K - 1
