@@ -43,7 +43,7 @@ def sample_indices(w, buckets):
     return np.unique(np.concatenate(parts).astype(np.int64))
 
 
-def run_sampled(torch, name, fused=False, bf16=False):
+def run_sampled(torch, name, fused=False, bf16=False, fold=1):
     from zero_mixed_precision_amd import _lib, FlatLayout
 
     w = WORKLOADS[name]
@@ -77,6 +77,8 @@ def run_sampled(torch, name, fused=False, bf16=False):
     p16 = torch.empty(n, dtype=torch.int16, device="cuda:0")
     synth.device_fill_grad16(torch, tabs, p16, w.p16_key(), synth.GradSpec(0.02, 1.0))
     g16 = torch.empty(n, dtype=torch.int16, device="cuda:0")
+    # fold > 1: the micro-batches of a group are held at once and folded in one pass
+    held = [g16] + [torch.empty(n, dtype=torch.int16, device="cuda:0") for _ in range(fold - 1)]
     acc = torch.empty(n, dtype=torch.float32, device="cuda:0") if K > 1 else None
     st = torch.zeros(_lib.ds_scaler_size(), dtype=torch.uint8, device="cuda:0")
     _lib.ds_state_init(st, init_scale, w.min_scale, w.window, w.hysteresis, 0, int(dynamic))
@@ -86,16 +88,23 @@ def run_sampled(torch, name, fused=False, bf16=False):
         inj = w.injection(s)
         gs_host = []
         for k in range(K):
-            synth.device_fill_grad16(torch, tabs, g16, w.grad_key(s, k), spec)
+            buf = held[k % fold]
+            synth.device_fill_grad16(torch, tabs, buf, w.grad_key(s, k), spec)
             gh = synth.host_grad16(w.grad_key(s, k), I, spec)
             if inj is not None and inj[0] == k:
-                g16[inj[1]] = torch.tensor(inf16, dtype=torch.int32).to(torch.int16)
+                buf[inj[1]] = torch.tensor(inf16, dtype=torch.int32).to(torch.int16)
                 gh[np.searchsorted(I, inj[1])] = inf16
             gs_host.append(gh)
-            if K > 1:
+            if K > 1 and fold == 1:
                 for start, size in buckets:
                     _lib.ds_accumulate(acc.data_ptr() + 4 * start, g16.data_ptr() + 2 * start, dt16, size,
                                        k == 0, st if k == K - 1 else None)
+            elif K > 1 and (k % fold == fold - 1 or k == K - 1):
+                first = k - k % fold
+                for start, size in buckets:
+                    _lib.ds_accumulate_multi(acc.data_ptr() + 4 * start,
+                                             [held[j % fold].data_ptr() + 2 * start for j in range(first, k + 1)],
+                                             dt16, size, first == 0, st if k == K - 1 else None)
         if K == 1:
             _lib.ds_check_overflow(st, g16, dt16, n)
         grad, dt = (g16, dt16) if K == 1 else (acc, _lib.DS_FP32)
@@ -115,7 +124,7 @@ def run_sampled(torch, name, fused=False, bf16=False):
                                    gu.host_f32(v[Id]), gu.host_u16(p16[Id]), o.master, o.m, o.v, o.p16)
             gu.say(f"[{name}] {fmt} step {s}: scale 2^{int(np.log2(o.scaler.scale))} applied {o.scaler.applied} "
                    f"max ulp {du}")
-    del master, m, v, p16, g16, acc, st
+    del master, m, v, p16, g16, held, acc, st
     torch.cuda.empty_cache()
     return o.scaler
 
@@ -153,6 +162,16 @@ def test_zero1_shard_of_70b_fused_scaler_update(torch):
 
 def test_ragged_layout_fused_scaler_update(torch):
     sc = run_sampled(torch, "ragged", fused=True)
+    assert sc.applied == 27 and sc.scale == 2.0 ** 14
+
+
+@pytest.mark.parametrize("fold", [8, 3])
+def test_ragged_layout_folded_accumulation(torch, fold):
+    """The launch bench.py --workload ragged --fold F times: the 8 micro-batches
+    held at once and folded per bucket (fold 3: groups of 3, 3 and 2), with the
+    injected overflows, at full size (eight 13 GB gradient buffers beside the
+    130 GB state)."""
+    sc = run_sampled(torch, "ragged", fused=True, fold=fold)
     assert sc.applied == 27 and sc.scale == 2.0 ** 14
 
 
