@@ -60,9 +60,11 @@ constexpr int kStepBlock = 256;    // lanes per block of the read/write kernels
 // covers the same 4096-element tile with 512 lanes x 2 quads: twice the waves
 // per CU hide more of the latency of a short kernel (step kernel time at 2^20 /
 // 2^22 / 2^24 elements: 11.5 / 24.5 / 73.9 us vs 12.0 / 27.4 / 74.8 us with
-// 256 x 4); on streamed partitions the two shapes tie or 256 x 4 wins.
+// 256 x 4); on streamed partitions the two shapes tie or 256 x 4 wins.  The
+// fold kernel (several micro-batch gradients per pass) takes this shape too,
+// except in its sum-of-squares form.
 constexpr int kSmallBlock = 512;
-static_assert(2 * kSmallBlock == 4 * kStepBlock, "both shapes of the fused kernel cover one tile per block");
+static_assert(2 * kSmallBlock == 4 * kStepBlock, "both shapes cover one 4096-element tile per block");
 constexpr int kCheckBlock = 1024;  // lanes per block of the read-only check
 constexpr int64_t kMaxBlocks = int64_t(1) << 22;
 constexpr int64_t kChunk = 4096;   // elements per chunk of the gradient sum of squares
@@ -746,21 +748,22 @@ __global__ __launch_bounds__(TPB) void accumulate_kernel(float* __restrict__ acc
 // pass: acc = (OVERWRITE ? g_0 : acc + g_0) + g_1 + ... + g_{count-1}, every
 // add an fp32 add in this order, so the result is bit for bit that of count
 // consecutive single-gradient passes, for 2 * count + 8 (or + 4 when
-// overwriting) bytes per element instead of 10 * count.  Tiling, hints, the
-// fused check and the sum-of-squares chunks are those of accumulate_kernel
-// with 256 lanes x 4 quads; the gradient list is indexed with compile-time
-// indices only (no dynamic indexing of the argument).
+// overwriting) bytes per element instead of 10 * count.  Tiling (one
+// 4096-element tile per block), hints, the fused check and the
+// sum-of-squares chunks are those of accumulate_kernel; the gradient list is
+// indexed with compile-time indices only (no dynamic indexing of the
+// argument).
 constexpr int kMaxFold = 8;
 struct GradList {
     const uint16_t* p[kMaxFold];
     int32_t count;
 };
 
-template <int GF, bool OVERWRITE, bool CHECK, bool SUMSQ, bool NT>
-__global__ __launch_bounds__(kStepBlock) void fold_kernel(float* __restrict__ acc, GradList gl, int64_t n,
-                                                          ds_scaler* __restrict__ st, double* __restrict__ part)
+template <int GF, bool OVERWRITE, bool CHECK, bool SUMSQ, bool NT, int TPB, int U>
+__global__ __launch_bounds__(TPB) void fold_kernel(float* __restrict__ acc, GradList gl, int64_t n,
+                                                   ds_scaler* __restrict__ st, double* __restrict__ part)
 {
-    constexpr int TPB = kStepBlock, U = 4, T = U * TPB;
+    constexpr int T = U * TPB;
     static_assert(!SUMSQ || (CHECK && T * 4 == kChunk), "a tile is one chunk");
     __shared__ double lds[SUMSQ ? TPB / 64 : 1];
     f32x4* A = reinterpret_cast<f32x4*>(acc);
@@ -1113,16 +1116,21 @@ template <int GF, bool OW>
 void launch_fold2(bool ck, bool sumsq, bool nt, unsigned blocks, hipStream_t s, float* acc, const GradList& gl,
                   int64_t n, ds_scaler* st, double* part)
 {
+    // the same 4096-element tile either way; the sum-of-squares form keeps
+    // 256 lanes x 4 quads so that its chunk sums are added in exactly the
+    // order of ds_accumulate_sumsq, the others take 512 x 2 (0.5-1.5 % faster:
+    // fewer registers per lane, twice the waves)
     const unsigned b = blocks;
+    constexpr int W = kSmallBlock;
     if (sumsq) {
-        if (nt) fold_kernel<GF, OW, true, true, true><<<b, kStepBlock, 0, s>>>(acc, gl, n, st, part);
-        else    fold_kernel<GF, OW, true, true, false><<<b, kStepBlock, 0, s>>>(acc, gl, n, st, part);
+        if (nt) fold_kernel<GF, OW, true, true, true, kStepBlock, 4><<<b, kStepBlock, 0, s>>>(acc, gl, n, st, part);
+        else    fold_kernel<GF, OW, true, true, false, kStepBlock, 4><<<b, kStepBlock, 0, s>>>(acc, gl, n, st, part);
     } else if (ck) {
-        if (nt) fold_kernel<GF, OW, true, false, true><<<b, kStepBlock, 0, s>>>(acc, gl, n, st, nullptr);
-        else    fold_kernel<GF, OW, true, false, false><<<b, kStepBlock, 0, s>>>(acc, gl, n, st, nullptr);
+        if (nt) fold_kernel<GF, OW, true, false, true, W, 2><<<b, W, 0, s>>>(acc, gl, n, st, nullptr);
+        else    fold_kernel<GF, OW, true, false, false, W, 2><<<b, W, 0, s>>>(acc, gl, n, st, nullptr);
     } else {
-        if (nt) fold_kernel<GF, OW, false, false, true><<<b, kStepBlock, 0, s>>>(acc, gl, n, nullptr, nullptr);
-        else    fold_kernel<GF, OW, false, false, false><<<b, kStepBlock, 0, s>>>(acc, gl, n, nullptr, nullptr);
+        if (nt) fold_kernel<GF, OW, false, false, true, W, 2><<<b, W, 0, s>>>(acc, gl, n, nullptr, nullptr);
+        else    fold_kernel<GF, OW, false, false, false, W, 2><<<b, W, 0, s>>>(acc, gl, n, nullptr, nullptr);
     }
 }
 
