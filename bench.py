@@ -58,13 +58,14 @@ def load_traffic(workload: str, half: str):
     or None if it is missing, was taken on another kernel source, or on another
     workload or 16-bit format (another instance of the kernel)."""
     try:
-        rec = json.load(open(TRAFFIC_FILE))
+        data = json.load(open(TRAFFIC_FILE))
     except (OSError, ValueError):
         return None
-    if (rec.get("kernel_source_sha256_16") != kernel_source_hash() or rec.get("workload") != workload
-            or rec.get("half") != half):
-        return None
-    return rec.get("traffic_bytes_per_launch")
+    for rec in data.get("records", [data]):
+        if (rec.get("kernel_source_sha256_16") == kernel_source_hash() and rec.get("workload") == workload
+                and rec.get("half") == half):
+            return rec.get("traffic_bytes_per_launch")
+    return None
 
 
 # ----------------------------------------------------------------------------

@@ -8,16 +8,21 @@ import bench
 
 
 def test_traffic_only_for_the_profiled_instance():
-    rec = json.load(open(bench.TRAFFIC_FILE))
-    assert bench.load_traffic(rec["workload"], "bf16" if rec["half"] == "fp16" else "fp16") is None
-    assert bench.load_traffic("ragged" if rec["workload"] != "ragged" else "tiny", rec["half"]) is None
-    got = bench.load_traffic(rec["workload"], rec["half"])
-    if rec["kernel_source_sha256_16"] == bench.kernel_source_hash():
-        # counters of the current source: within 0.1 % of the algorithmic bytes (no re-reads)
-        assert got == rec["traffic_bytes_per_launch"]
-        assert abs(got / rec["algorithmic_bytes_per_launch"] - 1) < 1e-3
-    else:
-        assert got is None
+    data = json.load(open(bench.TRAFFIC_FILE))
+    recs = data.get("records", [data])
+    profiled = {(r["workload"], r["half"]) for r in recs}
+    for half in ("fp16", "bf16"):
+        if ("zero2_7b", half) not in profiled:
+            assert bench.load_traffic("zero2_7b", half) is None
+    assert bench.load_traffic("no_such_workload", "fp16") is None
+    for rec in recs:
+        got = bench.load_traffic(rec["workload"], rec["half"])
+        if rec["kernel_source_sha256_16"] == bench.kernel_source_hash():
+            # counters of the current source: within 0.1 % of the algorithmic bytes (no re-reads)
+            assert got == rec["traffic_bytes_per_launch"]
+            assert abs(got / rec["algorithmic_bytes_per_launch"] - 1) < 1e-3
+        else:
+            assert got is None
 
 
 def test_more_than_one_gpu_is_refused(capsys):
