@@ -137,7 +137,8 @@ def gpu_run(args):
     # the run (checked once here), so the binding's per-call tensor checks stay out
     # of the host's launch loop
     for t, nb in ((master, 4 * n), (m, 4 * n), (v, 4 * n), (p16, 2 * n), (st, _lib.ds_scaler_size())):
-        assert t.is_cuda and t.is_contiguous() and t.numel() * t.element_size() >= nb
+        if not (t.is_cuda and t.is_contiguous() and t.numel() * t.element_size() >= nb):
+            raise RuntimeError("bench.py: a state array is not a contiguous device tensor of the expected size")
     st_p, master_p, m_p, v_p, p16_p = (t.data_ptr() for t in (st, master, m, v, p16))
     acc_p = acc.data_ptr() if acc is not None else None
     ws_p, ws_bytes = (ws.data_ptr(), ws.numel() * 8) if ws is not None else (None, 0)

@@ -103,13 +103,19 @@ def lib():
         L.zo_scaler_update.argtypes = [ctypes.POINTER(ZoScaler), i32]
         L.zo_scaler_update.restype = None
         L.zo_scaler_sizeof.argtypes, L.zo_scaler_sizeof.restype = [], i64
-        assert L.zo_scaler_sizeof() == ctypes.sizeof(ZoScaler)
+        _require(L.zo_scaler_sizeof() == ctypes.sizeof(ZoScaler))
         _lib = L
     return _lib
 
 
+def _require(ok: bool) -> None:
+    """Argument checks that guard the C calls (kept under ``python -O``)."""
+    if not ok:
+        raise ValueError("oracle: array of the wrong type, size or layout")
+
+
 def _ptr(a: np.ndarray) -> int:
-    assert a.flags["C_CONTIGUOUS"]
+    _require(a.flags["C_CONTIGUOUS"])
     return a.ctypes.data
 
 
@@ -158,14 +164,14 @@ def decode(h: np.ndarray, fmt: str = "fp16") -> np.ndarray:
 # -- the four steps ------------------------------------------------------------
 
 def accumulate(acc: np.ndarray, g16: np.ndarray, overwrite: bool, fmt: str = "fp16") -> None:
-    assert acc.dtype == np.float32 and g16.dtype == np.uint16 and acc.size == g16.size
+    _require(acc.dtype == np.float32 and g16.dtype == np.uint16 and acc.size == g16.size)
     lib().zo_accumulate(_ptr(acc), _ptr(g16), acc.size, int(bool(overwrite)), FMT[fmt])
 
 
 def any_nonfinite(grad: np.ndarray, fmt: str = "fp16") -> bool:
     if grad.dtype == np.uint16:
         return bool(lib().zo_any_nonfinite16(_ptr(grad), grad.size, FMT[fmt]))
-    assert grad.dtype == np.float32
+    _require(grad.dtype == np.float32)
     return bool(lib().zo_any_nonfinite32(_ptr(grad), grad.size))
 
 
@@ -186,8 +192,8 @@ def adam(grad, master, m, v, p16, *, scale, accum_steps, t, lr, beta1, beta2, ep
     the format of a 16-bit gradient, ``param_fmt`` that of the parameter copy."""
     n = master.size
     for a, dt in ((master, np.float32), (m, np.float32), (v, np.float32), (p16, np.uint16)):
-        assert a.dtype == dt and a.size == n and a.flags["C_CONTIGUOUS"]
-    assert grad.size == n and grad.dtype in (np.uint16, np.float32)
+        _require(a.dtype == dt and a.size == n and a.flags["C_CONTIGUOUS"])
+    _require(grad.size == n and grad.dtype in (np.uint16, np.float32))
     lib().zo_adam(_ptr(grad), _gfmt(grad, fmt), n, _ptr(master), _ptr(m), _ptr(v), _ptr(p16),
                   FMT[param_fmt], scale, int(accum_steps), int(t), lr, beta1, beta2, eps, weight_decay)
 
@@ -196,7 +202,7 @@ def adam_mult(grad, master, m, v, p16, *, mult, t, lr, beta1, beta2, eps, weight
               fmt="fp16", param_fmt="fp16") -> None:
     """One applied Adam step with an explicit gradient multiplier (fp32)."""
     n = master.size
-    assert grad.size == n and grad.dtype in (np.uint16, np.float32)
+    _require(grad.size == n and grad.dtype in (np.uint16, np.float32))
     lib().zo_adam_mult(_ptr(grad), _gfmt(grad, fmt), n, _ptr(master), _ptr(m), _ptr(v), _ptr(p16),
                        FMT[param_fmt], float(np.float32(mult)), int(t), lr, beta1, beta2, eps,
                        weight_decay)
@@ -227,7 +233,7 @@ def grad_sumsq(grad: np.ndarray, fmt: str = "fp16") -> float:
         for ex in np.unique(E):
             total += int(np.sum(M[E == ex] ** 2)) << int(2 * ex + 48)
         return total / (1 << 48)
-    assert grad.dtype == np.float32
+    _require(grad.dtype == np.float32)
     if not np.all(np.isfinite(grad)):
         return float("inf")
     return math.fsum((grad.astype(np.float64) ** 2).tolist())

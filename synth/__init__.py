@@ -247,7 +247,8 @@ def device_fill_master32(torch, tables: DeviceTables, out, key: int, sigma: floa
 def device_copy(torch, dst, src, stream=None) -> None:
     """Plain 16-byte-vector copy (bandwidth and counter calibration)."""
     nbytes = src.numel() * src.element_size()
-    assert nbytes % 16 == 0 and dst.numel() * dst.element_size() >= nbytes
+    if nbytes % 16 != 0 or dst.numel() * dst.element_size() < nbytes:
+        raise ValueError("device_copy: the source must be a whole number of 16-byte vectors and fit in dst")
     _check(device_lib().synth_copy(dst.data_ptr(), src.data_ptr(), nbytes // 16,
                                    _stream_ptr(torch, stream)), "synth_copy")
 
