@@ -49,14 +49,15 @@
  *    share a ds_scaler must be ordered on one stream.
  *  - Launch-shape knobs, read from the environment at each call (for tests
  *    and tuning; results are bit-identical under every setting):
- *    DSZERO_GRID=<blocks> pins the block count, DSZERO_UNROLL=2|4 sets the
- *    quads per lane of the read/write kernels (ds_adam_step_fused and the
- *    sum-of-squares accumulation ignore it: they always take 4096-element
- *    tiles, ds_adam_step_fused as 256 lanes x 4 quads with non-temporal
- *    hints and 512 lanes x 2 quads without), DSZERO_NT=0|1 turns their
- *    non-temporal load/store hints off or on (default: on above 2^24
- *    elements, off at and below, where the state stays in the Infinity Cache
- *    between steps).
+ *    DSZERO_GRID=<blocks> pins the block count; DSZERO_UNROLL=2 halves the
+ *    tile of ds_adam_step and ds_accumulate to 2048 elements (256 lanes x 2
+ *    quads; by default every read/write kernel takes 4096-element tiles, as
+ *    256 lanes x 4 quads, or 512 x 2 for ds_adam_step_fused without
+ *    non-temporal hints, the overwriting ds_accumulate and
+ *    ds_accumulate_multi without a sum of squares); DSZERO_NT=0|1 turns the
+ *    non-temporal load/store hints of the read/write kernels off or on
+ *    (default: on above 2^24 elements, off at and below, where the state
+ *    stays in the Infinity Cache between steps).
  */
 #ifndef DSZERO_H
 #define DSZERO_H
