@@ -49,12 +49,11 @@
  *    share a ds_scaler must be ordered on one stream.
  *  - Launch-shape knobs, read from the environment at each call (for tests
  *    and tuning; results are bit-identical under every setting):
- *    DSZERO_GRID=<blocks> pins the block count; DSZERO_UNROLL=2 halves the
- *    tile of ds_adam_step and ds_accumulate to 2048 elements (256 lanes x 2
- *    quads; by default every read/write kernel takes 4096-element tiles, as
- *    256 lanes x 4 quads, or 512 x 2 for ds_adam_step_fused without
- *    non-temporal hints, the overwriting ds_accumulate and
- *    ds_accumulate_multi without a sum of squares); DSZERO_NT=0|1 turns the
+ *    DSZERO_GRID=<blocks> pins the block count of every kernel of the call
+ *    (the kernels loop over their tiles or chunks); DSZERO_UNROLL=2 halves
+ *    the tile of ds_adam_step to 2048 elements (256 lanes x 2 quads; by
+ *    default 4096 elements as 256 lanes x 4 quads, or 512 x 2 for
+ *    ds_adam_step_fused without non-temporal hints); DSZERO_NT=0|1 turns the
  *    non-temporal load/store hints of the read/write kernels off or on
  *    (default: on above 2^24 elements, off at and below, where the state
  *    stays in the Infinity Cache between steps).
@@ -116,7 +115,8 @@ typedef struct ds_scaler {
     double grad_sumsq;              /* sum of squares of the step's gradient so far   */
     double last_grad_sumsq;         /* grad_sumsq consumed by the last update         */
     uint32_t blocks_done;           /* ds_adam_step_fused: blocks finished (0 between steps) */
-    uint8_t reserved[44];           /* zero                                           */
+    uint32_t sumsq_blocks_done;     /* sum-of-squares second pass: blocks finished (0 between calls) */
+    uint8_t reserved[40];           /* zero                                           */
 } ds_scaler;
 
 /* sizeof(ds_scaler) as compiled into the library (128). */
@@ -280,15 +280,18 @@ ds_status ds_update_loss_scale(ds_scaler* st, void* stream);
  * that already read the gradient.  Both add sum(x_i^2) over their n values
  * (the stored, still loss-scaled gradient: fp16 values, or the fp32
  * accumulation) into st->grad_sumsq, in fp64.  The sum is taken over fixed
- * chunks of consecutive elements (16,384 for the check, 4096 for the
- * accumulation), each reduced in a fixed order, and the chunk sums in a fixed
- * order, so the result does not depend on the launch shape.  Several calls
- * per step (disjoint ranges, e.g. buckets) add up in call order.
+ * chunks of consecutive elements (8192 for the check, 1024 for the
+ * accumulation), each reduced in a fixed order, then over groups of 4096
+ * chunk sums and the group sums, each in a fixed order, so the result does
+ * not depend on the launch shape.  Several calls per step (disjoint ranges,
+ * e.g. buckets) add up in call order.
  *
  * workspace: caller-owned DEVICE scratch of at least
- * ds_sumsq_workspace_bytes(n) bytes (one fp64 partial sum per chunk), 8-byte
- * aligned, no initial contents needed.  Each call is two kernels: the pass
- * over the data writes the chunk sums, a one-block kernel adds them in order.
+ * ds_sumsq_workspace_bytes(n) bytes (one fp64 partial sum per chunk and per
+ * group), 8-byte aligned, no initial contents needed.  Each call is two
+ * kernels: the pass over the data writes the chunk sums, a second pass adds
+ * them by groups, and its last block to finish adds the group sums (taking
+ * one ticket per block from st->sumsq_blocks_done, which it leaves at 0).
  * One workspace serves every call on one stream (calls that may run at the
  * same time need their own).
  * Errors as for the plain entry points; DS_ERR_NULL / DS_ERR_SIZE /

@@ -74,7 +74,7 @@ static void validation(void)
     EXPECT(ds_check_overflow(ST, E, (ds_dtype)9, 8, NULL) == DS_ERR_DTYPE);
     EXPECT(ds_check_overflow(ST, (char*)E + 8, DS_FP16, 8, NULL) == DS_ERR_ALIGN);
     const size_t ws = ds_sumsq_workspace_bytes(100000);
-    EXPECT(ws == 8 * 25);
+    EXPECT(ws == 8 * (98 + 1));   /* 98 chunks of 1024 elements, one group of chunk sums */
     EXPECT(ds_check_overflow_sumsq(ST, E, DS_FP16, 100000, A, ws - 8, NULL) == DS_ERR_SIZE);
     EXPECT(ds_accumulate_sumsq(f, (uint16_t*)B, DS_FP16, 100000, 1, ST, NULL, ws, NULL) == DS_ERR_NULL);
     EXPECT(ds_state_init(ST, 0.0f, 1.0f, 1000, 1, 0, 1, NULL) == DS_ERR_HPARAM);

@@ -21,6 +21,17 @@ L = _lib.lib
 
 # fake, never-dereferenced device addresses (validation fails before any launch)
 A, B, C, D, E, ST = (0x10000000 * k for k in range(1, 7))
+
+
+def _no_gpu():
+    import torch
+    return torch.cuda.device_count() == 0   # counts devices without initialising them
+
+
+# The tests that hand the library fake device addresses run only where no GPU
+# is visible: were a validation rule ever lost, the call must not reach a
+# kernel that would dereference them.
+fake_addresses = pytest.mark.skipif(not _no_gpu(), reason="fake device addresses: CPU-only test")
 STREAM = None
 HP = (1e-4, 0.9, 0.999, 1e-8, 0.0, 0.0, 1)
 
@@ -65,6 +76,7 @@ def test_status_strings():
     assert "unknown" in _lib.status_string(99)
 
 
+@fake_addresses
 def test_accumulate_validation():
     acc = L.ds_accumulate
     assert acc(A, B, DS_FP16, -1, 1, None, STREAM) == DS_ERR_SIZE
@@ -80,6 +92,7 @@ def test_accumulate_validation():
     assert acc(A, B, 9, 8, 0, None, STREAM) == DS_ERR_DTYPE
 
 
+@fake_addresses
 def test_accumulate_multi_validation():
     f = L.ds_accumulate_multi
     P = lambda *xs: (ctypes.c_void_p * len(xs))(*xs)
@@ -101,9 +114,10 @@ def test_accumulate_multi_validation():
     assert f(A, P(B, C), 2, DS_FP16, 100, 1, ST, D, ws - 8, STREAM) == DS_ERR_SIZE     # short workspace
     assert f(A, P(B, A + 16), 2, DS_FP16, 64, 1, None, None, 0, STREAM) == DS_ERR_ALIAS  # a gradient inside acc
     assert f(A, P(B, C), 2, DS_FP16, 64, 0, A + 32, None, 0, STREAM) == DS_ERR_ALIAS     # state inside acc
-    assert f(A, P(B, C), 2, DS_FP16, 64, 0, ST, C + 16, 8, STREAM) == DS_ERR_ALIAS       # workspace on a gradient
+    assert f(A, P(B, C), 2, DS_FP16, 64, 0, ST, C + 16, 16, STREAM) == DS_ERR_ALIAS      # workspace on a gradient
 
 
+@fake_addresses
 def test_check_overflow_validation():
     chk = L.ds_check_overflow
     assert chk(ST, A, DS_FP16, -1, STREAM) == DS_ERR_SIZE
@@ -117,6 +131,7 @@ def test_check_overflow_validation():
     assert chk(A + 32, A, DS_FP32, 10, STREAM) == DS_ERR_ALIAS
 
 
+@fake_addresses
 def test_sizes_beyond_any_device_are_refused():
     """n above 2^40 elements (more than any device holds) is DS_ERR_SIZE on every
     entry point that takes n, before any byte count is formed from it."""
@@ -157,6 +172,7 @@ def _adam(*, st=ST, ptrs=(A, B, C, D, E), dt=DS_FP16, pdt=DS_FP16, n=16, hp=HP):
     return L.ds_adam_step(st, master, m, v, p16, pdt, grad, dt, n, *hp, STREAM)
 
 
+@fake_addresses
 def test_adam_validation():
     assert _adam(n=-3) == DS_ERR_SIZE
     assert _adam(dt=0) == DS_ERR_DTYPE
@@ -182,6 +198,7 @@ def _sched_call(sched, st=ST, n=1024, hp=HP[1:]):
                                 ctypes.byref(sched) if sched is not None else None, *hp, STREAM)
 
 
+@fake_addresses
 def test_schedule_layout_and_validation():
     assert ctypes.sizeof(_lib.DsLrSchedule) == 32
     S = _lib.DsLrSchedule.make
@@ -212,6 +229,7 @@ def test_schedule_layout_and_validation():
 NAN, INF = float("nan"), float("inf")
 
 
+@fake_addresses
 @pytest.mark.parametrize("bad", [
     # lr, beta1, beta2, eps, weight_decay, max_grad_norm, accum_steps
     (-1e-4, 0.9, 0.999, 1e-8, 0.0, 0.0, 1), (NAN, 0.9, 0.999, 1e-8, 0.0, 0.0, 1),
@@ -228,9 +246,13 @@ def test_adam_hyperparameter_validation(bad):
     assert _adam(hp=bad) == DS_ERR_HPARAM
 
 
+@fake_addresses
 def test_sumsq_validation():
     ws_need = L.ds_sumsq_workspace_bytes(10000)
-    assert ws_need == 8 * 3 and L.ds_sumsq_workspace_bytes(0) == 0
+    # one fp64 per 1024-element chunk (10) and per group of 4096 chunk sums (1)
+    assert ws_need == 8 * (10 + 1) and L.ds_sumsq_workspace_bytes(0) == 0
+    assert L.ds_sumsq_workspace_bytes(1024 * 4096) == 8 * (4096 + 1)
+    assert L.ds_sumsq_workspace_bytes(1024 * 4096 + 1) == 8 * (4097 + 2)
     WS = 0x70000000
     chk = L.ds_check_overflow_sumsq
     assert chk(ST, A, DS_FP16, -1, WS, ws_need, STREAM) == DS_ERR_SIZE
@@ -256,6 +278,7 @@ def test_sumsq_validation():
     assert acc(A, B, DS_FP32, 10000, 1, ST, WS, ws_need, STREAM) == DS_ERR_DTYPE
 
 
+@fake_addresses
 def test_state_and_scalar_validation():
     init = L.ds_state_init
     assert init(None, 65536.0, 1.0, 1000, 1, 0, 1, STREAM) == DS_ERR_NULL
@@ -418,6 +441,7 @@ class _FakeDeviceTensor:
         return A
 
 
+@fake_addresses
 def test_binding_rejects_host_short_and_strided_tensors():
     """Python callers that pass tensors get an error, not a kernel reading an
     address it may not touch: host tensors, non-contiguous tensors and tensors

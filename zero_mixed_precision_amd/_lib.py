@@ -46,7 +46,8 @@ class DsScaler(ctypes.Structure):
         ("grad_sumsq", ctypes.c_double),
         ("last_grad_sumsq", ctypes.c_double),
         ("blocks_done", ctypes.c_uint32),
-        ("reserved", ctypes.c_uint8 * 44),
+        ("sumsq_blocks_done", ctypes.c_uint32),
+        ("reserved", ctypes.c_uint8 * 40),
     ]
 
     def as_dict(self) -> dict:

@@ -13,22 +13,29 @@
 // not ALU throughput.  Elements are handled in quads of four: each lane moves
 // one 16-byte vector per fp32 array (8 bytes per fp16 array) per quad, so
 // every wave-wide load or store covers one contiguous 1 KiB (fp32) or 512 B
-// (fp16) span.  The read/write kernels (Adam, accumulation) give each
-// 256-lane block one tile of U x 256 consecutive quads (U = 4: 4096
-// elements), issue all of the tile's loads before any arithmetic, and mark
-// loads and stores non-temporal (streamed data is touched once) on partitions
-// above 2^24 elements, whose step traffic is about twice the Infinity Cache or
-// more; the grid has one block per tile.  On the smaller, cache-resident
-// partitions the fused Adam kernel covers the same tile with 512 lanes x 2
-// quads.
-// Measured on MI355X with a 109M-element partition this
-// beats persistent grid-stride launches, whose extra waves per CU congest the
-// memory system under a 50/50 read/write mix.  The read-only overflow check
-// uses 1024-lane blocks, one 16-byte vector per lane, and ordinary (cache-
-// allocating) loads on purpose: the fp16 gradient it reads is read again by
-// the Adam pass right after it, and a partition's gradient of up to ~256 MB
-// (e.g. 109M elements) is then served from the Infinity Cache instead of HBM
-// (measured: 198 -> 214 Gparams/s per step at 109M elements).
+// (fp16) span.  Each block owns one tile of consecutive quads and issues all
+// of the tile's loads before any arithmetic; the grid has one block per tile
+// (up to 2^31 work-items per launch, the blocks loop past that), and loads and
+// stores are marked non-temporal (streamed data is touched once) on
+// partitions above 2^24 elements, whose step traffic is about twice the
+// Infinity Cache or more.  Tile shapes, measured on MI355X against each other
+// in one process (launch shapes of 64-1024 lanes x 1-4 quads, and 8 elements
+// per lane with 16-byte 16-bit accesses, which is 30 % slower for Adam):
+//   * Adam: 256 lanes x 4 quads (4096 elements); every shape tried lies within
+//     1.5 % of it at 1e8-9e9 elements.  On the smaller, cache-resident
+//     partitions the fused Adam kernel covers the same tile with 512 lanes x 2
+//     quads.
+//   * accumulation (one or several micro-batch gradients into the fp32
+//     buffer): one wave, one quad per lane (256 elements): 4-15 % faster than
+//     256 x 4 or 512 x 2 on 1.9e8- and 8.75e9-element ranges.  Their
+//     sum-of-squares forms take one 1024-element chunk per 256-lane block.
+// The read-only overflow check uses 1024-lane blocks, one 16-byte vector per
+// lane, and ordinary (cache-allocating) loads on purpose: the fp16 gradient
+// it reads is read again by the Adam pass right after it, and a partition's
+// gradient of up to ~256 MB (e.g. 109M elements) is then served from the
+// Infinity Cache instead of HBM (measured: 198 -> 214 Gparams/s per step at
+// 109M elements).  Its sum-of-squares form takes 8192-element chunks, 512
+// lanes x 2 vectors.
 //
 // Numerics: IEEE fp32, round to nearest even, one rounding per operation in
 // the written order (built with -ffp-contract=off; fp32 division and square
@@ -55,19 +62,34 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kStepBlock = 256;    // lanes per block of the read/write kernels
+constexpr int kStepBlock = 256;    // lanes per block of the Adam kernel (4 quads per lane)
 // The fused Adam kernel on a cache-resident partition (temporal accesses)
 // covers the same 4096-element tile with 512 lanes x 2 quads: twice the waves
 // per CU hide more of the latency of a short kernel (step kernel time at 2^20 /
 // 2^22 / 2^24 elements: 11.5 / 24.5 / 73.9 us vs 12.0 / 27.4 / 74.8 us with
-// 256 x 4); on streamed partitions the two shapes tie or 256 x 4 wins.  The
-// fold kernel (several micro-batch gradients per pass) takes this shape too,
-// except in its sum-of-squares form.
+// 256 x 4); on streamed partitions the two shapes tie or 256 x 4 wins.
 constexpr int kSmallBlock = 512;
 static_assert(2 * kSmallBlock == 4 * kStepBlock, "both shapes cover one 4096-element tile per block");
 constexpr int kCheckBlock = 1024;  // lanes per block of the read-only check
-constexpr int64_t kMaxBlocks = int64_t(1) << 22;
-constexpr int64_t kChunk = 4096;   // elements per chunk of the gradient sum of squares
+// Accumulation: one wave per block, one quad per lane (256-element tiles).
+constexpr int kAccBlock = 64;
+// Sum-of-squares forms of the accumulation: one chunk of 1024 elements per
+// block, 256 lanes x 1 quad.
+constexpr int kAccSumsqBlock = 256;
+constexpr int64_t kAccChunk = 4 * kAccSumsqBlock;
+// Check with the sum of squares: one chunk of 8192 elements per block, 512
+// lanes x 2 16-byte vectors (16-bit formats) or 4 (fp32).
+constexpr int kCheckSumsqBlock = 512;
+constexpr int64_t kCheckChunk = 8192;
+// Second pass of the sum of squares: each 256-lane block adds one group of
+// 4096 chunk sums (16 per lane, loaded before the adds), the last block to
+// finish adds the group sums.
+constexpr int kFinishBlock = 256;
+constexpr int kFinishPerLane = 16;
+constexpr int64_t kGroup = int64_t(kFinishBlock) * kFinishPerLane;
+// A dispatch counts its grid in work-items with 32 bits; launches stay within
+// 2^31 of them and the kernels loop over the tiles past that.
+constexpr int64_t kMaxWorkItems = int64_t(1) << 31;
 // Largest n any entry point accepts: 2^40 elements is far beyond one GPU's
 // memory (4 TiB of fp32), and keeps every byte count the validation computes
 // (at most 16 bytes per element) far from overflowing.
@@ -196,24 +218,35 @@ __device__ __forceinline__ void raise_flag(ds_scaler* st, uint32_t bad)
 // gradient sum of squares (global-norm clipping), deterministic
 // ---------------------------------------------------------------------------
 
-// Sum over a block in a fixed order: a fixed xor butterfly inside each wave
-// (lane 0's result is used), then the waves' sums in wave order.  The result
-// is meaningful in thread 0.  Every thread of the block must call it.
+// Sum over a block in a fixed order: a fixed xor butterfly inside each wave,
+// then the TPB / 64 wave sums combined by a fixed butterfly in the first wave.
+// The result is meaningful in thread 0.  Every thread of the block must call
+// it.  One barrier per call: `lds` holds two buffers of TPB / 64 doubles and
+// consecutive calls of a block alternate `parity`, so a call never writes the
+// buffer the previous call may still be reading.
 template <int TPB>
-__device__ __forceinline__ double block_sum_fixed(double x, double* lds)
+__device__ __forceinline__ double block_sum_fixed(double x, double* lds, int parity)
 {
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1)
         x = x + __shfl_xor(x, off);
-    if ((threadIdx.x & 63) == 0)
-        lds[threadIdx.x >> 6] = x;
-    __syncthreads();
-    double total = 0.0;
-    if (threadIdx.x == 0)
-        for (int w = 0; w < TPB / 64; ++w)
-            total = total + lds[w];
-    __syncthreads();
-    return total;
+    constexpr int kWaves = TPB / 64;
+    if constexpr (kWaves == 1) {
+        return x;
+    } else {
+        double* buf = lds + parity * kWaves;
+        if ((threadIdx.x & 63) == 0)
+            buf[threadIdx.x >> 6] = x;
+        __syncthreads();
+        double t = 0.0;
+        if (threadIdx.x < 64) {
+            t = threadIdx.x < kWaves ? buf[threadIdx.x] : 0.0;
+#pragma unroll
+            for (int off = kWaves / 2; off > 0; off >>= 1)
+                t = t + __shfl_xor(t, off);
+        }
+        return t;
+    }
 }
 
 __device__ __forceinline__ double sq(float x)
@@ -235,22 +268,55 @@ __device__ __forceinline__ double sq4_exact32(const f32x4& x)
            static_cast<double>(x.w * x.w);
 }
 
-// Second pass of the sum of squares: one block adds the chunk sums in a fixed
-// order (lane j takes chunks j, j + TPB, ..., then the fixed block sum) into
-// st->grad_sumsq.  The chunking is fixed by n, so the result does not depend
-// on the grid of the first pass.
-template <int TPB>
-__global__ __launch_bounds__(TPB) void sumsq_finish_kernel(ds_scaler* __restrict__ st,
-                                                           const double* __restrict__ part,
-                                                           int64_t nchunks)
+// Second pass of the sum of squares over the nparts chunk sums in part[]:
+// block g adds group g (chunk sums g * kGroup ... + kGroup - 1; lane l takes
+// j * kFinishBlock + l of the group for j = 0..15, in j order, then the fixed
+// block sum) into part2[g]; every block then takes a ticket, and the block
+// that takes the last one adds the group sums in a fixed order into
+// st->grad_sumsq and sets the ticket count back to 0.  The chunking is fixed
+// by n, so the result depends on neither grid.  The fences order each
+// block's group sum before its ticket, and the last block's reads after it
+// (the L2 caches of the XCDs are not coherent with one another).
+__global__ __launch_bounds__(kFinishBlock) void sumsq_finish_kernel(ds_scaler* __restrict__ st,
+                                                                    const double* __restrict__ part,
+                                                                    int64_t nparts, double* part2)
 {
-    __shared__ double lds[TPB / 64];
-    double s = 0.0;
-    for (int64_t i = threadIdx.x; i < nchunks; i += TPB)
-        s = s + part[i];
-    const double total = block_sum_fixed<TPB>(s, lds);
-    if (threadIdx.x == 0)
-        st->grad_sumsq = st->grad_sumsq + total;
+    __shared__ double lds[2 * (kFinishBlock / 64)];
+    __shared__ uint32_t is_last;
+    const int64_t ngroups = (nparts + kGroup - 1) / kGroup;
+    int parity = 0;
+    for (int64_t g = blockIdx.x; g < ngroups; g += gridDim.x) {
+        double x[kFinishPerLane];
+#pragma unroll
+        for (int j = 0; j < kFinishPerLane; ++j) {
+            const int64_t i = g * kGroup + static_cast<int64_t>(j) * kFinishBlock + threadIdx.x;
+            x[j] = i < nparts ? part[i] : 0.0;
+        }
+        double s = 0.0;
+#pragma unroll
+        for (int j = 0; j < kFinishPerLane; ++j)
+            s = s + x[j];
+        s = block_sum_fixed<kFinishBlock>(s, lds, parity);
+        parity ^= 1;
+        if (threadIdx.x == 0)
+            part2[g] = s;
+    }
+    if (threadIdx.x == 0) {
+        __threadfence();
+        is_last = atomicAdd(&st->sumsq_blocks_done, 1u) == gridDim.x - 1u ? 1u : 0u;
+    }
+    __syncthreads();
+    if (is_last) {
+        __threadfence();
+        double s = 0.0;
+        for (int64_t g = threadIdx.x; g < ngroups; g += kFinishBlock)
+            s = s + part2[g];
+        s = block_sum_fixed<kFinishBlock>(s, lds, parity);
+        if (threadIdx.x == 0) {
+            st->grad_sumsq = st->grad_sumsq + s;
+            st->sumsq_blocks_done = 0u;
+        }
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -577,14 +643,17 @@ __global__ __launch_bounds__(TPB) void check_kernel(ds_scaler* __restrict__ st,
     raise_flag(st, bad);
 }
 
-// Overflow check plus the chunk sums of squares.  A chunk is TPB lanes x
-// kVecs 16-byte vectors (16-bit formats: 1024 x 2 x 8, fp32: 1024 x 4 x 4 =
-// 16,384 elements); vector j of lane l is vector j * TPB + l of the chunk, so
-// each of the kVecs loads is one contiguous span across the block, and each
-// lane sums its elements in order.  An fp16 value squared is exact in fp32
-// (at most 22 significant bits, between 2^-48 and 65504^2), so fp16 squares
-// are taken in fp32 and widened for the fp64 sum -- the same values as fp64
-// squares, for less fp64 work; bf16 and fp32 squares are taken in fp64.
+// Overflow check plus the chunk sums of squares.  A chunk is kCheckChunk =
+// 8192 elements, TPB = 512 lanes x kVecs 16-byte vectors (16-bit formats: 2
+// vectors of 8, fp32: 4 of 4); vector j of lane l is vector j * TPB + l of
+// the chunk, so each of the kVecs loads is one contiguous span across the
+// block, and each lane sums its elements in order.  An fp16 value squared is
+// exact in fp32 (at most 22 significant bits, between 2^-48 and 65504^2), so
+// fp16 squares are taken in fp32 and widened for the fp64 sum -- the same
+// values as fp64 squares, for less fp64 work; bf16 and fp32 squares are taken
+// in fp64.  One block per chunk (measured at 1.9e8 and 8.75e9 elements: 6.6
+// TB/s, against 6.1-6.2 with 1024 lanes x 2 vectors per 16,384 elements and
+// a two-barrier block sum; the plain check reads at 6.7-6.8).
 template <int GF, int TPB>
 __global__ __launch_bounds__(TPB) void check_sumsq_kernel(ds_scaler* __restrict__ st,
                                                           const void* __restrict__ grad, int64_t n,
@@ -592,15 +661,15 @@ __global__ __launch_bounds__(TPB) void check_sumsq_kernel(ds_scaler* __restrict_
 {
     constexpr bool F32 = GF == kF32;
     constexpr int kPer = F32 ? 4 : 8;
-    constexpr int kVecs = static_cast<int>((4 * kChunk) / (static_cast<int64_t>(TPB) * kPer));
-    constexpr int64_t kCh = static_cast<int64_t>(TPB) * kVecs * kPer;
-    static_assert(kCh == 4 * kChunk, "four 4096-element units per chunk");
-    __shared__ double lds[TPB / 64];
+    constexpr int kVecs = static_cast<int>(kCheckChunk / (static_cast<int64_t>(TPB) * kPer));
+    static_assert(static_cast<int64_t>(TPB) * kVecs * kPer == kCheckChunk, "one chunk per block");
+    __shared__ double lds[2 * (TPB / 64)];
     const u32x4* G = static_cast<const u32x4*>(grad);
-    const int64_t nchunks = (n + kCh - 1) / kCh;
+    const int64_t nchunks = (n + kCheckChunk - 1) / kCheckChunk;
     uint32_t bad = 0u;
+    int parity = 0;
     for (int64_t c = blockIdx.x; c < nchunks; c += gridDim.x) {
-        const int64_t v0 = c * (kCh / kPer) + threadIdx.x;
+        const int64_t v0 = c * (kCheckChunk / kPer) + threadIdx.x;
         u32x4 w[kVecs];
         bool full[kVecs];
 #pragma unroll
@@ -650,7 +719,8 @@ __global__ __launch_bounds__(TPB) void check_sumsq_kernel(ds_scaler* __restrict_
                 }
             }
         }
-        const double cs = block_sum_fixed<TPB>(s, lds);
+        const double cs = block_sum_fixed<TPB>(s, lds, parity);
+        parity ^= 1;
         if (threadIdx.x == 0)
             part[c] = cs;
     }
@@ -661,181 +731,75 @@ __global__ __launch_bounds__(TPB) void check_sumsq_kernel(ds_scaler* __restrict_
 // gradient accumulation
 // ---------------------------------------------------------------------------
 
-// Same tiling as the Adam kernel.  With SUMSQ (which needs CHECK and U * TPB
-// * 4 == 4096) each tile is one chunk of the sum of squares of the result,
-// written to part[tile].
-template <int GF, bool OVERWRITE, bool CHECK, bool SUMSQ, bool NT, int TPB, int U>
-__global__ __launch_bounds__(TPB) void accumulate_kernel(float* __restrict__ acc,
-                                                         const uint16_t* __restrict__ g16,
-                                                         int64_t n, ds_scaler* __restrict__ st,
-                                                         double* __restrict__ part)
-{
-    static_assert(!SUMSQ || (CHECK && U * TPB * 4 == kChunk), "a tile is one chunk");
-    __shared__ double lds[SUMSQ ? TPB / 64 : 1];
-    f32x4* A = reinterpret_cast<f32x4*>(acc);
-    const u32x2* G = reinterpret_cast<const u32x2*>(g16);
-    constexpr int T = U * TPB;
-    const int64_t nq = n >> 2;
-    const int64_t ntiles = nq / T;
-    uint32_t bad = 0u;
-    for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
-        const int64_t q0 = tile * T + threadIdx.x;
-        f32x4 g[U], a[U];
-        double s = 0.0;
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            g[u] = widen4<GF>(load<NT>(G + q0 + u * TPB));
-            if constexpr (!OVERWRITE)
-                a[u] = load<NT>(A + q0 + u * TPB);
-        }
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            f32x4 r;
-            if constexpr (OVERWRITE)
-                r = g[u];
-            else
-                r = a[u] + g[u];
-            if constexpr (CHECK)
-                bad |= nonfinite_f32x4(r);
-            if constexpr (SUMSQ)
-                s = s + sq4(r);
-            store<NT>(A + q0 + u * TPB, r);
-        }
-        if constexpr (SUMSQ) {
-            const double cs = block_sum_fixed<TPB>(s, lds);
-            if (threadIdx.x == 0)
-                part[tile] = cs;
-        }
-    }
-    if (blockIdx.x == 0) {
-        double s = 0.0;
-        for (int64_t q = ntiles * T + threadIdx.x; q < nq; q += TPB) {
-            const f32x4 g = widen4<GF>(load<NT>(G + q));
-            f32x4 r;
-            if constexpr (OVERWRITE)
-                r = g;
-            else
-                r = load<NT>(A + q) + g;
-            if constexpr (CHECK)
-                bad |= nonfinite_f32x4(r);
-            if constexpr (SUMSQ)
-                s = s + sq4(r);
-            store<NT>(A + q, r);
-        }
-        if (static_cast<int64_t>(threadIdx.x) < (n & 3)) {
-            const int64_t i = (nq << 2) + threadIdx.x;
-            const float g = dec1<GF>(g16[i]);
-            const float r = OVERWRITE ? g : acc[i] + g;
-            if constexpr (CHECK)
-                bad |= nonfinite_f32(__float_as_uint(r));
-            if constexpr (SUMSQ)
-                s = s + sq(r);
-            acc[i] = r;
-        }
-        if constexpr (SUMSQ) {
-            if (ntiles * T * 4 < n) {          // a last, partial chunk exists
-                const double cs = block_sum_fixed<TPB>(s, lds);
-                if (threadIdx.x == 0)
-                    part[ntiles] = cs;
-            }
-        }
-    }
-    if constexpr (CHECK)
-        raise_flag(st, bad);
-}
-
-// Several micro-batch gradients folded into the accumulation buffer in one
+// count (1..8) micro-batch gradients folded into the fp32 buffer in one
 // pass: acc = (OVERWRITE ? g_0 : acc + g_0) + g_1 + ... + g_{count-1}, every
 // add an fp32 add in this order, so the result is bit for bit that of count
 // consecutive single-gradient passes, for 2 * count + 8 (or + 4 when
-// overwriting) bytes per element instead of 10 * count.  Tiling (one
-// 4096-element tile per block), hints, the fused check and the
-// sum-of-squares chunks are those of accumulate_kernel; the gradient list is
-// indexed with compile-time indices only (no dynamic indexing of the
-// argument).
+// overwriting) bytes per element instead of 10 * count.  One quad per lane,
+// one tile of TPB quads per block, every gradient's loads issued before the
+// first add.  With CHECK the pass ORs "a result is not finite" into the
+// overflow flag; with SUMSQ (which needs CHECK and a tile of kAccChunk
+// elements) each tile is one chunk of the sum of squares of the result,
+// written to part[tile].  The gradient list is indexed with compile-time
+// indices only (no dynamic indexing of the kernel argument, so no scratch).
 constexpr int kMaxFold = 8;
 struct GradList {
     const uint16_t* p[kMaxFold];
     int32_t count;
 };
 
-template <int GF, bool OVERWRITE, bool CHECK, bool SUMSQ, bool NT, int TPB, int U>
-__global__ __launch_bounds__(TPB) void fold_kernel(float* __restrict__ acc, GradList gl, int64_t n,
-                                                   ds_scaler* __restrict__ st, double* __restrict__ part)
+// One quad of a fold of F gradients (F known at compile time): the loads of
+// the accumulation buffer and of every gradient are issued before the adds.
+template <int GF, bool OVERWRITE, bool NT, int F>
+__device__ __forceinline__ f32x4 fold_quad(f32x4* A, const GradList& gl, int64_t q)
 {
-    constexpr int T = U * TPB;
-    static_assert(!SUMSQ || (CHECK && T * 4 == kChunk), "a tile is one chunk");
-    __shared__ double lds[SUMSQ ? TPB / 64 : 1];
+    f32x4 r;
+    if constexpr (!OVERWRITE)
+        r = load<NT>(A + q);
+    u32x2 raw[F];
+#pragma unroll
+    for (int k = 0; k < F; ++k)
+        raw[k] = load<NT>(reinterpret_cast<const u32x2*>(gl.p[k]) + q);
+    if constexpr (OVERWRITE)
+        r = widen4<GF>(raw[0]);
+    else
+        r = r + widen4<GF>(raw[0]);
+#pragma unroll
+    for (int k = 1; k < F; ++k)
+        r = r + widen4<GF>(raw[k]);
+    return r;
+}
+
+// The pass over [0, n) for a fold of F gradients: tiles of TPB quads dealt to
+// blocks round-robin; block 0 also takes the quads after the last whole tile
+// (fewer than TPB) and the last n % 4 elements.
+template <int GF, bool OVERWRITE, bool CHECK, bool SUMSQ, bool NT, int TPB, int F>
+__device__ __forceinline__ void accumulate_pass(float* __restrict__ acc, const GradList& gl, int64_t n,
+                                                ds_scaler* __restrict__ st, double* __restrict__ part, double* lds)
+{
     f32x4* A = reinterpret_cast<f32x4*>(acc);
     const int64_t nq = n >> 2;
-    const int64_t ntiles = nq / T;
+    const int64_t ntiles = nq / TPB;
     uint32_t bad = 0u;
+    int parity = 0;
     for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
-        const int64_t q0 = tile * T + threadIdx.x;
-        f32x4 r[U];
-        {
-            const u32x2* G = reinterpret_cast<const u32x2*>(gl.p[0]);
-            f32x4 g[U];
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                g[u] = widen4<GF>(load<NT>(G + q0 + u * TPB));
-                if constexpr (!OVERWRITE)
-                    r[u] = load<NT>(A + q0 + u * TPB);
-            }
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                if constexpr (OVERWRITE)
-                    r[u] = g[u];
-                else
-                    r[u] = r[u] + g[u];
-            }
-        }
-        // every gradient's loads issued before the first add (U x 8 B in flight
-        // per lane and gradient; measured 1-3 % faster than loading each
-        // gradient just before its add)
-        u32x2 raw[kMaxFold - 1][U];
-#pragma unroll
-        for (int k = 1; k < kMaxFold; ++k) {
-            if (k < gl.count) {
-                const u32x2* G = reinterpret_cast<const u32x2*>(gl.p[k]);
-#pragma unroll
-                for (int u = 0; u < U; ++u)
-                    raw[k - 1][u] = load<NT>(G + q0 + u * TPB);
-            }
-        }
-#pragma unroll
-        for (int k = 1; k < kMaxFold; ++k) {
-            if (k < gl.count) {
-#pragma unroll
-                for (int u = 0; u < U; ++u)
-                    r[u] = r[u] + widen4<GF>(raw[k - 1][u]);
-            }
-        }
-        double s = 0.0;
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            if constexpr (CHECK)
-                bad |= nonfinite_f32x4(r[u]);
-            if constexpr (SUMSQ)
-                s = s + sq4(r[u]);
-            store<NT>(A + q0 + u * TPB, r[u]);
-        }
+        const int64_t q = tile * TPB + threadIdx.x;
+        const f32x4 r = fold_quad<GF, OVERWRITE, NT, F>(A, gl, q);
+        if constexpr (CHECK)
+            bad |= nonfinite_f32x4(r);
+        store<NT>(A + q, r);
         if constexpr (SUMSQ) {
-            const double cs = block_sum_fixed<TPB>(s, lds);
+            const double cs = block_sum_fixed<TPB>(sq4(r), lds, parity);
+            parity ^= 1;
             if (threadIdx.x == 0)
                 part[tile] = cs;
         }
     }
     if (blockIdx.x == 0) {
         double s = 0.0;
-        for (int64_t q = ntiles * T + threadIdx.x; q < nq; q += TPB) {
-            f32x4 r = widen4<GF>(load<NT>(reinterpret_cast<const u32x2*>(gl.p[0]) + q));
-            if constexpr (!OVERWRITE)
-                r = load<NT>(A + q) + r;
-#pragma unroll
-            for (int k = 1; k < kMaxFold; ++k)
-                if (k < gl.count)
-                    r = r + widen4<GF>(load<NT>(reinterpret_cast<const u32x2*>(gl.p[k]) + q));
+        const int64_t q = ntiles * TPB + threadIdx.x;
+        if (q < nq) {
+            const f32x4 r = fold_quad<GF, OVERWRITE, NT, F>(A, gl, q);
             if constexpr (CHECK)
                 bad |= nonfinite_f32x4(r);
             if constexpr (SUMSQ)
@@ -848,9 +812,8 @@ __global__ __launch_bounds__(TPB) void fold_kernel(float* __restrict__ acc, Grad
             if constexpr (!OVERWRITE)
                 r = acc[i] + r;
 #pragma unroll
-            for (int k = 1; k < kMaxFold; ++k)
-                if (k < gl.count)
-                    r = r + dec1<GF>(gl.p[k][i]);
+            for (int k = 1; k < F; ++k)
+                r = r + dec1<GF>(gl.p[k][i]);
             if constexpr (CHECK)
                 bad |= nonfinite_f32(__float_as_uint(r));
             if constexpr (SUMSQ)
@@ -858,8 +821,8 @@ __global__ __launch_bounds__(TPB) void fold_kernel(float* __restrict__ acc, Grad
             acc[i] = r;
         }
         if constexpr (SUMSQ) {
-            if (ntiles * T * 4 < n) {          // a last, partial chunk exists
-                const double cs = block_sum_fixed<TPB>(s, lds);
+            if (ntiles * TPB * 4 < n) {          // a last, partial chunk exists
+                const double cs = block_sum_fixed<TPB>(s, lds, parity);
                 if (threadIdx.x == 0)
                     part[ntiles] = cs;
             }
@@ -867,6 +830,30 @@ __global__ __launch_bounds__(TPB) void fold_kernel(float* __restrict__ acc, Grad
     }
     if constexpr (CHECK)
         raise_flag(st, bad);
+}
+
+// MULTI = false: exactly one gradient.  MULTI = true: gl.count (2..8)
+// gradients, the pass chosen by a block-uniform switch, so every form is
+// straight-line code with all of its loads in flight together.
+template <int GF, bool OVERWRITE, bool CHECK, bool SUMSQ, bool NT, bool MULTI, int TPB>
+__global__ __launch_bounds__(TPB) void accumulate_kernel(float* __restrict__ acc, GradList gl, int64_t n,
+                                                         ds_scaler* __restrict__ st, double* __restrict__ part)
+{
+    static_assert(!SUMSQ || (CHECK && 4 * TPB == kAccChunk), "a tile is one chunk");
+    __shared__ double lds[SUMSQ ? 2 * (TPB / 64) : 1];
+    if constexpr (!MULTI) {
+        accumulate_pass<GF, OVERWRITE, CHECK, SUMSQ, NT, TPB, 1>(acc, gl, n, st, part, lds);
+    } else {
+        switch (gl.count) {
+        case 2: accumulate_pass<GF, OVERWRITE, CHECK, SUMSQ, NT, TPB, 2>(acc, gl, n, st, part, lds); break;
+        case 3: accumulate_pass<GF, OVERWRITE, CHECK, SUMSQ, NT, TPB, 3>(acc, gl, n, st, part, lds); break;
+        case 4: accumulate_pass<GF, OVERWRITE, CHECK, SUMSQ, NT, TPB, 4>(acc, gl, n, st, part, lds); break;
+        case 5: accumulate_pass<GF, OVERWRITE, CHECK, SUMSQ, NT, TPB, 5>(acc, gl, n, st, part, lds); break;
+        case 6: accumulate_pass<GF, OVERWRITE, CHECK, SUMSQ, NT, TPB, 6>(acc, gl, n, st, part, lds); break;
+        case 7: accumulate_pass<GF, OVERWRITE, CHECK, SUMSQ, NT, TPB, 7>(acc, gl, n, st, part, lds); break;
+        default: accumulate_pass<GF, OVERWRITE, CHECK, SUMSQ, NT, TPB, 8>(acc, gl, n, st, part, lds); break;
+        }
+    }
 }
 
 __global__ void write_state_kernel(ds_scaler* st, ds_scaler value) { *st = value; }
@@ -885,25 +872,24 @@ long env_long(const char* name, long dflt)
     return (end != s) ? v : dflt;
 }
 
-// Blocks for `units` units of work (tiles, sum-of-squares chunks, or the
-// check's groups of kCheckBlock vectors): one block per unit, at least one,
-// at most kMaxBlocks (the kernels loop past
-// that).  DSZERO_GRID pins the block count (launch-shape invariance tests,
-// sweeps).
-unsigned grid_blocks(int64_t units)
+// Blocks for `units` units of work (tiles, sum-of-squares chunks or groups,
+// or the check's groups of kCheckBlock vectors) of a kernel with `tpb` lanes
+// per block: one block per unit, at least one, at most kMaxWorkItems / tpb
+// (the kernels loop past that).  DSZERO_GRID pins the block count (launch-
+// shape invariance tests, sweeps).
+unsigned grid_blocks(int64_t units, int tpb)
 {
+    const int64_t cap = kMaxWorkItems / tpb;
     const long forced = env_long("DSZERO_GRID", 0);
-    if (forced > 0)
-        return static_cast<unsigned>(forced > kMaxBlocks ? kMaxBlocks : forced);
-    int64_t b = units;
-    if (b > kMaxBlocks)
-        b = kMaxBlocks;
+    int64_t b = forced > 0 ? static_cast<int64_t>(forced) : units;
+    if (b > cap)
+        b = cap;
     if (b < 1)
         b = 1;
     return static_cast<unsigned>(b);
 }
 
-// Variant knobs (default: quads per lane U = 4).
+// Quads per lane of the Adam kernel (default 4; DSZERO_UNROLL=2 halves the tile).
 int variant_unroll() { return env_long("DSZERO_UNROLL", 4) == 2 ? 2 : 4; }
 // Non-temporal hints on the read/write kernels' streams: on by default above
 // kTemporalMaxElems elements, where a step's 28-30 B per element is more than
@@ -998,67 +984,108 @@ void launch_adam(int gf, int pf, bool wd, bool nt, int unroll, bool fuse, unsign
     }
 }
 
-template <int GF, bool OW, bool CK, bool NT>
-void launch_acc4(int unroll, unsigned blocks, hipStream_t s, float* acc, const uint16_t* g16, int64_t n,
-                 ds_scaler* st)
+template <int GF, bool OW, bool CK, bool SQ>
+void launch_acc3(bool nt, hipStream_t s, float* acc, const GradList& gl, int64_t n, ds_scaler* st, double* part)
 {
-    if (unroll == 2) {
-        accumulate_kernel<GF, OW, CK, false, NT, kStepBlock, 2><<<blocks, kStepBlock, 0, s>>>(acc, g16, n, st, nullptr);
-    } else if constexpr (OW) {
-        // the first micro-batch (2 B in, 4 B out per element) takes the same
-        // 4096-element tile as 512 lanes x 2 quads: 184-186 us against
-        // 195-199 us with 256 x 4 on a 185.6M-element bucket (the adding
-        // passes tie, so they keep 256 x 4)
-        accumulate_kernel<GF, OW, CK, false, NT, kSmallBlock, 2><<<blocks, kSmallBlock, 0, s>>>(acc, g16, n, st,
-                                                                                               nullptr);
+    constexpr int TPB = SQ ? kAccSumsqBlock : kAccBlock;
+    const unsigned blocks = grid_blocks((n >> 2) / TPB, TPB);
+    if (gl.count == 1) {
+        if (nt) accumulate_kernel<GF, OW, CK, SQ, true, false, TPB><<<blocks, TPB, 0, s>>>(acc, gl, n, st, part);
+        else    accumulate_kernel<GF, OW, CK, SQ, false, false, TPB><<<blocks, TPB, 0, s>>>(acc, gl, n, st, part);
     } else {
-        accumulate_kernel<GF, OW, CK, false, NT, kStepBlock, 4><<<blocks, kStepBlock, 0, s>>>(acc, g16, n, st, nullptr);
+        if (nt) accumulate_kernel<GF, OW, CK, SQ, true, true, TPB><<<blocks, TPB, 0, s>>>(acc, gl, n, st, part);
+        else    accumulate_kernel<GF, OW, CK, SQ, false, true, TPB><<<blocks, TPB, 0, s>>>(acc, gl, n, st, part);
     }
 }
 
+// Accumulation pass: `ck` fuses the non-finite check of the result, a
+// non-null `part` (which needs `ck`) the chunk sums of squares.
 template <int GF>
-void launch_acc(bool ow, bool ck, bool nt, int unroll, unsigned blocks, hipStream_t s, float* acc,
-                const uint16_t* g16, int64_t n, ds_scaler* st)
+void launch_acc(bool ow, bool ck, bool nt, hipStream_t s, float* acc, const GradList& gl, int64_t n, ds_scaler* st,
+                double* part)
 {
-    if (nt) {
-        if (ow) { if (ck) launch_acc4<GF, true, true, true>(unroll, blocks, s, acc, g16, n, st);
-                  else    launch_acc4<GF, true, false, true>(unroll, blocks, s, acc, g16, n, st); }
-        else    { if (ck) launch_acc4<GF, false, true, true>(unroll, blocks, s, acc, g16, n, st);
-                  else    launch_acc4<GF, false, false, true>(unroll, blocks, s, acc, g16, n, st); }
+    if (part != nullptr) {
+        if (ow) launch_acc3<GF, true, true, true>(nt, s, acc, gl, n, st, part);
+        else    launch_acc3<GF, false, true, true>(nt, s, acc, gl, n, st, part);
+    } else if (ck) {
+        if (ow) launch_acc3<GF, true, true, false>(nt, s, acc, gl, n, st, nullptr);
+        else    launch_acc3<GF, false, true, false>(nt, s, acc, gl, n, st, nullptr);
     } else {
-        if (ow) { if (ck) launch_acc4<GF, true, true, false>(unroll, blocks, s, acc, g16, n, st);
-                  else    launch_acc4<GF, true, false, false>(unroll, blocks, s, acc, g16, n, st); }
-        else    { if (ck) launch_acc4<GF, false, true, false>(unroll, blocks, s, acc, g16, n, st);
-                  else    launch_acc4<GF, false, false, false>(unroll, blocks, s, acc, g16, n, st); }
+        if (ow) launch_acc3<GF, true, false, false>(nt, s, acc, gl, n, nullptr, nullptr);
+        else    launch_acc3<GF, false, false, false>(nt, s, acc, gl, n, nullptr, nullptr);
     }
 }
 
-template <int GF>
-void launch_acc_sumsq(bool ow, bool nt, unsigned blocks, hipStream_t s, float* acc, const uint16_t* g16,
-                      int64_t n, ds_scaler* st, double* part)
+int64_t acc_chunks(int64_t n) { return (n + kAccChunk - 1) / kAccChunk; }
+int64_t check_chunks(int64_t n) { return (n + kCheckChunk - 1) / kCheckChunk; }
+int64_t finish_groups(int64_t nparts) { return (nparts + kGroup - 1) / kGroup; }
+
+// Workspace of a sum of squares over n elements: the chunk sums of the
+// finer chunking (the accumulation's, 1024 elements) followed by the group
+// sums of the second pass.
+uint64_t sumsq_ws_bytes(int64_t n)
 {
-    if (nt) {
-        if (ow) accumulate_kernel<GF, true, true, true, true, kStepBlock, 4><<<blocks, kStepBlock, 0, s>>>(acc, g16, n, st, part);
-        else    accumulate_kernel<GF, false, true, true, true, kStepBlock, 4><<<blocks, kStepBlock, 0, s>>>(acc, g16, n, st, part);
-    } else {
-        if (ow) accumulate_kernel<GF, true, true, true, false, kStepBlock, 4><<<blocks, kStepBlock, 0, s>>>(acc, g16, n, st, part);
-        else    accumulate_kernel<GF, false, true, true, false, kStepBlock, 4><<<blocks, kStepBlock, 0, s>>>(acc, g16, n, st, part);
-    }
+    if (n <= 0)
+        return 0;
+    const int64_t p = acc_chunks(n);
+    return 8 * static_cast<uint64_t>(p + finish_groups(p));
 }
 
-int64_t sumsq_chunks(int64_t n) { return (n + kChunk - 1) / kChunk; }
-
-// validation shared by the two sum-of-squares entry points (one fp64 partial
-// sum per 4096-element chunk)
+// validation shared by the sum-of-squares entry points
 ds_status check_workspace(const void* ws, size_t ws_bytes, int64_t n)
 {
     if (ws == nullptr)
         return DS_ERR_NULL;
     if (!aligned(ws, 8))
         return DS_ERR_ALIGN;
-    if (ws_bytes < 8 * static_cast<size_t>(sumsq_chunks(n)))
+    if (ws_bytes < sumsq_ws_bytes(n))
         return DS_ERR_SIZE;
     return DS_OK;
+}
+
+// Second pass of a sum of squares whose first pass wrote `nparts` chunk sums
+// at ws: the group sums go right after them.
+ds_status launch_finish(ds_scaler* st, double* ws, int64_t nparts, hipStream_t s)
+{
+    const unsigned blocks = grid_blocks(finish_groups(nparts), kFinishBlock);
+    sumsq_finish_kernel<<<blocks, kFinishBlock, 0, s>>>(st, ws, nparts, ws + nparts);
+    return launched();
+}
+
+// Launches of the validated accumulation entry points: the pass over the
+// data, then (with a workspace) the second pass of the sum of squares.
+ds_status launch_accumulate(float* acc, const GradList& gl, ds_dtype gdt, int64_t n, bool overwrite,
+                            ds_scaler* st_or_null, double* ws_or_null, hipStream_t s)
+{
+    const bool nt = variant_nt(n);
+    const bool ck = st_or_null != nullptr;
+    if (gdt == DS_BF16)
+        launch_acc<kBF16>(overwrite, ck, nt, s, acc, gl, n, st_or_null, ws_or_null);
+    else
+        launch_acc<kF16>(overwrite, ck, nt, s, acc, gl, n, st_or_null, ws_or_null);
+    if (ws_or_null == nullptr)
+        return launched();
+    if (launched() != DS_OK)
+        return DS_ERR_HIP;
+    return launch_finish(st_or_null, ws_or_null, acc_chunks(n), s);
+}
+
+// Launch of the validated check with the sum of squares (workspace ws of at
+// least sumsq_ws_bytes(n) bytes).
+ds_status launch_check_sumsq(ds_scaler* st, const void* grad, ds_dtype dt, int64_t n, double* ws, hipStream_t s)
+{
+    constexpr int TPB = kCheckSumsqBlock;
+    const int64_t chunks = check_chunks(n);
+    const unsigned blocks = grid_blocks(chunks, TPB);
+    if (dt == DS_FP16)
+        check_sumsq_kernel<kF16, TPB><<<blocks, TPB, 0, s>>>(st, grad, n, ws);
+    else if (dt == DS_BF16)
+        check_sumsq_kernel<kBF16, TPB><<<blocks, TPB, 0, s>>>(st, grad, n, ws);
+    else
+        check_sumsq_kernel<kF32, TPB><<<blocks, TPB, 0, s>>>(st, grad, n, ws);
+    if (launched() != DS_OK)
+        return DS_ERR_HIP;
+    return launch_finish(st, ws, chunks, s);
 }
 
 bool schedule_ok(const ds_lr_schedule& q)
@@ -1112,42 +1139,12 @@ ds_status adam_step(const ds_scaler* st, float* master, float* m, float* v, uint
 
     hipStream_t s = static_cast<hipStream_t>(stream);
     const int unroll = fuse ? 4 : variant_unroll();
-    const unsigned blocks = grid_blocks(tiles_of(n, unroll));
     const bool nt = variant_nt(n);
+    const unsigned blocks = grid_blocks(tiles_of(n, unroll), fuse && !nt ? kSmallBlock : kStepBlock);
     const bool wd = weight_decay != 0.0f;
     const AdamArgs args{const_cast<ds_scaler*>(st), master, m, v, p16, grad, n, hp};
     launch_adam(fmt_of(dt), fmt_of(pdt), wd, nt, unroll, fuse, blocks, s, args);
     return launched();
-}
-
-template <int GF, bool OW>
-void launch_fold2(bool ck, bool sumsq, bool nt, unsigned blocks, hipStream_t s, float* acc, const GradList& gl,
-                  int64_t n, ds_scaler* st, double* part)
-{
-    // the same 4096-element tile either way; the sum-of-squares form keeps
-    // 256 lanes x 4 quads so that its chunk sums are added in exactly the
-    // order of ds_accumulate_sumsq, the others take 512 x 2 (0.5-1.5 % faster:
-    // fewer registers per lane, twice the waves)
-    const unsigned b = blocks;
-    constexpr int W = kSmallBlock;
-    if (sumsq) {
-        if (nt) fold_kernel<GF, OW, true, true, true, kStepBlock, 4><<<b, kStepBlock, 0, s>>>(acc, gl, n, st, part);
-        else    fold_kernel<GF, OW, true, true, false, kStepBlock, 4><<<b, kStepBlock, 0, s>>>(acc, gl, n, st, part);
-    } else if (ck) {
-        if (nt) fold_kernel<GF, OW, true, false, true, W, 2><<<b, W, 0, s>>>(acc, gl, n, st, nullptr);
-        else    fold_kernel<GF, OW, true, false, false, W, 2><<<b, W, 0, s>>>(acc, gl, n, st, nullptr);
-    } else {
-        if (nt) fold_kernel<GF, OW, false, false, true, W, 2><<<b, W, 0, s>>>(acc, gl, n, nullptr, nullptr);
-        else    fold_kernel<GF, OW, false, false, false, W, 2><<<b, W, 0, s>>>(acc, gl, n, nullptr, nullptr);
-    }
-}
-
-template <int GF>
-void launch_fold(bool ow, bool ck, bool sumsq, bool nt, unsigned blocks, hipStream_t s, float* acc,
-                 const GradList& gl, int64_t n, ds_scaler* st, double* part)
-{
-    if (ow) launch_fold2<GF, true>(ck, sumsq, nt, blocks, s, acc, gl, n, st, part);
-    else    launch_fold2<GF, false>(ck, sumsq, nt, blocks, s, acc, gl, n, st, part);
 }
 
 }  // namespace
@@ -1218,7 +1215,8 @@ ds_status ds_state_write(ds_scaler* st, const ds_scaler* host_in, void* stream)
     if (!aligned(st, 8))
         return DS_ERR_ALIGN;
     ds_scaler value = *host_in;
-    value.blocks_done = 0u;   // between steps the fused form's block count is 0
+    value.blocks_done = 0u;         // between steps the fused form's block count is 0
+    value.sumsq_blocks_done = 0u;   // and so is the sum of squares' second pass's
     write_state_kernel<<<1, 1, 0, static_cast<hipStream_t>(stream)>>>(st, value);
     return launched();
 }
@@ -1240,16 +1238,11 @@ ds_status ds_accumulate(float* acc, const uint16_t* g16, ds_dtype gdt, int64_t n
     if (overlap(acc, 4 * un, g16, 2 * un) || overlap(acc, 4 * un, st_or_null, sizeof(ds_scaler)) ||
         overlap(g16, 2 * un, st_or_null, sizeof(ds_scaler)))
         return DS_ERR_ALIAS;
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    const int unroll = variant_unroll();
-    const unsigned blocks = grid_blocks(tiles_of(n, unroll));
-    const bool nt = variant_nt(n);
-    const bool ow = overwrite != 0, ck = st_or_null != nullptr;
-    if (gdt == DS_BF16)
-        launch_acc<kBF16>(ow, ck, nt, unroll, blocks, s, acc, g16, n, st_or_null);
-    else
-        launch_acc<kF16>(ow, ck, nt, unroll, blocks, s, acc, g16, n, st_or_null);
-    return launched();
+    GradList gl{};
+    gl.p[0] = g16;
+    gl.count = 1;
+    return launch_accumulate(acc, gl, gdt, n, overwrite != 0, st_or_null, nullptr,
+                             static_cast<hipStream_t>(stream));
 }
 
 ds_status ds_check_overflow(ds_scaler* st, const void* grad, ds_dtype dt, int64_t n, void* stream)
@@ -1270,7 +1263,7 @@ ds_status ds_check_overflow(ds_scaler* st, const void* grad, ds_dtype dt, int64_
         return DS_ERR_ALIAS;
     hipStream_t s = static_cast<hipStream_t>(stream);
     const int64_t vecs = n / (dt == DS_FP32 ? 4 : 8);
-    const unsigned blocks = grid_blocks((vecs + kCheckBlock - 1) / kCheckBlock);
+    const unsigned blocks = grid_blocks((vecs + kCheckBlock - 1) / kCheckBlock, kCheckBlock);
     // ordinary loads: leave the gradient in the Infinity Cache for the Adam pass
     if (dt == DS_FP16)
         check_kernel<kF16, false, kCheckBlock><<<blocks, kCheckBlock, 0, s>>>(st, grad, n);
@@ -1324,7 +1317,7 @@ ds_status ds_adam_step_fused(ds_scaler* st, float* master, float* m, float* v, u
 
 size_t ds_sumsq_workspace_bytes(int64_t n)
 {
-    return 8 * static_cast<size_t>(sumsq_chunks(n > 0 ? n : 0));
+    return static_cast<size_t>(sumsq_ws_bytes(n));
 }
 
 ds_status ds_check_overflow_sumsq(ds_scaler* st, const void* grad, ds_dtype dt, int64_t n,
@@ -1345,24 +1338,11 @@ ds_status ds_check_overflow_sumsq(ds_scaler* st, const void* grad, ds_dtype dt, 
     if (const ds_status w = check_workspace(workspace, workspace_bytes, n); w != DS_OK)
         return w;
     const uint64_t gb = esize(dt) * static_cast<uint64_t>(n);
-    const uint64_t wb = 8 * static_cast<uint64_t>(sumsq_chunks(n));
+    const uint64_t wb = sumsq_ws_bytes(n);
     if (overlap(grad, gb, st, sizeof(ds_scaler)) || overlap(grad, gb, workspace, wb) ||
         overlap(st, sizeof(ds_scaler), workspace, wb))
         return DS_ERR_ALIAS;
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    const int64_t chunks = (n + 4 * kChunk - 1) / (4 * kChunk);   // 16,384-element chunks
-    const unsigned blocks = grid_blocks(chunks);
-    double* part = static_cast<double*>(workspace);
-    if (dt == DS_FP16)
-        check_sumsq_kernel<kF16, 1024><<<blocks, 1024, 0, s>>>(st, grad, n, part);
-    else if (dt == DS_BF16)
-        check_sumsq_kernel<kBF16, 1024><<<blocks, 1024, 0, s>>>(st, grad, n, part);
-    else
-        check_sumsq_kernel<kF32, 1024><<<blocks, 1024, 0, s>>>(st, grad, n, part);
-    if (launched() != DS_OK)
-        return DS_ERR_HIP;
-    sumsq_finish_kernel<1024><<<1, 1024, 0, s>>>(st, part, chunks);
-    return launched();
+    return launch_check_sumsq(st, grad, dt, n, static_cast<double*>(workspace), static_cast<hipStream_t>(stream));
 }
 
 ds_status ds_accumulate_sumsq(float* acc, const uint16_t* g16, ds_dtype gdt, int64_t n, int32_t overwrite,
@@ -1383,26 +1363,18 @@ ds_status ds_accumulate_sumsq(float* acc, const uint16_t* g16, ds_dtype gdt, int
     if (const ds_status w = check_workspace(workspace, workspace_bytes, n); w != DS_OK)
         return w;
     const uint64_t un = static_cast<uint64_t>(n);
-    const uint64_t wb = 8 * static_cast<uint64_t>(sumsq_chunks(n));
+    const uint64_t wb = sumsq_ws_bytes(n);
     const void* ptrs[4] = {acc, g16, st, workspace};
     const uint64_t sizes[4] = {4 * un, 2 * un, sizeof(ds_scaler), wb};
     for (int i = 0; i < 4; ++i)
         for (int j = i + 1; j < 4; ++j)
             if (overlap(ptrs[i], sizes[i], ptrs[j], sizes[j]))
                 return DS_ERR_ALIAS;
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    // the tile must be one 4096-element chunk: U = 4 whatever DSZERO_UNROLL says
-    const unsigned blocks = grid_blocks(tiles_of(n, 4));
-    double* part = static_cast<double*>(workspace);
-    const bool nt = variant_nt(n);
-    if (gdt == DS_BF16)
-        launch_acc_sumsq<kBF16>(overwrite != 0, nt, blocks, s, acc, g16, n, st, part);
-    else
-        launch_acc_sumsq<kF16>(overwrite != 0, nt, blocks, s, acc, g16, n, st, part);
-    if (launched() != DS_OK)
-        return DS_ERR_HIP;
-    sumsq_finish_kernel<1024><<<1, 1024, 0, s>>>(st, part, sumsq_chunks(n));
-    return launched();
+    GradList gl{};
+    gl.p[0] = g16;
+    gl.count = 1;
+    return launch_accumulate(acc, gl, gdt, n, overwrite != 0, st, static_cast<double*>(workspace),
+                             static_cast<hipStream_t>(stream));
 }
 
 ds_status ds_accumulate_multi(float* acc, const uint16_t* const* grads, int32_t count, ds_dtype gdt, int64_t n,
@@ -1435,7 +1407,7 @@ ds_status ds_accumulate_multi(float* acc, const uint16_t* const* grads, int32_t 
     // written: acc, the state, the workspace; read: the gradients (which may
     // repeat or overlap one another)
     const uint64_t un = static_cast<uint64_t>(n);
-    const uint64_t wb = sumsq ? 8 * static_cast<uint64_t>(sumsq_chunks(n)) : 0;
+    const uint64_t wb = sumsq ? sumsq_ws_bytes(n) : 0;
     const void* out[3] = {acc, st_or_null, workspace_or_null};
     const uint64_t out_bytes[3] = {4 * un, st_or_null != nullptr ? sizeof(ds_scaler) : 0, wb};
     for (int i = 0; i < 3; ++i) {
@@ -1450,21 +1422,8 @@ ds_status ds_accumulate_multi(float* acc, const uint16_t* const* grads, int32_t 
     for (int32_t k = 0; k < count; ++k)
         gl.p[k] = grads[k];
     gl.count = count;
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    const unsigned blocks = grid_blocks(tiles_of(n, 4));
-    const bool nt = variant_nt(n);
-    const bool ck = st_or_null != nullptr;
-    double* part = static_cast<double*>(workspace_or_null);
-    if (gdt == DS_BF16)
-        launch_fold<kBF16>(overwrite != 0, ck, sumsq, nt, blocks, s, acc, gl, n, st_or_null, part);
-    else
-        launch_fold<kF16>(overwrite != 0, ck, sumsq, nt, blocks, s, acc, gl, n, st_or_null, part);
-    if (!sumsq)
-        return launched();
-    if (launched() != DS_OK)
-        return DS_ERR_HIP;
-    sumsq_finish_kernel<1024><<<1, 1024, 0, s>>>(st_or_null, part, sumsq_chunks(n));
-    return launched();
+    return launch_accumulate(acc, gl, gdt, n, overwrite != 0, st_or_null, static_cast<double*>(workspace_or_null),
+                             static_cast<hipStream_t>(stream));
 }
 
 ds_status ds_update_loss_scale(ds_scaler* st, void* stream)
