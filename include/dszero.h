@@ -303,6 +303,26 @@ size_t ds_sumsq_workspace_bytes(int64_t n);
 ds_status ds_check_overflow_sumsq(ds_scaler* st, const void* grad, ds_dtype dt, int64_t n,
                                   void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * ds_check_overflow_sumsq without a caller workspace, for callers that cannot
+ * allocate device memory: code under stream or graph capture, tight serving
+ * loops, harnesses that forbid allocation.  The call allocates nothing: the
+ * chunk and group sums go to a scratch array of 2^21 fp64 values (16 MiB)
+ * that the library holds in each device's memory until the process ends.
+ * Flag and sum of squares are bit-identical to those of
+ * ds_check_overflow_sumsq.  n may be at most DS_NOALLOC_MAX_ELEMS (2,096,640
+ * chunks of 8192 elements); a larger n is DS_ERR_SIZE.  The first call on a
+ * device (the device of `stream`, or the current one for the null stream)
+ * looks up the address of that device's array and keeps it; DS_ERR_HIP if
+ * that fails.  Every call on one device shares that device's array, which
+ * keeps the last call's contents: calls that may run at the same time on one
+ * device (other streams, other threads) race and give wrong sums, so order
+ * them on one stream.  Nothing in the array needs to start at zero: every
+ * chunk and group sum is written before it is read.
+ */
+#define DS_NOALLOC_MAX_ELEMS 17175674880LL
+ds_status ds_check_overflow_sumsq_noalloc(ds_scaler* st, const void* grad, ds_dtype dt, int64_t n, void* stream);
+
 /* ds_accumulate with the fused overflow check (st required) plus the sum of
  * squares of the accumulated values, one pass: use it for the last
  * micro-batch of a clipped step. */

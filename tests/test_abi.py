@@ -478,3 +478,23 @@ def test_binding_rejects_host_short_and_strided_tensors():
     # integers are raw addresses and pass through to the library's own validation
     with pytest.raises(_lib.DsError, match="SIZE"):
         _lib.ds_check_overflow(ST, A, DS_FP16, -1, stream=0)
+
+
+@fake_addresses
+def test_noalloc_check_validation():
+    """ds_check_overflow_sumsq_noalloc validates like ds_check_overflow_sumsq and
+    refuses sizes beyond its scratch array before any device work."""
+    f = L.ds_check_overflow_sumsq_noalloc
+    assert _lib.DS_NOALLOC_MAX_ELEMS == (2 ** 21 - 512) * 8192
+    text = open(os.path.join(ROOT, "include", "dszero.h")).read()
+    assert re.search(r"#define DS_NOALLOC_MAX_ELEMS %dLL" % _lib.DS_NOALLOC_MAX_ELEMS, text)
+    assert f(ST, A, DS_FP16, -1, STREAM) == DS_ERR_SIZE
+    assert f(ST, A, DS_FP16, _lib.DS_NOALLOC_MAX_ELEMS + 1, STREAM) == DS_ERR_SIZE
+    assert f(ST, A, DS_FP16, 2 ** 40, STREAM) == DS_ERR_SIZE
+    assert f(ST, A, 9, 10, STREAM) == DS_ERR_DTYPE
+    assert f(None, A, DS_FP16, 10, STREAM) == DS_ERR_NULL
+    assert f(ST, A, DS_FP16, 0, STREAM) == DS_OK
+    assert f(ST, None, DS_FP16, 10, STREAM) == DS_ERR_NULL
+    assert f(ST, A + 8, DS_FP16, 10, STREAM) == DS_ERR_ALIGN
+    assert f(ST + 4, A, DS_FP16, 10, STREAM) == DS_ERR_ALIGN
+    assert f(A + 64, A, DS_FP16, 10000, STREAM) == DS_ERR_ALIAS

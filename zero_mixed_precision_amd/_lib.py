@@ -22,8 +22,9 @@ EXPORTED = (
     "ds_check_overflow", "ds_adam_step", "ds_update_loss_scale", "ds_adam_bias_scalars",
     "ds_layout_greedy", "ds_partition_range", "ds_status_string", "ds_sumsq_workspace_bytes",
     "ds_check_overflow_sumsq", "ds_accumulate_sumsq", "ds_adam_step_sched", "ds_lr_scalars",
-    "ds_adam_step_fused", "ds_accumulate_multi",
+    "ds_adam_step_fused", "ds_accumulate_multi", "ds_check_overflow_sumsq_noalloc",
 )
+DS_NOALLOC_MAX_ELEMS = 17175674880
 DS_LR_WARMUP, DS_LR_WARMUP_DECAY = 1, 2
 
 
@@ -117,6 +118,7 @@ def _load():
                           f32, i32, vp], ctypes.c_int),
         "ds_sumsq_workspace_bytes": ([i64], ctypes.c_size_t),
         "ds_check_overflow_sumsq": ([vp, vp, ctypes.c_int, i64, vp, ctypes.c_size_t, vp], ctypes.c_int),
+        "ds_check_overflow_sumsq_noalloc": ([vp, vp, ctypes.c_int, i64, vp], ctypes.c_int),
         "ds_accumulate_sumsq": ([vp, vp, ctypes.c_int, i64, i32, vp, vp, ctypes.c_size_t, vp], ctypes.c_int),
         "ds_accumulate_multi": ([vp, ctypes.POINTER(vp), i32, ctypes.c_int, i64, i32, vp, vp, ctypes.c_size_t, vp],
                                 ctypes.c_int),
@@ -275,6 +277,13 @@ def ds_check_overflow_sumsq(st, grad, dtype, n, workspace, workspace_bytes=None,
                                     _p(workspace, ds_sumsq_workspace_bytes(max(n, 0)), "workspace"),
                                     _nbytes(workspace, workspace_bytes), _s(stream)),
         "ds_check_overflow_sumsq")
+
+
+def ds_check_overflow_sumsq_noalloc(st, grad, dtype, n, stream=None) -> None:
+    n = int(n)
+    _ok(lib.ds_check_overflow_sumsq_noalloc(_scaler(st), _p(grad, _esize(dtype) * n, "gradient"), int(dtype), n,
+                                            _s(stream)),
+        "ds_check_overflow_sumsq_noalloc")
 
 
 def ds_accumulate_sumsq(acc, g16, gdt, n, overwrite, st, workspace, workspace_bytes=None,

@@ -44,10 +44,12 @@
 // hardware's exact widening and round-to-nearest-even narrowing.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
 #include <cstdint>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 
 #include "dszero.h"
 
@@ -1150,6 +1152,68 @@ ds_status adam_step(const ds_scaler* st, float* master, float* m, float* v, uint
 }  // namespace
 
 // ---------------------------------------------------------------------------
+// statically allocated scratch of ds_check_overflow_sumsq_noalloc
+// ---------------------------------------------------------------------------
+
+// The chunk and group sums of that entry point: 2^21 fp64 values (16 MiB),
+// held in each device's memory for the life of the process.  In host code the
+// array's name stands for no device address; the address of a device's copy
+// is looked up once per device (scratch_on) and passed to the kernels.
+constexpr int64_t kScratchDoubles = int64_t(1) << 21;
+static __device__ __align__(256) double scratch[kScratchDoubles];
+static_assert(DS_NOALLOC_MAX_ELEMS % kCheckChunk == 0, "the limit is a whole number of chunks");
+static_assert(DS_NOALLOC_MAX_ELEMS / kCheckChunk + (DS_NOALLOC_MAX_ELEMS / kCheckChunk + kGroup - 1) / kGroup <=
+                  kScratchDoubles, "the largest accepted n fits in the scratch array");
+static_assert((DS_NOALLOC_MAX_ELEMS / kCheckChunk + 1) + (DS_NOALLOC_MAX_ELEMS / kCheckChunk + kGroup) / kGroup >
+                  kScratchDoubles, "the limit is the largest n that fits");
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mutex;
+std::atomic<double*> scratch_ptr[kMaxDevices];
+
+// Device address of device `dev`'s copy of `scratch`: looked up on the first
+// call for that device, with that device current (and the caller's current
+// device restored), then kept.
+ds_status scratch_on(int dev, double** out)
+{
+    if (dev < 0 || dev >= kMaxDevices)
+        return DS_ERR_HIP;
+    double* p = scratch_ptr[dev].load(std::memory_order_acquire);
+    if (p == nullptr) {
+        std::lock_guard<std::mutex> lock(scratch_mutex);
+        p = scratch_ptr[dev].load(std::memory_order_relaxed);
+        if (p == nullptr) {
+            int cur = -1;
+            if (hipGetDevice(&cur) != hipSuccess)
+                return DS_ERR_HIP;
+            if (cur != dev && hipSetDevice(dev) != hipSuccess)
+                return DS_ERR_HIP;
+            void* addr = nullptr;
+            const hipError_t e = hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch));
+            const bool restored = cur == dev || hipSetDevice(cur) == hipSuccess;
+            if (e != hipSuccess || addr == nullptr || !restored)
+                return DS_ERR_HIP;
+            p = static_cast<double*>(addr);
+            scratch_ptr[dev].store(p, std::memory_order_release);
+        }
+    }
+    *out = p;
+    return DS_OK;
+}
+
+// The device a stream's work runs on (the current device for the null stream).
+ds_status stream_device(hipStream_t s, int* dev)
+{
+    if (s == nullptr)
+        return hipGetDevice(dev) == hipSuccess ? DS_OK : DS_ERR_HIP;
+    return hipStreamGetDevice(s, dev) == hipSuccess ? DS_OK : DS_ERR_HIP;
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
 // C ABI
 // ---------------------------------------------------------------------------
 
@@ -1343,6 +1407,35 @@ ds_status ds_check_overflow_sumsq(ds_scaler* st, const void* grad, ds_dtype dt, 
         overlap(st, sizeof(ds_scaler), workspace, wb))
         return DS_ERR_ALIAS;
     return launch_check_sumsq(st, grad, dt, n, static_cast<double*>(workspace), static_cast<hipStream_t>(stream));
+}
+
+ds_status ds_check_overflow_sumsq_noalloc(ds_scaler* st, const void* grad, ds_dtype dt, int64_t n, void* stream)
+{
+    if (n < 0 || n > DS_NOALLOC_MAX_ELEMS)
+        return DS_ERR_SIZE;
+    if (!known(dt))
+        return DS_ERR_DTYPE;
+    if (st == nullptr)
+        return DS_ERR_NULL;
+    if (n == 0)
+        return DS_OK;
+    if (grad == nullptr)
+        return DS_ERR_NULL;
+    if (!aligned(grad, 16) || !aligned(st, 8))
+        return DS_ERR_ALIGN;
+    if (overlap(grad, esize(dt) * static_cast<uint64_t>(n), st, sizeof(ds_scaler)))
+        return DS_ERR_ALIAS;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    int dev = -1;
+    if (stream_device(s, &dev) != DS_OK)
+        return DS_ERR_HIP;
+    double* ws = nullptr;
+    if (scratch_on(dev, &ws) != DS_OK)
+        return DS_ERR_HIP;
+    const uint64_t wb = 8 * static_cast<uint64_t>(kScratchDoubles);
+    if (overlap(grad, esize(dt) * static_cast<uint64_t>(n), ws, wb) || overlap(st, sizeof(ds_scaler), ws, wb))
+        return DS_ERR_ALIAS;
+    return launch_check_sumsq(st, grad, dt, n, ws, s);
 }
 
 ds_status ds_accumulate_sumsq(float* acc, const uint16_t* g16, ds_dtype gdt, int64_t n, int32_t overwrite,
