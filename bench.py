@@ -1,6 +1,6 @@
 """Benchmark of the ZeRO mixed-precision optimizer step on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload zero2_7b]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload zero1_70b]
 
 One step = the whole per-rank hot path over one synthetic batch: (K > 1:
 bucketed fp16 -> fp32 accumulation of every micro-batch, the last one with the
@@ -10,19 +10,27 @@ loss-scale update.  Inputs are
 resident in HBM before the timed region; gradients are drawn on the device
 (distinct buffers, reused cyclically when they do not all fit).
 
+The default workload is zero1_70b: one rank's ZeRO-1 share of a 70B model at
+N = 8, 8.75e9 elements (140 GB of state), the largest single-GPU workload.
+
 Prints one JSON line.  ``value`` is parameters updated per second (Gparams/s)
 over the timed steps; ``roofline`` is the Adam kernel's algorithmic HBM
 bandwidth (28 B/element with an fp16 gradient, 30 with the fp32 buffer) over
 its average duration, timed with HIP events on the launch stream, against
 the 8 TB/s HBM3E peak; ``traffic`` comes from the committed rocprofv3 counter
 summary when it was taken on the current kernel source; the median and minimum
-launch times and ``copy_mix_gbs`` (the same 14 B read + 14 B written per
-element with no arithmetic, on the same arrays, timed after the timed region)
-sit beside it; ``step_ms_*`` and ``pre_adam_ms_*`` (the check, or the
-accumulation with its fused check) come from an untimed pass with events
-around each part.  ``graph_replay`` times the same steps replayed from HIP
-graphs (one per position in the cycle of gradient buffers).  ``cpu_baseline`` times
-the CPU oracle on a bounded slice of the same workload.
+launch times sit beside it, ``roofline.step`` gives the whole step's
+algorithmic bytes per element (30 with a separately produced fp16 gradient)
+over the wall time per step, and ``roofline.references`` three data-movement
+references timed on the same arrays after the timed region: the step's
+14 B read + 14 B written per element with no arithmetic, a plain copy with one
+16-byte vector per lane, and the runtime's device-to-device copy
+(``torch.Tensor.copy_``, which is hipMemcpyAsync).  ``step_ms_*`` and
+``pre_adam_ms_*`` (the check, or the accumulation with its fused check) come
+from an untimed pass with events around each part.  ``graph_replay`` times the
+same steps replayed from HIP graphs (one per position in the cycle of gradient
+buffers).  ``cpu_baseline`` times the CPU oracle on a bounded slice of the
+same workload on the host cores the process may use.
 
     python bench.py --mode copy    # plain-copy and step-shaped data-movement references
 """
@@ -41,7 +49,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0
 METRIC = "Gparams/s per Adam step + achieved HBM GB/s (% of MI355X peak)"
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "adam_traffic_zero2_7b.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "adam_traffic.json")
 KERNEL_SRC = os.path.join(ROOT, "zero_mixed_precision_amd", "csrc", "dszero.hip")
 
 
@@ -113,7 +121,10 @@ def gpu_run(args):
     total_mb = (args.steps + args.warmup) * K
     free = torch.cuda.mem_get_info(dev)[0]
     fit = max(1, int((free - (4 << 30)) // (2 * n)))
-    nbuf = max(1, min(total_mb, fit, args.max_grad_buffers))
+    # a ring of at least 2 GiB of gradients (far beyond the 256 MB Infinity
+    # Cache), and never fewer buffers than one fold holds
+    enough = max(2, -(-(2 << 30) // (2 * n)), args.fold)
+    nbuf = max(1, min(total_mb, fit, args.max_grad_buffers, enough))
     if not 1 <= args.fold <= 8:
         sys.exit("bench.py: --fold takes 1..8")
     fold = min(args.fold, K)
@@ -253,23 +264,31 @@ def gpu_run(args):
     step_sorted = sorted(a.elapsed_time(b) for a, b in step_ev)
     pre_sorted = sorted(a.elapsed_time(b) for a, b in pre_ev)
 
-    # achievable-bandwidth reference, after the timed region: the step's data
-    # movement (14 B read + 14 B written per element) with no arithmetic, on the
-    # same arrays (it scrambles them; the run is over)
+    # data-movement references, after the timed region, on the same arrays
+    # (they scramble them; the run is over): the step's 14 B read + 14 B
+    # written per element with no arithmetic; a plain copy of master into m
+    # with one 16-byte vector per lane; the same copy by the runtime
+    # (torch's copy_ of a contiguous tensor on one device is hipMemcpyAsync)
+    def timed(fn, reps):
+        for _ in range(2):
+            fn()
+        evs = []
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            fn()
+            b.record(stream)
+            evs.append((a, b))
+        torch.cuda.synchronize()
+        return sum(a.elapsed_time(b) for a, b in evs) / len(evs) / 1e3
+
     nm = n - n % 4
     mix_args = (grads[0][:nm], master[:nm], m[:nm], v[:nm], p16[:nm])
-    for _ in range(2):
-        synth.device_stream_mix(torch, *mix_args, stream=stream)
-    mix_ev = []
-    for _ in range(8):
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record(stream)
-        synth.device_stream_mix(torch, *mix_args, stream=stream)
-        b.record(stream)
-        mix_ev.append((a, b))
-    torch.cuda.synchronize()
-    mix_s = sum(a.elapsed_time(b) for a, b in mix_ev) / len(mix_ev) / 1e3
+    mix_s = timed(lambda: synth.device_stream_mix(torch, *mix_args, stream=stream), 8)
     mix_gbs = 28 * nm / mix_s / 1e9
+    copy_s = timed(lambda: synth.device_copy(torch, m[:nm], master[:nm], stream=stream), 8)
+    memcpy_s = timed(lambda: m[:nm].copy_(master[:nm]), 8)
+    copy_gbs, memcpy_gbs = 8 * nm / copy_s / 1e9, 8 * nm / memcpy_s / 1e9
     bytes_per_elem = 28 if K == 1 else 30
     achieved = bytes_per_elem * n / adam_avg_s / 1e9
     if K == 1:
@@ -320,9 +339,14 @@ def gpu_run(args):
             "avg_launch_ms": round(adam_avg_s * 1e3, 4),
             "median_launch_ms": round(adam_sorted[len(adam_sorted) // 2], 4),
             "min_launch_ms": round(adam_sorted[0], 4),
-            "copy_mix_gbs": round(mix_gbs, 1),
+            "step": {"bytes_per_elem": step_bytes,
+                     "achieved": round(step_bytes * n * args.steps / wall / 1e9, 1),
+                     "frac": round(step_bytes * n * args.steps / wall / 1e9 / PEAK_HBM_GBS, 4)},
+            "references": {"step_shaped_no_arithmetic_gbs": round(mix_gbs, 1),
+                           "copy_one_vector_per_lane_gbs": round(copy_gbs, 1),
+                           "runtime_d2d_copy_gbs": round(memcpy_gbs, 1),
+                           "bytes": nm * 8},
         },
-        "step_hbm_gbs": round(step_bytes * n * args.steps / wall / 1e9, 1),
         "graph_replay": {"graphs": cycle, "ms_per_step": round(gwall / args.steps * 1e3, 4),
                          "value": round(n * args.steps / gwall / 1e9, 3)},
         "device": {"name": props.name, "arch": getattr(props, "gcnArchName", ""),
@@ -339,6 +363,35 @@ def gpu_run(args):
 # CPU baseline: the oracle on a bounded slice of the same workload
 # ----------------------------------------------------------------------------
 
+def cpu_share():
+    """Host CPUs this process may use: its affinity set, bounded by a cgroup CPU
+    quota when one is set (cgroup v2 cpu.max or v1 cfs quota), and by the
+    machine's OMP_NUM_THREADS when that states a smaller share."""
+    n = len(os.sched_getaffinity(0))
+    info = {"affinity_cpus": n}
+    quota = None
+    try:
+        q, period = open("/sys/fs/cgroup/cpu.max").read().split()[:2]
+        if q != "max":
+            quota = int(q) / int(period)
+    except (OSError, ValueError):
+        try:
+            q = int(open("/sys/fs/cgroup/cpu/cpu.cfs_quota_us").read())
+            period = int(open("/sys/fs/cgroup/cpu/cpu.cfs_period_us").read())
+            if q > 0:
+                quota = q / period
+        except (OSError, ValueError):
+            pass
+    if quota is not None:
+        info["cgroup_cpu_quota"] = quota
+        n = min(n, max(1, int(quota)))
+    omp = os.environ.get("OMP_NUM_THREADS", "")
+    if omp.isdigit() and int(omp) > 0:
+        info["omp_num_threads"] = int(omp)
+        n = min(n, int(omp))
+    return max(1, n), info
+
+
 def cpu_baseline(workload: str, min_seconds: float, slice_elems: int):
     from concurrent.futures import ThreadPoolExecutor
 
@@ -350,13 +403,14 @@ def cpu_baseline(workload: str, min_seconds: float, slice_elems: int):
 
     w = WORKLOADS[workload]
     n = min(slice_elems, w.psi)
-    threads = max(1, min(16, len(os.sched_getaffinity(0))))
+    threads, share = cpu_share()
     idx = np.arange(n)
     master = synth.host_master32(w.master_key(), idx, MASTER_SIGMA)
     m = np.zeros(n, np.float32)
     v = np.zeros(n, np.float32)
     p16 = np.zeros(n, np.uint16)
     grads = [synth.host_grad16(w.grad_key(s + 1), idx, w.grad_spec) for s in range(2)]
+    del idx
     sc = oracle.Scaler(w.init_scale, w.min_scale, w.window, w.hysteresis)
     cuts = np.linspace(0, n, threads + 1).astype(np.int64)
     sl = [slice(int(a), int(b)) for a, b in zip(cuts[:-1], cuts[1:])]
@@ -379,15 +433,17 @@ def cpu_baseline(workload: str, min_seconds: float, slice_elems: int):
     while True:
         step(grads[steps % 2])
         steps += 1
-        if time.perf_counter() - t0 >= min_seconds:
+        if steps >= 2 and time.perf_counter() - t0 >= min_seconds:
             break
     el = time.perf_counter() - t0
     pool.shutdown()
 
-    # the same step on one thread, over a 1/16 slice, for a quarter of the time
-    n1 = max(1, n // 16)
+    # the same step on one thread over a slice 1/threads as long (the oracle's
+    # loop is per element, so the rate does not depend on the length)
+    n1 = max(1, n // threads)
     g1 = [g[:n1].copy() for g in grads]
-    st1 = [master[:n1].copy(), np.zeros(n1, np.float32), np.zeros(n1, np.float32), np.zeros(n1, np.uint16)]
+    st1 = [synth.host_master32(w.master_key(), np.arange(n1), MASTER_SIGMA), np.zeros(n1, np.float32),
+           np.zeros(n1, np.float32), np.zeros(n1, np.uint16)]
     sc1 = oracle.Scaler(w.init_scale, w.min_scale, w.window, w.hysteresis)
     steps1 = 0
     t1 = time.perf_counter()
@@ -399,7 +455,7 @@ def cpu_baseline(workload: str, min_seconds: float, slice_elems: int):
                         beta2=BETA2, eps=EPS, weight_decay=WD)
         sc1.update(ov)
         steps1 += 1
-        if time.perf_counter() - t1 >= min_seconds / 4:
+        if steps1 >= 2 and time.perf_counter() - t1 >= min_seconds / 4:
             break
     el1 = time.perf_counter() - t1
     return {
@@ -409,6 +465,7 @@ def cpu_baseline(workload: str, min_seconds: float, slice_elems: int):
         "kind": "oracle",
         "sample": f"{n}-element slice of {workload} (K=1 steps: check + Adam + scaler update), "
                   f"{steps} steps in {el:.1f} s on {threads} threads",
+        "cpu_share": share,
         "single_thread_value": round(n1 * steps1 / el1 / 1e9, 4),
         "single_thread_sample": f"{n1}-element slice, {steps1} steps in {el1:.1f} s on 1 thread",
         "cpu_model": cpu_model(),
@@ -416,6 +473,20 @@ def cpu_baseline(workload: str, min_seconds: float, slice_elems: int):
 
 
 def cpu_model() -> str:
+    """lscpu's model name with the socket, core and thread counts, else /proc/cpuinfo's."""
+    import subprocess
+    try:
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        kv = dict(line.split(":", 1) for line in out.splitlines() if ":" in line)
+        kv = {k.strip(): v.strip() for k, v in kv.items()}
+        name = kv.get("Model name", "")
+        if name:
+            extra = ", ".join(f"{k} {kv[k]}" for k in ("CPU(s)", "Socket(s)", "Core(s) per socket",
+                                                         "Thread(s) per core", "CPU family", "Model")
+                              if k in kv)
+            return f"{name} ({extra})" if extra else name
+    except (OSError, ValueError, subprocess.SubprocessError):
+        pass
     try:
         with open("/proc/cpuinfo") as f:
             for line in f:
@@ -431,41 +502,42 @@ def cpu_model() -> str:
 # ----------------------------------------------------------------------------
 
 def copy_mode(args):
+    """Data-movement references on their own arrays: a 4 GiB copy by the plain
+    copy kernel and by the runtime (hipMemcpyAsync through torch's copy_), and
+    the step's 14 B read + 14 B written per element with no arithmetic on a
+    109M-element partition."""
     import torch
 
     import synth
     dev = torch.device("cuda:0")
     res = {}
+
+    def timed(fn, reps=10):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps / 1e3
+
     nbytes = 4 << 30
     src = torch.empty(nbytes // 4, dtype=torch.int32, device=dev).fill_(1)
     dst = torch.empty_like(src)
-    for _ in range(3):
-        synth.device_copy(torch, dst, src)
-    torch.cuda.synchronize()
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    reps = 10
-    a.record()
-    for _ in range(reps):
-        synth.device_copy(torch, dst, src)
-    b.record()
-    torch.cuda.synchronize()
-    t = a.elapsed_time(b) / reps / 1e3
-    res["copy"] = {"bytes_read": nbytes, "bytes_written": nbytes, "avg_ms": round(t * 1e3, 4),
-                   "GBps": round(2 * nbytes / t / 1e9, 1)}
+    for name, fn in (("copy_one_vector_per_lane", lambda: synth.device_copy(torch, dst, src)),
+                     ("runtime_d2d_copy", lambda: dst.copy_(src))):
+        t = timed(fn)
+        res[name] = {"bytes_read": nbytes, "bytes_written": nbytes, "avg_ms": round(t * 1e3, 4),
+                     "GBps": round(2 * nbytes / t / 1e9, 1)}
     del src, dst
     n = 109_375_000
     g = torch.zeros(n, dtype=torch.int16, device=dev)
     h = torch.zeros(n, dtype=torch.int16, device=dev)
     x, y, z = (torch.zeros(n, dtype=torch.float32, device=dev) for _ in range(3))
-    for _ in range(3):
-        synth.device_stream_mix(torch, g, x, y, z, h)
-    torch.cuda.synchronize()
-    a.record()
-    for _ in range(reps):
-        synth.device_stream_mix(torch, g, x, y, z, h)
-    b.record()
-    torch.cuda.synchronize()
-    t = a.elapsed_time(b) / reps / 1e3
+    t = timed(lambda: synth.device_stream_mix(torch, g, x, y, z, h))
     res["step_shaped_mix"] = {"elements": n, "bytes_per_elem": 28, "avg_ms": round(t * 1e3, 4),
                               "GBps": round(28 * n / t / 1e9, 1)}
     print(json.dumps({"mode": "copy", **res}), flush=True)
@@ -476,7 +548,7 @@ def main(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="zero2_7b")
+    ap.add_argument("--workload", default="zero1_70b")
     ap.add_argument("--mode", default="step", choices=["step", "copy"])
     ap.add_argument("--max-grad-buffers", type=int, default=8)
     ap.add_argument("--bf16", action="store_true",
@@ -484,7 +556,7 @@ def main(argv=None):
     ap.add_argument("--clip", type=float, default=0.0,
                     help="gradient_clipping max norm (0: the workloads' setting, no clipping)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
-    ap.add_argument("--cpu-slice", type=int, default=1 << 24)
+    ap.add_argument("--cpu-slice", type=int, default=109_375_000)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--fold", type=int, default=1,
                     help="micro-batches folded into the accumulation buffer per pass (1..8; K > 1 workloads; "

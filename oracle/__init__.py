@@ -92,6 +92,8 @@ def lib():
         L.zo_any_nonfinite32.argtypes, L.zo_any_nonfinite32.restype = [vp, i64], i32
         L.zo_adam_scalars.argtypes = [i64, f32, f32, f32, ctypes.POINTER(f32), ctypes.POINTER(f32)]
         L.zo_adam_scalars.restype = None
+        L.zo_adam_scalars_range.argtypes = [i64, i64, f32, f32, f32, vp]
+        L.zo_adam_scalars_range.restype = None
         L.zo_adam.argtypes = [vp, i32, i64, vp, vp, vp, vp, i32, f32, i32, i64, f32, f32, f32, f32, f32]
         L.zo_adam.restype = None
         L.zo_adam_mult.argtypes = [vp, i32, i64, vp, vp, vp, vp, i32, f32, i64, f32, f32, f32, f32, f32]
@@ -182,6 +184,13 @@ def adam_scalars(t: int, lr: float, beta1: float, beta2: float) -> tuple[float, 
     return a.value, b.value
 
 
+def adam_scalars_range(t0: int, count: int, lr: float, beta1: float, beta2: float) -> np.ndarray:
+    """float32[count, 2]: (step_size, rbc2) of the applied steps t0 .. t0 + count - 1."""
+    out = np.empty((int(count), 2), np.float32)
+    lib().zo_adam_scalars_range(int(t0), int(count), lr, beta1, beta2, _ptr(out))
+    return out
+
+
 def _gfmt(grad, fmt):
     return 2 if grad.dtype == np.float32 else FMT[fmt]
 
@@ -237,6 +246,48 @@ def grad_sumsq(grad: np.ndarray, fmt: str = "fp16") -> float:
     if not np.all(np.isfinite(grad)):
         return float("inf")
     return math.fsum((grad.astype(np.float64) ** 2).tolist())
+
+
+# Every finite fp32 square is an integer multiple of 2^-298 (the smallest
+# subnormal is 2^-149), so sums of fp32 squares are exact as Python integers
+# in that unit.
+SUMSQ32_UNIT_BITS = 298
+
+
+def sumsq32_exact_units(grad: np.ndarray):
+    """Exact sum of squares of fp32 values, as an integer count of 2^-298, or
+    None if a value is not finite.  Partial results of disjoint pieces add up
+    exactly, so a sum over an array too large to hold at once is the sum of
+    its pieces' results; ``units_to_float`` rounds it once.
+
+    From the binary32 definition: the value with exponent field e and fraction
+    f is M * 2^(E - 150) with M = f + 2^23, E = e for e >= 1, and M = f, E = 1
+    for e = 0, so its square is M^2 * 4^(E - 1) units.  M^2 < 2^48 is taken in
+    three parts (M = Mh * 2^12 + Ml, M^2 = Mh^2 * 2^24 + Mh*Ml * 2^13 + Ml^2),
+    each below 2^24, and every part is summed per exponent field in fp64,
+    which is exact while a piece holds at most 2^29 values."""
+    _require(grad.dtype == np.float32)
+    bits = np.ascontiguousarray(grad).view(np.uint32)
+    _require(bits.size <= 1 << 29)
+    e = ((bits >> 23) & 0xFF).astype(np.int64)
+    if np.any(e == 0xFF):
+        return None
+    f = (bits & 0x7FFFFF).astype(np.int64)
+    M = np.where(e == 0, f, f + (1 << 23))
+    Mh, Ml = M >> 12, M & 0xFFF
+    parts = [np.bincount(e, weights=(w).astype(np.float64), minlength=256)
+             for w in (Mh * Mh, Mh * Ml, Ml * Ml)]
+    total = 0
+    for ex in range(255):
+        hh, hl, ll = (int(p[ex]) for p in parts)
+        if hh or hl or ll:
+            total += ((hh << 24) + (hl << 13) + ll) << (2 * (max(ex, 1) - 1))
+    return total
+
+
+def units_to_float(total_units: int) -> float:
+    """An exact sum of squares in units of 2^-298, rounded once to fp64."""
+    return total_units / (1 << SUMSQ32_UNIT_BITS)
 
 
 def clip_multiplier(sumsq: float, scale: float, accum_steps: int, max_norm: float) -> np.float32:

@@ -238,6 +238,14 @@ void zo_adam_scalars(int64_t t, float lr, float beta1, float beta2,
     *rbc2 = (float)(1.0 / sqrt(1.0 - b2t));
 }
 
+/* zo_adam_scalars for the applied steps t0, t0 + 1, ..., t0 + count - 1:
+ * out2[2 j] = step_size, out2[2 j + 1] = rbc2 of step t0 + j. */
+void zo_adam_scalars_range(int64_t t0, int64_t count, float lr, float beta1, float beta2, float *out2)
+{
+    for (int64_t j = 0; j < count; ++j)
+        zo_adam_scalars(t0 + j, lr, beta1, beta2, &out2[2 * j], &out2[2 * j + 1]);
+}
+
 /* One applied Adam step over n elements of a flat partition.
  *
  * Algorithm (bias-corrected Adam, epsilon outside the square root):

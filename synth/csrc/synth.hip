@@ -72,12 +72,18 @@ __global__ __launch_bounds__(256) void fill_master32_kernel(float* out, int64_t 
         out[i] = master_at(key, start + i, table);
 }
 
-__global__ __launch_bounds__(256) void copy_kernel(uint4* __restrict__ dst,
-                                                   const uint4* __restrict__ src, int64_t n16)
+// Plain copy, one 16-byte vector per lane, 64-lane blocks, one block per 64
+// vectors (the blocks loop when there are more than 2^25 of them, keeping the
+// launch within 2^31 work-items); non-temporal hints.  Of the copy shapes
+// measured on MI355X (64-1024 lanes x 1-4 vectors) this one moves the most
+// bytes per second.
+typedef unsigned copy_u4 __attribute__((ext_vector_type(4)));
+__global__ __launch_bounds__(64) void copy_kernel(copy_u4* __restrict__ dst, const copy_u4* __restrict__ src,
+                                                  int64_t n16)
 {
-    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += stride)
-        dst[i] = src[i];
+    const int64_t stride = (int64_t)gridDim.x * 64;
+    for (int64_t i = (int64_t)blockIdx.x * 64 + threadIdx.x; i < n16; i += stride)
+        __builtin_nontemporal_store(__builtin_nontemporal_load(src + i), dst + i);
 }
 
 // Moves the bytes of one optimizer step without computing anything: per
@@ -163,8 +169,10 @@ int synth_copy(void* dst, const void* src, int64_t n16, void* stream)
     if (n16 <= 0) return 0;
     if (((reinterpret_cast<uintptr_t>(dst) | reinterpret_cast<uintptr_t>(src)) & 15u) != 0)
         return (int)hipErrorInvalidValue;
-    copy_kernel<<<grid_for(n16), 256, 0, static_cast<hipStream_t>(stream)>>>(
-        static_cast<uint4*>(dst), static_cast<const uint4*>(src), n16);
+    int64_t blocks = (n16 + 63) / 64;
+    if (blocks > (int64_t(1) << 25)) blocks = int64_t(1) << 25;
+    copy_kernel<<<(unsigned)blocks, 64, 0, static_cast<hipStream_t>(stream)>>>(
+        static_cast<copy_u4*>(dst), static_cast<const copy_u4*>(src), n16);
     return (int)hipGetLastError();
 }
 

@@ -85,3 +85,47 @@ def test_load_rejects_a_different_shard(torch, tmp_path):
         ShardStep(4104, cfg, device="cuda:0").load_checkpoint(str(tmp_path), tag="t0")
     with pytest.raises(ValueError, match="parameter copy"):
         ShardStep(4096, ZeroMPConfig(bf16=True), device="cuda:0").load_checkpoint(str(tmp_path), tag="t0")
+
+
+def test_load_on_a_raw_stream_handle_and_refuse_a_corrupt_scaler(torch, tmp_path):
+    """A shard driven on a raw hipStream_t handle (an int) saves and loads; a file
+    whose scaler state was tampered with (a zero loss scale) is refused before
+    anything is written to the shard."""
+    from safetensors import safe_open
+    from safetensors.torch import save_file
+
+    from zero_mixed_precision_amd import ShardStep, ZeroMPConfig
+    n = 8192
+    side = torch.cuda.Stream()
+    cfg = ZeroMPConfig(lr=1e-4)
+    g = gu.dev_u16(torch, synth.host_grad16(synth.stream_key(79, synth.ARR_GRAD), np.arange(n),
+                                            synth.GradSpec(1e-3, cfg.init_scale)))
+    a = ShardStep(n, cfg, device="cuda:0", stream=side.cuda_stream)
+    a.master.copy_(torch.from_numpy(synth.host_master32(synth.stream_key(79, synth.ARR_MASTER), np.arange(n),
+                                                        MASTER_SIGMA)))
+    torch.cuda.synchronize()
+    a.step(g)
+    path = a.save_checkpoint(str(tmp_path), tag="good")
+    b = ShardStep(n, cfg, device="cuda:0", stream=side.cuda_stream)
+    b.load_checkpoint(str(tmp_path), tag="good")
+    b.step(g)
+    a.step(g)
+    side.synchronize()
+    assert torch.equal(a.master.view(torch.int32), b.master.view(torch.int32))
+    assert a.scaler().as_dict() == b.scaler().as_dict()
+
+    with safe_open(path, framework="pt", device="cpu") as f:
+        meta = f.metadata()
+        tensors = {k: f.get_tensor(k) for k in f.keys()}
+    raw = tensors["scaler"].clone()
+    raw[0:4] = 0                                   # scale = 0.0
+    tensors["scaler"] = raw
+    bad = tmp_path / "bad" / "zero_shard_rank00000.safetensors"
+    bad.parent.mkdir()
+    save_file(tensors, str(bad), metadata=meta)
+    c = ShardStep(n, cfg, device="cuda:0", stream=side.cuda_stream)
+    c.master.fill_(7.0)
+    torch.cuda.synchronize()
+    with pytest.raises(ValueError, match="loss-scaler"):
+        c.load_checkpoint(str(tmp_path), tag="bad")
+    assert bool((c.master == 7.0).all())

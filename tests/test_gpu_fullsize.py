@@ -245,17 +245,27 @@ def test_ragged_layout_clipped(torch):
     """Clipping on the ragged layout with 8 micro-batches at full size (the launch
     bench.py --workload ragged --clip 1.0 times): the last micro-batch's
     accumulation also gathers the sum of squares of the fp32 sum, bucket by
-    bucket, into the state.  The whole sum cannot be formed on the host here, so
-    it is checked against torch's own fp64 sum of squares of the device's
-    accumulation buffer (a library routine, independent of these kernels) to
-    1e-12, and the sampled elements are updated by the oracle with the
-    multiplier of that sum; clipping is active (norm about 28, limit 1)."""
+    bucket, into the state.  The whole sum cannot be formed on the GPU machine's
+    host in a test, so the expected values were written beforehand by
+    tests/golden/make_ragged_clip_sumsq.py, which regenerates every micro-batch
+    gradient on the host, accumulates it with the oracle and sums the squares
+    exactly (tests/golden/ragged_clip_sumsq.json: the running sum after each
+    bucket and the total, rounded once).  The device's running sum must meet
+    every one of them to 1e-12, and the sampled elements are updated by the
+    oracle with the multiplier of the stored total; clipping is active (norm
+    about 28, limit 1)."""
+    import json
+    import os
+
     from zero_mixed_precision_amd import _lib, FlatLayout
 
     w = WORKLOADS["ragged"]
     n, K, max_norm, steps = w.psi, w.K, 1.0, 2
+    golden = json.load(open(os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden",
+                                         "ragged_clip_sumsq.json")))
     lay = FlatLayout(ragged_numels())
     buckets = [(b.start, b.size) for b in lay.buckets]
+    assert golden["elements"] == n and golden["buckets"] == [list(b) for b in buckets]
     I = sample_indices(w, buckets)
     spec = w.grad_spec
     master0 = synth.host_master32(w.master_key(), I, MASTER_SIGMA)
@@ -273,27 +283,30 @@ def test_ragged_layout_clipped(torch):
     st = torch.zeros(_lib.ds_scaler_size(), dtype=torch.uint8, device="cuda:0")
     _lib.ds_state_init(st, w.init_scale, w.min_scale, w.window, w.hysteresis, 0, 1)
     Id = torch.from_numpy(I).to("cuda:0")
-    chunk = 1 << 28
     for s in range(1, steps + 1):
+        want = golden["steps"][str(s)]
+        running = [float.fromhex(x) for x in want["cumulative_by_bucket"]]
+        total = float.fromhex(want["total"])
         acc_s = np.empty(I.size, np.float32)
         for k in range(K):
             key = w.grad_key(s, k)
             synth.device_fill_grad16(torch, tabs, g16, key, spec)
             oracle.accumulate(acc_s, synth.host_grad16(key, I, spec), overwrite=(k == 0))
-            for start, size in buckets:
+            for b, (start, size) in enumerate(buckets):
                 a, gp = acc.data_ptr() + 4 * start, g16.data_ptr() + 2 * start
                 if k == K - 1:
                     _lib.ds_accumulate_sumsq(a, gp, _lib.DS_FP16, size, k == 0, st, ws)
+                    got = _lib.ds_state_read(st).grad_sumsq
+                    assert abs(got - running[b]) <= 1e-12 * running[b], (s, b, got, running[b])
                 else:
                     _lib.ds_accumulate(a, gp, _lib.DS_FP16, size, k == 0)
-        ref = sum(float(acc[i:i + chunk].double().square().sum()) for i in range(0, n, chunk))
         got_pre = _lib.ds_state_read(st)
         assert got_pre.overflow == 0
-        assert abs(got_pre.grad_sumsq - ref) <= 1e-12 * ref, (got_pre.grad_sumsq, ref)
+        assert abs(got_pre.grad_sumsq - total) <= 1e-12 * total, (got_pre.grad_sumsq, total)
         _lib.ds_adam_step_fused(st, master, m, v, p16, _lib.DS_FP16, acc, _lib.DS_FP32, n, LR, None, BETA1, BETA2,
                                 EPS, 0.0, max_norm, K)
         got = _lib.ds_state_read(st)
-        mult = oracle.clip_multiplier(ref, o.scaler.scale, K, max_norm)
+        mult = oracle.clip_multiplier(total, o.scaler.scale, K, max_norm)
         assert mult < np.float32(1.0) / np.float32(w.init_scale * K)      # clipping is active
         oracle.adam_mult(acc_s, o.master, o.m, o.v, o.p16, mult=mult, t=o.scaler.applied + 1, lr=LR, beta1=BETA1,
                          beta2=BETA2, eps=EPS)
@@ -301,6 +314,7 @@ def test_ragged_layout_clipped(torch):
         gu.check_scaler(got, o.scaler, False, f"[ragged clipped] step {s}")
         du = gu.compare_arrays(f"[ragged clipped] step {s}", gu.host_f32(master[Id]), gu.host_f32(m[Id]),
                                gu.host_f32(v[Id]), gu.host_u16(p16[Id]), o.master, o.m, o.v, o.p16)
-        gu.say(f"[ragged clipped] step {s}: sumsq {ref:.6g}, max ulp {du}")
+        gu.say(f"[ragged clipped] step {s}: sumsq {total:.6g} (stored), device {got.last_grad_sumsq:.6g}, "
+               f"max ulp {du}")
     del master, m, v, p16, g16, acc, ws, st
     torch.cuda.empty_cache()

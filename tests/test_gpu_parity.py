@@ -301,6 +301,38 @@ def test_bias_correction_scalars_bit_exact(torch):
         assert np.array_equal(f32_bits(got[a]), f32_bits(want)), (lr, b1, b2)
 
 
+def test_bias_correction_scalars_for_every_step_to_a_million(torch):
+    """The device's per-step factors lr/(1-beta1^t) and 1/sqrt(1-beta2^t) (fp64,
+    rounded once) equal the oracle's bit for bit for every applied step t =
+    1..10^6, for three hyperparameter sets: this guards the lowering of the
+    fp64 divide and square root.  The applied-step count advances on the
+    device by one successful scaler update per t (static scale, no host
+    round trip), and each t's pair is written to its own slot."""
+    import ctypes
+
+    from zero_mixed_precision_amd import _lib
+    T = 10 ** 6
+    hps = [(1e-4, 0.9, 0.999), (3e-4, 0.95, 0.98), (1e-3, 0.5, 0.9999)]
+    L = _lib.lib
+    out = torch.zeros((T, 2), dtype=torch.float32, device="cuda:0")
+    st = torch.zeros(_lib.ds_scaler_size(), dtype=torch.uint8, device="cuda:0")
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    st_p, base = ctypes.c_void_p(st.data_ptr()), out.data_ptr()
+    bias, update = L.ds_adam_bias_scalars, L.ds_update_loss_scale
+    for lr, b1, b2 in hps:
+        gu.say(f"[bias scalars] lr={lr} betas=({b1}, {b2}) t=1..{T}")
+        _lib.ds_state_init(st, 1.0, 1.0, 1, 1, 0, 0)           # static scale: updates only advance t
+        flr, fb1, fb2 = ctypes.c_float(lr), ctypes.c_float(b1), ctypes.c_float(b2)
+        for j in range(T):
+            if bias(st_p, flr, fb1, fb2, ctypes.c_void_p(base + 8 * j), stream) != 0 or update(st_p, stream) != 0:
+                raise AssertionError(f"launch failed at t={j + 1}")
+        got = out.cpu().numpy()
+        assert _lib.ds_state_read(st).step == T
+        want = oracle.adam_scalars_range(1, T, lr, b1, b2)
+        bad = np.nonzero(f32_bits(got).ravel() != f32_bits(want).ravel())[0]
+        assert bad.size == 0, (lr, b1, b2, "first differing t", int(bad[0] // 2) + 1)
+
+
 @pytest.mark.parametrize("wd", [0.01, 0.1])
 def test_weight_decay(torch, wd):
     n = 65536 + 9

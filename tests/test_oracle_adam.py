@@ -364,3 +364,14 @@ def test_worked_example_fixture(oracle_lib):
             g = h16(s["grad16"]).view(np.float16).astype(np.float64) / S16
             delta = float(np.float32(LR)) * g / (np.abs(g) + float(np.float32(EPS)))
             assert np.all(np.abs(h32(s["master"]) - (p0 - delta)) <= ulp32(p0) + 1e-6 * np.abs(delta))
+
+
+def test_scalars_range_equals_the_scalar_function():
+    """The array form of the per-step factors is the per-step function, step by step."""
+    for lr, b1, b2 in ((1e-4, 0.9, 0.999), (3e-4, 0.95, 0.98)):
+        got = oracle.adam_scalars_range(1, 2000, lr, b1, b2)
+        want = np.array([oracle.adam_scalars(t, lr, b1, b2) for t in range(1, 2001)], np.float32)
+        assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
+        got = oracle.adam_scalars_range(10 ** 6 - 3, 4, lr, b1, b2)
+        want = np.array([oracle.adam_scalars(t, lr, b1, b2) for t in range(10 ** 6 - 3, 10 ** 6 + 1)], np.float32)
+        assert np.array_equal(got.view(np.uint32), want.view(np.uint32))

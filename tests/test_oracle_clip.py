@@ -129,3 +129,40 @@ def test_matches_torch_clip_grad_norm_then_adam(K):
     move_ref = ref.astype(np.float64) - p0
     assert np.all(np.abs(move - move_ref) <= 1e-5 * T * LR + 4 * ulp32(ref))
     assert np.allclose(st.m, opt.state[param]["exp_avg"].numpy(), rtol=1e-5, atol=1e-9)
+
+
+def test_sumsq32_exact_units_matches_rational_sums():
+    """The integer form of the fp32 sum of squares equals the exact rational sum
+    (in units of 2^-298), across the whole exponent range, subnormals, zeros of
+    either sign and the largest finite value; pieces add up to the whole."""
+    rng = np.random.default_rng(7)
+    unit = Fraction(1, 2 ** oracle.SUMSQ32_UNIT_BITS)
+    specials = np.array([0.0, -0.0, 1e-45, -1e-45, 1.1754942e-38, 1.1754944e-38, 3.4028235e38, -1.0, 2.0 ** -126],
+                        np.float32)
+    for trial in range(12):
+        n = int(rng.integers(1, 2500))
+        bits = rng.integers(0, 2 ** 32, n, dtype=np.uint64).astype(np.uint32)
+        bits = np.where(((bits >> 23) & 0xFF) == 0xFF, bits & 0x807FFFFF, bits).astype(np.uint32)
+        x = np.concatenate([bits.view(np.float32), specials])
+        exact = sum(Fraction(float(v)) ** 2 for v in x)
+        units = oracle.sumsq32_exact_units(x)
+        assert Fraction(units) * unit == exact
+        assert oracle.units_to_float(units) == float(exact)
+        cut = int(rng.integers(0, x.size))
+        assert oracle.sumsq32_exact_units(x[:cut]) + oracle.sumsq32_exact_units(x[cut:]) == units
+    # the accumulation buffer's values: sums of a few fp16 gradients
+    g = (rng.standard_normal((8, 4000)) * 30).astype(np.float16).astype(np.float32).sum(axis=0, dtype=np.float32)
+    assert oracle.units_to_float(oracle.sumsq32_exact_units(g)) == math.fsum((g.astype(np.float64) ** 2).tolist())
+    assert oracle.sumsq32_exact_units(np.array([1.0, np.inf], np.float32)) is None
+    assert oracle.sumsq32_exact_units(np.array([np.nan], np.float32)) is None
+    assert oracle.sumsq32_exact_units(np.zeros(0, np.float32)) == 0
+
+
+def test_sumsq32_exact_units_catches_a_dropped_term():
+    """A plausible slip in the integer form (the cross term's factor) changes
+    the sum: the three parts are all needed."""
+    x = np.array([1.0 + 2.0 ** -23, 3.0, 1e-40], np.float32)
+    exact = sum(Fraction(float(v)) ** 2 for v in x) * 2 ** oracle.SUMSQ32_UNIT_BITS
+    assert oracle.sumsq32_exact_units(x) == exact
+    M = (x.view(np.uint32) & 0x7FFFFF).astype(np.int64) + (1 << 23)
+    assert int(((M[:2] >> 12) * (M[:2] & 0xFFF)).sum()) != 0      # the cross term is not zero here

@@ -23,6 +23,48 @@ import os
 FORMAT = "zero-mp-shard-1"
 
 
+def torch_stream(stream, torch):
+    """The torch stream for a ShardStep's stream: None is torch's current
+    stream, a raw hipStream_t handle (an int) is wrapped, a torch stream is
+    used as it is."""
+    if stream is None:
+        return torch.cuda.current_stream()
+    if isinstance(stream, int):
+        return torch.cuda.ExternalStream(stream)
+    return stream
+
+
+def validate_scaler(sc, where: str = "scaler state") -> None:
+    """Refuse a restored loss-scaler state that the library would not have
+    produced between steps ("DeepSpeed complete guide" section 4.2: a dynamic
+    or static scale, loss_scale_window, hysteresis, min_loss_scale):
+    ds_state_write copies it as it is, so a corrupt or foreign file could
+    otherwise leave an unusable scale or disable growth.  Raises ValueError."""
+    import math
+
+    def bad(what):
+        raise ValueError(f"{where}: invalid loss-scaler state ({what})")
+
+    if not (math.isfinite(sc.scale) and sc.scale > 0):
+        bad(f"scale {sc.scale}")
+    if not (math.isfinite(sc.min_scale) and sc.min_scale > 0):
+        bad(f"min_scale {sc.min_scale}")
+    if sc.growth_window < 1:
+        bad(f"growth_window {sc.growth_window}")
+    if sc.hysteresis < 1:
+        bad(f"hysteresis {sc.hysteresis}")
+    if not 0 <= sc.growth_count < sc.growth_window:
+        bad(f"growth_count {sc.growth_count} of window {sc.growth_window}")
+    if not 1 <= sc.hysteresis_left <= sc.hysteresis:
+        bad(f"hysteresis_left {sc.hysteresis_left} of {sc.hysteresis}")
+    if sc.dynamic not in (0, 1) or sc.consecutive_hysteresis not in (0, 1):
+        bad("dynamic / consecutive_hysteresis not 0 or 1")
+    if min(sc.step, sc.iter, sc.skipped) < 0 or sc.step + sc.skipped != sc.iter:
+        bad(f"step counts (applied {sc.step} + skipped {sc.skipped} != all {sc.iter})")
+    if sc.overflow != 0 or sc.grad_sumsq != 0.0:
+        bad("taken inside a step (overflow flag or gradient sum of squares pending)")
+
+
 def _file(save_dir: str, tag: str, rank: int) -> str:
     return os.path.join(save_dir, str(tag), f"zero_shard_rank{int(rank):05d}.safetensors")
 
@@ -88,12 +130,13 @@ def load_checkpoint(step, load_dir: str, tag=None, rank: int = 0):
         if len(raw) != _lib.ds_scaler_size():
             raise ValueError(f"{path}: scaler state of {len(raw)} bytes")
         arrays = {k: f.get_tensor(k) for k in ("master", "exp_avg", "exp_avg_sq", "param16")}
-    stream = step.stream if step.stream is not None else torch.cuda.current_stream()
-    with torch.cuda.stream(stream):
+    sc = _lib.DsScaler.from_buffer_copy(raw)
+    validate_scaler(sc, path)
+    with torch.cuda.stream(torch_stream(step.stream, torch)):
         step.master.copy_(arrays["master"])
         step.m.copy_(arrays["exp_avg"])
         step.v.copy_(arrays["exp_avg_sq"])
         step.p16.view(torch.int16).copy_(arrays["param16"])
-    _lib.ds_state_write(step.state, _lib.DsScaler.from_buffer_copy(raw), step.stream)
+    _lib.ds_state_write(step.state, sc, step.stream)
     step._micro = 0
     return path, json.loads(meta["client_state"])

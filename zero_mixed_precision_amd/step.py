@@ -35,13 +35,53 @@ from .config import ZeroMPConfig
 
 
 def buckets_or_all(buckets, n):
-    return [(b.start, b.size) for b in buckets] if buckets else [(0, n)]
+    """(start, size) pairs of the accumulation buckets inside a partition of n
+    elements (objects with .start/.size, or pairs), or the whole partition.
+
+    The buckets must tile [0, n): sorted, the first at 0, each starting where
+    the previous one ends, the sizes adding up to n, and every start a multiple
+    of 8 elements (so that every array pointer the calls derive stays 16-byte
+    aligned).  Anything else raises ValueError: the calls receive raw
+    addresses, so a bucket past the end would be written out of bounds, and a
+    gap would leave part of the accumulation buffer stale and unchecked."""
+    if not buckets:
+        return [(0, int(n))]
+    pairs = [(int(b.start), int(b.size)) if hasattr(b, "start") else (int(b[0]), int(b[1])) for b in buckets]
+    end = 0
+    for start, size in pairs:
+        if start != end:
+            raise ValueError(f"bucket at {start} does not start where the previous one ends ({end}): "
+                             "buckets must tile [0, n) in order")
+        if size < 0:
+            raise ValueError(f"bucket at {start} has a negative size")
+        if start % 8:
+            raise ValueError(f"bucket at {start} does not start on a multiple of 8 elements")
+        end = start + size
+    if end != n:
+        raise ValueError(f"buckets cover [0, {end}), the partition has {n} elements")
+    return pairs
+
+
+def check_grad_dtype(dtype, bf16: bool, torch) -> None:
+    """The fp16 and bf16 formats are exclusive ("DeepSpeed complete guide"
+    section 4.2): a float16 gradient for a bf16 shard, or a bfloat16 one for an
+    fp16 shard, would be read bit for bit in the other format, so it is
+    refused.  int16 (and uint16) tensors pass as raw bit containers."""
+    raw = (torch.int16,) + ((torch.uint16,) if hasattr(torch, "uint16") else ())
+    if dtype in raw:
+        return
+    want = torch.bfloat16 if bf16 else torch.float16
+    if dtype != want:
+        raise ValueError(f"gradient of dtype {dtype} for a {'bf16' if bf16 else 'fp16'} shard "
+                         f"(expected {want}, or int16 raw bits)")
 
 
 class ShardStep:
     def __init__(self, n: int, cfg: ZeroMPConfig, device="cuda", buckets=None, stream=None):
         import torch
 
+        # accumulation granularity: the reduce buckets inside this partition
+        self.buckets = buckets_or_all(buckets, int(n))
         self.torch, self.n, self.cfg = torch, int(n), cfg
         self.K = int(cfg.gradient_accumulation_steps)
         self.stream = stream
@@ -64,8 +104,6 @@ class ShardStep:
             nbytes = _lib.ds_sumsq_workspace_bytes(self.n)
             self.ws = torch.zeros((nbytes + 7) // 8, dtype=torch.float64, device=device)
         self._ws_bytes = self.ws.numel() * 8 if self.ws is not None else 0
-        # accumulation granularity: the reduce buckets inside this partition
-        self.buckets = buckets_or_all(buckets, self.n)
         self._micro = 0
         _lib.ds_state_init(self.state, cfg.init_scale, cfg.min_loss_scale, cfg.loss_scale_window,
                            cfg.hysteresis, int(cfg.consecutive_hysteresis), int(cfg.dynamic),
@@ -76,6 +114,7 @@ class ShardStep:
             raise ValueError(f"expected a 16-bit gradient of {self.n} elements")
         if g16.device != self.master.device or not g16.is_contiguous():
             raise ValueError(f"the gradient must be a contiguous tensor on {self.master.device}")
+        check_grad_dtype(g16.dtype, self.cfg.bf16, self.torch)
 
     def accumulate(self, g16) -> None:
         """Add one fp16 micro-batch gradient (K > 1), or a list of up to 8 of them
