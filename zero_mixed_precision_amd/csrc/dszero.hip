@@ -653,9 +653,33 @@ __global__ __launch_bounds__(TPB) void check_kernel(ds_scaler* __restrict__ st,
 // exact in fp32 (at most 22 significant bits, between 2^-48 and 65504^2), so
 // fp16 squares are taken in fp32 and widened for the fp64 sum -- the same
 // values as fp64 squares, for less fp64 work; bf16 and fp32 squares are taken
-// in fp64.  One block per chunk (measured at 1.9e8 and 8.75e9 elements: 6.6
-// TB/s, against 6.1-6.2 with 1024 lanes x 2 vectors per 16,384 elements and
-// a two-barrier block sum; the plain check reads at 6.7-6.8).
+// in fp64.  One block per chunk; measured at 8.75e9 elements in one process:
+// 6.5 TB/s, against 6.1-6.2 with 1024 lanes x 2 vectors per 16,384 elements
+// and a two-barrier block sum, 6.3-6.5 with chunks of one wave (no barrier)
+// and 6.8 for the plain check.
+// One 16-byte vector of the gradient: ORs its non-finite test into `bad` and
+// adds the sums of its squares to `s`, four elements at a time in element
+// order.
+template <int GF>
+__device__ __forceinline__ void check_sq_vec(const u32x4& w, uint32_t& bad, double& s)
+{
+    if constexpr (GF == kF32) {
+        bad |= nonfinite_f32(w.x) | nonfinite_f32(w.y) | nonfinite_f32(w.z) | nonfinite_f32(w.w);
+        s = s + sq4(f32x4{__uint_as_float(w.x), __uint_as_float(w.y), __uint_as_float(w.z), __uint_as_float(w.w)});
+    } else {
+        bad |= nonfinite16x2<GF>(w.x) | nonfinite16x2<GF>(w.y) | nonfinite16x2<GF>(w.z) | nonfinite16x2<GF>(w.w);
+        const f32x4 a = widen4<GF>(u32x2{w.x, w.y});
+        const f32x4 b = widen4<GF>(u32x2{w.z, w.w});
+        if constexpr (GF == kF16) {
+            s = s + sq4_exact32(a);
+            s = s + sq4_exact32(b);
+        } else {
+            s = s + sq4(a);
+            s = s + sq4(b);
+        }
+    }
+}
+
 template <int GF, int TPB>
 __global__ __launch_bounds__(TPB) void check_sumsq_kernel(ds_scaler* __restrict__ st,
                                                           const void* __restrict__ grad, int64_t n,
@@ -667,46 +691,38 @@ __global__ __launch_bounds__(TPB) void check_sumsq_kernel(ds_scaler* __restrict_
     static_assert(static_cast<int64_t>(TPB) * kVecs * kPer == kCheckChunk, "one chunk per block");
     __shared__ double lds[2 * (TPB / 64)];
     const u32x4* G = static_cast<const u32x4*>(grad);
-    const int64_t nchunks = (n + kCheckChunk - 1) / kCheckChunk;
+    const int64_t nfull = n / kCheckChunk;
     uint32_t bad = 0u;
     int parity = 0;
-    for (int64_t c = blockIdx.x; c < nchunks; c += gridDim.x) {
+    // whole chunks: every vector in bounds, all loads issued before the arithmetic
+    for (int64_t c = blockIdx.x; c < nfull; c += gridDim.x) {
         const int64_t v0 = c * (kCheckChunk / kPer) + threadIdx.x;
+        double s = 0.0;
         u32x4 w[kVecs];
-        bool full[kVecs];
 #pragma unroll
+        for (int j = 0; j < kVecs; ++j)
+            w[j] = G[v0 + static_cast<int64_t>(j) * TPB];
+#pragma unroll
+        for (int j = 0; j < kVecs; ++j)
+            check_sq_vec<GF>(w[j], bad, s);
+        const double cs = block_sum_fixed<TPB>(s, lds, parity);
+        parity ^= 1;
+        if (threadIdx.x == 0)
+            part[c] = cs;
+    }
+    // the last, partial chunk, by block 0 after its whole chunks: whole vectors
+    // as above, then element by element (kept out of the loop above, where the
+    // extra paths cost the whole-chunk pass 9 % in time)
+    if (blockIdx.x == 0 && nfull * kCheckChunk < n) {
+        const int64_t v0 = nfull * (kCheckChunk / kPer) + threadIdx.x;
+        double s = 0.0;
         for (int j = 0; j < kVecs; ++j) {
             const int64_t v = v0 + static_cast<int64_t>(j) * TPB;
-            full[j] = (v + 1) * kPer <= n;
-            if (full[j])
-                w[j] = G[v];
-        }
-        double s = 0.0;
-#pragma unroll
-        for (int j = 0; j < kVecs; ++j) {
-            const int64_t e0 = (v0 + static_cast<int64_t>(j) * TPB) * kPer;
-            if (full[j]) {
-                if constexpr (F32) {
-                    bad |= nonfinite_f32(w[j].x) | nonfinite_f32(w[j].y) | nonfinite_f32(w[j].z) |
-                           nonfinite_f32(w[j].w);
-                    s = s + sq4(f32x4{__uint_as_float(w[j].x), __uint_as_float(w[j].y),
-                                      __uint_as_float(w[j].z), __uint_as_float(w[j].w)});
-                } else {
-                    bad |= nonfinite16x2<GF>(w[j].x) | nonfinite16x2<GF>(w[j].y) |
-                           nonfinite16x2<GF>(w[j].z) | nonfinite16x2<GF>(w[j].w);
-                    const f32x4 a = widen4<GF>(u32x2{w[j].x, w[j].y});
-                    const f32x4 b = widen4<GF>(u32x2{w[j].z, w[j].w});
-                    if constexpr (GF == kF16) {
-                        s = s + sq4_exact32(a);
-                        s = s + sq4_exact32(b);
-                    } else {
-                        s = s + sq4(a);
-                        s = s + sq4(b);
-                    }
-                }
+            if ((v + 1) * kPer <= n) {
+                check_sq_vec<GF>(G[v], bad, s);
             } else {
                 for (int k = 0; k < kPer; ++k) {
-                    const int64_t i = e0 + k;
+                    const int64_t i = v * kPer + k;
                     if (i < n) {
                         if constexpr (F32) {
                             const uint32_t bits = static_cast<const uint32_t*>(grad)[i];
@@ -722,9 +738,8 @@ __global__ __launch_bounds__(TPB) void check_sumsq_kernel(ds_scaler* __restrict_
             }
         }
         const double cs = block_sum_fixed<TPB>(s, lds, parity);
-        parity ^= 1;
         if (threadIdx.x == 0)
-            part[c] = cs;
+            part[nfull] = cs;
     }
     raise_flag(st, bad);
 }
