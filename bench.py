@@ -37,10 +37,12 @@ same workload on the host cores the process may use.
 from __future__ import annotations
 
 import argparse
+import ctypes
 import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -61,17 +63,17 @@ def kernel_source_hash() -> str:
     return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
 
 
-def load_traffic(workload: str, half: str):
+def load_traffic(workload: str, half: str, kernel: str):
     """Per-launch HBM bytes of the Adam kernel from the committed counter summary,
     or None if it is missing, was taken on another kernel source, or on another
-    workload or 16-bit format (another instance of the kernel)."""
+    workload, 16-bit format or kernel (another instance of the pass)."""
     try:
         data = json.load(open(TRAFFIC_FILE))
     except (OSError, ValueError):
         return None
     for rec in data.get("records", [data]):
         if (rec.get("kernel_source_sha256_16") == kernel_source_hash() and rec.get("workload") == workload
-                and rec.get("half") == half):
+                and rec.get("half") == half and re.search(r"\b%s<" % kernel, rec.get("kernel", ""))):
             return rec.get("traffic_bytes_per_launch")
     return None
 
@@ -115,6 +117,15 @@ def gpu_run(args):
         buckets = [(b.start, b.size) for b in FlatLayout(ragged_numels()).buckets]
     else:
         buckets = [(0, n)]
+    # double-buffered step (K = 1, no clipping): a second copy of master, m, v and
+    # the 16-bit copy; the overflow check is fused into the Adam pass
+    double = args.double_buffer and K == 1 and args.clip == 0
+    if args.double_buffer and not double:
+        log("bench.py: --double-buffer applies to K = 1 workloads without clipping; using the single copy")
+    copy1 = None
+    if double:
+        copy1 = [torch.empty(n, dtype=torch.float32, device=dev) for _ in range(3)] + \
+                [torch.empty(n, dtype=torch.int16, device=dev)]
 
     # resident gradient buffers, a ring of distinct draws (a real step rewrites one
     # contiguous gradient buffer; the ring is larger than the 256 MB Infinity Cache)
@@ -151,6 +162,11 @@ def gpu_run(args):
         if not (t.is_cuda and t.is_contiguous() and t.numel() * t.element_size() >= nb):
             raise RuntimeError("bench.py: a state array is not a contiguous device tensor of the expected size")
     st_p, master_p, m_p, v_p, p16_p = (t.data_ptr() for t in (st, master, m, v, p16))
+    if double:
+        V2 = ctypes.c_void_p * 2
+        db_arrays = (V2(master_p, copy1[0].data_ptr()), V2(m_p, copy1[1].data_ptr()), V2(v_p, copy1[2].data_ptr()),
+                     V2(p16_p, copy1[3].data_ptr()))
+        db_step = _lib.lib.ds_adam_step_double_buffered
     acc_p = acc.data_ptr() if acc is not None else None
     ws_p, ws_bytes = (ws.data_ptr(), ws.numel() * 8) if ws is not None else (None, 0)
     grad_p = [g.data_ptr() for g in grads]
@@ -162,7 +178,10 @@ def gpu_run(args):
             s0 = torch.cuda.Event(enable_timing=True)
             s0.record(q)
         base = i * K
-        if K == 1:
+        if double:
+            g = grad_p[base % nbuf]
+            gptr, dt = g, gdt16
+        elif K == 1:
             g = grad_p[base % nbuf]
             if ws is None:
                 _lib.ds_check_overflow(st_p, g, gdt16, n, q)
@@ -195,7 +214,12 @@ def gpu_run(args):
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a.record(q)
         # the Adam kernel also advances the loss scaler (one launch for both)
-        _lib.ds_adam_step_fused(st_p, master_p, m_p, v_p, p16_p, gdt16, gptr, dt, n, hp[0], None, *hp[1:], K, q)
+        if double:   # and performs the overflow check, writing the other copy
+            rc = db_step(st_p, *db_arrays, gdt16, gptr, dt, n, hp[0], None, *hp[1:5], K, q.cuda_stream)
+            if rc != 0:
+                raise RuntimeError(f"ds_adam_step_double_buffered: {_lib.ds_status_string(rc)}")
+        else:
+            _lib.ds_adam_step_fused(st_p, master_p, m_p, v_p, p16_p, gdt16, gptr, dt, n, hp[0], None, *hp[1:], K, q)
         if timed:
             b.record(q)
             ev.append((a, b))
@@ -291,12 +315,14 @@ def gpu_run(args):
     copy_gbs, memcpy_gbs = 8 * nm / copy_s / 1e9, 8 * nm / memcpy_s / 1e9
     bytes_per_elem = 28 if K == 1 else 30
     achieved = bytes_per_elem * n / adam_avg_s / 1e9
-    if K == 1:
+    if double:
+        step_bytes = 28
+    elif K == 1:
         step_bytes = 2 + 28
     else:   # each fold of f micro-batches: 2f + 4 bytes (the first, overwriting) or 2f + 8, then Adam's 30
         sizes = [min(fold, K - g0) for g0 in range(0, K, fold)]
         step_bytes = sum(2 * f + (4 if i == 0 else 8) for i, f in enumerate(sizes)) + 30
-    traffic = load_traffic(w.name, "bf16" if args.bf16 else "fp16")
+    traffic = load_traffic(w.name, "bf16" if args.bf16 else "fp16", "adam_db_kernel" if double else "adam_kernel")
     out = {
         "metric": METRIC,
         "value": round(n * args.steps / wall / 1e9, 3),
@@ -325,11 +351,13 @@ def gpu_run(args):
             "adam": {"lr": LR, "betas": [BETA1, BETA2], "eps": EPS, "weight_decay": WD},
             "gradient_clipping": args.clip,
             "half": "bf16" if args.bf16 else "fp16",
+            "step_form": ("double-buffered: overflow check fused into the Adam pass over two copies of the state"
+                          if double else "check (or accumulation with the fused check), then the in-place Adam pass"),
             "parallelism": "one GPU's ZeRO partition",
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": "adam_kernel",
+            "kernel": "adam_db_kernel" if double else "adam_kernel",
             "achieved": round(achieved, 1),
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",
@@ -354,7 +382,7 @@ def gpu_run(args):
                    "memory_gib": round(props.total_memory / 2 ** 30, 1)},
         "scaler_after": {"scale": sc.scale, "applied_steps": sc.step, "skipped": sc.skipped},
     }
-    del grads, master, m, v, p16, acc
+    del grads, master, m, v, p16, acc, copy1
     torch.cuda.empty_cache()
     return out
 
@@ -558,6 +586,9 @@ def main(argv=None):
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--cpu-slice", type=int, default=109_375_000)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--double-buffer", dest="double_buffer", action="store_true", default=False,
+                    help="K = 1 without clipping: two copies of the state, the overflow check fused into the Adam "
+                         "pass (ds_adam_step_double_buffered)")
     ap.add_argument("--fold", type=int, default=1,
                     help="micro-batches folded into the accumulation buffer per pass (1..8; K > 1 workloads; "
                          "needs that many gradient buffers held at once)")

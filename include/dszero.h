@@ -116,7 +116,11 @@ typedef struct ds_scaler {
     double last_grad_sumsq;         /* grad_sumsq consumed by the last update         */
     uint32_t blocks_done;           /* ds_adam_step_fused: blocks finished (0 between steps) */
     uint32_t sumsq_blocks_done;     /* sum-of-squares second pass: blocks finished (0 between calls) */
-    uint8_t reserved[40];           /* zero                                           */
+    uint32_t current;               /* ds_adam_step_double_buffered: copy holding the state (0 or 1) */
+    uint32_t reserved0;             /* zero                                           */
+    uint64_t db_tickets;            /* ds_adam_step_double_buffered: blocks finished (low 32 bits) and
+                                       blocks that found a non-finite gradient (high 32 bits); 0 between steps */
+    uint8_t reserved[24];           /* zero                                           */
 } ds_scaler;
 
 /* sizeof(ds_scaler) as compiled into the library (128). */
@@ -262,6 +266,40 @@ ds_status ds_adam_step_fused(ds_scaler* st, float* master, float* m, float* v, u
                              const void* grad, ds_dtype dt, int64_t n, float lr,
                              const ds_lr_schedule* sched_or_null, float beta1, float beta2, float eps,
                              float weight_decay, float max_grad_norm, int32_t accum_steps, void* stream);
+
+/*
+ * A whole step for a caller that keeps two copies (0 and 1) of the fp32
+ * master, m and v arrays and of the 16-bit parameter copy (30 bytes of device
+ * memory per element instead of 16), in one HBM pass: the overflow check of
+ * the gradient is fused into the Adam pass ([Guide] section 2, section 4.2
+ * dynamic loss scaling, section 5.1 step()).  st->current names the copy that
+ * holds the state.  The kernel reads the gradient and the current copy once,
+ * tests whether some gradient value is +-inf or NaN, and writes the Adam
+ * update of every element (the arithmetic of ds_adam_step) into the other
+ * copy; each block's finding travels in its ticket (st->db_tickets), and the
+ * last block to finish advances the scaler as ds_update_loss_scale does with
+ * the OR of all findings and st->overflow and, if the step applied (no
+ * overflow), makes the other copy current.  A skipped step leaves the current copy bit-identical
+ * (only the other copy, which holds no state, is written) and t unchanged.
+ * The step moves 28 bytes per element with an fp16 gradient instead of the
+ * 30 of ds_check_overflow + ds_adam_step_fused.  Call it once per step for the
+ * whole partition, in place of ds_check_overflow and ds_adam_step_fused (a flag
+ * already raised earlier in the step, e.g. by a fused accumulation check, also
+ * skips it).  No gradient clipping (it needs the whole gradient's norm before
+ * the update).
+ * master2, m2, v2: HOST arrays of 2 DEVICE pointers to fp32[n]; p16_2: HOST
+ * array of 2 DEVICE pointers to 16-bit[n] of type pdt; the eight arrays, grad
+ * and st must not overlap.  lr / sched_or_null, betas, eps, weight_decay,
+ * accum_steps, grad and dt: as for ds_adam_step_fused.  With n == 0 only the
+ * scaler advances (and the copies swap if the step applied).  The copy that
+ * is current after a call is read back with ds_state_read (st.current).
+ * Errors: as for ds_adam_step_fused; a NULL host array -> DS_ERR_NULL.
+ */
+ds_status ds_adam_step_double_buffered(ds_scaler* st, float* const* master2, float* const* m2, float* const* v2,
+                                       uint16_t* const* p16_2, ds_dtype pdt, const void* grad, ds_dtype dt,
+                                       int64_t n, float lr, const ds_lr_schedule* sched_or_null, float beta1,
+                                       float beta2, float eps, float weight_decay, int32_t accum_steps,
+                                       void* stream);
 
 /*
  * End of a step: advance the scaler by the step's overflow flag, then clear

@@ -498,3 +498,41 @@ def test_noalloc_check_validation():
     assert f(ST, A + 8, DS_FP16, 10, STREAM) == DS_ERR_ALIGN
     assert f(ST + 4, A, DS_FP16, 10, STREAM) == DS_ERR_ALIGN
     assert f(A + 64, A, DS_FP16, 10000, STREAM) == DS_ERR_ALIAS
+
+
+@fake_addresses
+def test_double_buffered_step_validation():
+    """ds_adam_step_double_buffered validates its eight arrays (two copies of
+    master, m, v and the 16-bit copy), the gradient and the state before any
+    device work."""
+    f = L.ds_adam_step_double_buffered
+    V2 = ctypes.c_void_p * 2
+    n = 1000
+    base = [0x20000000 * k for k in range(1, 9)]
+    mst, mm, vv, pp = V2(base[0], base[1]), V2(base[2], base[3]), V2(base[4], base[5]), V2(base[6], base[7])
+    G = 0x20000000 * 9
+    ok_hp = (1e-4, None, 0.9, 0.999, 1e-8, 0.0, 1)
+
+    def call(st=ST, m2=mst, mo=mm, vo=vv, p2=pp, pdt=DS_FP16, g=G, dt=DS_FP16, nn=n, hp=ok_hp):
+        lr, sched, b1, b2, eps, wd, K = hp
+        return f(st, m2, mo, vo, p2, pdt, g, dt, nn, lr, sched, b1, b2, eps, wd, K, STREAM)
+
+    assert call(nn=-1) == DS_ERR_SIZE
+    assert call(nn=2 ** 40 + 1) == DS_ERR_SIZE
+    assert call(dt=9) == DS_ERR_DTYPE
+    assert call(pdt=DS_FP32) == DS_ERR_DTYPE
+    assert call(st=None) == DS_ERR_NULL
+    assert call(m2=None) == DS_ERR_NULL
+    assert call(p2=V2(base[6], None)) == DS_ERR_NULL
+    assert call(g=None) == DS_ERR_NULL
+    assert call(m2=V2(base[0] + 4, base[1])) == DS_ERR_ALIGN
+    assert call(st=ST + 4) == DS_ERR_ALIGN
+    assert call(m2=V2(base[0], base[0] + 64)) == DS_ERR_ALIAS         # the two copies overlap
+    assert call(vo=V2(base[4], base[2] + 16)) == DS_ERR_ALIAS         # v copy 1 inside m copy 0
+    assert call(g=base[7] + 32) == DS_ERR_ALIAS                       # the gradient inside a p16 copy
+    assert call(st=base[3] + 8) == DS_ERR_ALIAS                       # the state inside an m copy
+    for bad in [(-1e-4, None, 0.9, 0.999, 1e-8, 0.0, 1), (1e-4, None, 1.0, 0.999, 1e-8, 0.0, 1),
+                (1e-4, None, 0.9, 0.999, 0.0, 0.0, 1), (1e-4, None, 0.9, 0.999, 1e-8, -1.0, 1),
+                (1e-4, None, 0.9, 0.999, 1e-8, 0.0, 0),
+                (1e-4, ctypes.byref(_lib.DsLrSchedule.make(7, 0.0, 1e-3, 1)), 0.9, 0.999, 1e-8, 0.0, 1)]:
+        assert call(hp=bad) == DS_ERR_HPARAM, bad

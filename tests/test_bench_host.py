@@ -7,20 +7,30 @@ import pytest
 import bench
 
 
+def _kernel_of(rec):
+    return "adam_db_kernel" if "adam_db_kernel" in rec["kernel"] else "adam_kernel"
+
+
 def test_traffic_only_for_the_profiled_instance():
     data = json.load(open(bench.TRAFFIC_FILE))
     recs = data.get("records", [data])
-    profiled = {(r["workload"], r["half"]) for r in recs}
+    profiled = {(r["workload"], r["half"], _kernel_of(r)) for r in recs}
     for half in ("fp16", "bf16"):
-        if ("zero2_7b", half) not in profiled:
-            assert bench.load_traffic("zero2_7b", half) is None
-    assert bench.load_traffic("no_such_workload", "fp16") is None
+        for kernel in ("adam_kernel", "adam_db_kernel"):
+            if ("zero2_7b", half, kernel) not in profiled:
+                assert bench.load_traffic("zero2_7b", half, kernel) is None
+    assert bench.load_traffic("no_such_workload", "fp16", "adam_kernel") is None
     for rec in recs:
-        got = bench.load_traffic(rec["workload"], rec["half"])
+        got = bench.load_traffic(rec["workload"], rec["half"], _kernel_of(rec))
+        other = bench.load_traffic(rec["workload"], rec["half"],
+                                   "adam_kernel" if _kernel_of(rec) == "adam_db_kernel" else "adam_db_kernel")
         if rec["kernel_source_sha256_16"] == bench.kernel_source_hash():
             # counters of the current source: within 0.1 % of the algorithmic bytes (no re-reads)
             assert got == rec["traffic_bytes_per_launch"]
             assert abs(got / rec["algorithmic_bytes_per_launch"] - 1) < 1e-3
+            if (rec["workload"], rec["half"], "adam_kernel" if _kernel_of(rec) == "adam_db_kernel"
+                    else "adam_db_kernel") not in profiled:
+                assert other is None
         else:
             assert got is None
 

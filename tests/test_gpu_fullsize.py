@@ -33,9 +33,9 @@ def torch():
     return t
 
 
-def sample_indices(w, buckets):
+def sample_indices(w, buckets, extra=()):
     rng = np.random.default_rng(20261202 + w.cid)
-    parts = [rng.integers(0, w.psi, 1 << 20), np.arange(4096), w.psi - 4096 + np.arange(4096)]
+    parts = [rng.integers(0, w.psi, 1 << 20), np.arange(4096), w.psi - 4096 + np.arange(4096), np.array(extra)]
     for start, size in buckets:
         parts += [start + np.arange(min(4096, size)), start + size - np.arange(1, min(4096, size) + 1)]
     for s in w.inject_steps:
@@ -43,7 +43,9 @@ def sample_indices(w, buckets):
     return np.unique(np.concatenate(parts).astype(np.int64))
 
 
-def run_sampled(torch, name, fused=False, bf16=False, fold=1):
+def run_sampled(torch, name, fused=False, bf16=False, fold=1, double=False, extra_inject=None):
+    """double: the double-buffered step (K = 1); extra_inject: {step: index} of
+    +inf gradients injected beside the workload's own."""
     from zero_mixed_precision_amd import _lib, FlatLayout
 
     w = WORKLOADS[name]
@@ -60,8 +62,10 @@ def run_sampled(torch, name, fused=False, bf16=False, fold=1):
         buckets = [(b.start, b.size) for b in lay.buckets]
     else:
         buckets = [(0, n)]
-    I = sample_indices(w, buckets)
-    gu.say(f"[{name}] psi={n} K={K} steps={w.steps} sample={I.size} fused={fused} {fmt}")
+    extra_inject = extra_inject or {}
+    assert not (double and K > 1)
+    I = sample_indices(w, buckets, list(extra_inject.values()))
+    gu.say(f"[{name}] psi={n} K={K} steps={w.steps} sample={I.size} fused={fused} double={double} {fmt}")
 
     # oracle state on the sample
     o = oracle.State(synth.host_master32(w.master_key(), I, MASTER_SIGMA), np.zeros(I.size, np.float32),
@@ -80,12 +84,17 @@ def run_sampled(torch, name, fused=False, bf16=False, fold=1):
     # fold > 1: the micro-batches of a group are held at once and folded in one pass
     held = [g16] + [torch.empty(n, dtype=torch.int16, device="cuda:0") for _ in range(fold - 1)]
     acc = torch.empty(n, dtype=torch.float32, device="cuda:0") if K > 1 else None
+    # the double-buffered step's second copy of the state (it holds no state yet)
+    copy1 = [torch.empty(n, dtype=torch.float32, device="cuda:0") for _ in range(3)] + \
+        [torch.empty(n, dtype=torch.int16, device="cuda:0")] if double else None
     st = torch.zeros(_lib.ds_scaler_size(), dtype=torch.uint8, device="cuda:0")
     _lib.ds_state_init(st, init_scale, w.min_scale, w.window, w.hysteresis, 0, int(dynamic))
     Id = torch.from_numpy(I).to("cuda:0")
 
     for s in range(1, w.steps + 1):
         inj = w.injection(s)
+        if inj is None and s in extra_inject:
+            inj = (0, int(extra_inject[s]))
         gs_host = []
         for k in range(K):
             buf = held[k % fold]
@@ -105,10 +114,14 @@ def run_sampled(torch, name, fused=False, bf16=False, fold=1):
                     _lib.ds_accumulate_multi(acc.data_ptr() + 4 * start,
                                              [held[j % fold].data_ptr() + 2 * start for j in range(first, k + 1)],
                                              dt16, size, first == 0, st if k == K - 1 else None)
-        if K == 1:
+        if K == 1 and not double:
             _lib.ds_check_overflow(st, g16, dt16, n)
         grad, dt = (g16, dt16) if K == 1 else (acc, _lib.DS_FP32)
-        if fused:   # one kernel: Adam, then the last block to finish advances the scaler
+        if double:   # one kernel: the check, Adam into the other copy, the scaler update
+            _lib.ds_adam_step_double_buffered(st, [master, copy1[0]], [m, copy1[1]], [v, copy1[2]],
+                                              [p16, copy1[3]], dt16, grad, dt, n, LR, None, BETA1, BETA2, EPS,
+                                              0.0, K)
+        elif fused:   # one kernel: Adam, then the last block to finish advances the scaler
             _lib.ds_adam_step_fused(st, master, m, v, p16, dt16, grad, dt, n, LR, None, BETA1, BETA2, EPS,
                                     0.0, 0.0, K)
         else:
@@ -118,13 +131,16 @@ def run_sampled(torch, name, fused=False, bf16=False, fold=1):
         assert ov == (inj is not None), f"[{name}] step {s}: oracle flag"
         got = _lib.ds_state_read(st)
         gu.check_scaler(got, o.scaler, ov, f"[{name}] step {s}")
-        assert got.blocks_done == 0, f"[{name}] step {s}: block count not reset"
-        if s in (1, w.steps // 2, w.steps):
-            du = gu.compare_arrays(f"[{name}] step {s}", gu.host_f32(master[Id]), gu.host_f32(m[Id]),
-                                   gu.host_f32(v[Id]), gu.host_u16(p16[Id]), o.master, o.m, o.v, o.p16)
+        assert got.blocks_done == 0 and got.db_tickets == 0, f"[{name}] step {s}: block count not reset"
+        cur = (master, m, v, p16) if not double or got.current == 0 else tuple(copy1)
+        if double:
+            assert got.current == o.scaler.applied % 2, f"[{name}] step {s}: current copy"
+        if s in (1, w.steps // 2, w.steps) or (double and inj is not None):
+            du = gu.compare_arrays(f"[{name}] step {s}", gu.host_f32(cur[0][Id]), gu.host_f32(cur[1][Id]),
+                                   gu.host_f32(cur[2][Id]), gu.host_u16(cur[3][Id]), o.master, o.m, o.v, o.p16)
             gu.say(f"[{name}] {fmt} step {s}: scale 2^{int(np.log2(o.scaler.scale))} applied {o.scaler.applied} "
                    f"max ulp {du}")
-    del master, m, v, p16, g16, held, acc, st
+    del master, m, v, p16, g16, held, acc, st, copy1, cur
     torch.cuda.empty_cache()
     return o.scaler
 
@@ -158,6 +174,24 @@ def test_zero1_shard_of_70b_fused_scaler_update(torch):
     blocks, each taking one ticket)."""
     sc = run_sampled(torch, "zero1_70b", fused=True)
     assert sc.applied == 10 and sc.scale == 2.0 ** 18
+
+
+def test_zero2_shard_of_7b_double_buffered(torch):
+    """The double-buffered step (overflow check fused into the Adam pass, the
+    update written to the other copy) at the shard's full size, with +inf
+    gradients injected at the partition's last element (the ragged tail that
+    block 0 takes) in step 7 and at an interior element in step 30."""
+    w = WORKLOADS["zero2_7b"]
+    sc = run_sampled(torch, "zero2_7b", double=True, extra_inject={7: w.psi - 1, 30: 54_321_987})
+    assert sc.applied == 48 and sc.s.skipped == 2
+
+
+def test_zero1_shard_of_70b_double_buffered(torch):
+    """The launch bench.py --double-buffer times: 8.75e9 elements in both copies
+    (245 GB of state beside the 17.5 GB gradient), with an overflow injected in
+    step 4."""
+    sc = run_sampled(torch, "zero1_70b", double=True, extra_inject={4: 6_123_456_789})
+    assert sc.applied == 9 and sc.s.skipped == 1
 
 
 def test_ragged_layout_fused_scaler_update(torch):

@@ -22,7 +22,7 @@ EXPORTED = (
     "ds_check_overflow", "ds_adam_step", "ds_update_loss_scale", "ds_adam_bias_scalars",
     "ds_layout_greedy", "ds_partition_range", "ds_status_string", "ds_sumsq_workspace_bytes",
     "ds_check_overflow_sumsq", "ds_accumulate_sumsq", "ds_adam_step_sched", "ds_lr_scalars",
-    "ds_adam_step_fused", "ds_accumulate_multi", "ds_check_overflow_sumsq_noalloc",
+    "ds_adam_step_fused", "ds_accumulate_multi", "ds_check_overflow_sumsq_noalloc", "ds_adam_step_double_buffered",
 )
 DS_NOALLOC_MAX_ELEMS = 17175674880
 DS_LR_WARMUP, DS_LR_WARMUP_DECAY = 1, 2
@@ -48,11 +48,14 @@ class DsScaler(ctypes.Structure):
         ("last_grad_sumsq", ctypes.c_double),
         ("blocks_done", ctypes.c_uint32),
         ("sumsq_blocks_done", ctypes.c_uint32),
-        ("reserved", ctypes.c_uint8 * 40),
+        ("current", ctypes.c_uint32),
+        ("reserved0", ctypes.c_uint32),
+        ("db_tickets", ctypes.c_uint64),
+        ("reserved", ctypes.c_uint8 * 24),
     ]
 
     def as_dict(self) -> dict:
-        return {name: getattr(self, name) for name, _ in self._fields_ if name != "reserved"}
+        return {name: getattr(self, name) for name, _ in self._fields_ if not name.startswith("reserved")}
 
 
 class DsLrSchedule(ctypes.Structure):
@@ -119,6 +122,9 @@ def _load():
         "ds_sumsq_workspace_bytes": ([i64], ctypes.c_size_t),
         "ds_check_overflow_sumsq": ([vp, vp, ctypes.c_int, i64, vp, ctypes.c_size_t, vp], ctypes.c_int),
         "ds_check_overflow_sumsq_noalloc": ([vp, vp, ctypes.c_int, i64, vp], ctypes.c_int),
+        "ds_adam_step_double_buffered": ([vp, ctypes.POINTER(vp), ctypes.POINTER(vp), ctypes.POINTER(vp),
+                                          ctypes.POINTER(vp), ctypes.c_int, vp, ctypes.c_int, i64, f32,
+                                          ctypes.POINTER(DsLrSchedule), f32, f32, f32, f32, i32, vp], ctypes.c_int),
         "ds_accumulate_sumsq": ([vp, vp, ctypes.c_int, i64, i32, vp, vp, ctypes.c_size_t, vp], ctypes.c_int),
         "ds_accumulate_multi": ([vp, ctypes.POINTER(vp), i32, ctypes.c_int, i64, i32, vp, vp, ctypes.c_size_t, vp],
                                 ctypes.c_int),
@@ -259,6 +265,25 @@ def ds_adam_step_fused(st, master, m, v, p16, pdt, grad, dtype, n, lr, sched, be
     _ok(lib.ds_adam_step_fused(_scaler(st), *_adam_arrays(master, m, v, p16, pdt, grad, dtype, n), lr, sched_p,
                                beta1, beta2, eps, weight_decay, max_grad_norm, int(accum_steps), _s(stream)),
         "ds_adam_step_fused")
+
+
+def ds_adam_step_double_buffered(st, master2, m2, v2, p16_2, pdt, grad, dtype, n, lr, sched, beta1, beta2, eps,
+                                 weight_decay, accum_steps, stream=None) -> None:
+    """The check fused into the Adam pass over two copies of the state: master2, m2, v2, p16_2 are pairs
+    (copy 0, copy 1) of tensors or device addresses; the copy holding the state is the state's ``current``."""
+    n = int(n)
+
+    def pair(arrs, nbytes, what):
+        if len(arrs) != 2:
+            raise ValueError(f"{what}: expected two copies")
+        return (ctypes.c_void_p * 2)(*[_p(a, nbytes, f"{what}[{k}]") for k, a in enumerate(arrs)])
+
+    sched_p = ctypes.byref(sched) if sched is not None else None
+    _ok(lib.ds_adam_step_double_buffered(_scaler(st), pair(master2, 4 * n, "master"), pair(m2, 4 * n, "m"),
+                                         pair(v2, 4 * n, "v"), pair(p16_2, 2 * n, "p16"), int(pdt),
+                                         _p(grad, _esize(dtype) * n, "gradient"), int(dtype), n, lr, sched_p,
+                                         beta1, beta2, eps, weight_decay, int(accum_steps), _s(stream)),
+        "ds_adam_step_double_buffered")
 
 
 def ds_sumsq_workspace_bytes(n) -> int:

@@ -85,11 +85,12 @@ def save_checkpoint(step, save_dir: str, tag=None, client_state=None, rank: int 
     path = _file(save_dir, tag, rank)
     os.makedirs(os.path.dirname(path), exist_ok=True)
     raw = ctypes.string_at(ctypes.addressof(sc), ctypes.sizeof(sc))
+    master, m, v, p16 = step.current()           # with double buffering: the copy holding the state
     tensors = {
-        "master": step.master.detach().cpu(),
-        "exp_avg": step.m.detach().cpu(),
-        "exp_avg_sq": step.v.detach().cpu(),
-        "param16": step.p16.detach().view(torch.int16).cpu(),
+        "master": master.detach().cpu(),
+        "exp_avg": m.detach().cpu(),
+        "exp_avg_sq": v.detach().cpu(),
+        "param16": p16.detach().view(torch.int16).cpu(),
         "scaler": torch.frombuffer(bytearray(raw), dtype=torch.uint8).clone(),
     }
     meta = {
@@ -132,6 +133,7 @@ def load_checkpoint(step, load_dir: str, tag=None, rank: int = 0):
         arrays = {k: f.get_tensor(k) for k in ("master", "exp_avg", "exp_avg_sq", "param16")}
     sc = _lib.DsScaler.from_buffer_copy(raw)
     validate_scaler(sc, path)
+    sc.current = 0                              # the arrays are restored into copy 0 (the attributes)
     with torch.cuda.stream(torch_stream(step.stream, torch)):
         step.master.copy_(arrays["master"])
         step.m.copy_(arrays["exp_avg"])

@@ -325,10 +325,10 @@ __global__ __launch_bounds__(kFinishBlock) void sumsq_finish_kernel(ds_scaler* _
 // loss-scaler state machine ([Guide] section 4.2), one work-item
 // ---------------------------------------------------------------------------
 
-__device__ __forceinline__ void advance_scaler(ds_scaler* st)
+__device__ __forceinline__ void advance_scaler_with(ds_scaler* st, uint32_t flag)
 {
     ds_scaler s = *st;
-    const uint32_t ov = s.overflow != 0u ? 1u : 0u;
+    const uint32_t ov = flag != 0u ? 1u : 0u;
     s.iter += 1;
     if (ov) {
         s.skipped += 1;
@@ -361,7 +361,20 @@ __device__ __forceinline__ void advance_scaler(ds_scaler* st)
     *st = s;
 }
 
+__device__ __forceinline__ void advance_scaler(ds_scaler* st) { advance_scaler_with(st, st->overflow); }
+
 __global__ void update_scale_kernel(ds_scaler* st) { advance_scaler(st); }
+
+// The double-buffered step's scaler update on an empty partition: advance,
+// and make the other copy current if the step applied.
+__global__ void update_scale_swap_kernel(ds_scaler* st)
+{
+    const uint32_t ov = st->overflow;
+    const uint32_t cur = st->current & 1u;
+    advance_scaler_with(st, ov);
+    if (ov == 0u)
+        st->current = cur ^ 1u;
+}
 
 // ---------------------------------------------------------------------------
 // Adam
@@ -587,6 +600,119 @@ __global__ __launch_bounds__(TPB) void adam_kernel(ds_scaler* __restrict__ st,
         if (threadIdx.x == 0 && atomicAdd(&st->blocks_done, 1u) == gridDim.x - 1u) {
             st->blocks_done = 0u;
             advance_scaler(st);
+        }
+    }
+}
+
+// Double-buffered step (ds_adam_step_double_buffered): copies 0 and 1 of
+// master, m, v and the 16-bit parameter copy; st->current names the copy that
+// holds the state.  One pass reads the gradient and the current copy, ORs the
+// gradient's non-finite test into the flag (the overflow check, fused: it needs
+// no pass of its own because nothing is written to the current copy) and writes
+// the update into the other copy.  Every block then takes a ticket; the block
+// with the last one reads the step's flag, advances the scaler and, if the step
+// applied, makes the other copy current.  A block's flag travels in its
+// ticket (one 64-bit atomic add on st->db_tickets: one in the low half, and
+// one in the high half if the block saw a non-finite value), so the last
+// block reads every block's finding from the value its own add returns and no
+// block needs a memory fence.  A flag raised before the call (st->overflow)
+// also skips the step.
+// Same tiling and arithmetic as adam_kernel.
+struct DbArrays {
+    float* master[2];
+    float* m[2];
+    float* v[2];
+    uint16_t* p16[2];
+};
+
+template <int GF, int PF, bool WD, bool NT, int TPB, int U>
+__global__ __launch_bounds__(TPB) void adam_db_kernel(ds_scaler* __restrict__ st, DbArrays a,
+                                                      const void* __restrict__ grad, int64_t n, AdamHyper hp)
+{
+    const AdamConsts c = make_consts(st, hp);
+    const uint32_t cur = st->current & 1u;
+    const f32x4* P = reinterpret_cast<const f32x4*>(cur ? a.master[1] : a.master[0]);
+    const f32x4* M = reinterpret_cast<const f32x4*>(cur ? a.m[1] : a.m[0]);
+    const f32x4* V = reinterpret_cast<const f32x4*>(cur ? a.v[1] : a.v[0]);
+    f32x4* Po = reinterpret_cast<f32x4*>(cur ? a.master[0] : a.master[1]);
+    f32x4* Mo = reinterpret_cast<f32x4*>(cur ? a.m[0] : a.m[1]);
+    f32x4* Vo = reinterpret_cast<f32x4*>(cur ? a.v[0] : a.v[1]);
+    uint16_t* p16o = cur ? a.p16[0] : a.p16[1];
+    u32x2* H = reinterpret_cast<u32x2*>(p16o);
+
+    constexpr int T = U * TPB;  // quads per tile
+    const int64_t nq = n >> 2;
+    const int64_t ntiles = nq / T;
+    uint32_t bad = 0u;
+    for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
+        const int64_t q0 = tile * T + threadIdx.x;
+        f32x4 g[U], p[U], m[U], v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t i = q0 + u * TPB;
+            g[u] = load_grad4<GF, NT>(grad, i);
+            p[u] = load<NT>(P + i);
+            m[u] = load<NT>(M + i);
+            v[u] = load<NT>(V + i);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t i = q0 + u * TPB;
+            bad |= nonfinite_f32x4(g[u]);
+            adam4<WD>(g[u], p[u], m[u], v[u], c);
+            store<NT>(Po + i, p[u]);
+            store<NT>(Mo + i, m[u]);
+            store<NT>(Vo + i, v[u]);
+            store<NT>(H + i, narrow4<PF>(p[u]));
+        }
+    }
+    if (blockIdx.x == 0) {
+        for (int64_t q = ntiles * T + threadIdx.x; q < nq; q += TPB) {
+            f32x4 g = load_grad4<GF, NT>(grad, q);
+            f32x4 p = load<NT>(P + q), m = load<NT>(M + q), v = load<NT>(V + q);
+            bad |= nonfinite_f32x4(g);
+            adam4<WD>(g, p, m, v, c);
+            store<NT>(Po + q, p);
+            store<NT>(Mo + q, m);
+            store<NT>(Vo + q, v);
+            store<NT>(H + q, narrow4<PF>(p));
+        }
+        if (static_cast<int64_t>(threadIdx.x) < (n & 3)) {
+            const int64_t i = (nq << 2) + threadIdx.x;
+            const float* ps = reinterpret_cast<const float*>(P);
+            const float* ms = reinterpret_cast<const float*>(M);
+            const float* vs = reinterpret_cast<const float*>(V);
+            float p = ps[i], m = ms[i], v = vs[i];
+            const float g = load_grad1<GF>(grad, i);
+            bad |= nonfinite_f32(__float_as_uint(g));
+            adam1<WD>(g, p, m, v, c);
+            reinterpret_cast<float*>(Po)[i] = p;
+            reinterpret_cast<float*>(Mo)[i] = m;
+            reinterpret_cast<float*>(Vo)[i] = v;
+            p16o[i] = static_cast<uint16_t>(enc1<PF>(p));
+        }
+    }
+    // One ticket per block, carrying the block's flag: each wave's OR goes to
+    // LDS; once the barrier has passed every lane has read the scaler state.
+    __shared__ uint32_t wave_bad[TPB / 64];
+    const bool wave_any = __ballot(bad != 0u) != 0ull;
+    if (__lane_id() == 0u)
+        wave_bad[threadIdx.x / 64] = wave_any ? 1u : 0u;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint32_t block_bad = 0u;
+#pragma unroll
+        for (int w = 0; w < TPB / 64; ++w)
+            block_bad |= wave_bad[w];
+        const unsigned long long mine = 1ull | (block_bad ? (1ull << 32) : 0ull);
+        const unsigned long long before =
+            atomicAdd(reinterpret_cast<unsigned long long*>(&st->db_tickets), mine);
+        if (static_cast<uint32_t>(before) == gridDim.x - 1u) {
+            const uint32_t ov = ((before + mine) >> 32) != 0ull || st->overflow != 0u ? 1u : 0u;
+            st->db_tickets = 0ull;
+            advance_scaler_with(st, ov);
+            if (ov == 0u)
+                st->current = cur ^ 1u;
         }
     }
 }
@@ -1001,6 +1127,39 @@ void launch_adam(int gf, int pf, bool wd, bool nt, int unroll, bool fuse, unsign
     }
 }
 
+template <int GF, int PF, bool WD>
+void launch_adam_db3(bool nt, unsigned blocks, hipStream_t s, ds_scaler* st, const DbArrays& a, const void* grad,
+                     int64_t n, const AdamHyper& hp)
+{
+    // the fused Adam kernel's shapes: 256 x 4 streamed, 512 x 2 on a cache-resident partition
+    if (nt)
+        adam_db_kernel<GF, PF, WD, true, kStepBlock, 4><<<blocks, kStepBlock, 0, s>>>(st, a, grad, n, hp);
+    else
+        adam_db_kernel<GF, PF, WD, false, kSmallBlock, 2><<<blocks, kSmallBlock, 0, s>>>(st, a, grad, n, hp);
+}
+
+template <int GF, int PF>
+void launch_adam_db2(bool wd, bool nt, unsigned blocks, hipStream_t s, ds_scaler* st, const DbArrays& a,
+                     const void* grad, int64_t n, const AdamHyper& hp)
+{
+    if (wd) launch_adam_db3<GF, PF, true>(nt, blocks, s, st, a, grad, n, hp);
+    else    launch_adam_db3<GF, PF, false>(nt, blocks, s, st, a, grad, n, hp);
+}
+
+void launch_adam_db(int gf, int pf, bool wd, bool nt, unsigned blocks, hipStream_t s, ds_scaler* st,
+                    const DbArrays& a, const void* grad, int64_t n, const AdamHyper& hp)
+{
+    if (pf == kBF16) {
+        if (gf == kF16)       launch_adam_db2<kF16, kBF16>(wd, nt, blocks, s, st, a, grad, n, hp);
+        else if (gf == kBF16) launch_adam_db2<kBF16, kBF16>(wd, nt, blocks, s, st, a, grad, n, hp);
+        else                  launch_adam_db2<kF32, kBF16>(wd, nt, blocks, s, st, a, grad, n, hp);
+    } else {
+        if (gf == kF16)       launch_adam_db2<kF16, kF16>(wd, nt, blocks, s, st, a, grad, n, hp);
+        else if (gf == kBF16) launch_adam_db2<kBF16, kF16>(wd, nt, blocks, s, st, a, grad, n, hp);
+        else                  launch_adam_db2<kF32, kF16>(wd, nt, blocks, s, st, a, grad, n, hp);
+    }
+}
+
 template <int GF, bool OW, bool CK, bool SQ>
 void launch_acc3(bool nt, hipStream_t s, float* acc, const GradList& gl, int64_t n, ds_scaler* st, double* part)
 {
@@ -1296,6 +1455,7 @@ ds_status ds_state_write(ds_scaler* st, const ds_scaler* host_in, void* stream)
     ds_scaler value = *host_in;
     value.blocks_done = 0u;         // between steps the fused form's block count is 0
     value.sumsq_blocks_done = 0u;   // and so is the sum of squares' second pass's
+    value.db_tickets = 0ull;        // and the double-buffered step's
     write_state_kernel<<<1, 1, 0, static_cast<hipStream_t>(stream)>>>(st, value);
     return launched();
 }
@@ -1392,6 +1552,64 @@ ds_status ds_adam_step_fused(ds_scaler* st, float* master, float* m, float* v, u
     }
     const AdamHyper hp{lr, beta1, beta2, eps, weight_decay, max_grad_norm, accum_steps, 0, 0.0f, 0, 0};
     return adam_step(st, master, m, v, p16, pdt, grad, dt, n, hp, true, stream);
+}
+
+ds_status ds_adam_step_double_buffered(ds_scaler* st, float* const* master2, float* const* m2, float* const* v2,
+                                       uint16_t* const* p16_2, ds_dtype pdt, const void* grad, ds_dtype dt,
+                                       int64_t n, float lr, const ds_lr_schedule* sched_or_null, float beta1,
+                                       float beta2, float eps, float weight_decay, int32_t accum_steps,
+                                       void* stream)
+{
+    AdamHyper hp{lr, beta1, beta2, eps, weight_decay, 0.0f, accum_steps, 0, 0.0f, 0, 0};
+    if (sched_or_null != nullptr) {
+        if (!schedule_ok(*sched_or_null))
+            return DS_ERR_HPARAM;
+        const ds_lr_schedule& q = *sched_or_null;
+        hp = AdamHyper{q.warmup_max_lr, beta1, beta2, eps, weight_decay, 0.0f, accum_steps,
+                       q.kind, q.warmup_min_lr, q.warmup_num_steps, q.total_num_steps};
+    }
+    if (!size_ok(n))
+        return DS_ERR_SIZE;
+    if (!known(dt) || !is16(pdt))
+        return DS_ERR_DTYPE;
+    if (!finite_ge0(hp.lr) || !beta_ok(beta1) || !beta_ok(beta2) || !std::isfinite(eps) || eps <= 0.0f ||
+        !finite_ge0(weight_decay) || accum_steps < 1)
+        return DS_ERR_HPARAM;
+    if (st == nullptr)
+        return DS_ERR_NULL;
+    if (!aligned(st, 8))
+        return DS_ERR_ALIGN;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (n == 0) {
+        update_scale_swap_kernel<<<1, 1, 0, s>>>(st);
+        return launched();
+    }
+    if (master2 == nullptr || m2 == nullptr || v2 == nullptr || p16_2 == nullptr || grad == nullptr)
+        return DS_ERR_NULL;
+    DbArrays a{};
+    for (int k = 0; k < 2; ++k) {
+        if (master2[k] == nullptr || m2[k] == nullptr || v2[k] == nullptr || p16_2[k] == nullptr)
+            return DS_ERR_NULL;
+        a.master[k] = master2[k];
+        a.m[k] = m2[k];
+        a.v[k] = v2[k];
+        a.p16[k] = p16_2[k];
+    }
+    const void* ptrs[10] = {a.master[0], a.master[1], a.m[0], a.m[1], a.v[0], a.v[1], a.p16[0], a.p16[1], grad, st};
+    for (int i = 0; i < 10; ++i)
+        if (!aligned(ptrs[i], i == 9 ? 8 : 16))
+            return DS_ERR_ALIGN;
+    const uint64_t un = static_cast<uint64_t>(n);
+    const uint64_t sizes[10] = {4 * un, 4 * un, 4 * un, 4 * un, 4 * un, 4 * un, 2 * un, 2 * un, esize(dt) * un,
+                                sizeof(ds_scaler)};
+    for (int i = 0; i < 10; ++i)
+        for (int j = i + 1; j < 10; ++j)
+            if (overlap(ptrs[i], sizes[i], ptrs[j], sizes[j]))
+                return DS_ERR_ALIAS;
+    const bool nt = variant_nt(n);
+    const unsigned blocks = grid_blocks(tiles_of(n, 4), nt ? kStepBlock : kSmallBlock);
+    launch_adam_db(fmt_of(dt), fmt_of(pdt), weight_decay != 0.0f, nt, blocks, s, st, a, grad, n, hp);
+    return launched();
 }
 
 size_t ds_sumsq_workspace_bytes(int64_t n)

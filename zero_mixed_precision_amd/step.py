@@ -14,6 +14,12 @@ scales and accumulates, step() updates):
 
 The Adam step covers the whole partition in one ds_adam_step_fused call,
 whose kernel also advances the loss scaler (ds_update_loss_scale's work).
+With ``double_buffer`` (K = 1, no clipping) the shard keeps two copies of
+master, m, v and the 16-bit copy, and a step is one
+ds_adam_step_double_buffered call: the overflow check is fused into the Adam
+pass, which writes the other copy, and the device makes that copy current
+only if the step applied (28 bytes per element instead of 30); ``current()``
+returns the copy holding the state.
 
 With gradient clipping configured the check passes are the _sumsq variants
 (ds_accumulate_sumsq / ds_check_overflow_sumsq), which also gather the
@@ -77,8 +83,14 @@ def check_grad_dtype(dtype, bf16: bool, torch) -> None:
 
 
 class ShardStep:
-    def __init__(self, n: int, cfg: ZeroMPConfig, device="cuda", buckets=None, stream=None):
+    def __init__(self, n: int, cfg: ZeroMPConfig, device="cuda", buckets=None, stream=None, double_buffer=False):
         import torch
+
+        self.double_buffer = bool(double_buffer)
+        if self.double_buffer and (int(cfg.gradient_accumulation_steps) != 1 or float(cfg.gradient_clipping) > 0):
+            raise ValueError("double_buffer is for gradient_accumulation_steps = 1 without gradient clipping (the "
+                             "check is fused into the Adam pass; with accumulation it is fused into the last "
+                             "micro-batch's pass instead, and clipping needs the norm before the update)")
 
         # accumulation granularity: the reduce buckets inside this partition
         self.buckets = buckets_or_all(buckets, int(n))
@@ -93,6 +105,13 @@ class ShardStep:
         self.v = torch.zeros(self.n, **f32)
         self.p16 = torch.empty(self.n, dtype=torch.bfloat16 if cfg.bf16 else torch.float16, device=device)
         self.acc = torch.empty(self.n, **f32) if self.K > 1 else None
+        # double_buffer: a second copy of master, m, v and the 16-bit copy; the
+        # state names the current one (initially copy 0, the attributes above)
+        self._copies = None
+        if self.double_buffer:
+            self._copies = ((self.master, self.m, self.v, self.p16),
+                            (torch.empty(self.n, **f32), torch.empty(self.n, **f32), torch.empty(self.n, **f32),
+                             torch.empty(self.n, dtype=self.p16.dtype, device=device)))
         self.state = torch.zeros(_lib.ds_scaler_size(), dtype=torch.uint8, device=device)
         # learning-rate schedule (None: the constant cfg.lr), read on the device
         # at the applied-step count, so a skipped step does not advance it
@@ -163,6 +182,17 @@ class ShardStep:
         """Finish the step: check (K = 1), gated Adam, scaler update."""
         c = self.cfg
         st = self.state.data_ptr()
+        if self.double_buffer:
+            # the check fused into the Adam pass, which writes the other copy
+            self._check_grad(g16)
+            a, b = self._copies
+            _lib.ds_adam_step_double_buffered(st, [a[0].data_ptr(), b[0].data_ptr()],
+                                              [a[1].data_ptr(), b[1].data_ptr()],
+                                              [a[2].data_ptr(), b[2].data_ptr()],
+                                              [a[3].data_ptr(), b[3].data_ptr()], self.pdt, g16.data_ptr(),
+                                              self.gdt, self.n, c.lr, self.sched, c.betas[0], c.betas[1], c.eps,
+                                              c.weight_decay, 1, self.stream)
+            return
         if self.K == 1:
             self._check_grad(g16)
             grad, dt = g16.data_ptr(), self.gdt
@@ -219,6 +249,13 @@ class ShardStep:
 
     def scaler(self) -> _lib.DsScaler:
         return _lib.ds_state_read(self.state, self.stream)
+
+    def current(self):
+        """(master, m, v, p16) holding the state: the attributes of the same names,
+        or with double_buffer the copy the state names (read back: one copy)."""
+        if not self.double_buffer:
+            return self.master, self.m, self.v, self.p16
+        return self._copies[self.scaler().current & 1]
 
     def save_checkpoint(self, save_dir, tag=None, client_state=None, rank=0) -> str:
         """Save this shard between steps ("DeepSpeed complete guide" section 5.2); see checkpoint.py."""
