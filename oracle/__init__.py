@@ -16,12 +16,13 @@ features: gradient accumulation and dynamic loss scaling).  The bucket packing
 oracle is in ``oracle.packing``.
 
 Parity pins: every function here is pinned by the ``-m "not gpu"`` tests in
-``tests/test_oracle_*.py``.  Parts of the scaler are parity unpinned: what
-happens after a hysteresis >= 2 decrease, ``consecutive_hysteresis`` and the
-uncapped growth (no workload exercises them and the pages give only the keys'
-one-line meaning); the static scale is pinned against torch's loss scaler held
-at a fixed scale, and the 1e-8 floor of the guide's section 13.1, where the
-scale stops being a power of two, is pinned.
+``tests/test_oracle_*.py``.  The scaler's branches that the pages give only
+the keys' one-line meaning for (what happens after a hysteresis >= 2
+decrease, ``consecutive_hysteresis``, the uncapped growth) are pinned to the
+run-length closed form of their reading at every step of seeded and
+structured overflow sequences; the static scale is pinned against torch's loss
+scaler held at a fixed scale, and the 1e-8 floor of the guide's section 13.1,
+where the scale stops being a power of two, is pinned.
 """
 from __future__ import annotations
 

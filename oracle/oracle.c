@@ -17,10 +17,11 @@
  * correction scalars are evaluated in fp64 and rounded once to fp32.
  *
  * Pins (tests/test_oracle_*.py) fix every function against the pages' values,
- * closed forms, exhaustive library comparisons and brute force.  Parity
- * unpinned: in zo_scaler_update, the restart of the hysteresis count after a
- * decrease, consecutive_hysteresis and the uncapped growth (the pages give
- * one-line meanings only and no workload exercises them).
+ * closed forms, exhaustive library comparisons and brute force.  The branches
+ * of zo_scaler_update that the pages give only a one-line meaning for (the
+ * restart of the hysteresis count after a decrease, consecutive_hysteresis,
+ * the uncapped growth) are pinned to their reading's run-length closed form:
+ * the readings themselves are choices the pages leave open.
  *
  * Build: gcc -O2 -std=c11 -fPIC -shared -ffp-contract=off -fno-fast-math
  *            -o liboracle.so oracle.c -lm

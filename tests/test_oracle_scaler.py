@@ -115,14 +115,91 @@ def test_floor_below_the_powers_of_two_from_pages(oracle_lib):
 
 
 def test_hysteresis_two_halves_every_second_overflow(oracle_lib):
-    """hysteresis = 2 (the pages' default): two overflows per decrease.
-    Parity unpinned: the pages give only the key's one-line meaning."""
+    """hysteresis = 2 (the pages' default): two overflows per decrease (the
+    key's one-line meaning on the page)."""
     sc = oracle.Scaler(2.0 ** 16, 1.0, 1000, 2)
     seq = []
     for _ in range(4):
         sc.update(True)
         seq.append(sc.scale)
     assert seq == [2.0 ** 16, 2.0 ** 15, 2.0 ** 15, 2.0 ** 14]
+
+
+def _closed_form(seq, H, W, consecutive):
+    """The scaler's state after each step of an overflow sequence, counted
+    over the sequence instead of stepped: the growth and hysteresis readings
+    as run lengths.
+
+    - growths: every maximal run of L successes doubles the scale floor(L / W)
+      times (the success count restarts at an overflow and at each growth);
+      the count left over is the current run's length mod W;
+    - decreases without consecutive_hysteresis: successes never refill the
+      count, which restarts only at a decrease, so O overflows in all halve
+      the scale floor(O / H) times and leave H - O mod H units;
+    - decreases with consecutive_hysteresis: a success refills the count, so
+      every maximal run of R overflows halves floor(R / H) times and leaves
+      H - R mod H units (H again once a success follows).
+    Exponents are relative to the initial scale; the floor is never reached."""
+    out = []
+    growths = decreases = overflows = 0
+    run_ok = run_ov = 0
+    for i, ov in enumerate(seq):
+        if ov:
+            run_ov = run_ov + 1 if i and seq[i - 1] else 1
+            run_ok = 0
+            overflows += 1
+            if consecutive:
+                if run_ov % H == 0:
+                    decreases += 1
+                left = H - run_ov % H
+            else:
+                decreases = overflows // H
+                left = H - overflows % H
+        else:
+            run_ok = run_ok + 1 if i and not seq[i - 1] else 1
+            run_ov = 0
+            if run_ok % W == 0:
+                growths += 1
+            left = H if consecutive else H - overflows % H
+        out.append((growths - decreases, run_ok % W if not ov else 0, left,
+                    overflows, i + 1 - overflows))
+    return out
+
+
+@pytest.mark.parametrize("consecutive", [False, True], ids=["spent_count", "consecutive_hysteresis"])
+@pytest.mark.parametrize("H", [1, 2, 3, 5])
+@pytest.mark.parametrize("W", [1, 2, 3, 7])
+def test_scaler_matches_run_length_closed_form(oracle_lib, consecutive, H, W):
+    """The hysteresis restart after a decrease, consecutive_hysteresis and
+    growth checked at every step against the run-length counts above, on
+    seeded random overflow sequences (overflow rates 0.1 to 0.9) and on
+    structured ones (long runs of each kind, alternation).  The floor 2^-100
+    and at most 80 steps keep the scale a power of two inside fp32's range, so
+    scale == 2^(16 + growths - decreases) exactly."""
+    rng = np.random.default_rng(1000 * H + 10 * W + consecutive)
+    seqs = [list(rng.random(80) < p) for p in (0.1, 0.3, 0.5, 0.7, 0.9) for _ in range(4)]
+    seqs += [[True] * 40 + [False] * 40, [False] * 40 + [True] * 40, [True, False] * 40,
+             [True, True, False] * 26, ([False] * 6 + [True] * 4) * 8]
+    for seq in seqs:
+        sc = oracle.Scaler(2.0 ** 16, 2.0 ** -100, W, H, consecutive_hysteresis=consecutive)
+        for i, (ov, want) in enumerate(zip(seq, _closed_form(seq, H, W, consecutive))):
+            sc.update(bool(ov))
+            e, good, left, skipped, applied = want
+            s = sc.s
+            ctx = f"H={H} W={W} consecutive={consecutive} step {i} of {''.join('x' if o else '.' for o in seq)}"
+            assert s.scale == 2.0 ** (16 + e), ctx
+            assert (s.good_steps, s.hyst_left, s.skipped, s.applied, s.iters) == (good, left, skipped, applied,
+                                                                                 i + 1), ctx
+
+
+def test_growth_is_not_capped(oracle_lib):
+    """No upper bound on the scale (none is stated): with a window of one the
+    scale doubles on every successful step up to fp32's largest power of two."""
+    sc = oracle.Scaler(2.0 ** 16, 1.0, 1, 2)
+    for k in range(1, 112):
+        sc.update(False)
+        assert sc.scale == 2.0 ** (16 + k)
+    assert sc.scale == 2.0 ** 127
 
 
 def test_static_scale_never_changes(oracle_lib):
