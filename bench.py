@@ -1,17 +1,27 @@
 """Benchmark of the ZeRO mixed-precision optimizer step on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload zero1_70b]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload zero1_70b] [--step-form auto]
 
-One step = the whole per-rank hot path over one synthetic batch: (K > 1:
-bucketed fp16 -> fp32 accumulation of every micro-batch, the last one with the
-fused inf/NaN check; K = 1: the inf/NaN check of the fp16 gradient), then the
-gated fused Adam update with the fp16 copy, whose kernel also performs the
-loss-scale update.  Inputs are
-resident in HBM before the timed region; gradients are drawn on the device
-(distinct buffers, reused cyclically when they do not all fit).
+One step = the whole per-rank hot path over one synthetic batch: the inf/NaN
+check of the gradient (K > 1: fused into the bucketed fp16 -> fp32
+accumulation of the last micro-batch), the gated Adam update with the fp16
+copy, and the loss-scale update.  With K = 1 and no clipping the default
+(--step-form auto) is the double-buffered form: the check fused into the
+Adam pass, which reads the copy of master/m/v/p16 that holds the state and
+writes the other one (28 B per element in one launch; 30 bytes of device
+memory per element instead of 16, so it is used where the second copy and a
+gradient buffer fit, and where the gradient is larger than the 256 MB
+Infinity Cache: a smaller one is still cached when the in-place form reads it
+again, which makes that form as fast).  The in-place form (the check, then the Adam pass that
+rewrites the one copy, 30 B per element in two launches) is then timed after
+it on the same arrays and reported as ``in_place_form``; --step-form in_place
+makes it the timed form.  Inputs are resident in HBM before the timed region;
+gradients are drawn on the device (distinct buffers, reused cyclically when
+they do not all fit).
 
 The default workload is zero1_70b: one rank's ZeRO-1 share of a 70B model at
-N = 8, 8.75e9 elements (140 GB of state), the largest single-GPU workload.
+N = 8, 8.75e9 elements (140 GB of state, 262.5 GB with the second copy), the
+largest single-GPU workload.
 
 Prints one JSON line.  ``value`` is parameters updated per second (Gparams/s)
 over the timed steps; ``roofline`` is the Adam kernel's algorithmic HBM
@@ -20,13 +30,13 @@ its average duration, timed with HIP events on the launch stream, against
 the 8 TB/s HBM3E peak; ``traffic`` comes from the committed rocprofv3 counter
 summary when it was taken on the current kernel source; the median and minimum
 launch times sit beside it, ``roofline.step`` gives the whole step's
-algorithmic bytes per element (30 with a separately produced fp16 gradient)
-over the wall time per step, and ``roofline.references`` three data-movement
-references timed on the same arrays after the timed region: the step's
-14 B read + 14 B written per element with no arithmetic, a plain copy with one
-16-byte vector per lane, and the runtime's device-to-device copy
-(``torch.Tensor.copy_``, which is hipMemcpyAsync).  ``step_ms_*`` and
-``pre_adam_ms_*`` (the check, or the accumulation with its fused check) come
+algorithmic bytes per element over the wall time per step, and
+``roofline.references`` three data-movement references timed on the same
+arrays after the timed region: the step's 14 B read + 14 B written per
+element with no arithmetic, a plain copy with one 16-byte vector per lane,
+and the runtime's device-to-device copy (``torch.Tensor.copy_``, which is
+hipMemcpyAsync).  ``step_ms_*`` and ``pre_adam_ms_*`` (the check, or the
+accumulation with its fused check; nothing in the double-buffered form) come
 from an untimed pass with events around each part.  ``graph_replay`` times the
 same steps replayed from HIP graphs (one per position in the cycle of gradient
 buffers).  ``cpu_baseline`` times the CPU oracle on a bounded slice of the
@@ -50,6 +60,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0
+INFINITY_CACHE_BYTES = 256 << 20   # MI355X's last-level (MALL) cache
 METRIC = "Gparams/s per Adam step + achieved HBM GB/s (% of MI355X peak)"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "adam_traffic.json")
 KERNEL_SRC = os.path.join(ROOT, "zero_mixed_precision_amd", "csrc", "dszero.hip")
@@ -118,14 +129,28 @@ def gpu_run(args):
     else:
         buckets = [(0, n)]
     # double-buffered step (K = 1, no clipping): a second copy of master, m, v and
-    # the 16-bit copy; the overflow check is fused into the Adam pass
-    double = args.double_buffer and K == 1 and args.clip == 0
-    if args.double_buffer and not double:
-        log("bench.py: --double-buffer applies to K = 1 workloads without clipping; using the single copy")
+    # the 16-bit copy; the overflow check is fused into the Adam pass.  "auto"
+    # takes it where it applies, where the gradient is larger than the 256 MB
+    # Infinity Cache (a smaller one is still cached when the in-place form's
+    # Adam pass reads it again after the check, which makes that form as fast)
+    # and where the second copy leaves room for a gradient buffer
+    double = False
     copy1 = None
-    if double:
-        copy1 = [torch.empty(n, dtype=torch.float32, device=dev) for _ in range(3)] + \
-                [torch.empty(n, dtype=torch.int16, device=dev)]
+    applies = K == 1 and args.clip == 0
+    if args.step_form == "double" and not applies:
+        log("bench.py: the double-buffered step applies to K = 1 workloads without clipping; using the in-place form")
+    if applies and (args.step_form == "double" or (args.step_form == "auto" and 2 * n > INFINITY_CACHE_BYTES)):
+        try:
+            copy1 = [torch.empty(n, dtype=torch.float32, device=dev) for _ in range(3)] + \
+                    [torch.empty(n, dtype=torch.int16, device=dev)]
+            if torch.cuda.mem_get_info(dev)[0] < 2 * n + (4 << 30):
+                raise torch.cuda.OutOfMemoryError("no room for a gradient buffer beside two copies")
+            double = True
+        except torch.cuda.OutOfMemoryError as e:
+            copy1 = None
+            torch.cuda.empty_cache()
+            log(f"bench.py: two copies of the state do not fit ({str(e).splitlines()[0][:120]}); "
+                "using the in-place form")
 
     # resident gradient buffers, a ring of distinct draws (a real step rewrites one
     # contiguous gradient buffer; the ring is larger than the 256 MB Infinity Cache)
@@ -162,10 +187,12 @@ def gpu_run(args):
         if not (t.is_cuda and t.is_contiguous() and t.numel() * t.element_size() >= nb):
             raise RuntimeError("bench.py: a state array is not a contiguous device tensor of the expected size")
     st_p, master_p, m_p, v_p, p16_p = (t.data_ptr() for t in (st, master, m, v, p16))
+    # the arrays the in-place form updates (the current copy when there are two)
+    ip = [master_p, m_p, v_p, p16_p]
     if double:
         V2 = ctypes.c_void_p * 2
-        db_arrays = (V2(master_p, copy1[0].data_ptr()), V2(m_p, copy1[1].data_ptr()), V2(v_p, copy1[2].data_ptr()),
-                     V2(p16_p, copy1[3].data_ptr()))
+        copies = (ip[:], [t.data_ptr() for t in copy1])
+        db_arrays = tuple(V2(copies[0][k], copies[1][k]) for k in range(4))
         db_step = _lib.lib.ds_adam_step_double_buffered
     acc_p = acc.data_ptr() if acc is not None else None
     ws_p, ws_bytes = (ws.data_ptr(), ws.numel() * 8) if ws is not None else (None, 0)
@@ -173,12 +200,13 @@ def gpu_run(args):
 
     step_ev, pre_ev = [], []   # whole steps; their check (K = 1) or accumulation + check (K > 1) part
 
-    def one_step(i, timed, q=stream, whole=False):
+    def one_step(i, timed, q=stream, whole=False, form=None, evs=None):
+        dbl = double if form is None else form == "double"
         if whole:
             s0 = torch.cuda.Event(enable_timing=True)
             s0.record(q)
         base = i * K
-        if double:
+        if dbl:
             g = grad_p[base % nbuf]
             gptr, dt = g, gdt16
         elif K == 1:
@@ -214,15 +242,15 @@ def gpu_run(args):
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a.record(q)
         # the Adam kernel also advances the loss scaler (one launch for both)
-        if double:   # and performs the overflow check, writing the other copy
+        if dbl:   # and performs the overflow check, writing the other copy
             rc = db_step(st_p, *db_arrays, gdt16, gptr, dt, n, hp[0], None, *hp[1:5], K, q.cuda_stream)
             if rc != 0:
                 raise RuntimeError(f"ds_adam_step_double_buffered: {_lib.ds_status_string(rc)}")
         else:
-            _lib.ds_adam_step_fused(st_p, master_p, m_p, v_p, p16_p, gdt16, gptr, dt, n, hp[0], None, *hp[1:], K, q)
+            _lib.ds_adam_step_fused(st_p, *ip, gdt16, gptr, dt, n, hp[0], None, *hp[1:], K, q)
         if timed:
             b.record(q)
-            ev.append((a, b))
+            (ev if evs is None else evs).append((a, b))
         if whole:
             s1 = torch.cuda.Event(enable_timing=True)
             s1.record(q)
@@ -281,6 +309,34 @@ def gpu_run(args):
     torch.cuda.synchronize()
     gwall = time.perf_counter() - t0
     del graphs
+
+    # with two copies, the in-place form (check, then the in-place Adam pass) on
+    # the copy that holds the state, timed the same way after the rest
+    in_place = None
+    if double:
+        ip[:] = copies[_lib.ds_state_read(st, stream).current]
+        ip_ev = []
+        for i in range(args.warmup):
+            one_step(i, False, form="in_place")
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.warmup, args.warmup + args.steps):
+            one_step(i, True, form="in_place", evs=ip_ev)
+        torch.cuda.synchronize()
+        ip_wall = time.perf_counter() - t0
+        ip_adam_s = sum(a.elapsed_time(b) for a, b in ip_ev) / len(ip_ev) / 1e3
+        in_place = {
+            "step_form": "check, then the in-place Adam pass (one copy of the state)",
+            "value": round(n * args.steps / ip_wall / 1e9, 3),
+            "ms_per_step": round(ip_wall / args.steps * 1e3, 4),
+            "kernel": "adam_kernel",
+            "avg_launch_ms": round(ip_adam_s * 1e3, 4),
+            "achieved": round(28 * n / ip_adam_s / 1e9, 1),
+            "frac": round(28 * n / ip_adam_s / 1e9 / PEAK_HBM_GBS, 4),
+            "traffic": load_traffic(w.name, "bf16" if args.bf16 else "fp16", "adam_kernel"),
+            "step": {"bytes_per_elem": 30, "achieved": round(30 * n * args.steps / ip_wall / 1e9, 1),
+                     "frac": round(30 * n * args.steps / ip_wall / 1e9 / PEAK_HBM_GBS, 4)},
+        }
 
     adam_ms = [a.elapsed_time(b) for a, b in ev]
     adam_avg_s = sum(adam_ms) / len(adam_ms) / 1e3
@@ -351,8 +407,9 @@ def gpu_run(args):
             "adam": {"lr": LR, "betas": [BETA1, BETA2], "eps": EPS, "weight_decay": WD},
             "gradient_clipping": args.clip,
             "half": "bf16" if args.bf16 else "fp16",
-            "step_form": ("double-buffered: overflow check fused into the Adam pass over two copies of the state"
-                          if double else "check (or accumulation with the fused check), then the in-place Adam pass"),
+            "step_form": ("double-buffered: the overflow check fused into the Adam pass, which writes the "
+                          "second copy of the state" if double else
+                          "check (or accumulation with the fused check), then the in-place Adam pass"),
             "parallelism": "one GPU's ZeRO partition",
         },
         "roofline": {
@@ -375,6 +432,7 @@ def gpu_run(args):
                            "runtime_d2d_copy_gbs": round(memcpy_gbs, 1),
                            "bytes": nm * 8},
         },
+        "in_place_form": in_place,
         "graph_replay": {"graphs": cycle, "ms_per_step": round(gwall / args.steps * 1e3, 4),
                          "value": round(n * args.steps / gwall / 1e9, 3)},
         "device": {"name": props.name, "arch": getattr(props, "gcnArchName", ""),
@@ -586,9 +644,13 @@ def main(argv=None):
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--cpu-slice", type=int, default=109_375_000)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--double-buffer", dest="double_buffer", action="store_true", default=False,
-                    help="K = 1 without clipping: two copies of the state, the overflow check fused into the Adam "
-                         "pass (ds_adam_step_double_buffered)")
+    ap.add_argument("--step-form", default="auto", choices=["auto", "double", "in_place"],
+                    help="double: two copies of the state, the overflow check fused into the Adam pass "
+                         "(ds_adam_step_double_buffered; K = 1 without clipping); in_place: the check (or the "
+                         "accumulation), then the in-place Adam pass; auto (default): double where it applies "
+                         "and fits, and the in-place form timed after it on the same arrays")
+    ap.add_argument("--double-buffer", dest="step_form", action="store_const", const="double",
+                    help="the same as --step-form double")
     ap.add_argument("--fold", type=int, default=1,
                     help="micro-batches folded into the accumulation buffer per pass (1..8; K > 1 workloads; "
                          "needs that many gradient buffers held at once)")
