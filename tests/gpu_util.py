@@ -92,6 +92,17 @@ class DevState:
         return self.lib.ds_state_read(self.state)
 
 
+def count_nonfinite16(torch, t, fmt="fp16", chunk=1 << 28) -> int:
+    """Non-finite values in a device buffer of 16-bit gradient bits, counted by
+    torch's isfinite (a library routine, independent of the kernels and of the
+    oracle) over chunks, so that no full-size temporary is made."""
+    view = t.view(torch.bfloat16 if fmt == "bf16" else torch.float16)
+    bad = 0
+    for s in range(0, view.numel(), chunk):
+        bad += int((~torch.isfinite(view[s:s + chunk])).sum().item())
+    return bad
+
+
 def check_scaler(dev_sc, orc: "oracle.Scaler", overflow: bool, ctx=""):
     s = orc.s
     assert bool(dev_sc.last_overflow) == bool(overflow), f"{ctx}: overflow flag"

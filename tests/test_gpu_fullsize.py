@@ -11,7 +11,8 @@ Every element's update depends only on its own inputs and on the step's
 overflow flag, so sampling is exact provided the oracle's flag is the global
 one.  It is: the generator only emits entries of finite lookup tables (pinned
 on the CPU), so the only non-finite gradients are the injected ones, and all of
-those are in the sample.
+those are in the sample; each full micro-batch buffer is also scanned with
+torch's isfinite, which must find exactly the injected values.
 """
 import numpy as np
 import pytest
@@ -103,6 +104,9 @@ def run_sampled(torch, name, fused=False, bf16=False, fold=1, double=False, extr
             if inj is not None and inj[0] == k:
                 buf[inj[1]] = torch.tensor(inf16, dtype=torch.int32).to(torch.int16)
                 gh[np.searchsorted(I, inj[1])] = inf16
+            # the whole buffer's non-finite values are exactly the injected one (if any)
+            assert gu.count_nonfinite16(torch, buf, fmt) == int(inj is not None and inj[0] == k), \
+                f"[{name}] step {s} micro-batch {k}: non-finite values beyond the injected ones"
             gs_host.append(gh)
             if K > 1 and fold == 1:
                 for start, size in buckets:
@@ -325,6 +329,7 @@ def test_ragged_layout_clipped(torch):
         for k in range(K):
             key = w.grad_key(s, k)
             synth.device_fill_grad16(torch, tabs, g16, key, spec)
+            assert gu.count_nonfinite16(torch, g16) == 0, (s, k)
             oracle.accumulate(acc_s, synth.host_grad16(key, I, spec), overwrite=(k == 0))
             for b, (start, size) in enumerate(buckets):
                 a, gp = acc.data_ptr() + 4 * start, g16.data_ptr() + 2 * start
