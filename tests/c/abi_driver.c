@@ -6,11 +6,14 @@
  *
  *   abi_driver DIR
  *
- * DIR/params.txt   n K steps init_scale window lr beta1 beta2 eps weight_decay max_grad_norm
+ * DIR/params.txt   n K steps init_scale window lr beta1 beta2 eps weight_decay max_grad_norm [double]
+ *                  (double = 1: ds_adam_step_double_buffered over two copies of the state in place
+ *                  of the check, ds_adam_step and ds_update_loss_scale; needs max_grad_norm = 0)
  * DIR/master.bin   float32[n]                initial fp32 master copy
  * DIR/grads.bin    uint16[steps][K][n]       fp16 gradients, micro-batch by micro-batch
  * writes
- * DIR/master_out.bin, m_out.bin, v_out.bin (float32[n]), p16_out.bin (uint16[n])
+ * DIR/master_out.bin, m_out.bin, v_out.bin (float32[n]), p16_out.bin (uint16[n]) of the copy
+ *                  that holds the state
  * DIR/scaler.txt   one line per step: last_overflow scale step iter skipped
  *
  * Device memory comes from hipMalloc, the work runs on a stream created here,
@@ -80,18 +83,24 @@ int main(int argc, char** argv)
         return 1;
     }
     const char* dir = argv[1];
-    long long n_ll, K_l, steps_l, window_l;
+    long long n_ll, K_l, steps_l, window_l, double_l = 0;
     float init_scale, lr, b1, b2, eps, wd, clip;
     {
         char path[4096];
         snprintf(path, sizeof path, "%s/params.txt", dir);
         FILE* f = fopen(path, "r");
-        if (f == NULL || fscanf(f, "%lld %lld %lld %f %lld %f %f %f %f %f %f", &n_ll, &K_l, &steps_l,
-                                &init_scale, &window_l, &lr, &b1, &b2, &eps, &wd, &clip) != 11) {
+        int got = f == NULL ? 0 : fscanf(f, "%lld %lld %lld %f %lld %f %f %f %f %f %f %lld", &n_ll, &K_l, &steps_l,
+                                         &init_scale, &window_l, &lr, &b1, &b2, &eps, &wd, &clip, &double_l);
+        if (got != 11 && got != 12) {
             fprintf(stderr, "%s: bad parameters\n", path);
             return 4;
         }
         fclose(f);
+    }
+    const int dbl = double_l != 0;
+    if (dbl && clip > 0.0f) {
+        fprintf(stderr, "the double-buffered step takes no clipping\n");
+        return 4;
     }
     const int64_t n = n_ll;
     const int32_t K = (int32_t)K_l, steps = (int32_t)steps_l;
@@ -113,6 +122,9 @@ int main(int argc, char** argv)
     CHECK_HIP(hipStreamCreate(&stream));
     float *master, *m, *v, *acc = NULL;
     uint16_t *p16, *g16;
+    /* the double-buffered step's two copies: copy 0 is master/m/v/p16 */
+    float *master2[2], *m2[2], *v2[2];
+    uint16_t* p16_2[2];
     void *state, *ws = NULL;
     const size_t ws_bytes = ds_sumsq_workspace_bytes(n);
     CHECK_HIP(hipMalloc((void**)&master, 4 * (size_t)n));
@@ -130,6 +142,16 @@ int main(int argc, char** argv)
     CHECK_HIP(hipMemsetAsync(v, 0, 4 * (size_t)n, stream));
     CHECK_HIP(hipMemsetAsync(p16, 0, 2 * (size_t)n, stream));
     CHECK_DS(ds_state_init((ds_scaler*)state, init_scale, 1.0f, (int32_t)window_l, 1, 0, 1, stream));
+    master2[0] = master;
+    m2[0] = m;
+    v2[0] = v;
+    p16_2[0] = p16;
+    if (dbl) {   /* copy 1 holds no state until the first applied step writes it */
+        CHECK_HIP(hipMalloc((void**)&master2[1], 4 * (size_t)n));
+        CHECK_HIP(hipMalloc((void**)&m2[1], 4 * (size_t)n));
+        CHECK_HIP(hipMalloc((void**)&v2[1], 4 * (size_t)n));
+        CHECK_HIP(hipMalloc((void**)&p16_2[1], 2 * (size_t)n));
+    }
 
     char path[4096];
     snprintf(path, sizeof path, "%s/scaler.txt", dir);
@@ -145,7 +167,9 @@ int main(int argc, char** argv)
         }
         const void* grad = g16;
         ds_dtype gdt = DS_FP16;
-        if (K == 1) {
+        if (K == 1 && dbl) {
+            /* the check runs inside the double-buffered pass */
+        } else if (K == 1) {
             if (clip > 0.0f)
                 CHECK_DS(ds_check_overflow_sumsq((ds_scaler*)state, g16, DS_FP16, n, ws, ws_bytes, stream));
             else
@@ -172,9 +196,14 @@ int main(int argc, char** argv)
             grad = acc;
             gdt = DS_FP32;
         }
-        CHECK_DS(ds_adam_step((const ds_scaler*)state, master, m, v, p16, DS_FP16, grad, gdt, n, lr, b1, b2, eps,
-                              wd, clip, K, stream));
-        CHECK_DS(ds_update_loss_scale((ds_scaler*)state, stream));
+        if (dbl) {
+            CHECK_DS(ds_adam_step_double_buffered((ds_scaler*)state, master2, m2, v2, p16_2, DS_FP16, grad, gdt, n,
+                                                  lr, NULL, b1, b2, eps, wd, K, stream));
+        } else {
+            CHECK_DS(ds_adam_step((const ds_scaler*)state, master, m, v, p16, DS_FP16, grad, gdt, n, lr, b1, b2,
+                                  eps, wd, clip, K, stream));
+            CHECK_DS(ds_update_loss_scale((ds_scaler*)state, stream));
+        }
         ds_scaler sc;
         CHECK_DS(ds_state_read((const ds_scaler*)state, &sc, stream));
         fprintf(trace, "%u %.9g %lld %lld %lld\n", sc.last_overflow, (double)sc.scale, (long long)sc.step,
@@ -186,15 +215,28 @@ int main(int argc, char** argv)
     uint16_t* out16 = malloc(2 * (size_t)n);
     if (out == NULL || out16 == NULL)
         return 4;
+    int cur = 0;
+    if (dbl) {
+        ds_scaler sc;
+        CHECK_DS(ds_state_read((const ds_scaler*)state, &sc, stream));
+        cur = (int)(sc.current & 1u);
+        printf("current copy: %d\n", cur);
+    }
     CHECK_HIP(hipStreamSynchronize(stream));
-    CHECK_HIP(hipMemcpy(out, master, 4 * (size_t)n, hipMemcpyDeviceToHost));
+    CHECK_HIP(hipMemcpy(out, master2[cur], 4 * (size_t)n, hipMemcpyDeviceToHost));
     write_file(dir, "master_out.bin", out, 4 * (size_t)n);
-    CHECK_HIP(hipMemcpy(out, m, 4 * (size_t)n, hipMemcpyDeviceToHost));
+    CHECK_HIP(hipMemcpy(out, m2[cur], 4 * (size_t)n, hipMemcpyDeviceToHost));
     write_file(dir, "m_out.bin", out, 4 * (size_t)n);
-    CHECK_HIP(hipMemcpy(out, v, 4 * (size_t)n, hipMemcpyDeviceToHost));
+    CHECK_HIP(hipMemcpy(out, v2[cur], 4 * (size_t)n, hipMemcpyDeviceToHost));
     write_file(dir, "v_out.bin", out, 4 * (size_t)n);
-    CHECK_HIP(hipMemcpy(out16, p16, 2 * (size_t)n, hipMemcpyDeviceToHost));
+    CHECK_HIP(hipMemcpy(out16, p16_2[cur], 2 * (size_t)n, hipMemcpyDeviceToHost));
     write_file(dir, "p16_out.bin", out16, 2 * (size_t)n);
+    if (dbl) {
+        CHECK_HIP(hipFree(master2[1]));
+        CHECK_HIP(hipFree(m2[1]));
+        CHECK_HIP(hipFree(v2[1]));
+        CHECK_HIP(hipFree(p16_2[1]));
+    }
 
     CHECK_HIP(hipFree(master));
     CHECK_HIP(hipFree(m));

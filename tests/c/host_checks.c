@@ -83,6 +83,42 @@ static void validation(void)
     EXPECT(ds_adam_bias_scalars(ST, 1e-4f, 0.9f, 1.5f, (float*)A, NULL) == DS_ERR_HPARAM);
     ds_lr_schedule good = {DS_LR_WARMUP_DECAY, 0, 2000, 100000, 0.0f, 3e-4f};
     EXPECT(ds_lr_scalars(ST, &good, 0.9f, 0.999f, (float*)((char*)ST + 8), NULL) == DS_ERR_ALIAS);
+    /* the double-buffered step: two copies of every state array, each rejected path */
+    float* c_master[2] = {(float*)A, (float*)((char*)A + 0x100000)};
+    float* c_m[2] = {(float*)B, (float*)((char*)B + 0x100000)};
+    float* c_v[2] = {(float*)C, (float*)((char*)C + 0x100000)};
+    uint16_t* c_p16[2] = {(uint16_t*)D, (uint16_t*)((char*)D + 0x100000)};
+    float* c_null[2] = {(float*)B, NULL};
+    float* c_odd[2] = {(float*)A, (float*)((char*)A + 0x100004)};
+    float* c_alias[2] = {(float*)B, (float*)((char*)A + 16)};   /* inside master copy 0 */
+    EXPECT(ds_adam_step_double_buffered(ST, c_master, c_m, c_v, c_p16, DS_FP16, E, DS_FP16, -1, 1e-4f, NULL, 0.9f,
+                                        0.999f, 1e-8f, 0.0f, 1, NULL) == DS_ERR_SIZE);
+    EXPECT(ds_adam_step_double_buffered(ST, c_master, c_m, c_v, c_p16, DS_FP16, E, DS_FP16, INT64_MAX, 1e-4f, NULL,
+                                        0.9f, 0.999f, 1e-8f, 0.0f, 1, NULL) == DS_ERR_SIZE);
+    EXPECT(ds_adam_step_double_buffered(ST, c_master, c_m, c_v, c_p16, DS_FP32, E, DS_FP16, 8, 1e-4f, NULL, 0.9f,
+                                        0.999f, 1e-8f, 0.0f, 1, NULL) == DS_ERR_DTYPE);
+    EXPECT(ds_adam_step_double_buffered(ST, c_master, c_m, c_v, c_p16, DS_FP16, E, DS_FP16, 8, 1e-4f, NULL, 1.0f,
+                                        0.999f, 1e-8f, 0.0f, 1, NULL) == DS_ERR_HPARAM);
+    EXPECT(ds_adam_step_double_buffered(ST, c_master, c_m, c_v, c_p16, DS_FP16, E, DS_FP16, 8, 1e-4f, &bad, 0.9f,
+                                        0.999f, 1e-8f, 0.0f, 1, NULL) == DS_ERR_HPARAM);
+    EXPECT(ds_adam_step_double_buffered(NULL, c_master, c_m, c_v, c_p16, DS_FP16, E, DS_FP16, 8, 1e-4f, NULL, 0.9f,
+                                        0.999f, 1e-8f, 0.0f, 1, NULL) == DS_ERR_NULL);
+    EXPECT(ds_adam_step_double_buffered(ST, c_master, NULL, c_v, c_p16, DS_FP16, E, DS_FP16, 8, 1e-4f, NULL, 0.9f,
+                                        0.999f, 1e-8f, 0.0f, 1, NULL) == DS_ERR_NULL);
+    EXPECT(ds_adam_step_double_buffered(ST, c_master, c_null, c_v, c_p16, DS_FP16, E, DS_FP16, 8, 1e-4f, NULL, 0.9f,
+                                        0.999f, 1e-8f, 0.0f, 1, NULL) == DS_ERR_NULL);
+    EXPECT(ds_adam_step_double_buffered(ST, c_odd, c_m, c_v, c_p16, DS_FP16, E, DS_FP16, 8, 1e-4f, NULL, 0.9f,
+                                        0.999f, 1e-8f, 0.0f, 1, NULL) == DS_ERR_ALIGN);
+    EXPECT(ds_adam_step_double_buffered(ST, c_master, c_alias, c_v, c_p16, DS_FP16, E, DS_FP16, 8, 1e-4f, NULL,
+                                        0.9f, 0.999f, 1e-8f, 0.0f, 1, NULL) == DS_ERR_ALIAS);
+    EXPECT(ds_adam_step_double_buffered(ST, c_master, c_m, c_v, c_p16, DS_FP16, (char*)A + 0x100000 + 16,
+                                        DS_FP16, 8, 1e-4f, NULL, 0.9f, 0.999f, 1e-8f, 0.0f, 1, NULL) == DS_ERR_ALIAS);
+    /* the allocation-free check: every rejection comes before the scratch array is looked up */
+    EXPECT(ds_check_overflow_sumsq_noalloc(ST, E, DS_FP16, DS_NOALLOC_MAX_ELEMS + 1, NULL) == DS_ERR_SIZE);
+    EXPECT(ds_check_overflow_sumsq_noalloc(ST, E, (ds_dtype)9, 8, NULL) == DS_ERR_DTYPE);
+    EXPECT(ds_check_overflow_sumsq_noalloc(NULL, E, DS_FP16, 8, NULL) == DS_ERR_NULL);
+    EXPECT(ds_check_overflow_sumsq_noalloc(ST, (char*)E + 8, DS_FP16, 8, NULL) == DS_ERR_ALIGN);
+    EXPECT(ds_check_overflow_sumsq_noalloc(ST, (void*)ST, DS_FP16, 8, NULL) == DS_ERR_ALIAS);
     for (int s = -2; s < 10; ++s)
         EXPECT(ds_status_string((ds_status)s) != NULL && strlen(ds_status_string((ds_status)s)) > 0);
     EXPECT(ds_scaler_size() == 128);

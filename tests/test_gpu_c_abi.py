@@ -18,9 +18,12 @@ pytestmark = pytest.mark.gpu
 DRIVER = os.path.join(os.path.dirname(os.path.abspath(__file__)), "c", "abi_driver")
 
 
-@pytest.mark.parametrize("n,K,wd,clip", [(4099, 1, 0.0, 0.0), (20_003, 3, 0.01, 0.0), (65_541, 1, 0.0, 1.0),
-                                         (10_007, 2, 0.0, 1.0)])
-def test_c_program_matches_oracle(tmp_path, n, K, wd, clip):
+@pytest.mark.parametrize("n,K,wd,clip,double", [(4099, 1, 0.0, 0.0, 0), (20_003, 3, 0.01, 0.0, 0),
+                                                (65_541, 1, 0.0, 1.0, 0), (10_007, 2, 0.0, 1.0, 0),
+                                                (30_011, 1, 0.01, 0.0, 1), (8_195, 2, 0.0, 0.0, 1)])
+def test_c_program_matches_oracle(tmp_path, n, K, wd, clip, double):
+    """double = 1: ds_adam_step_double_buffered over two hipMalloc'd copies of
+    the state; the driver writes out the copy that the state names current."""
     if not os.path.exists(DRIVER):
         pytest.fail(f"{DRIVER} is not built: run __graft_entry__.build()")
     steps, scale, window = 5, 2.0 ** 12, 2
@@ -33,10 +36,10 @@ def test_c_program_matches_oracle(tmp_path, n, K, wd, clip):
             grads[s, k] = synth.host_grad16(synth.stream_key(601, synth.ARR_GRAD, s, k), idx, spec)
     grads[2, K - 1, n // 2] = 0x7C00                    # one overflowed step
     (tmp_path / "params.txt").write_text(
-        f"{n} {K} {steps} {scale!r} {window} {LR!r} {BETA1!r} {BETA2!r} {EPS!r} {wd!r} {clip!r}\n")
+        f"{n} {K} {steps} {scale!r} {window} {LR!r} {BETA1!r} {BETA2!r} {EPS!r} {wd!r} {clip!r} {double}\n")
     master.tofile(tmp_path / "master.bin")
     grads.tofile(tmp_path / "grads.bin")
-    gu.say(f"[c-abi] n={n} K={K} wd={wd} clip={clip}")
+    gu.say(f"[c-abi] n={n} K={K} wd={wd} clip={clip} double={double}")
     r = subprocess.run([DRIVER, str(tmp_path)], capture_output=True, text=True, timeout=120)
     assert r.returncode == 0, r.stdout + r.stderr
     assert "rejected as expected" in r.stdout
@@ -53,5 +56,7 @@ def test_c_program_matches_oracle(tmp_path, n, K, wd, clip):
         assert (int(applied), int(it), int(skipped)) == (o.scaler.applied, o.scaler.s.iters, o.scaler.s.skipped)
     got = [np.fromfile(tmp_path / f, dtype=dt) for f, dt in (("master_out.bin", np.float32), ("m_out.bin", np.float32),
                                                               ("v_out.bin", np.float32), ("p16_out.bin", np.uint16))]
+    if double:   # 4 of the 5 steps applied: copy 0 holds the state again
+        assert "current copy: 0" in r.stdout, r.stdout
     du = gu.compare_arrays(f"c-abi n={n} K={K}", *got, o.master, o.m, o.v, o.p16)
     gu.say(f"[c-abi] n={n} K={K}: max ulp {du}")

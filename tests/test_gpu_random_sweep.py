@@ -8,7 +8,10 @@ floor), Adam's hyperparameters (including beta 0 and weight decay), a
 constant learning rate or a WarmupLR / WarmupDecayLR schedule, clipping (off,
 active or never reached), the fused or the separate scaler update, one
 accumulation pass per micro-batch or folds of several (ds_accumulate_multi),
-and non-finite values planted in random steps, micro-batches and positions.  The
+without clipping the double-buffered step (ds_adam_step_double_buffered, the
+check inside the Adam pass, two copies of the state) in place of the check and
+the in-place update, and non-finite values planted in random steps,
+micro-batches and positions.  The
 device runs the step through the C ABI; the oracle runs the same steps.
 
 Bar: scaler state exact after every step; without clipping every array
@@ -81,6 +84,9 @@ def draw_case(seed):
         c["groups"] = [list(range(0, cut)), list(range(cut, c["K"]))] if cut < c["K"] else [list(range(c["K"]))]
     else:
         c["groups"] = None
+    # also drawn apart: the double-buffered step (only without clipping)
+    rd = np.random.default_rng(9_000_011 * seed + 3)
+    c["double"] = c["clip"] == 0.0 and bool(rd.random() < 0.5)
     return c
 
 
@@ -106,6 +112,9 @@ def test_random_configuration(torch, seed):
     v = torch.zeros(max(n, 1), device=dev)
     p16 = torch.zeros(max(n, 1), dtype=torch.int16, device=dev)
     acc = torch.empty(max(n, 1), device=dev) if K > 1 else None
+    # the double-buffered step's second copy (it holds no state yet)
+    copy1 = ([torch.empty(max(n, 1), device=dev) for _ in range(3)] +
+             [torch.empty(max(n, 1), dtype=torch.int16, device=dev)]) if c["double"] else None
     st = torch.zeros(_lib.ds_scaler_size(), dtype=torch.uint8, device=dev)
     ws = torch.zeros(max(1, (_lib.ds_sumsq_workspace_bytes(n) + 7) // 8), dtype=torch.float64, device=dev)
     _lib.ds_state_init(st, c["scale"], c["min_scale"], c["window"], c["hyst"], int(c["consec"]), int(c["dynamic"]))
@@ -128,7 +137,9 @@ def test_random_configuration(torch, seed):
         ov = oracle.step(o, hg if K > 1 else hg[0], lr=lr_o, beta1=c["b1"], beta2=c["b2"], eps=c["eps"],
                          weight_decay=c["wd"], max_grad_norm=clip, fmt=fmt)
         gs = [gu.dev_u16(torch, g) if n > 0 else torch.zeros(1, dtype=torch.int16, device=dev) for g in hg]
-        if K == 1:
+        if K == 1 and c["double"]:   # the check runs inside the double-buffered pass
+            grad, dt = gs[0], dt16
+        elif K == 1:
             if clip > 0:
                 _lib.ds_check_overflow_sumsq(st, gs[0], dt16, n, ws)
             else:
@@ -154,7 +165,11 @@ def test_random_configuration(torch, seed):
             grad, dt = acc, _lib.DS_FP32
         args = (master, m, v, p16, dt16, grad, dt, n)
         tail = (c["b1"], c["b2"], c["eps"], c["wd"], clip, K)
-        if c["fused"]:
+        if c["double"]:
+            _lib.ds_adam_step_double_buffered(st, [master, copy1[0]], [m, copy1[1]], [v, copy1[2]],
+                                              [p16, copy1[3]], dt16, grad, dt, n, lr, sched, c["b1"], c["b2"],
+                                              c["eps"], c["wd"], K)
+        elif c["fused"]:
             _lib.ds_adam_step_fused(st, *args, lr, sched, *tail)
         else:
             if sched is not None:
@@ -163,9 +178,14 @@ def test_random_configuration(torch, seed):
                 _lib.ds_adam_step(st, *args, lr, *tail)
             _lib.ds_update_loss_scale(st)
         ctx = f"[sweep {seed}] step {s}"
-        gu.check_scaler(_lib.ds_state_read(st), o.scaler, ov, ctx)
+        got = _lib.ds_state_read(st)
+        gu.check_scaler(got, o.scaler, ov, ctx)
+        cur = (master, m, v, p16)
+        if c["double"]:
+            assert got.current == o.scaler.applied % 2 and got.db_tickets == 0, ctx
+            cur = cur if got.current == 0 else tuple(copy1)
         if n > 0:
-            du = gu.compare_arrays(ctx, gu.host_f32(master), gu.host_f32(m[:n]), gu.host_f32(v[:n]),
-                                   gu.host_u16(p16[:n]), o.master, o.m, o.v, o.p16)
+            du = gu.compare_arrays(ctx, gu.host_f32(cur[0][:n]), gu.host_f32(cur[1][:n]), gu.host_f32(cur[2][:n]),
+                                   gu.host_u16(cur[3][:n]), o.master, o.m, o.v, o.p16)
             if clip == 0.0:
                 assert max(du.values()) == 0, f"{ctx}: {du}"
