@@ -89,6 +89,13 @@ def load_traffic(workload: str, half: str, kernel: str):
     return None
 
 
+def fold_bytes(sizes) -> int:
+    """Algorithmic bytes per element of the accumulation passes over groups of
+    micro-batches of these sizes: 2f + 4 for the first (it overwrites the
+    running sum), 2f + 8 for each later one (it reads and writes it)."""
+    return sum(2 * f + (4 if i == 0 else 8) for i, f in enumerate(sizes))
+
+
 # ----------------------------------------------------------------------------
 # GPU leg
 # ----------------------------------------------------------------------------
@@ -118,7 +125,6 @@ def gpu_run(args):
     v = torch.zeros(n, dtype=torch.float32, device=dev)
     p16 = torch.empty(n, dtype=torch.int16, device=dev)
     synth.device_fill_grad16(torch, tabs, p16, w.p16_key(), synth.GradSpec(0.02, 1.0))
-    acc = torch.empty(n, dtype=torch.float32, device=dev) if K > 1 else None
     st = torch.zeros(_lib.ds_scaler_size(), dtype=torch.uint8, device=dev)
     if args.bf16:
         _lib.ds_state_init(st, 1.0, 1.0, w.window, w.hysteresis, 0, 0)
@@ -128,42 +134,50 @@ def gpu_run(args):
         buckets = [(b.start, b.size) for b in FlatLayout(ragged_numels()).buckets]
     else:
         buckets = [(0, n)]
-    # double-buffered step (K = 1, no clipping): a second copy of master, m, v and
-    # the 16-bit copy; the overflow check is fused into the Adam pass.  "auto"
-    # takes it where it applies, where the gradient is larger than the 256 MB
-    # Infinity Cache (a smaller one is still cached when the in-place form's
-    # Adam pass reads it again after the check, which makes that form as fast)
-    # and where the second copy leaves room for a gradient buffer
+    if not 1 <= args.fold <= 8:
+        sys.exit("bench.py: --fold takes 1..8")
+    fold = min(args.fold, K)
+    # resident gradient buffers, a ring of distinct draws (a real step rewrites one
+    # contiguous gradient buffer): at least 2 GiB of them (far beyond the 256 MB
+    # Infinity Cache), and never fewer than one fold holds
+    total_mb = (args.steps + args.warmup) * K
+    enough = min(max(2, -(-(2 << 30) // (2 * n)), fold), total_mb, args.max_grad_buffers)
+    headroom = 4 << 30
+
+    # double-buffered step (no clipping): a second copy of master, m, v and the
+    # 16-bit copy; the overflow check is fused into the Adam pass, and with K > 1
+    # so is the accumulation of the last micro-batch (or of the last fold).
+    # "auto" takes it where it applies, where (K = 1) the gradient is larger than
+    # the 256 MB Infinity Cache (a smaller one is still cached when the in-place
+    # form's Adam pass reads it again after the check, which makes that form as
+    # fast), and where the second copy leaves room for the gradient buffers and
+    # the running sum the step needs
     double = False
     copy1 = None
-    applies = K == 1 and args.clip == 0
+    applies = args.clip == 0
     if args.step_form == "double" and not applies:
-        log("bench.py: the double-buffered step applies to K = 1 workloads without clipping; using the in-place form")
-    if applies and (args.step_form == "double" or (args.step_form == "auto" and 2 * n > INFINITY_CACHE_BYTES)):
+        log("bench.py: the double-buffered step takes no clipping; using the in-place form")
+    wanted = args.step_form == "double" or (args.step_form == "auto" and (K > 1 or 2 * n > INFINITY_CACHE_BYTES))
+    if applies and wanted:
+        need = enough * 2 * n + (4 * n if fold < K else 0) + headroom
         try:
             copy1 = [torch.empty(n, dtype=torch.float32, device=dev) for _ in range(3)] + \
                     [torch.empty(n, dtype=torch.int16, device=dev)]
-            if torch.cuda.mem_get_info(dev)[0] < 2 * n + (4 << 30):
-                raise torch.cuda.OutOfMemoryError("no room for a gradient buffer beside two copies")
+            if torch.cuda.mem_get_info(dev)[0] < need:
+                raise torch.cuda.OutOfMemoryError("no room for the gradient buffers beside two copies")
             double = True
         except torch.cuda.OutOfMemoryError as e:
             copy1 = None
             torch.cuda.empty_cache()
             log(f"bench.py: two copies of the state do not fit ({str(e).splitlines()[0][:120]}); "
                 "using the in-place form")
+    # the fp32 running sum of the micro-batches (not needed when the last fold
+    # of the double-buffered form takes all of them)
+    acc = torch.empty(n, dtype=torch.float32, device=dev) if K > 1 and not (double and fold >= K) else None
 
-    # resident gradient buffers, a ring of distinct draws (a real step rewrites one
-    # contiguous gradient buffer; the ring is larger than the 256 MB Infinity Cache)
-    total_mb = (args.steps + args.warmup) * K
     free = torch.cuda.mem_get_info(dev)[0]
-    fit = max(1, int((free - (4 << 30)) // (2 * n)))
-    # a ring of at least 2 GiB of gradients (far beyond the 256 MB Infinity
-    # Cache), and never fewer buffers than one fold holds
-    enough = max(2, -(-(2 << 30) // (2 * n)), args.fold)
-    nbuf = max(1, min(total_mb, fit, args.max_grad_buffers, enough))
-    if not 1 <= args.fold <= 8:
-        sys.exit("bench.py: --fold takes 1..8")
-    fold = min(args.fold, K)
+    fit = max(1, int((free - headroom) // (2 * n)))
+    nbuf = max(1, min(fit, enough))
     if fold > nbuf:
         sys.exit(f"bench.py: --fold {fold} needs {fold} gradient buffers at once; {nbuf} fit")
     grads = []
@@ -173,7 +187,8 @@ def gpu_run(args):
         synth.device_fill_grad16(torch, tabs, g, w.grad_key(s + 1, k), gspec)
         grads.append(g)
     torch.cuda.synchronize()
-    log(f"workload {w.name}: psi={n} K={K} grad buffers={nbuf} (of {total_mb} micro-batches)")
+    log(f"workload {w.name}: psi={n} K={K} grad buffers={nbuf} (of {total_mb} micro-batches) "
+        f"step form={'double-buffered' if double else 'in place'}")
 
     hp = (LR, BETA1, BETA2, EPS, WD, args.clip)
     ws = None
@@ -194,6 +209,8 @@ def gpu_run(args):
         copies = (ip[:], [t.data_ptr() for t in copy1])
         db_arrays = tuple(V2(copies[0][k], copies[1][k]) for k in range(4))
         db_step = _lib.lib.ds_adam_step_double_buffered
+        db_fold = _lib.lib.ds_accumulate_adam_double_buffered
+        db_update = _lib.lib.ds_update_loss_scale_double_buffered
     acc_p = acc.data_ptr() if acc is not None else None
     ws_p, ws_bytes = (ws.data_ptr(), ws.numel() * 8) if ws is not None else (None, 0)
     grad_p = [g.data_ptr() for g in grads]
@@ -206,9 +223,21 @@ def gpu_run(args):
             s0 = torch.cuda.Event(enable_timing=True)
             s0.record(q)
         base = i * K
-        if dbl:
+        if dbl and K == 1:
             g = grad_p[base % nbuf]
             gptr, dt = g, gdt16
+        elif dbl:   # every fold but the last into the running sum; the last goes into the Adam pass
+            groups = [list(range(g0, min(g0 + fold, K))) for g0 in range(0, K, fold)]
+            for gi, grp in enumerate(groups[:-1]):
+                for start, size in buckets:
+                    gp = [grad_p[(base + k) % nbuf] + 2 * start for k in grp]
+                    if len(gp) == 1:
+                        _lib.ds_accumulate(acc_p + 4 * start, gp[0], gdt16, size, gi == 0, None, q)
+                    else:
+                        _lib.ds_accumulate_multi(acc_p + 4 * start, gp, gdt16, size, gi == 0, None, None, 0,
+                                                 stream=q)
+            last = (ctypes.c_void_p * len(groups[-1]))(*[grad_p[(base + k) % nbuf] for k in groups[-1]])
+            last_acc = acc_p if len(groups) > 1 else None
         elif K == 1:
             g = grad_p[base % nbuf]
             if ws is None:
@@ -242,10 +271,18 @@ def gpu_run(args):
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a.record(q)
         # the Adam kernel also advances the loss scaler (one launch for both)
-        if dbl:   # and performs the overflow check, writing the other copy
+        if dbl and K == 1:   # and performs the overflow check, writing the other copy
             rc = db_step(st_p, *db_arrays, gdt16, gptr, dt, n, hp[0], None, *hp[1:5], K, q.cuda_stream)
             if rc != 0:
                 raise RuntimeError(f"ds_adam_step_double_buffered: {_lib.ds_status_string(rc)}")
+        elif dbl:            # the last fold, the check and Adam into the other copy; then the scaler
+            rc = db_fold(st_p, *db_arrays, gdt16, last_acc, last, len(last), gdt16, n, hp[0], None, *hp[1:5], K,
+                         q.cuda_stream)
+            if rc != 0:
+                raise RuntimeError(f"ds_accumulate_adam_double_buffered: {_lib.ds_status_string(rc)}")
+            rc = db_update(st_p, q.cuda_stream)
+            if rc != 0:
+                raise RuntimeError(f"ds_update_loss_scale_double_buffered: {_lib.ds_status_string(rc)}")
         else:
             _lib.ds_adam_step_fused(st_p, *ip, gdt16, gptr, dt, n, hp[0], None, *hp[1:], K, q)
         if timed:
@@ -313,8 +350,20 @@ def gpu_run(args):
     # with two copies, the in-place form (check, then the in-place Adam pass) on
     # the copy that holds the state, timed the same way after the rest
     in_place = None
+    groups_sizes = [min(fold, K - g0) for g0 in range(0, K, fold)]
+    ip_step_bytes = 30 if K == 1 else fold_bytes(groups_sizes) + 30
     if double:
-        ip[:] = copies[_lib.ds_state_read(st, stream).current]
+        # keep the copy that holds the state; the in-place form updates it (and,
+        # with K > 1, needs the running sum, which may take the other copy's room)
+        cur = _lib.ds_state_read(st, stream).current
+        keep = (master, m, v, p16) if cur == 0 else tuple(copy1)
+        master, m, v, p16 = keep
+        copy1 = keep = None
+        torch.cuda.empty_cache()
+        if K > 1 and acc is None:
+            acc = torch.empty(n, dtype=torch.float32, device=dev)
+            acc_p = acc.data_ptr()
+        ip[:] = [t.data_ptr() for t in (master, m, v, p16)]
         ip_ev = []
         for i in range(args.warmup):
             one_step(i, False, form="in_place")
@@ -325,17 +374,20 @@ def gpu_run(args):
         torch.cuda.synchronize()
         ip_wall = time.perf_counter() - t0
         ip_adam_s = sum(a.elapsed_time(b) for a, b in ip_ev) / len(ip_ev) / 1e3
+        ip_bpe = 28 if K == 1 else 30
         in_place = {
-            "step_form": "check, then the in-place Adam pass (one copy of the state)",
+            "step_form": ("check, then the in-place Adam pass" if K == 1 else
+                          "accumulation with the fused check, then the in-place Adam pass") + " (one copy of the state)",
             "value": round(n * args.steps / ip_wall / 1e9, 3),
             "ms_per_step": round(ip_wall / args.steps * 1e3, 4),
             "kernel": "adam_kernel",
             "avg_launch_ms": round(ip_adam_s * 1e3, 4),
-            "achieved": round(28 * n / ip_adam_s / 1e9, 1),
-            "frac": round(28 * n / ip_adam_s / 1e9 / PEAK_HBM_GBS, 4),
+            "achieved": round(ip_bpe * n / ip_adam_s / 1e9, 1),
+            "frac": round(ip_bpe * n / ip_adam_s / 1e9 / PEAK_HBM_GBS, 4),
             "traffic": load_traffic(w.name, "bf16" if args.bf16 else "fp16", "adam_kernel"),
-            "step": {"bytes_per_elem": 30, "achieved": round(30 * n * args.steps / ip_wall / 1e9, 1),
-                     "frac": round(30 * n * args.steps / ip_wall / 1e9 / PEAK_HBM_GBS, 4)},
+            "step": {"bytes_per_elem": ip_step_bytes,
+                     "achieved": round(ip_step_bytes * n * args.steps / ip_wall / 1e9, 1),
+                     "frac": round(ip_step_bytes * n * args.steps / ip_wall / 1e9 / PEAK_HBM_GBS, 4)},
         }
 
     adam_ms = [a.elapsed_time(b) for a, b in ev]
@@ -369,16 +421,20 @@ def gpu_run(args):
     copy_s = timed(lambda: synth.device_copy(torch, m[:nm], master[:nm], stream=stream), 8)
     memcpy_s = timed(lambda: m[:nm].copy_(master[:nm]), 8)
     copy_gbs, memcpy_gbs = 8 * nm / copy_s / 1e9, 8 * nm / memcpy_s / 1e9
-    bytes_per_elem = 28 if K == 1 else 30
+    if double and K > 1:   # the last fold with the Adam pass: its gradients, the running sum if any, the state
+        last = groups_sizes[-1]
+        bytes_per_elem = 2 * last + (30 if len(groups_sizes) > 1 else 26)
+        step_bytes = fold_bytes(groups_sizes[:-1]) + bytes_per_elem
+        kernel = "fold_adam_db_kernel"
+    elif double:
+        bytes_per_elem = step_bytes = 28
+        kernel = "adam_db_kernel"
+    else:
+        bytes_per_elem = 28 if K == 1 else 30
+        step_bytes = ip_step_bytes
+        kernel = "adam_kernel"
     achieved = bytes_per_elem * n / adam_avg_s / 1e9
-    if double:
-        step_bytes = 28
-    elif K == 1:
-        step_bytes = 2 + 28
-    else:   # each fold of f micro-batches: 2f + 4 bytes (the first, overwriting) or 2f + 8, then Adam's 30
-        sizes = [min(fold, K - g0) for g0 in range(0, K, fold)]
-        step_bytes = sum(2 * f + (4 if i == 0 else 8) for i, f in enumerate(sizes)) + 30
-    traffic = load_traffic(w.name, "bf16" if args.bf16 else "fp16", "adam_db_kernel" if double else "adam_kernel")
+    traffic = load_traffic(w.name, "bf16" if args.bf16 else "fp16", kernel)
     out = {
         "metric": METRIC,
         "value": round(n * args.steps / wall / 1e9, 3),
@@ -408,13 +464,15 @@ def gpu_run(args):
             "gradient_clipping": args.clip,
             "half": "bf16" if args.bf16 else "fp16",
             "step_form": ("double-buffered: the overflow check fused into the Adam pass, which writes the "
-                          "second copy of the state" if double else
+                          "second copy of the state" if double and K == 1 else
+                          "double-buffered: the earlier micro-batches accumulated, the last fold summed, checked "
+                          "and fed to the Adam pass, which writes the second copy of the state" if double else
                           "check (or accumulation with the fused check), then the in-place Adam pass"),
             "parallelism": "one GPU's ZeRO partition",
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": "adam_db_kernel" if double else "adam_kernel",
+            "kernel": kernel,
             "achieved": round(achieved, 1),
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",

@@ -302,6 +302,55 @@ ds_status ds_adam_step_double_buffered(ds_scaler* st, float* const* master2, flo
                                        void* stream);
 
 /*
+ * The last micro-batches of a step folded into the double-buffered Adam pass
+ * ([Guide] section 4.3 gradient accumulation, [Overview] gradient
+ * accumulation; [Guide] section 4.2 dynamic loss scaling, section 5.1
+ * step()).  The gradient of element i is the fp32 sum, in micro-batch order,
+ * of acc_or_null[i] (the running sum of the step's earlier micro-batches as
+ * ds_accumulate / ds_accumulate_multi leave it; NULL when grads are all of the
+ * step's micro-batches, the first of them then starting the sum) and of
+ * grads[0][i] .. grads[count-1][i]: the sum ds_accumulate would have formed,
+ * which is used, not stored.  The pass ORs "some sum is +-inf or NaN" into
+ * st->overflow and writes the Adam update of every element of [0, n) (the
+ * arithmetic of ds_adam_step with that sum as the fp32 gradient) into the copy
+ * of master, m, v and the 16-bit copy that does not hold the state
+ * (st->current names the one that does); nothing else in st changes.  Call it
+ * once for the partition, or once per bucket (disjoint ranges, each with its
+ * own offsets into every array), then ds_update_loss_scale_double_buffered
+ * exactly once.  The step's earlier micro-batches go through ds_accumulate
+ * (with st_or_null NULL or not: a flag raised there also skips the step).
+ * Bytes per element: 2 * count + 30 with the running sum (read only), 2 *
+ * count + 26 without, against 2 * count + 8 (or + 4) for the fold and 30 for
+ * the Adam pass done separately.  No gradient clipping (it needs the whole
+ * gradient's norm before the update).
+ * master2, m2, v2, p16_2, pdt, lr / sched_or_null, betas, eps, weight_decay,
+ * accum_steps (K, the unscale divisor), stream: as for
+ * ds_adam_step_double_buffered.  grads: HOST array of count (1-8) DEVICE
+ * pointers to 16-bit[n] of format gdt (fp16 or bf16); they may repeat but
+ * must not overlap acc, st or the eight state arrays, which must not overlap
+ * one another.  acc_or_null: DEVICE fp32[n] or NULL.
+ * Errors: count outside 1..8 -> DS_ERR_SIZE; gdt or pdt not a 16-bit format ->
+ * DS_ERR_DTYPE; acc_or_null NULL with count != accum_steps, or non-NULL with
+ * count >= accum_steps -> DS_ERR_HPARAM; otherwise as for
+ * ds_adam_step_double_buffered.  With n == 0 nothing is launched.
+ */
+ds_status ds_accumulate_adam_double_buffered(ds_scaler* st, float* const* master2, float* const* m2,
+                                             float* const* v2, uint16_t* const* p16_2, ds_dtype pdt,
+                                             const float* acc_or_null, const uint16_t* const* grads, int32_t count,
+                                             ds_dtype gdt, int64_t n, float lr, const ds_lr_schedule* sched_or_null,
+                                             float beta1, float beta2, float eps, float weight_decay,
+                                             int32_t accum_steps, void* stream);
+
+/*
+ * End of a double-buffered step taken with ds_accumulate_adam_double_buffered
+ * ([Guide] section 4.2): advance the scaler by the step's flag as
+ * ds_update_loss_scale does and, if the step applied (no overflow), make the
+ * other copy current (st->current ^= 1).  Call exactly once per step.
+ * Errors: st NULL -> DS_ERR_NULL; st not 8-byte aligned -> DS_ERR_ALIGN.
+ */
+ds_status ds_update_loss_scale_double_buffered(ds_scaler* st, void* stream);
+
+/*
  * End of a step: advance the scaler by the step's overflow flag, then clear
  * the flag ([Guide] section 4.2).  Overflow: skipped += 1, growth_count = 0;
  * if dynamic, one more overflow is charged to the hysteresis and, when it is

@@ -113,6 +113,27 @@ static void validation(void)
                                         0.9f, 0.999f, 1e-8f, 0.0f, 1, NULL) == DS_ERR_ALIAS);
     EXPECT(ds_adam_step_double_buffered(ST, c_master, c_m, c_v, c_p16, DS_FP16, (char*)A + 0x100000 + 16,
                                         DS_FP16, 8, 1e-4f, NULL, 0.9f, 0.999f, 1e-8f, 0.0f, 1, NULL) == DS_ERR_ALIAS);
+    /* the last micro-batches folded into the double-buffered pass, and its scaler update */
+    const uint16_t* g1[1] = {(const uint16_t*)E};
+    const uint16_t* g8[8] = {(const uint16_t*)E, (const uint16_t*)E, (const uint16_t*)E, (const uint16_t*)E,
+                             (const uint16_t*)E, (const uint16_t*)E, (const uint16_t*)E, (const uint16_t*)E};
+    const float* sum = (const float*)((char*)E + 0x100000);
+    EXPECT(ds_accumulate_adam_double_buffered(ST, c_master, c_m, c_v, c_p16, DS_FP16, sum, g1, 0, DS_FP16, 8, 1e-4f,
+                                              NULL, 0.9f, 0.999f, 1e-8f, 0.0f, 8, NULL) == DS_ERR_SIZE);
+    EXPECT(ds_accumulate_adam_double_buffered(ST, c_master, c_m, c_v, c_p16, DS_FP16, sum, g1, 1, DS_FP32, 8, 1e-4f,
+                                              NULL, 0.9f, 0.999f, 1e-8f, 0.0f, 8, NULL) == DS_ERR_DTYPE);
+    EXPECT(ds_accumulate_adam_double_buffered(ST, c_master, c_m, c_v, c_p16, DS_FP16, NULL, g1, 1, DS_FP16, 8, 1e-4f,
+                                              NULL, 0.9f, 0.999f, 1e-8f, 0.0f, 8, NULL) == DS_ERR_HPARAM);
+    EXPECT(ds_accumulate_adam_double_buffered(ST, c_master, c_m, c_v, c_p16, DS_FP16, sum, g8, 8, DS_FP16, 8, 1e-4f,
+                                              NULL, 0.9f, 0.999f, 1e-8f, 0.0f, 8, NULL) == DS_ERR_HPARAM);
+    EXPECT(ds_accumulate_adam_double_buffered(ST, c_master, c_null, c_v, c_p16, DS_FP16, sum, g1, 1, DS_FP16, 8,
+                                              1e-4f, NULL, 0.9f, 0.999f, 1e-8f, 0.0f, 8, NULL) == DS_ERR_NULL);
+    EXPECT(ds_accumulate_adam_double_buffered(ST, c_master, c_m, c_v, c_p16, DS_FP16, (const float*)((char*)A + 16),
+                                              g1, 1, DS_FP16, 8, 1e-4f, NULL, 0.9f, 0.999f, 1e-8f, 0.0f, 8,
+                                              NULL) == DS_ERR_ALIAS);
+    EXPECT(ds_accumulate_adam_double_buffered(ST, c_master, c_m, c_v, c_p16, DS_FP16, NULL, g8, 8, DS_FP16, 0, 1e-4f,
+                                              NULL, 0.9f, 0.999f, 1e-8f, 0.0f, 8, NULL) == DS_OK);
+    EXPECT(ds_update_loss_scale_double_buffered(NULL, NULL) == DS_ERR_NULL);
     /* the allocation-free check: every rejection comes before the scratch array is looked up */
     EXPECT(ds_check_overflow_sumsq_noalloc(ST, E, DS_FP16, DS_NOALLOC_MAX_ELEMS + 1, NULL) == DS_ERR_SIZE);
     EXPECT(ds_check_overflow_sumsq_noalloc(ST, E, (ds_dtype)9, 8, NULL) == DS_ERR_DTYPE);

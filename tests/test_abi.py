@@ -536,3 +536,56 @@ def test_double_buffered_step_validation():
                 (1e-4, None, 0.9, 0.999, 1e-8, 0.0, 0),
                 (1e-4, ctypes.byref(_lib.DsLrSchedule.make(7, 0.0, 1e-3, 1)), 0.9, 0.999, 1e-8, 0.0, 1)]:
         assert call(hp=bad) == DS_ERR_HPARAM, bad
+
+
+@fake_addresses
+def test_fold_into_double_buffered_step_validation():
+    """ds_accumulate_adam_double_buffered validates the eight state arrays, the
+    running sum, the gradient list (1 to 8, consistent with accum_steps) and the
+    state before any device work; ds_update_loss_scale_double_buffered checks
+    its state pointer."""
+    f = L.ds_accumulate_adam_double_buffered
+    V2 = ctypes.c_void_p * 2
+    n = 1000
+    base = [0x20000000 * k for k in range(1, 9)]
+    mst, mm, vv, pp = V2(base[0], base[1]), V2(base[2], base[3]), V2(base[4], base[5]), V2(base[6], base[7])
+    ACC, G = 0x20000000 * 9, 0x20000000 * 10
+    ok_hp = (1e-4, None, 0.9, 0.999, 1e-8, 0.0, 8)
+
+    def grads(*ptrs):
+        return (ctypes.c_void_p * max(len(ptrs), 1))(*ptrs), len(ptrs)
+
+    def call(st=ST, m2=mst, mo=mm, vo=vv, p2=pp, pdt=DS_FP16, acc=ACC, gl=None, gdt=DS_FP16, nn=n, hp=ok_hp):
+        lr, sched, b1, b2, eps, wd, K = hp
+        g, count = gl if gl is not None else grads(G)
+        return f(st, m2, mo, vo, p2, pdt, acc, g, count, gdt, nn, lr, sched, b1, b2, eps, wd, K, STREAM)
+
+    assert call(nn=-1) == DS_ERR_SIZE
+    assert call(nn=2 ** 40 + 1) == DS_ERR_SIZE
+    assert call(gl=grads()) == DS_ERR_SIZE                              # no gradient
+    assert call(gl=grads(*[G] * 9)) == DS_ERR_SIZE                      # more than 8
+    assert call(gdt=DS_FP32) == DS_ERR_DTYPE
+    assert call(pdt=9) == DS_ERR_DTYPE
+    assert call(acc=None) == DS_ERR_HPARAM                              # 1 gradient, no sum, K = 8
+    assert call(gl=grads(*[G] * 8)) == DS_ERR_HPARAM                    # a sum and all 8 gradients
+    assert call(st=None) == DS_ERR_NULL
+    assert call(m2=None) == DS_ERR_NULL
+    assert call(p2=V2(base[6], None)) == DS_ERR_NULL
+    assert call(gl=grads(None)) == DS_ERR_NULL
+    assert call(m2=V2(base[0] + 4, base[1])) == DS_ERR_ALIGN
+    assert call(acc=ACC + 8) == DS_ERR_ALIGN
+    assert call(gl=grads(G + 8)) == DS_ERR_ALIGN
+    assert call(st=ST + 4) == DS_ERR_ALIGN
+    assert call(m2=V2(base[0], base[0] + 64)) == DS_ERR_ALIAS           # the two copies overlap
+    assert call(acc=base[2] + 16) == DS_ERR_ALIAS                       # the sum inside an m copy
+    assert call(gl=grads(ACC + 32)) == DS_ERR_ALIAS                     # a gradient inside the sum
+    assert call(gl=grads(G, base[7] + 32)) == DS_ERR_ALIAS              # a gradient inside a p16 copy
+    assert call(st=ACC + 8) == DS_ERR_ALIAS                             # the state inside the sum
+    for bad in [(-1e-4, None, 0.9, 0.999, 1e-8, 0.0, 8), (1e-4, None, 1.0, 0.999, 1e-8, 0.0, 8),
+                (1e-4, None, 0.9, 0.999, 0.0, 0.0, 8), (1e-4, None, 0.9, 0.999, 1e-8, -1.0, 8),
+                (1e-4, None, 0.9, 0.999, 1e-8, 0.0, 0),
+                (1e-4, ctypes.byref(_lib.DsLrSchedule.make(7, 0.0, 1e-3, 1)), 0.9, 0.999, 1e-8, 0.0, 8)]:
+        assert call(hp=bad) == DS_ERR_HPARAM, bad
+    assert call(nn=0) == DS_OK                                          # nothing to do: no launch
+    assert L.ds_update_loss_scale_double_buffered(None, STREAM) == DS_ERR_NULL
+    assert L.ds_update_loss_scale_double_buffered(ST + 4, STREAM) == DS_ERR_ALIGN

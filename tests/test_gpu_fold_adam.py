@@ -1,0 +1,299 @@
+"""GPU parity of the step's last micro-batches folded into the double-buffered
+Adam pass (ds_accumulate_adam_double_buffered, then
+ds_update_loss_scale_double_buffered): "DeepSpeed complete guide" section 4.3
+(gradient accumulation: the micro-batch gradients summed before the step),
+section 2 (fp32 master and moments, 16-bit copy), section 4.2 (a non-finite
+gradient skips the step and backs the scale off).
+
+The earlier micro-batches go through ds_accumulate / ds_accumulate_multi into
+the fp32 running sum; the pass adds the last ones in order, tests the sum and
+writes the Adam update into the copy that does not hold the state; the update
+call advances the scaler and switches copies only if the step applied.
+Against the oracle (accumulate in order -> check -> Adam or skip -> scaler
+update): the current copy bit for bit after every step, its index, the
+scaler; every grouping of 8 micro-batches (all folded into the pass, one per
+pass, groups of 3, 3 and 2, ...), non-finite values in a folded micro-batch or
+an earlier one, flags raised by an earlier pass, ragged sizes, bucketed
+calls, formats, weight decay with a schedule, launch shapes, the same bits as
+the in-place path, and ShardStep(double_buffer=True) with K > 1.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from synth.workloads import BETA1, BETA2, EPS, LR, MASTER_SIGMA
+from tests import gpu_util as gu
+
+pytestmark = pytest.mark.gpu
+
+HP = dict(lr=LR, beta1=BETA1, beta2=BETA2, eps=EPS)
+
+
+@pytest.fixture(scope="module")
+def torch():
+    return gu.torch_mod()
+
+
+def _bits(a):
+    return np.ascontiguousarray(a).view(np.uint32 if a.dtype == np.float32 else np.uint16)
+
+
+class FoldDb:
+    """Two device copies of a partition's state, the fp32 running sum and a
+    ds_scaler; one step = the earlier groups of micro-batches accumulated, the
+    last group folded into the double-buffered pass, then the scaler update."""
+
+    def __init__(self, torch, master, *, init_scale, window, hysteresis=1, fmt="fp16", param_fmt="fp16"):
+        from zero_mixed_precision_amd import _lib
+        self.torch, self.L, self.n = torch, _lib, master.size
+        self.gdt = _lib.DS_BF16 if fmt == "bf16" else _lib.DS_FP16
+        self.pdt = _lib.DS_BF16 if param_fmt == "bf16" else _lib.DS_FP16
+        n1 = max(self.n, 1)
+        dev = "cuda:0"
+        self.master = [gu.dev_f32(torch, master) if self.n else torch.zeros(1, device=dev),
+                       torch.full((n1,), 7.0, device=dev)]
+        self.m = [torch.zeros(n1, device=dev), torch.full((n1,), 7.0, device=dev)]
+        self.v = [torch.zeros(n1, device=dev), torch.full((n1,), 7.0, device=dev)]
+        self.p16 = [torch.zeros(n1, dtype=torch.int16, device=dev),
+                    torch.full((n1,), 0x1234, dtype=torch.int16, device=dev)]
+        self.acc = torch.full((n1,), 3.0, device=dev)     # holds nothing until a step writes it
+        self.state = torch.zeros(_lib.ds_scaler_size(), dtype=torch.uint8, device=dev)
+        _lib.ds_state_init(self.state, init_scale, 1.0, window, hysteresis, 0, 1 if fmt == "fp16" else 0)
+
+    def step(self, grads, groups, *, lr=LR, sched=None, wd=0.0, buckets=None, early_check=False):
+        """grads: K device tensors; groups: lists of micro-batch indices in
+        order, the last one folded into the pass; buckets: (start, size) spans
+        each taken by its own calls; early_check: the last earlier pass also
+        checks (raising the flag before the fused pass)."""
+        L, n = self.L, self.n
+        K = len(grads)
+        spans = buckets or [(0, n)]
+        for gi, grp in enumerate(groups[:-1]):
+            first, last_early = gi == 0, gi == len(groups) - 2
+            st = self.state if (early_check and last_early) else None
+            for start, size in spans:
+                a = self.acc.data_ptr() + 4 * start
+                ptrs = [grads[k].data_ptr() + 2 * start for k in grp]
+                if len(grp) == 1:
+                    L.ds_accumulate(a, ptrs[0], self.gdt, size, first, st)
+                else:
+                    L.ds_accumulate_multi(a, ptrs, self.gdt, size, first, st)
+        last = groups[-1]
+        acc = None if len(groups) == 1 else self.acc
+        for start, size in spans:
+            def off(t, e):
+                return t.data_ptr() + e * start
+            L.ds_accumulate_adam_double_buffered(
+                self.state, [off(x, 4) for x in self.master], [off(x, 4) for x in self.m],
+                [off(x, 4) for x in self.v], [off(x, 2) for x in self.p16], self.pdt,
+                None if acc is None else off(acc, 4), [off(grads[k], 2) for k in last], self.gdt, size, lr, sched,
+                BETA1, BETA2, EPS, wd, K)
+        L.ds_update_loss_scale_double_buffered(self.state)
+
+    def scaler(self):
+        return self.L.ds_state_read(self.state)
+
+    def current(self):
+        c = self.scaler().current
+        assert c in (0, 1)
+        n = self.n
+        return (gu.host_f32(self.master[c][:n]), gu.host_f32(self.m[c][:n]), gu.host_f32(self.v[c][:n]),
+                gu.host_u16(self.p16[c][:n])), c
+
+
+NONFINITE = {"fp16": (0x7C00, 0xFC00, 0x7E01), "bf16": (0x7F80, 0xFF80, 0x7FC1)}
+
+
+def _run(torch, n, K, groups, steps, *, fmt="fp16", param_fmt="fp16", inject=None, scale=2.0 ** 12, window=1000,
+         wd=0.0, sched=None, buckets=None, early_check=False, seed=0):
+    """inject: {step: (micro-batch, which non-finite)}; returns (FoldDb, oracle state)."""
+    idx = np.arange(n)
+    master0 = synth.host_master32(synth.stream_key(1500 + seed, synth.ARR_MASTER), idx, MASTER_SIGMA)
+    o = oracle.State(master0.copy(), np.zeros(n, np.float32), np.zeros(n, np.float32), np.zeros(n, np.uint16),
+                     oracle.Scaler(scale, 1.0, window, 1, dynamic=fmt == "fp16"), param_fmt=param_fmt)
+    d = FoldDb(torch, master0, init_scale=scale, window=window, fmt=fmt, param_fmt=param_fmt)
+    dsched = None
+    if sched is not None:
+        from zero_mixed_precision_amd import _lib
+        dsched = _lib.DsLrSchedule.make(sched.kind, sched.min_lr, sched.max_lr, sched.warmup, sched.total)
+    spec = synth.GradSpec(1e-3, scale if fmt == "fp16" else 1.0, fmt=fmt)
+    inject = inject or {}
+    for s in range(steps):
+        hg = [synth.host_grad16(synth.stream_key(1600 + seed, synth.ARR_GRAD, s, k), idx, spec) for k in range(K)]
+        if s in inject and n:
+            k, which = inject[s]
+            hg[k][(s * 7919 + k) % n] = NONFINITE[fmt][which]
+        before, c0 = d.current()
+        gd = [gu.dev_u16(torch, g) if n else torch.zeros(8, dtype=torch.int16, device="cuda:0") for g in hg]
+        d.step(gd, groups, sched=dsched, wd=wd, buckets=buckets, early_check=early_check)
+        ov = oracle.step(o, hg, fmt=fmt, weight_decay=wd, **dict(HP, lr=sched if sched is not None else LR))
+        ctx = f"n={n} K={K} groups={groups} step {s}"
+        got = d.scaler()
+        gu.check_scaler(got, o.scaler, ov, ctx)
+        after, c1 = d.current()
+        assert c1 == (c0 if ov else 1 - c0), ctx
+        if ov:
+            for x, y in zip(before, after):
+                assert np.array_equal(_bits(x), _bits(y)), f"{ctx}: a skipped step changed the state"
+        for x, y in zip(after, (o.master, o.m, o.v, o.p16)):
+            assert np.array_equal(_bits(x), _bits(y)), f"{ctx}: state differs from the oracle"
+    return d, o
+
+
+@pytest.mark.parametrize("n", [0, 1, 3, 4, 5, 255, 1023, 1024, 1025, 4099, 70_003])
+def test_ragged_sizes_last_micro_batch_folded(torch, n):
+    _run(torch, n, 3, [[0], [1], [2]], 4, inject={1: (2, 0), 2: (0, 2)})
+
+
+GROUPINGS_8 = [
+    [list(range(8))],                                  # all eight folded into the pass, no running sum
+    [[0], [1], [2], [3], [4], [5], [6], [7]],          # one pass each, the last one folded
+    [[0, 1, 2], [3, 4, 5], [6, 7]],
+    [[0, 1, 2, 3], [4, 5, 6, 7]],
+    [list(range(7)), [7]],
+    [[0], list(range(1, 8))],
+]
+
+
+@pytest.mark.parametrize("groups", GROUPINGS_8, ids=["fold8", "singles", "3-3-2", "4-4", "7-1", "1-7"])
+def test_every_grouping_of_eight(torch, groups):
+    """Non-finite values in a folded micro-batch (step 1), in an earlier one
+    (step 3: micro-batch 0, accumulated before the pass unless all are folded)
+    and a NaN in the middle one (step 5)."""
+    _run(torch, 10_007, 8, groups, 7, inject={1: (7, 0), 3: (0, 1), 5: (4, 2)})
+
+
+def test_flag_raised_by_an_earlier_pass(torch):
+    """The last earlier accumulation also checks its sum (st passed): a non-finite
+    value there raises the flag before the fused pass, which then writes the
+    other copy but the update call keeps the current one."""
+    _run(torch, 20_000, 4, [[0, 1], [2], [3]], 5, inject={2: (1, 0)}, early_check=True)
+
+
+@pytest.mark.parametrize("fmt,param_fmt", [("bf16", "bf16"), ("fp16", "bf16"), ("bf16", "fp16")])
+def test_formats(torch, fmt, param_fmt):
+    _run(torch, 9_001, 3, [[0, 1], [2]], 5, fmt=fmt, param_fmt=param_fmt,
+         scale=1.0 if fmt == "bf16" else 2.0 ** 12, inject={2: (1, 0)})
+
+
+def test_weight_decay_schedule_and_growth(torch):
+    sched = oracle.LrSchedule(oracle.LR_WARMUP_DECAY, 1e-5, 3e-4, 3, 9)
+    d, o = _run(torch, 33_333, 2, [[0], [1]], 12, wd=0.01, sched=sched, window=3, inject={5: (0, 0)})
+    # growth after steps 2, 8 and 11 (three successes each), a halving at step 5
+    assert o.scaler.scale == 2.0 ** 14
+
+
+def test_bucketed_calls(torch):
+    """Each bucket of a ragged cut takes its own accumulation and fused calls
+    (offsets into every array); one scaler update ends the step."""
+    n = 50_000
+    cuts = [0, 8, 4096, 4104, 31_000, n]
+    buckets = [(a, b - a) for a, b in zip(cuts[:-1], cuts[1:])]
+    _run(torch, n, 3, [[0], [1, 2]], 5, buckets=buckets, inject={3: (2, 0)})
+
+
+def test_launch_shape_invariance(torch, monkeypatch):
+    n = 3 * 1024 + 517
+    ref = None
+    for env in [{}, {"DSZERO_GRID": "1"}, {"DSZERO_GRID": "3"}, {"DSZERO_GRID": "100000"}, {"DSZERO_NT": "1"},
+                {"DSZERO_NT": "1", "DSZERO_GRID": "2"}]:
+        for k in ("DSZERO_GRID", "DSZERO_NT"):
+            monkeypatch.delenv(k, raising=False)
+        for k, val in env.items():
+            monkeypatch.setenv(k, val)
+        d, _ = _run(torch, n, 2, [[0], [1]], 3, inject={1: (0, 0)})
+        got = d.current()[0]
+        if ref is None:
+            ref = got
+        for x, y in zip(got, ref):
+            assert np.array_equal(_bits(x), _bits(y)), env
+
+
+def test_same_bits_as_the_in_place_path(torch):
+    """The same steps through ds_accumulate (the last one checking) and
+    ds_adam_step_fused in place end in the same bits and scaler state."""
+    from zero_mixed_precision_amd import _lib
+    n, K = 100_003, 4
+    idx = np.arange(n)
+    master0 = synth.host_master32(synth.stream_key(1701, synth.ARR_MASTER), idx, MASTER_SIGMA)
+    d = FoldDb(torch, master0, init_scale=2.0 ** 12, window=2)
+    master, m, v = gu.dev_f32(torch, master0), torch.zeros(n, device="cuda:0"), torch.zeros(n, device="cuda:0")
+    p16 = torch.zeros(n, dtype=torch.int16, device="cuda:0")
+    acc = torch.empty(n, device="cuda:0")
+    st = torch.zeros(_lib.ds_scaler_size(), dtype=torch.uint8, device="cuda:0")
+    _lib.ds_state_init(st, 2.0 ** 12, 1.0, 2, 1, 0, 1)
+    for s in range(7):
+        hg = [synth.host_grad16(synth.stream_key(1702, synth.ARR_GRAD, s, k), idx, synth.GradSpec(1e-3, 2.0 ** 12))
+              for k in range(K)]
+        if s in (2, 5):
+            hg[s % K][(s * 104729) % n] = 0x7C00
+        gd = [gu.dev_u16(torch, g) for g in hg]
+        d.step(gd, [[0, 1], [2, 3]])
+        for k in range(K):
+            _lib.ds_accumulate(acc, gd[k], _lib.DS_FP16, n, k == 0, st if k == K - 1 else None)
+        _lib.ds_adam_step_fused(st, master, m, v, p16, _lib.DS_FP16, acc, _lib.DS_FP32, n, LR, None, BETA1, BETA2,
+                                EPS, 0.0, 0.0, K)
+    cur, _ = d.current()
+    for x, y in zip(cur, (gu.host_f32(master), gu.host_f32(m), gu.host_f32(v), gu.host_u16(p16))):
+        assert np.array_equal(_bits(x), _bits(y))
+    a, b = d.scaler(), _lib.ds_state_read(st)
+    for f in ("scale", "step", "iter", "skipped", "growth_count", "hysteresis_left", "last_overflow"):
+        assert getattr(a, f) == getattr(b, f), f
+
+
+def test_shard_step_double_buffered_with_accumulation(torch, tmp_path):
+    """ShardStep(double_buffer=True) with K = 4 against the in-place ShardStep:
+    micro-batches one at a time, as a fold of all four and as 2 + 2, a graph of
+    full_step replayed with eager work and synchronisation between replays, and
+    a checkpoint round trip while copy 1 holds the state."""
+    from zero_mixed_precision_amd import ShardStep, ZeroMPConfig
+    n, K = 40_961, 4
+    cfg = ZeroMPConfig.from_dict({"fp16": {"enabled": True, "initial_scale_power": 12, "loss_scale_window": 3},
+                                  "optimizer": {"type": "AdamW", "params": {"lr": 2e-4, "weight_decay": 0.01}},
+                                  "gradient_accumulation_steps": K})
+    master0 = torch.from_numpy(synth.host_master32(synth.stream_key(1801, synth.ARR_MASTER), np.arange(n),
+                                                   MASTER_SIGMA)).to("cuda:0")
+    host = [[synth.host_grad16(synth.stream_key(1802, synth.ARR_GRAD, s, k), np.arange(n),
+                               synth.GradSpec(1e-3, 2.0 ** 12)) for k in range(K)] for s in range(7)]
+    host[2][3][99] = 0x7C00
+    ref = ShardStep(n, cfg)
+    dbs = [ShardStep(n, cfg, double_buffer=True) for _ in range(4)]
+    for s in [ref] + dbs:
+        s.master.copy_(master0)
+        s.p16.zero_()
+    bufs = [torch.empty(n, dtype=torch.int16, device="cuda:0") for _ in range(K)]
+    graph = dbs[3].graph(bufs)
+    resumed = None
+    for s in range(7):
+        gs = [gu.dev_u16(torch, g) for g in host[s]]
+        ref.full_step(gs)
+        for g in gs:                       # one at a time: the last is folded into step()
+            dbs[0].accumulate(g)
+        dbs[0].step()
+        dbs[1].full_step(gs)               # all four folded into the pass
+        dbs[2].accumulate(gs[:2])
+        dbs[2].accumulate(gs[2:])
+        dbs[2].step()
+        for b, g in zip(bufs, gs):
+            b.copy_(g)
+        graph.replay()
+        if resumed is not None:
+            resumed.full_step(gs)
+        torch.cuda.synchronize()
+        want = [gu.host_f32(x) if x.dtype == torch.float32 else gu.host_u16(x) for x in ref.current()]
+        for k, d in enumerate(dbs):
+            got = [gu.host_f32(x) if x.dtype == torch.float32 else gu.host_u16(x) for x in d.current()]
+            for x, y in zip(got, want):
+                assert np.array_equal(_bits(x), _bits(y)), (s, k)
+            assert d.scaler().scale == ref.scaler().scale
+        if s == 3:
+            assert dbs[0].scaler().current == 1      # 3 applied steps of 4 (step 2 overflowed)
+            dbs[0].save_checkpoint(tmp_path, tag="t")
+            resumed = ShardStep(n, cfg, double_buffer=True)
+            resumed.load_checkpoint(tmp_path, tag="t")
+            assert resumed.scaler().current == 0
+    for x, y in zip(resumed.current(), dbs[0].current()):      # steps 4-6 after the resume
+        a = gu.host_f32(x) if x.dtype == torch.float32 else gu.host_u16(x)
+        b = gu.host_f32(y) if y.dtype == torch.float32 else gu.host_u16(y)
+        assert np.array_equal(_bits(a), _bits(b))

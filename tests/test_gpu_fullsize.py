@@ -64,7 +64,6 @@ def run_sampled(torch, name, fused=False, bf16=False, fold=1, double=False, extr
     else:
         buckets = [(0, n)]
     extra_inject = extra_inject or {}
-    assert not (double and K > 1)
     I = sample_indices(w, buckets, list(extra_inject.values()))
     gu.say(f"[{name}] psi={n} K={K} steps={w.steps} sample={I.size} fused={fused} double={double} {fmt}")
 
@@ -84,7 +83,8 @@ def run_sampled(torch, name, fused=False, bf16=False, fold=1, double=False, extr
     g16 = torch.empty(n, dtype=torch.int16, device="cuda:0")
     # fold > 1: the micro-batches of a group are held at once and folded in one pass
     held = [g16] + [torch.empty(n, dtype=torch.int16, device="cuda:0") for _ in range(fold - 1)]
-    acc = torch.empty(n, dtype=torch.float32, device="cuda:0") if K > 1 else None
+    # the running sum (not needed when one fold folds all K into the double-buffered pass)
+    acc = torch.empty(n, dtype=torch.float32, device="cuda:0") if K > 1 and not (double and fold >= K) else None
     # the double-buffered step's second copy of the state (it holds no state yet)
     copy1 = [torch.empty(n, dtype=torch.float32, device="cuda:0") for _ in range(3)] + \
         [torch.empty(n, dtype=torch.int16, device="cuda:0")] if double else None
@@ -108,7 +108,24 @@ def run_sampled(torch, name, fused=False, bf16=False, fold=1, double=False, extr
             assert gu.count_nonfinite16(torch, buf, fmt) == int(inj is not None and inj[0] == k), \
                 f"[{name}] step {s} micro-batch {k}: non-finite values beyond the injected ones"
             gs_host.append(gh)
-            if K > 1 and fold == 1:
+            group_end = k % fold == fold - 1 or k == K - 1
+            if double and K > 1 and k == K - 1:
+                # the last fold: summed onto the running sum (if any), checked, and fed to
+                # the Adam pass, which writes the other copy; then the scaler update
+                first = k - k % fold
+                arrays = [[x.data_ptr() for x in (master, copy1[0])], [x.data_ptr() for x in (m, copy1[1])],
+                          [x.data_ptr() for x in (v, copy1[2])], [x.data_ptr() for x in (p16, copy1[3])]]
+                _lib.ds_accumulate_adam_double_buffered(st, *arrays, dt16, acc if first > 0 else None,
+                                                        [held[j % fold] for j in range(first, k + 1)], dt16, n, LR,
+                                                        None, BETA1, BETA2, EPS, 0.0, K)
+                _lib.ds_update_loss_scale_double_buffered(st)
+            elif double and K > 1 and group_end:
+                first = k - k % fold
+                for start, size in buckets:
+                    _lib.ds_accumulate_multi(acc.data_ptr() + 4 * start,
+                                             [held[j % fold].data_ptr() + 2 * start for j in range(first, k + 1)],
+                                             dt16, size, first == 0, None)
+            elif K > 1 and fold == 1:
                 for start, size in buckets:
                     _lib.ds_accumulate(acc.data_ptr() + 4 * start, g16.data_ptr() + 2 * start, dt16, size,
                                        k == 0, st if k == K - 1 else None)
@@ -121,7 +138,9 @@ def run_sampled(torch, name, fused=False, bf16=False, fold=1, double=False, extr
         if K == 1 and not double:
             _lib.ds_check_overflow(st, g16, dt16, n)
         grad, dt = (g16, dt16) if K == 1 else (acc, _lib.DS_FP32)
-        if double:   # one kernel: the check, Adam into the other copy, the scaler update
+        if double and K > 1:
+            pass     # the step ended with the last fold above
+        elif double:   # one kernel: the check, Adam into the other copy, the scaler update
             _lib.ds_adam_step_double_buffered(st, [master, copy1[0]], [m, copy1[1]], [v, copy1[2]],
                                               [p16, copy1[3]], dt16, grad, dt, n, LR, None, BETA1, BETA2, EPS,
                                               0.0, K)
@@ -196,6 +215,17 @@ def test_zero1_shard_of_70b_double_buffered(torch):
     step 4."""
     sc = run_sampled(torch, "zero1_70b", double=True, extra_inject={4: 6_123_456_789})
     assert sc.applied == 9 and sc.s.skipped == 1
+
+
+@pytest.mark.parametrize("fold", [1, 8, 3])
+def test_ragged_layout_double_buffered(torch, fold):
+    """The launch bench.py --workload ragged [--fold F] times by default: two
+    copies of the 130 GB state, the earlier micro-batches (or folds) summed per
+    bucket, the last micro-batch (fold 1), all eight (fold 8, no running sum) or
+    the last two (folds of 3, 3, 2) folded into the double-buffered Adam pass,
+    with the workload's injected overflows (in steps 3, 4, 17)."""
+    sc = run_sampled(torch, "ragged", fold=fold, double=True)
+    assert sc.applied == 27 and sc.scale == 2.0 ** 14
 
 
 def test_ragged_layout_fused_scaler_update(torch):

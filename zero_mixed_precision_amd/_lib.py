@@ -23,6 +23,7 @@ EXPORTED = (
     "ds_layout_greedy", "ds_partition_range", "ds_status_string", "ds_sumsq_workspace_bytes",
     "ds_check_overflow_sumsq", "ds_accumulate_sumsq", "ds_adam_step_sched", "ds_lr_scalars",
     "ds_adam_step_fused", "ds_accumulate_multi", "ds_check_overflow_sumsq_noalloc", "ds_adam_step_double_buffered",
+    "ds_accumulate_adam_double_buffered", "ds_update_loss_scale_double_buffered",
 )
 DS_NOALLOC_MAX_ELEMS = 17175674880
 DS_LR_WARMUP, DS_LR_WARMUP_DECAY = 1, 2
@@ -125,6 +126,11 @@ def _load():
         "ds_adam_step_double_buffered": ([vp, ctypes.POINTER(vp), ctypes.POINTER(vp), ctypes.POINTER(vp),
                                           ctypes.POINTER(vp), ctypes.c_int, vp, ctypes.c_int, i64, f32,
                                           ctypes.POINTER(DsLrSchedule), f32, f32, f32, f32, i32, vp], ctypes.c_int),
+        "ds_accumulate_adam_double_buffered": ([vp, ctypes.POINTER(vp), ctypes.POINTER(vp), ctypes.POINTER(vp),
+                                                ctypes.POINTER(vp), ctypes.c_int, vp, ctypes.POINTER(vp), i32,
+                                                ctypes.c_int, i64, f32, ctypes.POINTER(DsLrSchedule), f32, f32, f32,
+                                                f32, i32, vp], ctypes.c_int),
+        "ds_update_loss_scale_double_buffered": ([vp, vp], ctypes.c_int),
         "ds_accumulate_sumsq": ([vp, vp, ctypes.c_int, i64, i32, vp, vp, ctypes.c_size_t, vp], ctypes.c_int),
         "ds_accumulate_multi": ([vp, ctypes.POINTER(vp), i32, ctypes.c_int, i64, i32, vp, vp, ctypes.c_size_t, vp],
                                 ctypes.c_int),
@@ -284,6 +290,31 @@ def ds_adam_step_double_buffered(st, master2, m2, v2, p16_2, pdt, grad, dtype, n
                                          _p(grad, _esize(dtype) * n, "gradient"), int(dtype), n, lr, sched_p,
                                          beta1, beta2, eps, weight_decay, int(accum_steps), _s(stream)),
         "ds_adam_step_double_buffered")
+
+
+def ds_accumulate_adam_double_buffered(st, master2, m2, v2, p16_2, pdt, acc, grads, gdt, n, lr, sched, beta1, beta2,
+                                       eps, weight_decay, accum_steps, stream=None) -> None:
+    """The step's last micro-batches (``grads``: 1..8 tensors or device addresses, in order) folded into the
+    double-buffered Adam pass; ``acc`` is the running sum of the earlier ones (or None when ``grads`` are all
+    of them).  End the step with ds_update_loss_scale_double_buffered."""
+    n = int(n)
+
+    def pair(arrs, nbytes, what):
+        if len(arrs) != 2:
+            raise ValueError(f"{what}: expected two copies")
+        return (ctypes.c_void_p * 2)(*[_p(a, nbytes, f"{what}[{k}]") for k, a in enumerate(arrs)])
+
+    ptrs = (ctypes.c_void_p * max(len(grads), 1))(*[_p(g, 2 * n, f"gradient {k}") for k, g in enumerate(grads)])
+    sched_p = ctypes.byref(sched) if sched is not None else None
+    _ok(lib.ds_accumulate_adam_double_buffered(_scaler(st), pair(master2, 4 * n, "master"), pair(m2, 4 * n, "m"),
+                                               pair(v2, 4 * n, "v"), pair(p16_2, 2 * n, "p16"), int(pdt),
+                                               _p(acc, 4 * n, "acc"), ptrs, len(grads), int(gdt), n, lr, sched_p,
+                                               beta1, beta2, eps, weight_decay, int(accum_steps), _s(stream)),
+        "ds_accumulate_adam_double_buffered")
+
+
+def ds_update_loss_scale_double_buffered(st, stream=None) -> None:
+    _ok(lib.ds_update_loss_scale_double_buffered(_scaler(st), _s(stream)), "ds_update_loss_scale_double_buffered")
 
 
 def ds_sumsq_workspace_bytes(n) -> int:

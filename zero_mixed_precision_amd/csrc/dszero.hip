@@ -75,6 +75,8 @@ static_assert(2 * kSmallBlock == 4 * kStepBlock, "both shapes cover one 4096-ele
 constexpr int kCheckBlock = 1024;  // lanes per block of the read-only check
 // Accumulation: one wave per block, one quad per lane (256-element tiles).
 constexpr int kAccBlock = 64;
+constexpr int kFoldAdamBlock = 64;   // fold + double-buffered Adam: lanes per block
+constexpr int kFoldAdamUnroll = 1;   // and quads per lane
 // Sum-of-squares forms of the accumulation: one chunk of 1024 elements per
 // block, 256 lanes x 1 quad.
 constexpr int kAccSumsqBlock = 256;
@@ -999,6 +1001,132 @@ __global__ __launch_bounds__(TPB) void accumulate_kernel(float* __restrict__ acc
     }
 }
 
+// The step's last micro-batches folded into the double-buffered Adam pass
+// (ds_accumulate_adam_double_buffered).  Per element, the gradient is the fp32
+// sum, in micro-batch order, of the running sum in acc (HAS_ACC; without it
+// the first of the F gradients starts the sum) and of the F 16-bit gradients
+// of gl; the sum is tested, fed to Adam (the arithmetic of adam_kernel), which
+// reads the current copy of master, m, v and writes the other copy and its
+// 16-bit parameter copy, and is not stored.  Tiles of U x TPB quads are dealt
+// to blocks round-robin, every load of a tile issued before its arithmetic;
+// block 0 also takes the quads after the last whole tile and the last n % 4
+// elements.  A non-finite sum raises st->overflow (one atomic per wave that
+// saw one); the scaler and the copy index are left to the one-thread update
+// that ends the step, so a step may take one such pass per bucket.
+template <int GF, int PF, bool WD, bool HAS_ACC, bool NT, int TPB, int U, int F>
+__device__ __forceinline__ void fold_adam_pass(const DbArrays& a, uint32_t cur, const float* __restrict__ acc,
+                                               const GradList& gl, int64_t n, const AdamConsts& c, uint32_t& bad)
+{
+    const f32x4* P = reinterpret_cast<const f32x4*>(cur ? a.master[1] : a.master[0]);
+    const f32x4* M = reinterpret_cast<const f32x4*>(cur ? a.m[1] : a.m[0]);
+    const f32x4* V = reinterpret_cast<const f32x4*>(cur ? a.v[1] : a.v[0]);
+    f32x4* Po = reinterpret_cast<f32x4*>(cur ? a.master[0] : a.master[1]);
+    f32x4* Mo = reinterpret_cast<f32x4*>(cur ? a.m[0] : a.m[1]);
+    f32x4* Vo = reinterpret_cast<f32x4*>(cur ? a.v[0] : a.v[1]);
+    uint16_t* p16o = cur ? a.p16[0] : a.p16[1];
+    u32x2* H = reinterpret_cast<u32x2*>(p16o);
+    const f32x4* A = reinterpret_cast<const f32x4*>(acc);
+
+    constexpr int T = U * TPB;  // quads per tile
+    const int64_t nq = n >> 2;
+    const int64_t ntiles = nq / T;
+    for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
+        const int64_t q0 = tile * T + threadIdx.x;
+        f32x4 r[U], p[U], m[U], v[U];
+        u32x2 raw[U][F];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t i = q0 + u * TPB;
+            if constexpr (HAS_ACC)
+                r[u] = load<NT>(A + i);
+#pragma unroll
+            for (int k = 0; k < F; ++k)
+                raw[u][k] = load<NT>(reinterpret_cast<const u32x2*>(gl.p[k]) + i);
+            p[u] = load<NT>(P + i);
+            m[u] = load<NT>(M + i);
+            v[u] = load<NT>(V + i);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t i = q0 + u * TPB;
+            if constexpr (HAS_ACC)
+                r[u] = r[u] + widen4<GF>(raw[u][0]);
+            else
+                r[u] = widen4<GF>(raw[u][0]);
+#pragma unroll
+            for (int k = 1; k < F; ++k)
+                r[u] = r[u] + widen4<GF>(raw[u][k]);
+            bad |= nonfinite_f32x4(r[u]);
+            adam4<WD>(r[u], p[u], m[u], v[u], c);
+            store<NT>(Po + i, p[u]);
+            store<NT>(Mo + i, m[u]);
+            store<NT>(Vo + i, v[u]);
+            store<NT>(H + i, narrow4<PF>(p[u]));
+        }
+    }
+    if (blockIdx.x == 0) {
+        for (int64_t q = ntiles * T + threadIdx.x; q < nq; q += TPB) {
+            f32x4 r;
+            if constexpr (HAS_ACC)
+                r = load<NT>(A + q) + widen4<GF>(load<NT>(reinterpret_cast<const u32x2*>(gl.p[0]) + q));
+            else
+                r = widen4<GF>(load<NT>(reinterpret_cast<const u32x2*>(gl.p[0]) + q));
+#pragma unroll
+            for (int k = 1; k < F; ++k)
+                r = r + widen4<GF>(load<NT>(reinterpret_cast<const u32x2*>(gl.p[k]) + q));
+            f32x4 p = load<NT>(P + q), m = load<NT>(M + q), v = load<NT>(V + q);
+            bad |= nonfinite_f32x4(r);
+            adam4<WD>(r, p, m, v, c);
+            store<NT>(Po + q, p);
+            store<NT>(Mo + q, m);
+            store<NT>(Vo + q, v);
+            store<NT>(H + q, narrow4<PF>(p));
+        }
+        if (static_cast<int64_t>(threadIdx.x) < (n & 3)) {
+            const int64_t i = (nq << 2) + threadIdx.x;
+            float r = dec1<GF>(gl.p[0][i]);
+            if constexpr (HAS_ACC)
+                r = acc[i] + r;
+#pragma unroll
+            for (int k = 1; k < F; ++k)
+                r = r + dec1<GF>(gl.p[k][i]);
+            const float* ps = reinterpret_cast<const float*>(P);
+            const float* ms = reinterpret_cast<const float*>(M);
+            const float* vs = reinterpret_cast<const float*>(V);
+            float p = ps[i], m = ms[i], v = vs[i];
+            bad |= nonfinite_f32(__float_as_uint(r));
+            adam1<WD>(r, p, m, v, c);
+            reinterpret_cast<float*>(Po)[i] = p;
+            reinterpret_cast<float*>(Mo)[i] = m;
+            reinterpret_cast<float*>(Vo)[i] = v;
+            p16o[i] = static_cast<uint16_t>(enc1<PF>(p));
+        }
+    }
+}
+
+// gl.count (1..8) chosen by a block-uniform switch, so each form is
+// straight-line code with every load of a tile in flight together.
+template <int GF, int PF, bool WD, bool HAS_ACC, bool NT, int TPB, int U>
+__global__ __launch_bounds__(TPB) void fold_adam_db_kernel(ds_scaler* __restrict__ st, DbArrays a,
+                                                           const float* __restrict__ acc, GradList gl, int64_t n,
+                                                           AdamHyper hp)
+{
+    const AdamConsts c = make_consts(st, hp);
+    const uint32_t cur = st->current & 1u;
+    uint32_t bad = 0u;
+    switch (gl.count) {
+    case 1: fold_adam_pass<GF, PF, WD, HAS_ACC, NT, TPB, U, 1>(a, cur, acc, gl, n, c, bad); break;
+    case 2: fold_adam_pass<GF, PF, WD, HAS_ACC, NT, TPB, U, 2>(a, cur, acc, gl, n, c, bad); break;
+    case 3: fold_adam_pass<GF, PF, WD, HAS_ACC, NT, TPB, U, 3>(a, cur, acc, gl, n, c, bad); break;
+    case 4: fold_adam_pass<GF, PF, WD, HAS_ACC, NT, TPB, U, 4>(a, cur, acc, gl, n, c, bad); break;
+    case 5: fold_adam_pass<GF, PF, WD, HAS_ACC, NT, TPB, U, 5>(a, cur, acc, gl, n, c, bad); break;
+    case 6: fold_adam_pass<GF, PF, WD, HAS_ACC, NT, TPB, U, 6>(a, cur, acc, gl, n, c, bad); break;
+    case 7: fold_adam_pass<GF, PF, WD, HAS_ACC, NT, TPB, U, 7>(a, cur, acc, gl, n, c, bad); break;
+    default: fold_adam_pass<GF, PF, WD, HAS_ACC, NT, TPB, U, 8>(a, cur, acc, gl, n, c, bad); break;
+    }
+    raise_flag(st, bad);
+}
+
 __global__ void write_state_kernel(ds_scaler* st, ds_scaler value) { *st = value; }
 
 // ---------------------------------------------------------------------------
@@ -1157,6 +1285,41 @@ void launch_adam_db(int gf, int pf, bool wd, bool nt, unsigned blocks, hipStream
         if (gf == kF16)       launch_adam_db2<kF16, kF16>(wd, nt, blocks, s, st, a, grad, n, hp);
         else if (gf == kBF16) launch_adam_db2<kBF16, kF16>(wd, nt, blocks, s, st, a, grad, n, hp);
         else                  launch_adam_db2<kF32, kF16>(wd, nt, blocks, s, st, a, grad, n, hp);
+    }
+}
+
+template <int GF, int PF, bool WD, bool HA>
+void launch_fold_adam4(bool nt, unsigned blocks, hipStream_t s, ds_scaler* st, const DbArrays& a, const float* acc,
+                       const GradList& gl, int64_t n, const AdamHyper& hp)
+{
+    constexpr int TPB = kFoldAdamBlock, U = kFoldAdamUnroll;
+    if (nt) fold_adam_db_kernel<GF, PF, WD, HA, true, TPB, U><<<blocks, TPB, 0, s>>>(st, a, acc, gl, n, hp);
+    else    fold_adam_db_kernel<GF, PF, WD, HA, false, TPB, U><<<blocks, TPB, 0, s>>>(st, a, acc, gl, n, hp);
+}
+
+template <int GF, int PF>
+void launch_fold_adam3(bool wd, bool ha, bool nt, unsigned blocks, hipStream_t s, ds_scaler* st, const DbArrays& a,
+                       const float* acc, const GradList& gl, int64_t n, const AdamHyper& hp)
+{
+    if (wd) {
+        if (ha) launch_fold_adam4<GF, PF, true, true>(nt, blocks, s, st, a, acc, gl, n, hp);
+        else    launch_fold_adam4<GF, PF, true, false>(nt, blocks, s, st, a, acc, gl, n, hp);
+    } else {
+        if (ha) launch_fold_adam4<GF, PF, false, true>(nt, blocks, s, st, a, acc, gl, n, hp);
+        else    launch_fold_adam4<GF, PF, false, false>(nt, blocks, s, st, a, acc, gl, n, hp);
+    }
+}
+
+void launch_fold_adam(int gf, int pf, bool wd, bool nt, unsigned blocks, hipStream_t s, ds_scaler* st,
+                      const DbArrays& a, const float* acc, const GradList& gl, int64_t n, const AdamHyper& hp)
+{
+    const bool ha = acc != nullptr;
+    if (gf == kBF16) {
+        if (pf == kBF16) launch_fold_adam3<kBF16, kBF16>(wd, ha, nt, blocks, s, st, a, acc, gl, n, hp);
+        else             launch_fold_adam3<kBF16, kF16>(wd, ha, nt, blocks, s, st, a, acc, gl, n, hp);
+    } else {
+        if (pf == kBF16) launch_fold_adam3<kF16, kBF16>(wd, ha, nt, blocks, s, st, a, acc, gl, n, hp);
+        else             launch_fold_adam3<kF16, kF16>(wd, ha, nt, blocks, s, st, a, acc, gl, n, hp);
     }
 }
 
@@ -1609,6 +1772,93 @@ ds_status ds_adam_step_double_buffered(ds_scaler* st, float* const* master2, flo
     const bool nt = variant_nt(n);
     const unsigned blocks = grid_blocks(tiles_of(n, 4), nt ? kStepBlock : kSmallBlock);
     launch_adam_db(fmt_of(dt), fmt_of(pdt), weight_decay != 0.0f, nt, blocks, s, st, a, grad, n, hp);
+    return launched();
+}
+
+ds_status ds_accumulate_adam_double_buffered(ds_scaler* st, float* const* master2, float* const* m2,
+                                             float* const* v2, uint16_t* const* p16_2, ds_dtype pdt,
+                                             const float* acc_or_null, const uint16_t* const* grads, int32_t count,
+                                             ds_dtype gdt, int64_t n, float lr, const ds_lr_schedule* sched_or_null,
+                                             float beta1, float beta2, float eps, float weight_decay,
+                                             int32_t accum_steps, void* stream)
+{
+    AdamHyper hp{lr, beta1, beta2, eps, weight_decay, 0.0f, accum_steps, 0, 0.0f, 0, 0};
+    if (sched_or_null != nullptr) {
+        if (!schedule_ok(*sched_or_null))
+            return DS_ERR_HPARAM;
+        const ds_lr_schedule& q = *sched_or_null;
+        hp = AdamHyper{q.warmup_max_lr, beta1, beta2, eps, weight_decay, 0.0f, accum_steps,
+                       q.kind, q.warmup_min_lr, q.warmup_num_steps, q.total_num_steps};
+    }
+    if (!size_ok(n) || count < 1 || count > kMaxFold)
+        return DS_ERR_SIZE;
+    if (!is16(gdt) || !is16(pdt))
+        return DS_ERR_DTYPE;
+    if (!finite_ge0(hp.lr) || !beta_ok(beta1) || !beta_ok(beta2) || !std::isfinite(eps) || eps <= 0.0f ||
+        !finite_ge0(weight_decay) || accum_steps < 1)
+        return DS_ERR_HPARAM;
+    // without the running sum these are all of the step's micro-batches; with
+    // it, the last of them
+    if (acc_or_null == nullptr ? count != accum_steps : count >= accum_steps)
+        return DS_ERR_HPARAM;
+    if (st == nullptr)
+        return DS_ERR_NULL;
+    if (!aligned(st, 8))
+        return DS_ERR_ALIGN;
+    if (n == 0)
+        return DS_OK;
+    if (master2 == nullptr || m2 == nullptr || v2 == nullptr || p16_2 == nullptr || grads == nullptr)
+        return DS_ERR_NULL;
+    DbArrays a{};
+    for (int k = 0; k < 2; ++k) {
+        if (master2[k] == nullptr || m2[k] == nullptr || v2[k] == nullptr || p16_2[k] == nullptr)
+            return DS_ERR_NULL;
+        a.master[k] = master2[k];
+        a.m[k] = m2[k];
+        a.v[k] = v2[k];
+        a.p16[k] = p16_2[k];
+    }
+    GradList gl{};
+    for (int32_t k = 0; k < count; ++k) {
+        if (grads[k] == nullptr)
+            return DS_ERR_NULL;
+        if (!aligned(grads[k], 16))
+            return DS_ERR_ALIGN;
+        gl.p[k] = grads[k];
+    }
+    gl.count = count;
+    // the eight state arrays, the running sum and the state must not overlap
+    // one another or a gradient (the gradients, only read, may repeat)
+    const void* ptrs[10] = {a.master[0], a.master[1], a.m[0], a.m[1], a.v[0], a.v[1], a.p16[0], a.p16[1],
+                            acc_or_null, st};
+    for (int i = 0; i < 10; ++i)
+        if (ptrs[i] != nullptr && !aligned(ptrs[i], i == 9 ? 8 : 16))
+            return DS_ERR_ALIGN;
+    const uint64_t un = static_cast<uint64_t>(n);
+    const uint64_t sizes[10] = {4 * un, 4 * un, 4 * un, 4 * un, 4 * un, 4 * un, 2 * un, 2 * un,
+                                acc_or_null != nullptr ? 4 * un : 0, sizeof(ds_scaler)};
+    for (int i = 0; i < 10; ++i) {
+        for (int j = i + 1; j < 10; ++j)
+            if (overlap(ptrs[i], sizes[i], ptrs[j], sizes[j]))
+                return DS_ERR_ALIAS;
+        for (int32_t k = 0; k < count; ++k)
+            if (overlap(ptrs[i], sizes[i], grads[k], 2 * un))
+                return DS_ERR_ALIAS;
+    }
+    const bool nt = variant_nt(n);
+    const unsigned blocks = grid_blocks((n >> 2) / (kFoldAdamBlock * kFoldAdamUnroll), kFoldAdamBlock);
+    launch_fold_adam(fmt_of(gdt), fmt_of(pdt), weight_decay != 0.0f, nt, blocks, static_cast<hipStream_t>(stream),
+                     st, a, acc_or_null, gl, n, hp);
+    return launched();
+}
+
+ds_status ds_update_loss_scale_double_buffered(ds_scaler* st, void* stream)
+{
+    if (st == nullptr)
+        return DS_ERR_NULL;
+    if (!aligned(st, 8))
+        return DS_ERR_ALIGN;
+    update_scale_swap_kernel<<<1, 1, 0, static_cast<hipStream_t>(stream)>>>(st);
     return launched();
 }
 

@@ -14,12 +14,16 @@ scales and accumulates, step() updates):
 
 The Adam step covers the whole partition in one ds_adam_step_fused call,
 whose kernel also advances the loss scaler (ds_update_loss_scale's work).
-With ``double_buffer`` (K = 1, no clipping) the shard keeps two copies of
-master, m, v and the 16-bit copy, and a step is one
-ds_adam_step_double_buffered call: the overflow check is fused into the Adam
-pass, which writes the other copy, and the device makes that copy current
-only if the step applied (28 bytes per element instead of 30); ``current()``
-returns the copy holding the state.
+With ``double_buffer`` (no clipping) the shard keeps two copies of master, m,
+v and the 16-bit copy, and the overflow check is fused into the Adam pass,
+which writes the other copy; the device makes that copy current only if the
+step applied.  K = 1: one ds_adam_step_double_buffered call (28 bytes per
+element instead of 30).  K > 1: the micro-batches before the last call to
+accumulate() are summed as above, and step() folds the last call's
+gradients into the Adam pass (ds_accumulate_adam_double_buffered, which uses
+the sum without storing it), then ds_update_loss_scale_double_buffered ends
+the step (a fold of all 8 of 8 micro-batches: 42 bytes per element instead of
+50).  ``current()`` returns the copy holding the state.
 
 With gradient clipping configured the check passes are the _sumsq variants
 (ds_accumulate_sumsq / ds_check_overflow_sumsq), which also gather the
@@ -87,10 +91,9 @@ class ShardStep:
         import torch
 
         self.double_buffer = bool(double_buffer)
-        if self.double_buffer and (int(cfg.gradient_accumulation_steps) != 1 or float(cfg.gradient_clipping) > 0):
-            raise ValueError("double_buffer is for gradient_accumulation_steps = 1 without gradient clipping (the "
-                             "check is fused into the Adam pass; with accumulation it is fused into the last "
-                             "micro-batch's pass instead, and clipping needs the norm before the update)")
+        if self.double_buffer and float(cfg.gradient_clipping) > 0:
+            raise ValueError("double_buffer takes no gradient clipping (clipping needs the whole gradient's norm "
+                             "before the update)")
 
         # accumulation granularity: the reduce buckets inside this partition
         self.buckets = buckets_or_all(buckets, int(n))
@@ -124,6 +127,9 @@ class ShardStep:
             self.ws = torch.zeros((nbytes + 7) // 8, dtype=torch.float64, device=device)
         self._ws_bytes = self.ws.numel() * 8 if self.ws is not None else 0
         self._micro = 0
+        # double_buffer with K > 1: the step's last micro-batch gradients, folded
+        # into the Adam pass by step(), and whether they are all K of them
+        self._pending, self._pending_all = None, False
         _lib.ds_state_init(self.state, cfg.init_scale, cfg.min_loss_scale, cfg.loss_scale_window,
                            cfg.hysteresis, int(cfg.consecutive_hysteresis), int(cfg.dynamic),
                            self.stream)
@@ -139,7 +145,9 @@ class ShardStep:
         """Add one fp16 micro-batch gradient (K > 1), or a list of up to 8 of them
         in micro-batch order, folded into the buffer in one pass (the same result
         as one call each, with less memory traffic); the call that completes the
-        K micro-batches also checks the sum."""
+        K micro-batches also checks the sum.  With double_buffer that call only
+        records its gradients: step() folds them into the Adam pass, so they must
+        stay unchanged until then."""
         if self.K == 1:
             raise RuntimeError("accumulate() is for gradient_accumulation_steps > 1; pass the gradient to step()")
         if isinstance(g16, (list, tuple)):
@@ -150,6 +158,10 @@ class ShardStep:
         self._check_grad(g16)
         k = self._micro
         last = k == self.K - 1
+        if last and self.double_buffer:
+            self._pending, self._pending_all = [g16], False
+            self._micro = k + 1
+            return
         st, acc, g0 = self.state.data_ptr(), self.acc.data_ptr(), g16.data_ptr()
         for start, size in self.buckets:
             a, g = acc + 4 * start, g0 + 2 * start
@@ -170,6 +182,10 @@ class ShardStep:
         for g in grads:
             self._check_grad(g)
         first, last = self._micro == 0, self._micro + count == self.K
+        if last and self.double_buffer:
+            self._pending, self._pending_all = list(grads), first
+            self._micro += count
+            return
         st, acc = self.state.data_ptr(), self.acc.data_ptr()
         base = [g.data_ptr() for g in grads]
         for start, size in self.buckets:
@@ -182,6 +198,22 @@ class ShardStep:
         """Finish the step: check (K = 1), gated Adam, scaler update."""
         c = self.cfg
         st = self.state.data_ptr()
+        if self.double_buffer and self.K > 1:
+            # the last micro-batches folded into the Adam pass, which checks their
+            # sum and writes the other copy; then the scaler update swaps copies
+            if self._micro != self.K or self._pending is None:
+                raise RuntimeError(f"accumulate() must be called {self.K} times before step() "
+                                   f"(called {self._micro} times)")
+            a, b = self._copies
+            _lib.ds_accumulate_adam_double_buffered(
+                st, [a[0].data_ptr(), b[0].data_ptr()], [a[1].data_ptr(), b[1].data_ptr()],
+                [a[2].data_ptr(), b[2].data_ptr()], [a[3].data_ptr(), b[3].data_ptr()], self.pdt,
+                None if self._pending_all else self.acc.data_ptr(), [g.data_ptr() for g in self._pending],
+                self.gdt, self.n, c.lr, self.sched, c.betas[0], c.betas[1], c.eps, c.weight_decay, self.K,
+                self.stream)
+            _lib.ds_update_loss_scale_double_buffered(st, self.stream)
+            self._pending, self._pending_all, self._micro = None, False, 0
+            return
         if self.double_buffer:
             # the check fused into the Adam pass, which writes the other copy
             self._check_grad(g16)
