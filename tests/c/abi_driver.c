@@ -8,7 +8,10 @@
  *
  * DIR/params.txt   n K steps init_scale window lr beta1 beta2 eps weight_decay max_grad_norm [double]
  *                  (double = 1: ds_adam_step_double_buffered over two copies of the state in place
- *                  of the check, ds_adam_step and ds_update_loss_scale; needs max_grad_norm = 0)
+ *                  of the check, ds_adam_step and ds_update_loss_scale; double = 2, K > 1: micro-batches
+ *                  1..K-1 summed by ds_accumulate, the last one folded into the double-buffered pass by
+ *                  ds_accumulate_adam_double_buffered, then ds_update_loss_scale_double_buffered; both
+ *                  need max_grad_norm = 0)
  * DIR/master.bin   float32[n]                initial fp32 master copy
  * DIR/grads.bin    uint16[steps][K][n]       fp16 gradients, micro-batch by micro-batch
  * writes
@@ -98,8 +101,9 @@ int main(int argc, char** argv)
         fclose(f);
     }
     const int dbl = double_l != 0;
-    if (dbl && clip > 0.0f) {
-        fprintf(stderr, "the double-buffered step takes no clipping\n");
+    const int fold_last = double_l == 2;
+    if ((dbl && clip > 0.0f) || (fold_last && K_l < 2)) {
+        fprintf(stderr, "the double-buffered step takes no clipping; folding the last micro-batch needs K > 1\n");
         return 4;
     }
     const int64_t n = n_ll;
@@ -169,6 +173,10 @@ int main(int argc, char** argv)
         ds_dtype gdt = DS_FP16;
         if (K == 1 && dbl) {
             /* the check runs inside the double-buffered pass */
+        } else if (fold_last) {
+            /* micro-batches 1..K-1 into the running sum; the last one goes into the pass below */
+            for (int32_t k = 0; k < K - 1; ++k)
+                CHECK_DS(ds_accumulate(acc, g16 + (size_t)k * stride, DS_FP16, n, k == 0, NULL, stream));
         } else if (K == 1) {
             if (clip > 0.0f)
                 CHECK_DS(ds_check_overflow_sumsq((ds_scaler*)state, g16, DS_FP16, n, ws, ws_bytes, stream));
@@ -196,7 +204,12 @@ int main(int argc, char** argv)
             grad = acc;
             gdt = DS_FP32;
         }
-        if (dbl) {
+        if (fold_last) {
+            const uint16_t* last[1] = {g16 + (size_t)(K - 1) * stride};
+            CHECK_DS(ds_accumulate_adam_double_buffered((ds_scaler*)state, master2, m2, v2, p16_2, DS_FP16, acc, last,
+                                                        1, DS_FP16, n, lr, NULL, b1, b2, eps, wd, K, stream));
+            CHECK_DS(ds_update_loss_scale_double_buffered((ds_scaler*)state, stream));
+        } else if (dbl) {
             CHECK_DS(ds_adam_step_double_buffered((ds_scaler*)state, master2, m2, v2, p16_2, DS_FP16, grad, gdt, n,
                                                   lr, NULL, b1, b2, eps, wd, K, stream));
         } else {

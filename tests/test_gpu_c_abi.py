@@ -20,10 +20,12 @@ DRIVER = os.path.join(os.path.dirname(os.path.abspath(__file__)), "c", "abi_driv
 
 @pytest.mark.parametrize("n,K,wd,clip,double", [(4099, 1, 0.0, 0.0, 0), (20_003, 3, 0.01, 0.0, 0),
                                                 (65_541, 1, 0.0, 1.0, 0), (10_007, 2, 0.0, 1.0, 0),
-                                                (30_011, 1, 0.01, 0.0, 1), (8_195, 2, 0.0, 0.0, 1)])
+                                                (30_011, 1, 0.01, 0.0, 1), (8_195, 2, 0.0, 0.0, 1),
+                                                (12_347, 3, 0.01, 0.0, 2)])
 def test_c_program_matches_oracle(tmp_path, n, K, wd, clip, double):
     """double = 1: ds_adam_step_double_buffered over two hipMalloc'd copies of
-    the state; the driver writes out the copy that the state names current."""
+    the state; double = 2: the last micro-batch folded into the double-buffered
+    pass; the driver writes out the copy that the state names current."""
     if not os.path.exists(DRIVER):
         pytest.fail(f"{DRIVER} is not built: run __graft_entry__.build()")
     steps, scale, window = 5, 2.0 ** 12, 2

@@ -10,7 +10,9 @@ active or never reached), the fused or the separate scaler update, one
 accumulation pass per micro-batch or folds of several (ds_accumulate_multi),
 without clipping the double-buffered step (ds_adam_step_double_buffered, the
 check inside the Adam pass, two copies of the state) in place of the check and
-the in-place update, and non-finite values planted in random steps,
+the in-place update, or with K > 1 the last micro-batch or fold summed into
+that pass per bucket (ds_accumulate_adam_double_buffered and
+ds_update_loss_scale_double_buffered), and non-finite values planted in random steps,
 micro-batches and positions.  The
 device runs the step through the C ABI; the oracle runs the same steps.
 
@@ -87,6 +89,8 @@ def draw_case(seed):
     # also drawn apart: the double-buffered step (only without clipping)
     rd = np.random.default_rng(9_000_011 * seed + 3)
     c["double"] = c["clip"] == 0.0 and bool(rd.random() < 0.5)
+    rq = np.random.default_rng(11_000_027 * seed + 9)
+    c["fold_into_pass"] = c["double"] and c["K"] > 1 and bool(rq.random() < 0.6)
     return c
 
 
@@ -139,6 +143,24 @@ def test_random_configuration(torch, seed):
         gs = [gu.dev_u16(torch, g) if n > 0 else torch.zeros(1, dtype=torch.int16, device=dev) for g in hg]
         if K == 1 and c["double"]:   # the check runs inside the double-buffered pass
             grad, dt = gs[0], dt16
+        elif c["fold_into_pass"]:    # earlier groups into the sum; the last one into the pass, per bucket
+            grps = c["groups"] if c["groups"] is not None else [[k] for k in range(K)]
+            for gi, grp in enumerate(grps[:-1]):
+                for start, size in c["spans"]:
+                    ptrs = [gs[k].data_ptr() + 2 * start for k in grp]
+                    if len(ptrs) == 1:
+                        _lib.ds_accumulate(acc.data_ptr() + 4 * start, ptrs[0], dt16, size, gi == 0, None)
+                    else:
+                        _lib.ds_accumulate_multi(acc.data_ptr() + 4 * start, ptrs, dt16, size, gi == 0, None)
+            two = [[x.data_ptr() for x in (a, b)] for a, b in zip((master, m, v, p16), copy1)]
+            for start, size in c["spans"]:
+                _lib.ds_accumulate_adam_double_buffered(
+                    st, *[[x + e * start for x in pair] for pair, e in zip(two, (4, 4, 4, 2))], dt16,
+                    acc.data_ptr() + 4 * start if len(grps) > 1 else None,
+                    [gs[k].data_ptr() + 2 * start for k in grps[-1]], dt16, size, lr, sched, c["b1"], c["b2"],
+                    c["eps"], c["wd"], K)
+            _lib.ds_update_loss_scale_double_buffered(st)
+            grad, dt = None, None
         elif K == 1:
             if clip > 0:
                 _lib.ds_check_overflow_sumsq(st, gs[0], dt16, n, ws)
@@ -165,7 +187,9 @@ def test_random_configuration(torch, seed):
             grad, dt = acc, _lib.DS_FP32
         args = (master, m, v, p16, dt16, grad, dt, n)
         tail = (c["b1"], c["b2"], c["eps"], c["wd"], clip, K)
-        if c["double"]:
+        if c["fold_into_pass"]:
+            pass                     # the step ended with the update above
+        elif c["double"]:
             _lib.ds_adam_step_double_buffered(st, [master, copy1[0]], [m, copy1[1]], [v, copy1[2]],
                                               [p16, copy1[3]], dt16, grad, dt, n, lr, sched, c["b1"], c["b2"],
                                               c["eps"], c["wd"], K)
