@@ -74,17 +74,18 @@ def kernel_source_hash() -> str:
     return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
 
 
-def load_traffic(workload: str, half: str, kernel: str):
+def load_traffic(workload: str, half: str, kernel: str, fold: int = 1):
     """Per-launch HBM bytes of the Adam kernel from the committed counter summary,
     or None if it is missing, was taken on another kernel source, or on another
-    workload, 16-bit format or kernel (another instance of the pass)."""
+    workload, 16-bit format, fold or kernel (another instance of the pass)."""
     try:
         data = json.load(open(TRAFFIC_FILE))
     except (OSError, ValueError):
         return None
     for rec in data.get("records", [data]):
         if (rec.get("kernel_source_sha256_16") == kernel_source_hash() and rec.get("workload") == workload
-                and rec.get("half") == half and re.search(r"\b%s<" % kernel, rec.get("kernel", ""))):
+                and rec.get("half") == half and rec.get("fold", 1) == fold
+                and re.search(r"\b%s<" % kernel, rec.get("kernel", ""))):
             return rec.get("traffic_bytes_per_launch")
     return None
 
@@ -384,7 +385,7 @@ def gpu_run(args):
             "avg_launch_ms": round(ip_adam_s * 1e3, 4),
             "achieved": round(ip_bpe * n / ip_adam_s / 1e9, 1),
             "frac": round(ip_bpe * n / ip_adam_s / 1e9 / PEAK_HBM_GBS, 4),
-            "traffic": load_traffic(w.name, "bf16" if args.bf16 else "fp16", "adam_kernel"),
+            "traffic": load_traffic(w.name, "bf16" if args.bf16 else "fp16", "adam_kernel", fold),
             "step": {"bytes_per_elem": ip_step_bytes,
                      "achieved": round(ip_step_bytes * n * args.steps / ip_wall / 1e9, 1),
                      "frac": round(ip_step_bytes * n * args.steps / ip_wall / 1e9 / PEAK_HBM_GBS, 4)},
@@ -434,7 +435,7 @@ def gpu_run(args):
         step_bytes = ip_step_bytes
         kernel = "adam_kernel"
     achieved = bytes_per_elem * n / adam_avg_s / 1e9
-    traffic = load_traffic(w.name, "bf16" if args.bf16 else "fp16", kernel)
+    traffic = load_traffic(w.name, "bf16" if args.bf16 else "fp16", kernel, fold)
     out = {
         "metric": METRIC,
         "value": round(n * args.steps / wall / 1e9, 3),
