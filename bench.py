@@ -5,16 +5,18 @@
 One step = the whole per-rank hot path over one synthetic batch: the inf/NaN
 check of the gradient (K > 1: fused into the bucketed fp16 -> fp32
 accumulation of the last micro-batch), the gated Adam update with the fp16
-copy, and the loss-scale update.  With K = 1 and no clipping the default
+copy, and the loss-scale update.  Without clipping the default
 (--step-form auto) is the double-buffered form: the check fused into the
 Adam pass, which reads the copy of master/m/v/p16 that holds the state and
-writes the other one (28 B per element in one launch; 30 bytes of device
-memory per element instead of 16, so it is used where the second copy and a
-gradient buffer fit, and where the gradient is larger than the 256 MB
-Infinity Cache: a smaller one is still cached when the in-place form reads it
-again, which makes that form as fast).  The in-place form (the check, then the Adam pass that
-rewrites the one copy, 30 B per element in two launches) is then timed after
-it on the same arrays and reported as ``in_place_form``; --step-form in_place
+writes the other one (K = 1: 28 B per element in one launch; K > 1: the last
+micro-batch or fold also summed inside that pass, the sum never stored).  It
+needs 30 bytes of device memory per element instead of 16, so it is used
+where the second copy and the gradient buffers fit, and (K = 1) where the
+gradient is larger than the 256 MB Infinity Cache: a smaller one is still
+cached when the in-place form reads it again, which makes that form as fast.
+The in-place form (the check or the accumulation with its fused check, then
+the Adam pass that rewrites the one copy) is then timed after it on the copy
+that holds the state and reported as ``in_place_form``; --step-form in_place
 makes it the timed form.  Inputs are resident in HBM before the timed region;
 gradients are drawn on the device (distinct buffers, reused cyclically when
 they do not all fit).
@@ -704,10 +706,12 @@ def main(argv=None):
     ap.add_argument("--cpu-slice", type=int, default=109_375_000)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--step-form", default="auto", choices=["auto", "double", "in_place"],
-                    help="double: two copies of the state, the overflow check fused into the Adam pass "
-                         "(ds_adam_step_double_buffered; K = 1 without clipping); in_place: the check (or the "
-                         "accumulation), then the in-place Adam pass; auto (default): double where it applies "
-                         "and fits, and the in-place form timed after it on the same arrays")
+                    help="double: two copies of the state, the overflow check (and with K > 1 the last "
+                         "micro-batch or fold) fused into the Adam pass (ds_adam_step_double_buffered, "
+                         "ds_accumulate_adam_double_buffered; no clipping); in_place: the check (or the "
+                         "accumulation), then the in-place Adam pass; auto (default): double where it applies, "
+                         "(K = 1) the gradient is larger than the 256 MB Infinity Cache and the second copy fits, "
+                         "then the in-place form timed after it on the copy that holds the state")
     ap.add_argument("--double-buffer", dest="step_form", action="store_const", const="double",
                     help="the same as --step-form double")
     ap.add_argument("--fold", type=int, default=1,
