@@ -5,7 +5,8 @@ overflow flag and the same fp64 sum of squares, bit for bit, as
 ds_check_overflow_sumsq with a caller-owned workspace, on consecutive calls
 (the array keeps the previous call's contents), the later ones smaller, in
 every gradient format; the sum also meets the oracle's exact sum of squares
-to 1e-13.
+to 1e-13.  At the largest size the array takes, the two forms agree bit for
+bit as well.
 """
 import ctypes
 
@@ -91,3 +92,35 @@ def test_noalloc_through_the_raw_c_abi(env):
     assert L.lib.ds_check_overflow_sumsq_noalloc(ctypes.c_void_p(st.data_ptr()), ctypes.c_void_p(gd.data_ptr()),
                                                  L.DS_FP16, L.DS_NOALLOC_MAX_ELEMS + 1,
                                                  ctypes.c_void_p(stream.cuda_stream)) == L.DS_ERR_SIZE
+
+
+def test_noalloc_at_its_maximum_size(env):
+    """At exactly DS_NOALLOC_MAX_ELEMS fp16 elements (a 34 GB gradient drawn on
+    the device), where the chunk sums and their group sums fill the library's
+    array to its last slot: the same sum of squares, bit for bit, as the
+    workspace form on a clean gradient, and the flag on one with an infinity
+    in its last chunk (the maximum is a whole number of 8192-element chunks)."""
+    torch, L = env
+    n = L.DS_NOALLOC_MAX_ELEMS
+    tabs = synth.DeviceTables(torch, "cuda:0")
+    g = torch.empty(n, dtype=torch.int16, device="cuda:0")
+    synth.device_fill_grad16(torch, tabs, g, synth.stream_key(4243, synth.ARR_GRAD, 0),
+                             synth.GradSpec(1e-3, 2.0 ** 15))
+    ws = torch.empty((L.ds_sumsq_workspace_bytes(n) + 7) // 8, dtype=torch.float64, device="cuda:0")
+    for inject in (None, n - 3):
+        if inject is not None:
+            g[inject] = 0x7C00
+        st_ws, st_na = _scaler(torch, L), _scaler(torch, L)
+        gu.say(f"[noalloc max] n={n} inject={inject}")
+        L.ds_check_overflow_sumsq(st_ws, g, L.DS_FP16, n, ws)
+        L.ds_check_overflow_sumsq_noalloc(st_na, g, L.DS_FP16, n)
+        a, b = L.ds_state_read(st_ws), L.ds_state_read(st_na)
+        assert a.overflow == b.overflow == (0 if inject is None else 1)
+        if inject is None:
+            assert np.isfinite(a.grad_sumsq) and a.grad_sumsq > 0
+            assert np.float64(a.grad_sumsq).view(np.uint64) == np.float64(b.grad_sumsq).view(np.uint64), \
+                (a.grad_sumsq, b.grad_sumsq)
+        assert b.sumsq_blocks_done == 0
+    del g, ws
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
