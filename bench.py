@@ -35,9 +35,10 @@ launch times sit beside it, ``roofline.step`` gives the whole step's
 algorithmic bytes per element over the wall time per step, and
 ``roofline.references`` three data-movement references timed on the same
 arrays after the timed region: the step's 14 B read + 14 B written per
-element with no arithmetic, a plain copy with one 16-byte vector per lane,
-and the runtime's device-to-device copy (``torch.Tensor.copy_``, which is
-hipMemcpyAsync).  ``step_ms_*`` and ``pre_adam_ms_*`` (the check, or the
+element with no arithmetic (in the step's 256 x 4 tiling, and in 64-lane
+blocks of one quad per lane, the copy's shape), a plain copy with one 16-byte
+vector per lane, and the runtime's device-to-device copy
+(``torch.Tensor.copy_``, which is hipMemcpyAsync).  ``step_ms_*`` and ``pre_adam_ms_*`` (the check, or the
 accumulation with its fused check; nothing in the double-buffered form) come
 from an untimed pass with events around each part.  ``graph_replay`` times the
 same steps replayed from HIP graphs (one per position in the cycle of gradient
@@ -421,6 +422,8 @@ def gpu_run(args):
     mix_args = (grads[0][:nm], master[:nm], m[:nm], v[:nm], p16[:nm])
     mix_s = timed(lambda: synth.device_stream_mix(torch, *mix_args, stream=stream), 8)
     mix_gbs = 28 * nm / mix_s / 1e9
+    mix64_s = timed(lambda: synth.device_stream_mix(torch, *mix_args, stream=stream, small_tiles=True), 8)
+    mix64_gbs = 28 * nm / mix64_s / 1e9
     copy_s = timed(lambda: synth.device_copy(torch, m[:nm], master[:nm], stream=stream), 8)
     memcpy_s = timed(lambda: m[:nm].copy_(master[:nm]), 8)
     copy_gbs, memcpy_gbs = 8 * nm / copy_s / 1e9, 8 * nm / memcpy_s / 1e9
@@ -489,6 +492,7 @@ def gpu_run(args):
                      "achieved": round(step_bytes * n * args.steps / wall / 1e9, 1),
                      "frac": round(step_bytes * n * args.steps / wall / 1e9 / PEAK_HBM_GBS, 4)},
             "references": {"step_shaped_no_arithmetic_gbs": round(mix_gbs, 1),
+                           "step_shaped_no_arithmetic_64x1_gbs": round(mix64_gbs, 1),
                            "copy_one_vector_per_lane_gbs": round(copy_gbs, 1),
                            "runtime_d2d_copy_gbs": round(memcpy_gbs, 1),
                            "bytes": nm * 8},

@@ -191,7 +191,9 @@ def device_lib():
         L.synth_fill_master32.argtypes = [vp, i64, i64, u64, vp, vp]
         L.synth_copy.argtypes = [vp, vp, i64, vp]
         L.synth_stream_mix.argtypes = [vp, vp, vp, vp, vp, i64, vp]
-        for f in (L.synth_fill_grad16, L.synth_fill_master32, L.synth_copy, L.synth_stream_mix):
+        L.synth_stream_mix_shape.argtypes = [vp, vp, vp, vp, vp, i64, ctypes.c_int32, vp]
+        for f in (L.synth_fill_grad16, L.synth_fill_master32, L.synth_copy, L.synth_stream_mix,
+                  L.synth_stream_mix_shape):
             f.restype = ctypes.c_int
         _dlib = L
     return _dlib
@@ -253,10 +255,13 @@ def device_copy(torch, dst, src, stream=None) -> None:
                                    _stream_ptr(torch, stream)), "synth_copy")
 
 
-def device_stream_mix(torch, g16, a, b, c, h16, stream=None) -> None:
+def device_stream_mix(torch, g16, a, b, c, h16, stream=None, small_tiles=False) -> None:
     """Data movement of the optimizer step with no arithmetic: reads 14 B and
-    writes 14 B per element (fp16 + 3 x fp32 in, 3 x fp32 + fp16 out)."""
+    writes 14 B per element (fp16 + 3 x fp32 in, 3 x fp32 + fp16 out), in
+    256-lane blocks of 4 quads per lane (the step's tiling) or, with
+    small_tiles, 64-lane blocks of one quad per lane."""
     n = a.numel()
-    _check(device_lib().synth_stream_mix(g16.data_ptr(), a.data_ptr(), b.data_ptr(), c.data_ptr(),
-                                         h16.data_ptr(), n, _stream_ptr(torch, stream)),
+    _check(device_lib().synth_stream_mix_shape(g16.data_ptr(), a.data_ptr(), b.data_ptr(), c.data_ptr(),
+                                               h16.data_ptr(), n, int(bool(small_tiles)),
+                                               _stream_ptr(torch, stream)),
            "synth_stream_mix")

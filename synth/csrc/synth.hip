@@ -93,14 +93,16 @@ __global__ __launch_bounds__(64) void copy_kernel(copy_u4* __restrict__ dst, con
 // loads all of it, then stores all of it, with non-temporal hints.
 typedef float mix_f4 __attribute__((ext_vector_type(4)));
 typedef unsigned mix_u2 __attribute__((ext_vector_type(2)));
-constexpr int kMixLanes = 256, kMixQuads = 4;
-
-__global__ __launch_bounds__(kMixLanes) void stream_mix_kernel(const mix_u2* __restrict__ g,
-                                                               mix_f4* __restrict__ a,
-                                                               mix_f4* __restrict__ b,
-                                                               mix_f4* __restrict__ c,
-                                                               mix_u2* __restrict__ h, int64_t n4)
+// LANES lanes per block, QUADS quads per lane, one tile of LANES x QUADS quads
+// per block: 256 x 4 is the optimizer step's tiling, 64 x 1 the plain copy's.
+template <int LANES, int QUADS>
+__global__ __launch_bounds__(LANES) void stream_mix_kernel(const mix_u2* __restrict__ g,
+                                                           mix_f4* __restrict__ a,
+                                                           mix_f4* __restrict__ b,
+                                                           mix_f4* __restrict__ c,
+                                                           mix_u2* __restrict__ h, int64_t n4)
 {
+    constexpr int kMixLanes = LANES, kMixQuads = QUADS;
     const int64_t first = (int64_t)blockIdx.x * (kMixLanes * kMixQuads) + threadIdx.x;
     mix_u2 gv[kMixQuads];
     mix_f4 av[kMixQuads], bv[kMixQuads], cv[kMixQuads];
@@ -177,7 +179,17 @@ int synth_copy(void* dst, const void* src, int64_t n16, void* stream)
 }
 
 // n elements, n a multiple of 4, all pointers 16-byte aligned (g, h: 8-byte).
+int synth_stream_mix_shape(const void* g, void* a, void* b, void* c, void* h, int64_t n, int32_t small_tiles,
+                           void* stream);
+
 int synth_stream_mix(const void* g, void* a, void* b, void* c, void* h, int64_t n, void* stream)
+{
+    return synth_stream_mix_shape(g, a, b, c, h, n, 0, stream);
+}
+
+// small_tiles = 0: 256 lanes x 4 quads per block; 1: 64 lanes x 1 quad
+int synth_stream_mix_shape(const void* g, void* a, void* b, void* c, void* h, int64_t n, int32_t small_tiles,
+                           void* stream)
 {
     if (n <= 0) return 0;
     if (n % 4 != 0) return (int)hipErrorInvalidValue;
@@ -186,11 +198,17 @@ int synth_stream_mix(const void* g, void* a, void* b, void* c, void* h, int64_t 
         ((reinterpret_cast<uintptr_t>(g) | reinterpret_cast<uintptr_t>(h)) & 7u) != 0)
         return (int)hipErrorInvalidValue;
     const int64_t n4 = n / 4;
-    const int64_t tiles = (n4 + kMixLanes * kMixQuads - 1) / (kMixLanes * kMixQuads);
+    const int64_t per = small_tiles ? 64 : 256 * 4;
+    const int64_t tiles = (n4 + per - 1) / per;
     if (tiles > 0x7FFFFFFF) return (int)hipErrorInvalidValue;
-    stream_mix_kernel<<<(unsigned)tiles, kMixLanes, 0, static_cast<hipStream_t>(stream)>>>(
-        static_cast<const mix_u2*>(g), static_cast<mix_f4*>(a), static_cast<mix_f4*>(b),
-        static_cast<mix_f4*>(c), static_cast<mix_u2*>(h), n4);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const mix_u2* gp = static_cast<const mix_u2*>(g);
+    if (small_tiles)
+        stream_mix_kernel<64, 1><<<(unsigned)tiles, 64, 0, s>>>(gp, static_cast<mix_f4*>(a), static_cast<mix_f4*>(b),
+                                                                static_cast<mix_f4*>(c), static_cast<mix_u2*>(h), n4);
+    else
+        stream_mix_kernel<256, 4><<<(unsigned)tiles, 256, 0, s>>>(gp, static_cast<mix_f4*>(a), static_cast<mix_f4*>(b),
+                                                                  static_cast<mix_f4*>(c), static_cast<mix_u2*>(h), n4);
     return (int)hipGetLastError();
 }
 
