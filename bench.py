@@ -262,10 +262,10 @@ def gpu_run(args):
         else:   # groups of `fold` micro-batches, each folded into the buffer in one pass
             for g0 in range(0, K, fold):
                 grp = [grad_p[(base + k) % nbuf] for k in range(g0, min(g0 + fold, K))]
-                last = g0 + fold >= K
+                final = g0 + fold >= K
                 for start, size in buckets:
                     _lib.ds_accumulate_multi(acc_p + 4 * start, [g + 2 * start for g in grp], gdt16, size, g0 == 0,
-                                             st_p if last else None, ws_p if (last and ws is not None) else None,
+                                             st_p if final else None, ws_p if (final and ws is not None) else None,
                                              ws_bytes, stream=q)
             gptr, dt = acc_p, _lib.DS_FP32
         if whole:
@@ -279,19 +279,20 @@ def gpu_run(args):
             rc = db_step(st_p, *db_arrays, gdt16, gptr, dt, n, hp[0], None, *hp[1:5], K, q.cuda_stream)
             if rc != 0:
                 raise RuntimeError(f"ds_adam_step_double_buffered: {_lib.ds_status_string(rc)}")
-        elif dbl:            # the last fold, the check and Adam into the other copy; then the scaler
+        elif dbl:            # the last fold, the check and Adam into the other copy
             rc = db_fold(st_p, *db_arrays, gdt16, last_acc, last, len(last), gdt16, n, hp[0], None, *hp[1:5], K,
                          q.cuda_stream)
             if rc != 0:
                 raise RuntimeError(f"ds_accumulate_adam_double_buffered: {_lib.ds_status_string(rc)}")
-            rc = db_update(st_p, q.cuda_stream)
-            if rc != 0:
-                raise RuntimeError(f"ds_update_loss_scale_double_buffered: {_lib.ds_status_string(rc)}")
         else:
             _lib.ds_adam_step_fused(st_p, *ip, gdt16, gptr, dt, n, hp[0], None, *hp[1:], K, q)
         if timed:
             b.record(q)
             (ev if evs is None else evs).append((a, b))
+        if dbl and K > 1:    # then the one-work-item scaler update, which switches copies if the step applied
+            rc = db_update(st_p, q.cuda_stream)
+            if rc != 0:
+                raise RuntimeError(f"ds_update_loss_scale_double_buffered: {_lib.ds_status_string(rc)}")
         if whole:
             s1 = torch.cuda.Event(enable_timing=True)
             s1.record(q)
