@@ -93,6 +93,44 @@ def load_traffic(workload: str, half: str, kernel: str, fold: int = 1):
     return None
 
 
+HEADROOM_BYTES = 4 << 30   # device memory left free beside the run's arrays
+
+
+def grad_ring(n: int, K: int, fold: int, steps: int, warmup: int, max_buffers: int) -> int:
+    """Gradient buffers wanted: a ring of distinct draws (a real step rewrites one
+    contiguous gradient buffer) of at least 2 GiB, far beyond the 256 MB Infinity
+    Cache, never fewer than one fold holds, and no more than the run draws or the
+    caller allows."""
+    return min(max(2, -(-(2 << 30) // (2 * n)), fold), (steps + warmup) * K, max_buffers)
+
+
+def double_wanted(step_form: str, clip: float, K: int, n: int) -> bool:
+    """Whether to try the double-buffered form: never with clipping (it needs the
+    whole gradient's norm before the update); "double" asks for it; "auto" takes
+    it with K > 1, and with K = 1 where the gradient is larger than the Infinity
+    Cache (a smaller one is still cached when the in-place form's Adam pass reads
+    it again after the check, which makes that form as fast)."""
+    if clip > 0:
+        return False
+    return step_form == "double" or (step_form == "auto" and (K > 1 or 2 * n > INFINITY_CACHE_BYTES))
+
+
+def needs_running_sum(K: int, fold: int, double: bool) -> bool:
+    """The fp32 running sum is needed with K > 1, except when the double-buffered
+    form folds all K micro-batches into its Adam pass."""
+    return K > 1 and not (double and fold >= K)
+
+
+def room_beside_second_copy(n: int, K: int, fold: int, ring: int) -> int:
+    """Bytes that must stay free once the second copy is allocated: the gradient
+    buffers, the running sum if the form needs one, and the headroom."""
+    return ring * 2 * n + (4 * n if needs_running_sum(K, fold, True) else 0) + HEADROOM_BYTES
+
+
+def buffers_that_fit(free: int, n: int, ring: int) -> int:
+    return max(1, min(int((free - HEADROOM_BYTES) // (2 * n)), ring))
+
+
 def fold_bytes(sizes) -> int:
     """Algorithmic bytes per element of the accumulation passes over groups of
     micro-batches of these sizes: 2f + 4 for the first (it overwrites the
@@ -141,33 +179,22 @@ def gpu_run(args):
     if not 1 <= args.fold <= 8:
         sys.exit("bench.py: --fold takes 1..8")
     fold = min(args.fold, K)
-    # resident gradient buffers, a ring of distinct draws (a real step rewrites one
-    # contiguous gradient buffer): at least 2 GiB of them (far beyond the 256 MB
-    # Infinity Cache), and never fewer than one fold holds
-    total_mb = (args.steps + args.warmup) * K
-    enough = min(max(2, -(-(2 << 30) // (2 * n)), fold), total_mb, args.max_grad_buffers)
-    headroom = 4 << 30
+    ring = grad_ring(n, K, fold, args.steps, args.warmup, args.max_grad_buffers)
 
     # double-buffered step (no clipping): a second copy of master, m, v and the
     # 16-bit copy; the overflow check is fused into the Adam pass, and with K > 1
-    # so is the accumulation of the last micro-batch (or of the last fold).
-    # "auto" takes it where it applies, where (K = 1) the gradient is larger than
-    # the 256 MB Infinity Cache (a smaller one is still cached when the in-place
-    # form's Adam pass reads it again after the check, which makes that form as
-    # fast), and where the second copy leaves room for the gradient buffers and
-    # the running sum the step needs
+    # so is the accumulation of the last micro-batch (or of the last fold); it is
+    # used if the second copy leaves room for the gradient buffers and the
+    # running sum the step needs
     double = False
     copy1 = None
-    applies = args.clip == 0
-    if args.step_form == "double" and not applies:
+    if args.step_form == "double" and args.clip > 0:
         log("bench.py: the double-buffered step takes no clipping; using the in-place form")
-    wanted = args.step_form == "double" or (args.step_form == "auto" and (K > 1 or 2 * n > INFINITY_CACHE_BYTES))
-    if applies and wanted:
-        need = enough * 2 * n + (4 * n if fold < K else 0) + headroom
+    if double_wanted(args.step_form, args.clip, K, n):
         try:
             copy1 = [torch.empty(n, dtype=torch.float32, device=dev) for _ in range(3)] + \
                     [torch.empty(n, dtype=torch.int16, device=dev)]
-            if torch.cuda.mem_get_info(dev)[0] < need:
+            if torch.cuda.mem_get_info(dev)[0] < room_beside_second_copy(n, K, fold, ring):
                 raise torch.cuda.OutOfMemoryError("no room for the gradient buffers beside two copies")
             double = True
         except torch.cuda.OutOfMemoryError as e:
@@ -175,13 +202,9 @@ def gpu_run(args):
             torch.cuda.empty_cache()
             log(f"bench.py: two copies of the state do not fit ({str(e).splitlines()[0][:120]}); "
                 "using the in-place form")
-    # the fp32 running sum of the micro-batches (not needed when the last fold
-    # of the double-buffered form takes all of them)
-    acc = torch.empty(n, dtype=torch.float32, device=dev) if K > 1 and not (double and fold >= K) else None
+    acc = torch.empty(n, dtype=torch.float32, device=dev) if needs_running_sum(K, fold, double) else None
 
-    free = torch.cuda.mem_get_info(dev)[0]
-    fit = max(1, int((free - headroom) // (2 * n)))
-    nbuf = max(1, min(fit, enough))
+    nbuf = buffers_that_fit(torch.cuda.mem_get_info(dev)[0], n, ring)
     if fold > nbuf:
         sys.exit(f"bench.py: --fold {fold} needs {fold} gradient buffers at once; {nbuf} fit")
     grads = []
@@ -191,7 +214,7 @@ def gpu_run(args):
         synth.device_fill_grad16(torch, tabs, g, w.grad_key(s + 1, k), gspec)
         grads.append(g)
     torch.cuda.synchronize()
-    log(f"workload {w.name}: psi={n} K={K} grad buffers={nbuf} (of {total_mb} micro-batches) "
+    log(f"workload {w.name}: psi={n} K={K} grad buffers={nbuf} (of {(args.steps + args.warmup) * K} micro-batches) "
         f"step form={'double-buffered' if double else 'in place'}")
 
     hp = (LR, BETA1, BETA2, EPS, WD, args.clip)

@@ -46,3 +46,36 @@ def test_more_than_one_gpu_is_refused(capsys):
         bench.main(["--gpus", "2"])
     assert e.value.code != 0
     assert "one GPU" in capsys.readouterr().err
+
+
+def test_memory_plan_of_the_workloads():
+    """The step form and buffers bench.py plans for each workload (no GPU):
+    the double-buffered form where it applies, the running sum only where the
+    step needs it, the gradient ring and the room left beside the second copy."""
+    from synth.workloads import WORKLOADS
+    GiB = 1 << 30
+    c5, c2, c4, c1 = (WORKLOADS[k] for k in ("zero1_70b", "zero2_7b", "ragged", "tiny"))
+    # 8.75e9 elements, K = 1: a 17.5 GB gradient, far beyond the Infinity Cache
+    assert bench.double_wanted("auto", 0.0, 1, c5.psi)
+    assert not bench.double_wanted("auto", 1.0, 1, c5.psi)              # clipping: in place
+    assert not bench.double_wanted("double", 1.0, 1, c5.psi)
+    ring = bench.grad_ring(c5.psi, 1, 1, 50, 5, 8)
+    assert ring == 2
+    assert bench.room_beside_second_copy(c5.psi, 1, 1, ring) == 2 * 2 * c5.psi + 4 * GiB
+    assert not bench.needs_running_sum(1, 1, True)
+    # the 7B ZeRO-2 shard: its 219 MB gradient stays in the 256 MB cache, so auto keeps the in-place form
+    assert not bench.double_wanted("auto", 0.0, 1, c2.psi) and bench.double_wanted("double", 0.0, 1, c2.psi)
+    assert not bench.double_wanted("auto", 0.0, 1, c1.psi)
+    assert not bench.double_wanted("in_place", 0.0, 8, c4.psi)
+    # the ragged layout with 8 micro-batches: double-buffered, the sum needed unless all 8 are folded at once
+    assert bench.double_wanted("auto", 0.0, 8, c4.psi)
+    assert bench.needs_running_sum(8, 1, True) and bench.needs_running_sum(8, 3, True)
+    assert not bench.needs_running_sum(8, 8, True) and bench.needs_running_sum(8, 8, False)
+    assert bench.grad_ring(c4.psi, 8, 8, 10, 2, 8) == 8 and bench.grad_ring(c4.psi, 8, 1, 10, 2, 8) == 2
+    assert bench.room_beside_second_copy(c4.psi, 8, 8, 8) == 8 * 2 * c4.psi + 4 * GiB
+    assert bench.room_beside_second_copy(c4.psi, 8, 1, 2) == 2 * 2 * c4.psi + 4 * c4.psi + 4 * GiB
+    # small partitions: a 2 GiB ring, capped by the run's draws and the caller's limit
+    assert bench.grad_ring(c1.psi, 1, 1, 50, 5, 8) == 8 and bench.grad_ring(c1.psi, 1, 1, 2, 1, 8) == 3
+    assert bench.buffers_that_fit(10 * GiB, c5.psi, 2) == 1                # never fewer than one
+    assert bench.buffers_that_fit(200 * GiB, c4.psi, 8) == 8
+    assert bench.fold_bytes([8]) == 20 and bench.fold_bytes([3, 3, 2]) == 10 + 14 + 12
