@@ -12,8 +12,10 @@ writes the other one (K = 1: 28 B per element in one launch; K > 1: the last
 micro-batch or fold also summed inside that pass, the sum never stored).  It
 needs 30 bytes of device memory per element instead of 16, so it is used
 where the second copy and the gradient buffers fit, and (K = 1) where the
-gradient is larger than the 256 MB Infinity Cache: a smaller one is still
-cached when the in-place form reads it again, which makes that form as fast.
+gradient is larger than the 256 MB Infinity Cache (a smaller one is still
+cached when the in-place form reads it again, which makes that form as fast)
+or where the whole state fits in that cache (the step is then launch-bound,
+and the double-buffered form is one launch instead of two).
 The in-place form (the check or the accumulation with its fused check, then
 the Adam pass that rewrites the one copy) is then timed after it on the copy
 that holds the state and reported as ``in_place_form``; --step-form in_place
@@ -109,10 +111,13 @@ def double_wanted(step_form: str, clip: float, K: int, n: int) -> bool:
     whole gradient's norm before the update); "double" asks for it; "auto" takes
     it with K > 1, and with K = 1 where the gradient is larger than the Infinity
     Cache (a smaller one is still cached when the in-place form's Adam pass reads
-    it again after the check, which makes that form as fast)."""
+    it again after the check, which makes that form as fast) or where the whole
+    state fits in it (the step is then launch-bound, and the double-buffered
+    form is one launch instead of two)."""
     if clip > 0:
         return False
-    return step_form == "double" or (step_form == "auto" and (K > 1 or 2 * n > INFINITY_CACHE_BYTES))
+    launch_bound = 16 * n <= INFINITY_CACHE_BYTES
+    return step_form == "double" or (step_form == "auto" and (K > 1 or 2 * n > INFINITY_CACHE_BYTES or launch_bound))
 
 
 def needs_running_sum(K: int, fold: int, double: bool) -> bool:
@@ -738,8 +743,9 @@ def main(argv=None):
                          "micro-batch or fold) fused into the Adam pass (ds_adam_step_double_buffered, "
                          "ds_accumulate_adam_double_buffered; no clipping); in_place: the check (or the "
                          "accumulation), then the in-place Adam pass; auto (default): double where it applies, "
-                         "(K = 1) the gradient is larger than the 256 MB Infinity Cache and the second copy fits, "
-                         "then the in-place form timed after it on the copy that holds the state")
+                         "the second copy fits and (K = 1) the gradient is larger than the 256 MB Infinity Cache "
+                         "or the whole state fits in it, then the in-place form timed after it on the copy that "
+                         "holds the state")
     ap.add_argument("--double-buffer", dest="step_form", action="store_const", const="double",
                     help="the same as --step-form double")
     ap.add_argument("--fold", type=int, default=1,
