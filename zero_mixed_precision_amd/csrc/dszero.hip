@@ -29,6 +29,13 @@
 //     buffer): one wave, one quad per lane (256 elements): 4-15 % faster than
 //     256 x 4 or 512 x 2 on 1.9e8- and 8.75e9-element ranges.  Their
 //     sum-of-squares forms take one 1024-element chunk per 256-lane block.
+//   * the double-buffered Adam pass: the Adam tile; each block takes one
+//     ticket (a 64-bit atomic add on one address, about 12 ns each,
+//     serialised), which the 2.1 million blocks of an 8.75e9-element
+//     partition hide under the stream but 64 x 1 blocks would not.
+//   * the last micro-batches folded into the double-buffered pass: one wave,
+//     one quad per lane, like the accumulation (64-512 lanes x 1-2 quads
+//     within 4 % at 4e9 elements); it takes no ticket.
 // The read-only overflow check uses 1024-lane blocks, one 16-byte vector per
 // lane, and ordinary (cache-allocating) loads on purpose: the fp16 gradient
 // it reads is read again by the Adam pass right after it, and a partition's
