@@ -209,6 +209,13 @@ def test_zero2_shard_of_7b_double_buffered(torch):
     assert sc.applied == 48 and sc.s.skipped == 2
 
 
+def test_zero2_shard_of_7b_bf16_double_buffered(torch):
+    """bf16 gradients and parameter copy (a static scale of 1) through the
+    double-buffered step at the shard's full size, with an injected infinity."""
+    sc = run_sampled(torch, "zero2_7b", double=True, bf16=True, extra_inject={11: 98_765_431})
+    assert sc.applied == 49 and sc.s.skipped == 1 and sc.scale == 1.0
+
+
 def test_zero1_shard_of_70b_double_buffered(torch):
     """The launch bench.py --double-buffer times: 8.75e9 elements in both copies
     (245 GB of state beside the 17.5 GB gradient), with an overflow injected in
