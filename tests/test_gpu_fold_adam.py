@@ -297,3 +297,48 @@ def test_shard_step_double_buffered_with_accumulation(torch, tmp_path):
         a = gu.host_f32(x) if x.dtype == torch.float32 else gu.host_u16(x)
         b = gu.host_f32(y) if y.dtype == torch.float32 else gu.host_u16(y)
         assert np.array_equal(_bits(a), _bits(b))
+
+
+def test_part_of_the_partition_double_buffered(torch):
+    """The entry points compose: with room for a second copy of only part A of
+    the partition, A takes the double-buffered pass (the K = 1 form of
+    ds_accumulate_adam_double_buffered: its one gradient is the sum), the rest B
+    is checked and updated in place, and one ds_update_loss_scale_double_buffered
+    ends the step, switching A's copies only if the whole step applied: 28 bytes
+    per element on A, 30 on B.  Against the oracle on the whole partition, with
+    overflows in A (step 2) and in B (step 4)."""
+    from zero_mixed_precision_amd import _lib
+    n, na = 50_003, 30_000
+    idx = np.arange(n)
+    master0 = synth.host_master32(synth.stream_key(1901, synth.ARR_MASTER), idx, MASTER_SIGMA)
+    o = oracle.State(master0.copy(), np.zeros(n, np.float32), np.zeros(n, np.float32), np.zeros(n, np.uint16),
+                     oracle.Scaler(2.0 ** 12, 1.0, 3, 1))
+    a = FoldDb(torch, master0[:na], init_scale=2.0 ** 12, window=3)
+    st = a.state
+    dev = "cuda:0"
+    bm, bmm, bv = gu.dev_f32(torch, master0[na:]), torch.zeros(n - na, device=dev), torch.zeros(n - na, device=dev)
+    bp = torch.zeros(n - na, dtype=torch.int16, device=dev)
+    for s in range(7):
+        g = synth.host_grad16(synth.stream_key(1902, synth.ARR_GRAD, s), idx, synth.GradSpec(1e-3, 2.0 ** 12))
+        if s == 2:
+            g[123] = 0x7C00
+        if s == 4:
+            g[na + 4567] = 0xFC00
+        gd = gu.dev_u16(torch, g)
+        ga, gb = gd[:na], gd[na:]
+        (ca, c0) = a.current()
+        _lib.ds_accumulate_adam_double_buffered(st, a.master, a.m, a.v, a.p16, _lib.DS_FP16, None, [ga], _lib.DS_FP16,
+                                                na, LR, None, BETA1, BETA2, EPS, 0.0, 1)
+        _lib.ds_check_overflow(st, gb, _lib.DS_FP16, n - na)
+        _lib.ds_adam_step(st, bm, bmm, bv, bp, _lib.DS_FP16, gb, _lib.DS_FP16, n - na, LR, BETA1, BETA2, EPS, 0.0,
+                          0.0, 1)
+        _lib.ds_update_loss_scale_double_buffered(st)
+        ov = oracle.step(o, g, **HP)
+        assert ov == (s in (2, 4))
+        gu.check_scaler(a.scaler(), o.scaler, ov, f"step {s}")
+        (cur, c1) = a.current()
+        assert c1 == (c0 if ov else 1 - c0)
+        whole = [np.concatenate([x, y]) for x, y in zip(cur, (gu.host_f32(bm), gu.host_f32(bmm), gu.host_f32(bv),
+                                                              gu.host_u16(bp)))]
+        for x, y in zip(whole, (o.master, o.m, o.v, o.p16)):
+            assert np.array_equal(_bits(x), _bits(y)), f"step {s}"
