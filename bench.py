@@ -410,7 +410,8 @@ def gpu_run(args):
         ip_bpe = 28 if K == 1 else 30
         in_place = {
             "step_form": ("check, then the in-place Adam pass" if K == 1 else
-                          "accumulation with the fused check, then the in-place Adam pass") + " (one copy of the state)",
+                          "accumulation with the fused check, then the in-place Adam pass")
+                         + " (one copy of the state)",
             "value": round(n * args.steps / ip_wall / 1e9, 3),
             "ms_per_step": round(ip_wall / args.steps * 1e3, 4),
             "kernel": "adam_kernel",

@@ -279,8 +279,9 @@ ds_status ds_adam_step_fused(ds_scaler* st, float* master, float* m, float* v, u
  * copy; each block's finding travels in its ticket (st->db_tickets), and the
  * last block to finish advances the scaler as ds_update_loss_scale does with
  * the OR of all findings and st->overflow and, if the step applied (no
- * overflow), makes the other copy current.  A skipped step leaves the current copy bit-identical
- * (only the other copy, which holds no state, is written) and t unchanged.
+ * overflow), makes the other copy current.  A skipped step leaves the current
+ * copy bit-identical (only the other copy, which holds no state, is written)
+ * and t unchanged.
  * The step moves 28 bytes per element with an fp16 gradient instead of the
  * 30 of ds_check_overflow + ds_adam_step_fused.  Call it once per step for the
  * whole partition, in place of ds_check_overflow and ds_adam_step_fused (a flag
