@@ -235,6 +235,14 @@ def test_ragged_layout_double_buffered(torch, fold):
     assert sc.applied == 27 and sc.scale == 2.0 ** 14
 
 
+def test_ragged_layout_bf16_double_buffered_fold_of_eight(torch):
+    """bf16 gradients and parameter copy (a static scale of 1) on the ragged
+    layout, all eight micro-batches summed inside the double-buffered Adam pass,
+    with the workload's injected infinities."""
+    sc = run_sampled(torch, "ragged", fold=8, double=True, bf16=True)
+    assert sc.applied == 27 and sc.scale == 1.0
+
+
 def test_ragged_layout_fused_scaler_update(torch):
     sc = run_sampled(torch, "ragged", fused=True)
     assert sc.applied == 27 and sc.scale == 2.0 ** 14
