@@ -273,20 +273,22 @@ def ds_adam_step_fused(st, master, m, v, p16, pdt, grad, dtype, n, lr, sched, be
         "ds_adam_step_fused")
 
 
+def _pair(arrs, nbytes, what):
+    """Host array of the two copies' device addresses (tensors are checked as by _p)."""
+    if len(arrs) != 2:
+        raise ValueError(f"{what}: expected two copies")
+    return (ctypes.c_void_p * 2)(*[_p(a, nbytes, f"{what}[{k}]") for k, a in enumerate(arrs)])
+
+
 def ds_adam_step_double_buffered(st, master2, m2, v2, p16_2, pdt, grad, dtype, n, lr, sched, beta1, beta2, eps,
                                  weight_decay, accum_steps, stream=None) -> None:
     """The check fused into the Adam pass over two copies of the state: master2, m2, v2, p16_2 are pairs
     (copy 0, copy 1) of tensors or device addresses; the copy holding the state is the state's ``current``."""
     n = int(n)
 
-    def pair(arrs, nbytes, what):
-        if len(arrs) != 2:
-            raise ValueError(f"{what}: expected two copies")
-        return (ctypes.c_void_p * 2)(*[_p(a, nbytes, f"{what}[{k}]") for k, a in enumerate(arrs)])
-
     sched_p = ctypes.byref(sched) if sched is not None else None
-    _ok(lib.ds_adam_step_double_buffered(_scaler(st), pair(master2, 4 * n, "master"), pair(m2, 4 * n, "m"),
-                                         pair(v2, 4 * n, "v"), pair(p16_2, 2 * n, "p16"), int(pdt),
+    _ok(lib.ds_adam_step_double_buffered(_scaler(st), _pair(master2, 4 * n, "master"), _pair(m2, 4 * n, "m"),
+                                         _pair(v2, 4 * n, "v"), _pair(p16_2, 2 * n, "p16"), int(pdt),
                                          _p(grad, _esize(dtype) * n, "gradient"), int(dtype), n, lr, sched_p,
                                          beta1, beta2, eps, weight_decay, int(accum_steps), _s(stream)),
         "ds_adam_step_double_buffered")
@@ -299,15 +301,10 @@ def ds_accumulate_adam_double_buffered(st, master2, m2, v2, p16_2, pdt, acc, gra
     of them).  End the step with ds_update_loss_scale_double_buffered."""
     n = int(n)
 
-    def pair(arrs, nbytes, what):
-        if len(arrs) != 2:
-            raise ValueError(f"{what}: expected two copies")
-        return (ctypes.c_void_p * 2)(*[_p(a, nbytes, f"{what}[{k}]") for k, a in enumerate(arrs)])
-
     ptrs = (ctypes.c_void_p * max(len(grads), 1))(*[_p(g, 2 * n, f"gradient {k}") for k, g in enumerate(grads)])
     sched_p = ctypes.byref(sched) if sched is not None else None
-    _ok(lib.ds_accumulate_adam_double_buffered(_scaler(st), pair(master2, 4 * n, "master"), pair(m2, 4 * n, "m"),
-                                               pair(v2, 4 * n, "v"), pair(p16_2, 2 * n, "p16"), int(pdt),
+    _ok(lib.ds_accumulate_adam_double_buffered(_scaler(st), _pair(master2, 4 * n, "master"), _pair(m2, 4 * n, "m"),
+                                               _pair(v2, 4 * n, "v"), _pair(p16_2, 2 * n, "p16"), int(pdt),
                                                _p(acc, 4 * n, "acc"), ptrs, len(grads), int(gdt), n, lr, sched_p,
                                                beta1, beta2, eps, weight_decay, int(accum_steps), _s(stream)),
         "ds_accumulate_adam_double_buffered")
