@@ -7,6 +7,7 @@
  * status strings.  Exit status 0 when every expectation holds; the
  * sanitizers abort on any memory or undefined-behaviour error.
  */
+#include <stddef.h>
 #include <stdint.h>
 #include <stdio.h>
 #include <stdlib.h>
@@ -15,6 +16,15 @@
 #include "dszero.h"
 
 static int failures = 0;
+
+/* the header's layout of the state, as the Python binding mirrors it */
+_Static_assert(sizeof(ds_scaler) == 128, "ds_scaler is 128 bytes");
+_Static_assert(offsetof(ds_scaler, overflow) == 28 && offsetof(ds_scaler, step) == 32, "ds_scaler layout");
+_Static_assert(offsetof(ds_scaler, last_overflow) == 60 && offsetof(ds_scaler, grad_sumsq) == 64, "ds_scaler layout");
+_Static_assert(offsetof(ds_scaler, blocks_done) == 80 && offsetof(ds_scaler, sumsq_blocks_done) == 84,
+               "ds_scaler layout");
+_Static_assert(offsetof(ds_scaler, current) == 88 && offsetof(ds_scaler, db_tickets) == 96,
+               "ds_scaler layout: the 64-bit ticket is 8-byte aligned");
 
 #define EXPECT(cond)                                                   \
     do {                                                               \

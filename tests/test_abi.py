@@ -68,6 +68,9 @@ def test_scaler_layout():
     offs = {n: getattr(_lib.DsScaler, n).offset for n, _ in _lib.DsScaler._fields_}
     assert offs["overflow"] == 28 and offs["step"] == 32 and offs["last_overflow"] == 60
     assert offs["grad_sumsq"] == 64 and offs["last_grad_sumsq"] == 72
+    # the tickets and the double-buffered step's copy index; the 64-bit ticket is 8-byte aligned for its atomic
+    assert offs["blocks_done"] == 80 and offs["sumsq_blocks_done"] == 84 and offs["current"] == 88
+    assert offs["db_tickets"] == 96 and offs["db_tickets"] % 8 == 0
 
 
 def test_status_strings():
