@@ -49,6 +49,9 @@ def run_sampled(torch, name, fused=False, bf16=False, fold=1, double=False, extr
     +inf gradients injected beside the workload's own."""
     from zero_mixed_precision_amd import _lib, FlatLayout
 
+    # the largest cases hold up to 285 GB: release what earlier tests left in torch's cache first
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
     w = WORKLOADS[name]
     n, K = w.psi, w.K
     # bf16 mode: bf16 gradients N(0, sigma) and bf16 parameter copy, no loss scaling (a static scale of 1)
